@@ -1,0 +1,160 @@
+"""Dense fp64 masked softmax attention, forward and backward.
+
+TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the benchmark's
+CPU-baseline leg, never by the product path.
+
+This is the plain definition the pages' methods reach exactly (up to rounding
+order): "a drop-in replacement for F.scaled_dot_product_attention ... where an
+(N, N) bool mask is given" (BinFlash, intro) and "matches the hand-written
+masked-softmax computation" (tensorplay omni_attention, intro). No tiles, no
+online softmax: per (batch, query head) the full score rows are formed, masked,
+normalised and applied.
+
+Conventions (readings where the pages are silent):
+
+* inputs are cast exactly to fp64 (bf16 and fp32 are exact in fp64);
+* GQA/MQA: query head hq reads key/value head hq // (Hq // Hkv), i.e. groups of
+  consecutive query heads share one KV head (opentau page: H % Hkv == 0);
+* a query with no allowed key gets output 0 and log-sum-exp -inf, and in the
+  backward contributes nothing (its dQ row is 0);
+* the log-sum-exp is natural-log of sum over allowed keys of exp(scale q.k),
+  layout (B, Hq, Sq) ("Outputs" section of omni_attention: log-sum-exp of the
+  attention weights);
+* masks are given as a bool array (Bm, Hm, Sq, Sk) with Bm in {1, B} and Hm in
+  {1, Hkv, Hq} (head index hq * Hm // Hq), or as a callable
+  ``allowed(b, hm, rows) -> (len(rows), Sk) bool`` for row-sampled checks at
+  sizes where the dense mask does not fit in memory.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(x):
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.float64)
+
+
+def _mask_rows(allowed, b, hm, rows, Sk):
+    if callable(allowed):
+        m = np.asarray(allowed(b, hm, rows), dtype=bool)
+    else:
+        a = np.asarray(allowed)
+        bb = b if a.shape[0] > 1 else 0
+        m = a[bb, hm][rows]
+    return np.broadcast_to(m, (len(rows), Sk))
+
+
+def _mask_heads(allowed, Hq):
+    if callable(allowed):
+        return getattr(allowed, "heads", Hq)
+    return np.asarray(allowed).shape[1]
+
+
+def attention_fwd(q, k, v, allowed, scale, rows=None, chunk=1024):
+    """Masked softmax attention. q (B, Sq, Hq, D); k, v (B, Sk, Hkv, D).
+
+    Returns (out (B, nrows, Hq, D) fp64, lse (B, Hq, nrows) fp64) for the query
+    rows ``rows`` (default: all).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    Hm = _mask_heads(allowed, Hq)
+    rows = np.arange(Sq) if rows is None else np.asarray(rows)
+    out = np.zeros((B, rows.size, Hq, D))
+    lse = np.full((B, Hq, rows.size), -np.inf)
+    for b in range(B):
+        for hq in range(Hq):
+            hk = hq // G
+            hm = hq * Hm // Hq
+            for c0 in range(0, rows.size, chunk):
+                rr = rows[c0:c0 + chunk]
+                s = scale * (q[b, rr, hq, :] @ k[b, :, hk, :].T)
+                a = _mask_rows(allowed, b, hm, rr, Sk)
+                has = a.any(axis=1)
+                sm = np.where(a, s, -np.inf)
+                m = np.where(has, sm.max(axis=1, initial=-np.inf), 0.0)
+                e = np.where(a, np.exp(sm - m[:, None]), 0.0)
+                l = e.sum(axis=1)
+                o = e @ v[b, :, hk, :]
+                safe_l = np.where(has, l, 1.0)
+                out[b, c0:c0 + rr.size, hq, :] = np.where(has[:, None], o / safe_l[:, None], 0.0)
+                lse[b, hq, c0:c0 + rr.size] = np.where(has, m + np.log(safe_l), -np.inf)
+    return out, lse
+
+
+def attention_bwd(q, k, v, dout, allowed, scale):
+    """Gradients of sum(out * dout) with respect to q, k, v (fp64, dense).
+
+    P_ij = exp(s_ij - LSE_i) on allowed entries, 0 elsewhere;
+    dV_j = sum_i P_ij dO_i;  dP_ij = dO_i . v_j;  Delta_i = sum_j P_ij dP_ij;
+    dS_ij = P_ij (dP_ij - Delta_i);  dQ_i = scale sum_j dS_ij k_j;
+    dK_j = scale sum_i dS_ij q_i; dK/dV sum over the query heads of a group.
+    The two-pass split (dK/dV over key blocks, dQ over query blocks) of the
+    BinFlash method is a schedule of these same sums.
+    Returns dq, dk, dv, out, lse, delta (delta (B, Hq, Sq)).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    Hm = _mask_heads(allowed, Hq)
+    out, lse = attention_fwd(q, k, v, allowed, scale)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    delta = np.zeros((B, Hq, Sq))
+    rows = np.arange(Sq)
+    for b in range(B):
+        for hq in range(Hq):
+            hk = hq // G
+            hm = hq * Hm // Hq
+            a = _mask_rows(allowed, b, hm, rows, Sk)
+            s = scale * (q[b, :, hq, :] @ k[b, :, hk, :].T)
+            L = lse[b, hq]
+            finite = np.isfinite(L)
+            P = np.where(a & finite[:, None], np.exp(s - np.where(finite, L, 0.0)[:, None]), 0.0)
+            dv[b, :, hk, :] += P.T @ do[b, :, hq, :]
+            dP = do[b, :, hq, :] @ v[b, :, hk, :].T
+            dl = (P * dP).sum(axis=1)
+            delta[b, hq] = dl
+            dS = P * (dP - dl[:, None])
+            dq[b, :, hq, :] = scale * (dS @ k[b, :, hk, :])
+            dk[b, :, hk, :] += scale * (dS.T @ q[b, :, hq, :])
+    return dq, dk, dv, out, lse, delta
+
+
+def varlen_attention_fwd(q, k, v, cu_q, cu_k, scale, causal, left, right, rows=None):
+    """Packed variable-length attention (tensorplay varlen "Packed layout").
+
+    q (Tq, Hq, D), k/v (Tk, Hkv, D); query row t of sequence s may see key u
+    iff u is in sequence s and the window predicate holds on local positions.
+    Returns out (n, Hq, D), lse (Hq, n) for the rows ``rows`` (default all).
+    """
+    cq = np.asarray(cu_q).astype(np.int64)
+    ck = np.asarray(cu_k).astype(np.int64)
+    Tk = int(ck[-1])
+    seq_of = np.searchsorted(cq, np.arange(int(cq[-1])), side="right") - 1
+    kidx = np.arange(Tk)
+
+    def allowed(b, hm, rr):
+        s = seq_of[rr]
+        i = rr - cq[s]
+        j = kidx[None, :] - ck[s][:, None]
+        in_seq = (j >= 0) & (j < (ck[s + 1] - ck[s])[:, None])
+        from .masks import window_allows
+        return in_seq & window_allows(i[:, None], j, causal, left, right)
+
+    allowed.heads = 1
+    out, lse = attention_fwd(_f64(q)[None], _f64(k)[None], _f64(v)[None], allowed, scale, rows=rows)
+    return out[0], lse[0]

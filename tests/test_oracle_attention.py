@@ -1,0 +1,185 @@
+"""Pins for the oracle's fp64 attention (CPU only).
+
+Library cross-checks use torch's CPU float64 scaled_dot_product_attention and
+autograd; the rest are closed forms, invariants and finite differences.
+"""
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import attention as A
+from oracle import masks as M
+import workloads as W
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _sdpa(q, k, v, mask, scale, gqa=False):
+    """torch CPU float64 SDPA in (B, H, S, D); q/k/v given as (B, S, H, D) numpy."""
+    t = [torch.from_numpy(np.ascontiguousarray(x.transpose(0, 2, 1, 3))) for x in (q, k, v)]
+    m = None if mask is None else torch.from_numpy(mask)
+    o = F.scaled_dot_product_attention(t[0], t[1], t[2], attn_mask=m, scale=scale, enable_gqa=gqa)
+    return o.numpy().transpose(0, 2, 1, 3)
+
+
+def test_all_true_equals_sdpa():
+    q, k, v = _rand((2, 37, 3, 16), 1), _rand((2, 53, 3, 16), 2), _rand((2, 53, 3, 16), 3)
+    allowed = np.ones((1, 1, 37, 53), bool)
+    out, lse = A.attention_fwd(q, k, v, allowed, 0.3)
+    np.testing.assert_allclose(out, _sdpa(q, k, v, None, 0.3), rtol=1e-12, atol=1e-12)
+    assert lse.shape == (2, 3, 37)
+
+
+def test_masked_equals_sdpa_with_bool_mask():
+    rng = np.random.default_rng(4)
+    q, k, v = _rand((2, 40, 4, 8), 5), _rand((2, 31, 4, 8), 6), _rand((2, 31, 4, 8), 7)
+    mask = rng.random((2, 4, 40, 31)) < 0.3
+    mask[..., 0] = True  # no empty rows (SDPA returns NaN for them)
+    out, _ = A.attention_fwd(q, k, v, mask, 0.25)
+    np.testing.assert_allclose(out, _sdpa(q, k, v, mask, 0.25), rtol=1e-12, atol=1e-12)
+
+
+def test_gqa_equals_sdpa_enable_gqa_and_repeat_interleave():
+    rng = np.random.default_rng(8)
+    q, k, v = _rand((1, 20, 6, 8), 9), _rand((1, 24, 2, 8), 10), _rand((1, 24, 2, 8), 11)
+    mask = rng.random((1, 1, 20, 24)) < 0.5
+    mask[..., 3] = True
+    out, lse = A.attention_fwd(q, k, v, mask, 0.5)
+    np.testing.assert_allclose(out, _sdpa(q, k, v, mask, 0.5, gqa=True), rtol=1e-12, atol=1e-12)
+    out2, lse2 = A.attention_fwd(q, np.repeat(k, 3, axis=2), np.repeat(v, 3, axis=2), mask, 0.5)
+    np.testing.assert_array_equal(out, out2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+def test_single_allowed_key_and_zero_query():
+    q, k, v = _rand((1, 6, 1, 4), 12), _rand((1, 9, 1, 4), 13), _rand((1, 9, 1, 4), 14)
+    mask = np.zeros((1, 1, 6, 9), bool)
+    for i in range(6):
+        mask[0, 0, i, (2 * i + 1) % 9] = True
+    out, lse = A.attention_fwd(q, k, v, mask, 0.7)
+    for i in range(6):
+        j = (2 * i + 1) % 9
+        np.testing.assert_array_equal(out[0, i, 0], v[0, j, 0])
+        assert lse[0, 0, i] == pytest.approx(0.7 * q[0, i, 0] @ k[0, j, 0], rel=1e-14)
+    q0 = np.zeros_like(q)
+    mask2 = np.random.default_rng(15).random((1, 1, 6, 9)) < 0.5
+    mask2[..., 0] = True
+    out, lse = A.attention_fwd(q0, k, v, mask2, 0.7)
+    for i in range(6):
+        sel = mask2[0, 0, i]
+        np.testing.assert_allclose(out[0, i, 0], v[0, sel, 0].mean(axis=0), rtol=1e-13, atol=1e-15)
+        assert lse[0, 0, i] == pytest.approx(np.log(sel.sum()), abs=1e-14)
+
+
+def test_two_keys_sigmoid_weights():
+    q, k, v = _rand((1, 1, 1, 5), 16), _rand((1, 2, 1, 5), 17), _rand((1, 2, 1, 5), 18)
+    s = 0.4 * (k[0, :, 0] @ q[0, 0, 0])
+    w0 = 1.0 / (1.0 + np.exp(s[1] - s[0]))
+    out, lse = A.attention_fwd(q, k, v, np.ones((1, 1, 1, 2), bool), 0.4)
+    np.testing.assert_allclose(out[0, 0, 0], w0 * v[0, 0, 0] + (1 - w0) * v[0, 1, 0], rtol=1e-13)
+    assert lse[0, 0, 0] == pytest.approx(s[0] + np.log1p(np.exp(s[1] - s[0])), rel=1e-13)
+
+
+def test_fully_masked_rows_convention():
+    q, k, v = _rand((1, 4, 2, 4), 19), _rand((1, 5, 2, 4), 20), _rand((1, 5, 2, 4), 21)
+    mask = np.ones((1, 1, 4, 5), bool)
+    mask[0, 0, 2] = False
+    out, lse = A.attention_fwd(q, k, v, mask, 1.0)
+    assert np.all(out[0, 2] == 0.0) and np.all(np.isneginf(lse[0, :, 2]))
+    assert np.all(np.isfinite(lse[0, :, [0, 1, 3]]))
+
+
+def test_lse_identity_and_masked_keys_do_not_matter():
+    q, k, v = _rand((1, 8, 1, 6), 22), _rand((1, 10, 1, 6), 23), _rand((1, 10, 1, 6), 24)
+    mask = np.random.default_rng(25).random((1, 1, 8, 10)) < 0.6
+    mask[..., 9] = True
+    out, lse = A.attention_fwd(q, k, v, mask, 0.5)
+    s = 0.5 * (q[0, :, 0] @ k[0, :, 0].T)
+    p = np.where(mask[0, 0], np.exp(s - lse[0, 0][:, None]), 0.0)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=1e-13)
+    np.testing.assert_allclose(p @ v[0, :, 0], out[0, :, 0], rtol=1e-12, atol=1e-14)
+    k2 = np.concatenate([k, 100 * _rand((1, 4, 1, 6), 26)], axis=1)
+    v2 = np.concatenate([v, _rand((1, 4, 1, 6), 27)], axis=1)
+    m2 = np.concatenate([mask, np.zeros((1, 1, 8, 4), bool)], axis=3)
+    out2, lse2 = A.attention_fwd(q, k2, v2, m2, 0.5)
+    np.testing.assert_array_equal(out, out2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+def test_row_sampling_matches_full():
+    q, k, v = _rand((2, 30, 2, 4), 28), _rand((2, 30, 2, 4), 29), _rand((2, 30, 2, 4), 30)
+    mask = np.random.default_rng(31).random((2, 2, 30, 30)) < 0.5
+    out, lse = A.attention_fwd(q, k, v, mask, 0.5)
+    rows = np.array([0, 7, 29])
+    o2, l2 = A.attention_fwd(q, k, v, mask, 0.5, rows=rows, chunk=2)
+    np.testing.assert_allclose(o2, out[:, rows], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(l2, lse[:, :, rows], rtol=1e-13)
+
+
+def test_varlen_equals_per_sequence():
+    lengths = [5, 17, 1, 9]
+    cu = M.cu_seqlens(lengths)
+    T = int(cu[-1])
+    q, k, v = _rand((T, 3, 4), 32), _rand((T, 3, 4), 33), _rand((T, 3, 4), 34)
+    out, lse = A.varlen_attention_fwd(q, k, v, cu, cu, 0.5, True, 3, 0)
+    for s, L in enumerate(lengths):
+        sl = slice(cu[s], cu[s + 1])
+        i, j = np.meshgrid(np.arange(L), np.arange(L), indexing="ij")
+        m = (j <= i) & (i - j < 4)
+        o_s, l_s = A.attention_fwd(q[None, sl], k[None, sl], v[None, sl], m[None, None], 0.5)
+        np.testing.assert_allclose(out[sl], o_s[0], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(lse[:, sl], l_s[0], rtol=1e-13)
+
+
+def test_varlen_with_workload_recipe_small():
+    w = W.varlen_window(nseq=3, lo=10, hi=40, H=2, D=8, window=8, seed=35, dtype=torch.float64)
+    cu = M.cu_seqlens(w["lengths"])
+    out, _ = A.varlen_attention_fwd(w["q"], w["k"], w["v"], cu, cu, w["scale"], True, 7, 0)
+    m = M.varlen_mask(cu, cu, True, 7, 0)
+    o2, _ = A.attention_fwd(w["q"][None], w["k"][None], w["v"][None], m[None, None], w["scale"])
+    np.testing.assert_allclose(out, o2[0], rtol=1e-13, atol=1e-15)
+
+
+# --- backward -----------------------------------------------------------------
+
+def _loss(q, k, v, do, mask, scale):
+    return float((A.attention_fwd(q, k, v, mask, scale)[0] * do).sum())
+
+
+def test_backward_finite_differences():
+    q, k, v = _rand((1, 5, 4, 3), 40), _rand((1, 6, 2, 3), 41), _rand((1, 6, 2, 3), 42)
+    do = _rand((1, 5, 4, 3), 43)
+    mask = np.random.default_rng(44).random((1, 2, 5, 6)) < 0.6
+    mask[0, 0, 1] = False  # an empty row in one head group
+    dq, dk, dv, out, lse, delta = A.attention_bwd(q, k, v, do, mask, 0.6)
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [xp if y is x else y for y in (q, k, v)]
+            args_m = [xm if y is x else y for y in (q, k, v)]
+            num[idx] = (_loss(*args_p, do, mask, 0.6) - _loss(*args_m, do, mask, 0.6)) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(delta, np.einsum("bshd,bshd->bhs", do, out), rtol=1e-12, atol=1e-14)
+    assert np.all(dq[0, 1, :2] == 0.0)  # heads 0, 1 share mask head 0, whose row 1 is empty
+
+
+def test_backward_equals_torch_autograd_sdpa():
+    rng = np.random.default_rng(45)
+    q, k, v = _rand((2, 24, 4, 8), 46), _rand((2, 30, 2, 8), 47), _rand((2, 30, 2, 8), 48)
+    do = _rand((2, 24, 4, 8), 49)
+    mask = rng.random((2, 1, 24, 30)) < 0.4
+    mask[..., 5] = True
+    dq, dk, dv, *_ = A.attention_bwd(q, k, v, do, mask, 0.35)
+    t = [torch.tensor(x.transpose(0, 2, 1, 3), requires_grad=True) for x in (q, k, v)]
+    o = F.scaled_dot_product_attention(*t, attn_mask=torch.from_numpy(mask), scale=0.35, enable_gqa=True)
+    o.backward(torch.from_numpy(do.transpose(0, 2, 1, 3).copy()))
+    for g, tt in zip((dq, dk, dv), t):
+        np.testing.assert_allclose(g, tt.grad.numpy().transpose(0, 2, 1, 3), rtol=1e-11, atol=1e-12)
