@@ -1,0 +1,357 @@
+"""masked_flash_attention_amd: masked flash attention on AMD MI355X (gfx950).
+
+A thin Python binding over libmfa's C ABI (include/mfa.h). torch supplies
+device memory and the current stream; every step of the computation runs in
+the library's HIP kernels. The library must be built first
+(``python -m masked_flash_attention_amd.build``); nothing here falls back to
+another implementation.
+
+Entry points mirror the C calls: ``make_block_ids``, ``blockid_tile_summary``,
+``compact_dense_mask``, ``bsr_validate``, ``bsr_prepare``, ``varlen_schedule``,
+``attn_fwd``, ``attn_bwd_preprocess``, ``attn_bwd_dkdv``, ``attn_bwd_dq``. Mask
+representations are passed to the attention calls as ``MaskRep`` objects.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass, field
+
+import torch
+
+from . import _ffi
+from ._ffi import MfaError
+
+__all__ = ["MfaError", "MaskRep", "is_available", "load_error", "make_block_ids", "blockid_tile_summary",
+           "compact_dense_mask", "bsr_validate", "bsr_prepare", "varlen_schedule", "attn_fwd",
+           "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd", "TILE_M", "TILE_N"]
+
+TILE_M, TILE_N = 128, 64  # query rows x key columns of one attention tile
+
+
+def _lib():
+    return _ffi.load()
+
+
+def is_available() -> bool:
+    """True if libmfa is built and a gfx950 device can run it."""
+    try:
+        return bool(_lib().mfa_is_available())
+    except ImportError:
+        return False
+
+
+def load_error():
+    """Why the library is unavailable (build/load error or device message), else None."""
+    try:
+        lib = _lib()
+    except ImportError as e:
+        return str(e)
+    if lib.mfa_is_available():
+        return None
+    return lib.mfa_last_error().decode()
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _u8(t):
+    return t if t.dtype == torch.uint8 else t.to(torch.uint8)
+
+
+def _i32(t):
+    return t if t.dtype == torch.int32 else t.to(torch.int32)
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+# ---------------------------------------------------------------------------
+# mask representations
+# ---------------------------------------------------------------------------
+
+def make_block_ids(pad_masks, att_masks, n_cross_att_tokens=None, cross_att_pad_masks=None):
+    """(q_blk, k_blk, q_valid, k_valid) from pad/att masks (mfa_make_block_ids).
+
+    q_blk int32 (B, N); k_blk int32 (B, Nc + N); q_valid / k_valid bool.
+    """
+    if (n_cross_att_tokens is None) != (cross_att_pad_masks is None):
+        raise ValueError("cross_att_pad_masks is required iff n_cross_att_tokens is set")
+    pad = _u8(pad_masks).contiguous()
+    att = _i32(att_masks).contiguous()
+    B, N = pad.shape
+    nc = int(n_cross_att_tokens or 0)
+    cross = None if cross_att_pad_masks is None else _u8(cross_att_pad_masks).contiguous()
+    dev = pad.device
+    q_blk = torch.empty(B, N, dtype=torch.int32, device=dev)
+    k_blk = torch.empty(B, nc + N, dtype=torch.int32, device=dev)
+    q_valid = torch.empty(B, N, dtype=torch.uint8, device=dev)
+    k_valid = torch.empty(B, nc + N, dtype=torch.uint8, device=dev)
+    _ffi.check(_lib().mfa_make_block_ids(_p(pad), _p(att), B, N, nc, _p(cross), _p(q_blk), _p(k_blk),
+                                         _p(q_valid), _p(k_valid), _stream()))
+    return q_blk, k_blk, q_valid.view(torch.bool), k_valid.view(torch.bool)
+
+
+def blockid_tile_summary(q_blk, k_blk, q_valid, k_valid, BM=TILE_M, BN=TILE_N):
+    """(qsum (B, nQt, 4), ksum (B, nKt, 4), kv_bits (B, ceil(Sk/32))) (mfa_blockid_tile_summary)."""
+    q_blk, k_blk = _i32(q_blk).contiguous(), _i32(k_blk).contiguous()
+    q_valid, k_valid = _u8(q_valid).contiguous(), _u8(k_valid).contiguous()
+    B, Sq = q_blk.shape
+    Sk = k_blk.shape[1]
+    dev = q_blk.device
+    qsum = torch.empty(B, _cdiv(Sq, BM), 4, dtype=torch.int32, device=dev)
+    ksum = torch.empty(B, _cdiv(Sk, BN), 4, dtype=torch.int32, device=dev)
+    kv_bits = torch.empty(B, _cdiv(Sk, 32), dtype=torch.int32, device=dev)
+    _ffi.check(_lib().mfa_blockid_tile_summary(_p(q_blk), _p(k_blk), _p(q_valid), _p(k_valid), B, Sq, Sk, BM, BN,
+                                               _p(qsum), _p(ksum), _p(kv_bits), _stream()))
+    return qsum, ksum, kv_bits
+
+
+def compact_dense_mask(mask, BM=TILE_M, BN=TILE_N):
+    """Tile map, packed fine bits and CSR of non-empty tiles (mfa_compact_dense_mask).
+
+    col_idx / col_kind are allocated at full capacity (nQt * nKt); the first
+    row_ptr[-1] entries are meaningful (reading that count would need a sync).
+    """
+    m = _u8(mask).contiguous()
+    Nq, Nk = m.shape
+    nQt, nKt = _cdiv(Nq, BM), _cdiv(Nk, BN)
+    dev = m.device
+    out = {
+        "tile_kind": torch.empty(nQt, nKt, dtype=torch.uint8, device=dev),
+        "fine_bits": torch.empty(Nq, _cdiv(Nk, 32), dtype=torch.int32, device=dev),
+        "row_ptr": torch.empty(nQt + 1, dtype=torch.int32, device=dev),
+        "col_idx": torch.empty(max(1, nQt * nKt), dtype=torch.int32, device=dev),
+        "col_kind": torch.empty(max(1, nQt * nKt), dtype=torch.uint8, device=dev),
+    }
+    _ffi.check(_lib().mfa_compact_dense_mask(_p(m), Nq, Nk, BM, BN, _p(out["tile_kind"]), _p(out["fine_bits"]),
+                                             _p(out["row_ptr"]), _p(out["col_idx"]), _p(out["col_kind"]),
+                                             _stream()))
+    return out
+
+
+def bsr_validate(block_indptr, block_indices, n_kv_blocks):
+    """Synchronously check canonical BSR rows; return the widest row (mfa_bsr_validate)."""
+    ip, ix = _i32(block_indptr).contiguous(), _i32(block_indices).contiguous()
+    B, H, R1 = ip.shape
+    w = C.c_int(0)
+    _ffi.check(_lib().mfa_bsr_validate(_p(ip), _p(ix), B, H, R1 - 1, n_kv_blocks, ix.numel(), C.byref(w), _stream()))
+    return w.value
+
+
+def bsr_prepare(block_indptr, block_indices, q_block, kv_block, Sq, Skv, causal):
+    """(col_kind (nnz,) u8, csc_ptr (B, H, nKb+1), csc_idx (nnz,)) (mfa_bsr_prepare)."""
+    ip, ix = _i32(block_indptr).contiguous(), _i32(block_indices).contiguous()
+    B, H, R1 = ip.shape
+    nKb = _cdiv(Skv, kv_block)
+    nnz = ix.numel()
+    dev = ip.device
+    col_kind = torch.empty(max(1, nnz), dtype=torch.uint8, device=dev)
+    csc_ptr = torch.empty(B, H, nKb + 1, dtype=torch.int32, device=dev)
+    csc_idx = torch.empty(max(1, nnz), dtype=torch.int32, device=dev)
+    _ffi.check(_lib().mfa_bsr_prepare(_p(ip), _p(ix), B, H, R1 - 1, nKb, nnz, q_block, kv_block, Sq, Skv,
+                                      int(bool(causal)), _p(col_kind), _p(csc_ptr), _p(csc_idx), _stream()))
+    return col_kind[:nnz], csc_ptr, csc_idx[:nnz]
+
+
+def varlen_schedule(len_q, len_k=None, causal=True, window=(-1, -1), BM=TILE_M, BN=TILE_N, work_cap=None):
+    """cu_seqlens, max lengths and the longest-first tile list (mfa_varlen_schedule).
+
+    ``work_cap`` defaults to an upper bound computed on the host from the
+    total length (sum ceil(L/BM) <= T/BM + nseq) so no sync is needed.
+    """
+    lq = _i32(len_q).contiguous()
+    lk = lq if len_k is None else _i32(len_k).contiguous()
+    nseq = lq.numel()
+    dev = lq.device
+    if work_cap is None:
+        raise ValueError("work_cap is required (e.g. total_q // BM + nseq)")
+    out = {
+        "cu_q": torch.empty(nseq + 1, dtype=torch.int32, device=dev),
+        "cu_k": torch.empty(nseq + 1, dtype=torch.int32, device=dev),
+        "max_len": torch.empty(2, dtype=torch.int32, device=dev),
+        "work": torch.empty(max(1, work_cap), 2, dtype=torch.int32, device=dev),
+        "n_work": torch.empty(1, dtype=torch.int32, device=dev),
+        "work_cap": work_cap,
+    }
+    left, right = window
+    _ffi.check(_lib().mfa_varlen_schedule(_p(lq), _p(lk), nseq, BM, BN, int(bool(causal)), left, right,
+                                          _p(out["cu_q"]), _p(out["cu_k"]), _p(out["max_len"]), _p(out["work"]),
+                                          work_cap, _p(out["n_work"]), _stream()))
+    return out
+
+
+@dataclass
+class MaskRep:
+    """A mask representation for ``attn_fwd`` (fields as in mfa_mask)."""
+    kind: int
+    tensors: dict = field(default_factory=dict)
+    ints: dict = field(default_factory=dict)
+
+    @staticmethod
+    def none():
+        return MaskRep(_ffi.MASK_NONE)
+
+    @staticmethod
+    def tiles(compacted):
+        return MaskRep(_ffi.MASK_TILES, {k: compacted[k] for k in
+                                         ("tile_kind", "fine_bits", "row_ptr", "col_idx", "col_kind")})
+
+    @staticmethod
+    def blockid(q_blk, k_blk, q_valid, k_valid, summary=None):
+        if summary is None:
+            summary = blockid_tile_summary(q_blk, k_blk, q_valid, k_valid)
+        qsum, ksum, kv_bits = summary
+        return MaskRep(_ffi.MASK_BLOCKID, {"q_blk": _i32(q_blk).contiguous(), "k_blk": _i32(k_blk).contiguous(),
+                                           "q_valid": _u8(q_valid).contiguous(),
+                                           "k_valid": _u8(k_valid).contiguous(),
+                                           "qsum": qsum, "ksum": ksum, "kv_bits": kv_bits})
+
+    @staticmethod
+    def bsr(block_indptr, block_indices, bsr_kind, q_block=64, kv_block=64, causal=True, csc_ptr=None,
+            csc_idx=None):
+        t = {"indptr": _i32(block_indptr).contiguous(), "indices": _i32(block_indices).contiguous(),
+             "bsr_kind": bsr_kind}
+        if csc_ptr is not None:
+            t["csc_ptr"], t["csc_idx"] = csc_ptr, csc_idx
+        return MaskRep(_ffi.MASK_BSR, t, {"q_block": q_block, "kv_block": kv_block, "causal": int(bool(causal))})
+
+    @staticmethod
+    def varlen(sched, max_q, max_k, causal=True, window=(-1, -1), err=None):
+        t = {"cu_q": sched["cu_q"], "cu_k": sched["cu_k"], "work": sched["work"]}
+        if err is not None:
+            t["err"] = err
+        return MaskRep(_ffi.MASK_VARLEN, t, {"work_cap": sched["work_cap"], "max_q": int(max_q),
+                                             "max_k": int(max_k), "causal": int(bool(causal)),
+                                             "win_left": int(window[0]), "win_right": int(window[1])})
+
+    def to_c(self):
+        m = _ffi.Mask()
+        m.kind = self.kind
+        for k, v in self.tensors.items():
+            setattr(m, k, v.data_ptr())
+        for k, v in self.ints.items():
+            setattr(m, k, v)
+        if self.kind != _ffi.MASK_VARLEN:
+            m.win_left = m.win_right = -1
+        return m
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def _bsh_strides(t, layout):
+    """(batch, seq, head) element strides of a 4-D tensor or a 3-D packed one."""
+    if t.stride(-1) != 1:
+        raise ValueError("the head-dim axis must be contiguous")
+    if layout == "bshd":
+        return (t.stride(0), t.stride(1), t.stride(2))
+    if layout == "bhsd":
+        return (t.stride(0), t.stride(2), t.stride(1))
+    if layout == "thd":
+        return (0, t.stride(0), t.stride(1))
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def _dims(q, k, layout):
+    if layout == "bshd":
+        B, Sq, Hq, D = q.shape
+        Sk, Hkv = k.shape[1], k.shape[2]
+    elif layout == "bhsd":
+        B, Hq, Sq, D = q.shape
+        Hkv, Sk = k.shape[1], k.shape[2]
+    else:
+        B = 1
+        Sq, Hq, D = q.shape
+        Sk, Hkv = k.shape[0], k.shape[1]
+    return B, Sq, Sk, Hq, Hkv, D
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return _ffi.MFA_BF16
+    if t.dtype == torch.float32:
+        return _ffi.MFA_F32
+    raise MfaError(3, f"dtype {t.dtype} not supported (bfloat16, or float32 test mode)")
+
+
+def attn_fwd(q, k, v, mask: MaskRep, scale=None, layout="bshd", out=None, return_lse=True, lse=None):
+    """Masked attention forward (mfa_attn_fwd). Returns (out, lse or None).
+
+    layout: "bshd" (B, S, H, D), "bhsd" (B, H, S, D) or "thd" (packed varlen).
+    lse is fp32 (B, Hq, Sq) ((Hq, T) for "thd").
+    """
+    B, Sq, Sk, Hq, Hkv, D = _dims(q, k, layout)
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, Sq) if layout == "thd" else (B, Hq, Sq), dtype=torch.float32, device=q.device)
+    a = _ffi.AttnArgs()
+    a.dtype = _dtype_code(q)
+    a.B, a.Sq, a.Sk, a.Hq, a.Hkv, a.D = B, Sq, Sk, Hq, Hkv, D
+    a.q, a.k, a.v, a.out = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
+    a.lse = lse.data_ptr() if (return_lse and lse is not None) else None
+    a.q_stride = _ffi.i64x3(*_bsh_strides(q, layout))
+    a.k_stride = _ffi.i64x3(*_bsh_strides(k, layout))
+    a.v_stride = _ffi.i64x3(*_bsh_strides(v, layout))
+    a.o_stride = _ffi.i64x3(*_bsh_strides(out, layout))
+    m = mask.to_c()
+    _ffi.check(_lib().mfa_attn_fwd(C.byref(a), C.byref(m), float(scale), _stream()))
+    return out, (lse if return_lse else None)
+
+
+def _bwd_args(q, k, v, out, lse, dout, dq, dk, dv, delta, layout):
+    B, Sq, Sk, Hq, Hkv, D = _dims(q, k, layout)
+    a = _ffi.BwdArgs()
+    f = a.fwd
+    f.dtype = _dtype_code(q)
+    f.B, f.Sq, f.Sk, f.Hq, f.Hkv, f.D = B, Sq, Sk, Hq, Hkv, D
+    f.q, f.k, f.v, f.out, f.lse = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr()
+    f.q_stride = _ffi.i64x3(*_bsh_strides(q, layout))
+    f.k_stride = _ffi.i64x3(*_bsh_strides(k, layout))
+    f.v_stride = _ffi.i64x3(*_bsh_strides(v, layout))
+    f.o_stride = _ffi.i64x3(*_bsh_strides(out, layout))
+    a.dout, a.dq, a.dk, a.dv, a.delta = dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), \
+        delta.data_ptr()
+    a.do_stride = _ffi.i64x3(*_bsh_strides(dout, layout))
+    a.dq_stride = _ffi.i64x3(*_bsh_strides(dq, layout))
+    a.dk_stride = _ffi.i64x3(*_bsh_strides(dk, layout))
+    a.dv_stride = _ffi.i64x3(*_bsh_strides(dv, layout))
+    return a
+
+
+def attn_bwd_preprocess(args):
+    _ffi.check(_lib().mfa_attn_bwd_preprocess(C.byref(args), _stream()))
+
+
+def attn_bwd_dkdv(args, mask: MaskRep, scale):
+    m = mask.to_c()
+    _ffi.check(_lib().mfa_attn_bwd_dkdv(C.byref(args), C.byref(m), float(scale), _stream()))
+
+
+def attn_bwd_dq(args, mask: MaskRep, scale):
+    m = mask.to_c()
+    _ffi.check(_lib().mfa_attn_bwd_dq(C.byref(args), C.byref(m), float(scale), _stream()))
+
+
+def attn_bwd(q, k, v, out, lse, dout, mask: MaskRep, scale=None, layout="bshd"):
+    """Two-pass backward: preprocess, dK/dV over key blocks, dQ over query blocks."""
+    B, Sq, Sk, Hq, Hkv, D = _dims(q, k, layout)
+    if scale is None:
+        scale = D ** -0.5
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(B, Hq, Sq, dtype=torch.float32, device=q.device)
+    a = _bwd_args(q, k, v, out, lse, dout, dq, dk, dv, delta, layout)
+    attn_bwd_preprocess(a)
+    attn_bwd_dkdv(a, mask, scale)
+    attn_bwd_dq(a, mask, scale)
+    return dq, dk, dv

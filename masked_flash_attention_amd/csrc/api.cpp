@@ -1,0 +1,425 @@
+// C ABI of libmfa: host-side validation, then kernel launches.
+// Every entry point validates its arguments before touching the device and
+// reports failures through a status code plus a thread-local message.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.hpp"
+
+namespace mfa {
+hipError_t launch_attn_fwd(int dtype, int D, int BM, const FwdDev& p, const MaskDev& m, hipStream_t s);
+hipError_t launch_block_ids(const uint8_t*, const int32_t*, int, int, int, const uint8_t*, int32_t*, int32_t*,
+                            uint8_t*, uint8_t*, hipStream_t);
+hipError_t launch_blockid_summary(const int32_t*, const int32_t*, const uint8_t*, const uint8_t*, int, int, int, int,
+                                  int, int32_t*, int32_t*, uint32_t*, hipStream_t);
+hipError_t launch_compact(const uint8_t*, int, int, uint8_t*, uint32_t*, int32_t*, int32_t*, uint8_t*, hipStream_t);
+hipError_t launch_bsr_prepare(const int32_t*, const int32_t*, int, int, int, int, int64_t, int, int, int, int, int,
+                              uint8_t*, int32_t*, int32_t*, hipStream_t);
+hipError_t launch_varlen_schedule(const int32_t*, const int32_t*, int, int, int, int, int, int, int32_t*, int32_t*,
+                                  int32_t*, int32_t*, int, int32_t*, hipStream_t);
+}  // namespace mfa
+
+using namespace mfa;
+
+namespace {
+
+thread_local std::string g_err;
+
+mfa_status fail(mfa_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+mfa_status ok() { return MFA_OK; }
+
+#define MFA_TRY(expr)                      \
+    do {                                   \
+        mfa_status _s = (expr);            \
+        if (_s != MFA_OK) return _s;       \
+    } while (0)
+
+mfa_status ensure_device() {
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess || n == 0) {
+        (void)hipGetLastError();
+        return fail(MFA_E_NO_DEVICE, "no HIP device available (%s)", hipGetErrorString(e));
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(MFA_E_NO_DEVICE, "hipGetDevice failed");
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(MFA_E_NO_DEVICE, "hipGetDeviceProperties failed");
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(MFA_E_NO_DEVICE, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
+    return ok();
+}
+
+mfa_status dev_ptr(const void* p, const char* name, bool nullable = false) {
+    if (!p) return nullable ? ok() : fail(MFA_E_ARG, "%s is NULL", name);
+    hipPointerAttribute_t a;
+    hipError_t e = hipPointerGetAttributes(&a, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MFA_E_NOT_DEVICE, "%s (%p) is not device memory", name, p);
+    }
+    if (a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeManaged)
+        return fail(MFA_E_NOT_DEVICE, "%s (%p) is host memory; device memory is required", name, p);
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (a.device != dev)
+        return fail(MFA_E_NOT_DEVICE, "%s lives on device %d but the current device is %d", name, a.device, dev);
+    return ok();
+}
+
+mfa_status hip_ok(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(MFA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mfa_last_error(void) { return g_err.c_str(); }
+
+const char* mfa_status_name(mfa_status s) {
+    switch (s) {
+        case MFA_OK: return "MFA_OK";
+        case MFA_E_ARG: return "MFA_E_ARG";
+        case MFA_E_SHAPE: return "MFA_E_SHAPE";
+        case MFA_E_DTYPE: return "MFA_E_DTYPE";
+        case MFA_E_UNSUPPORTED: return "MFA_E_UNSUPPORTED";
+        case MFA_E_NOT_DEVICE: return "MFA_E_NOT_DEVICE";
+        case MFA_E_NONCANONICAL: return "MFA_E_NONCANONICAL";
+        case MFA_E_HIP: return "MFA_E_HIP";
+        case MFA_E_NO_DEVICE: return "MFA_E_NO_DEVICE";
+    }
+    return "MFA_E_UNKNOWN";
+}
+
+int mfa_is_available(void) { return ensure_device() == MFA_OK ? 1 : 0; }
+
+mfa_status mfa_make_block_ids(const uint8_t* pad, const int32_t* att, int B, int N, int n_cross,
+                              const uint8_t* cross_pad, int32_t* q_blk, int32_t* k_blk, uint8_t* q_valid,
+                              uint8_t* k_valid, hipStream_t stream) {
+    if (B < 0 || N < 0 || n_cross < 0) return fail(MFA_E_SHAPE, "negative size (B=%d, N=%d, n_cross=%d)", B, N, n_cross);
+    if ((n_cross > 0) != (cross_pad != nullptr))
+        return fail(MFA_E_ARG, "cross_pad is required iff n_cross > 0 (n_cross=%d, cross_pad=%p)", n_cross, cross_pad);
+    if (B == 0 || (N == 0 && n_cross == 0)) return ok();
+    MFA_TRY(ensure_device());
+    if (N > 0) {
+        MFA_TRY(dev_ptr(pad, "pad"));
+        MFA_TRY(dev_ptr(att, "att"));
+        MFA_TRY(dev_ptr(q_blk, "q_blk"));
+        MFA_TRY(dev_ptr(q_valid, "q_valid"));
+    }
+    MFA_TRY(dev_ptr(k_blk, "k_blk"));
+    MFA_TRY(dev_ptr(k_valid, "k_valid"));
+    if (n_cross > 0) MFA_TRY(dev_ptr(cross_pad, "cross_pad"));
+    return hip_ok(launch_block_ids(pad, att, B, N, n_cross, cross_pad, q_blk, k_blk, q_valid, k_valid, stream),
+                  "block_ids launch");
+}
+
+mfa_status mfa_blockid_tile_summary(const int32_t* q_blk, const int32_t* k_blk, const uint8_t* q_valid,
+                                    const uint8_t* k_valid, int B, int Sq, int Sk, int BM, int BN, int32_t* qsum,
+                                    int32_t* ksum, uint32_t* kv_bits, hipStream_t stream) {
+    if (B < 0 || Sq < 0 || Sk < 0) return fail(MFA_E_SHAPE, "negative size");
+    if (!(BM == 64 || BM == 128) || BN != 64)
+        return fail(MFA_E_UNSUPPORTED, "summaries are built for BM in {64, 128} and BN = 64 (got %d, %d)", BM, BN);
+    if (B == 0 || (Sq == 0 && Sk == 0)) return ok();
+    MFA_TRY(ensure_device());
+    if (Sq > 0) {
+        MFA_TRY(dev_ptr(q_blk, "q_blk"));
+        MFA_TRY(dev_ptr(q_valid, "q_valid"));
+        MFA_TRY(dev_ptr(qsum, "qsum"));
+    }
+    if (Sk > 0) {
+        MFA_TRY(dev_ptr(k_blk, "k_blk"));
+        MFA_TRY(dev_ptr(k_valid, "k_valid"));
+        MFA_TRY(dev_ptr(ksum, "ksum"));
+        MFA_TRY(dev_ptr(kv_bits, "kv_bits"));
+    }
+    return hip_ok(launch_blockid_summary(q_blk, k_blk, q_valid, k_valid, B, Sq, Sk, BM, BN, qsum, ksum, kv_bits, stream),
+                  "tile summary launch");
+}
+
+mfa_status mfa_compact_dense_mask(const uint8_t* mask, int Nq, int Nk, int BM, int BN, uint8_t* tile_kind,
+                                  uint32_t* fine_bits, int32_t* row_ptr, int32_t* col_idx, uint8_t* col_kind,
+                                  hipStream_t stream) {
+    if (Nq < 0 || Nk < 0) return fail(MFA_E_SHAPE, "negative size (Nq=%d, Nk=%d)", Nq, Nk);
+    if (BM != 128 || BN != 64)
+        return fail(MFA_E_UNSUPPORTED, "dense-mask tiles are built for BM=128, BN=64 (got %d, %d)", BM, BN);
+    MFA_TRY(ensure_device());
+    MFA_TRY(dev_ptr(row_ptr, "row_ptr"));
+    if (Nq > 0 && Nk > 0) {
+        MFA_TRY(dev_ptr(mask, "mask"));
+        MFA_TRY(dev_ptr(tile_kind, "tile_kind"));
+        MFA_TRY(dev_ptr(fine_bits, "fine_bits"));
+        MFA_TRY(dev_ptr(col_idx, "col_idx"));
+        MFA_TRY(dev_ptr(col_kind, "col_kind"));
+    }
+    return hip_ok(launch_compact(mask, Nq, Nk, tile_kind, fine_bits, row_ptr, col_idx, col_kind, stream),
+                  "compaction launch");
+}
+
+mfa_status mfa_bsr_validate(const int32_t* indptr, const int32_t* indices, int B, int Hkv, int nQb, int nKb,
+                            int64_t nnz, int* max_row_width, hipStream_t stream) {
+    if (B < 0 || Hkv < 0 || nQb < 0 || nKb < 0 || nnz < 0) return fail(MFA_E_SHAPE, "negative size");
+    if (!max_row_width) return fail(MFA_E_ARG, "max_row_width is NULL");
+    *max_row_width = 0;
+    const size_t np = (size_t)B * Hkv * (nQb + 1);
+    if (np == 0) return ok();
+    MFA_TRY(ensure_device());
+    MFA_TRY(dev_ptr(indptr, "indptr"));
+    if (nnz > 0) MFA_TRY(dev_ptr(indices, "indices"));
+    std::vector<int32_t> ip(np), ix((size_t)nnz);
+    MFA_TRY(hip_ok(hipMemcpyAsync(ip.data(), indptr, np * 4, hipMemcpyDeviceToHost, stream), "copy indptr"));
+    if (nnz > 0)
+        MFA_TRY(hip_ok(hipMemcpyAsync(ix.data(), indices, (size_t)nnz * 4, hipMemcpyDeviceToHost, stream),
+                       "copy indices"));
+    MFA_TRY(hip_ok(hipStreamSynchronize(stream), "stream sync"));
+    int widest = 0;
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < Hkv; ++h) {
+            const int32_t* p = ip.data() + ((size_t)b * Hkv + h) * (nQb + 1);
+            if (p[0] < 0 || p[nQb] > nnz)
+                return fail(MFA_E_NONCANONICAL, "row offsets of (b=%d, h=%d) leave [0, %lld]", b, h, (long long)nnz);
+            for (int r = 0; r < nQb; ++r) {
+                if (p[r + 1] < p[r])
+                    return fail(MFA_E_NONCANONICAL, "row offsets of (b=%d, h=%d) decrease at row %d", b, h, r);
+                for (int e = p[r]; e < p[r + 1]; ++e) {
+                    if (ix[e] < 0 || ix[e] >= nKb)
+                        return fail(MFA_E_NONCANONICAL, "block id %d out of [0, %d) in (b=%d, h=%d, r=%d)", ix[e], nKb,
+                                    b, h, r);
+                    if (e > p[r] && ix[e] <= ix[e - 1])
+                        return fail(MFA_E_NONCANONICAL, "block ids not strictly ascending in (b=%d, h=%d, r=%d)", b,
+                                    h, r);
+                }
+                widest = std::max(widest, p[r + 1] - p[r]);
+            }
+        }
+    *max_row_width = widest;
+    return ok();
+}
+
+mfa_status mfa_bsr_prepare(const int32_t* indptr, const int32_t* indices, int B, int Hkv, int nQb, int nKb,
+                           int64_t nnz, int q_block, int kv_block, int Sq, int Skv, int causal, uint8_t* col_kind,
+                           int32_t* csc_ptr, int32_t* csc_idx, hipStream_t stream) {
+    if (B < 0 || Hkv < 0 || nQb < 0 || nKb < 0 || nnz < 0 || Sq < 0 || Skv < 0)
+        return fail(MFA_E_SHAPE, "negative size");
+    if (q_block <= 0 || kv_block <= 0) return fail(MFA_E_ARG, "block sizes must be positive");
+    if (nQb != cdiv(Sq, q_block) || nKb != cdiv(Skv, kv_block))
+        return fail(MFA_E_SHAPE, "nQb=%d / nKb=%d do not match ceil(Sq/q_block)=%d / ceil(Skv/kv_block)=%d", nQb, nKb,
+                    cdiv(Sq, q_block), cdiv(Skv, kv_block));
+    if (nKb > 16384) return fail(MFA_E_UNSUPPORTED, "nKb=%d exceeds the 16384 KV blocks the CSC pass holds in LDS", nKb);
+    if ((size_t)B * Hkv == 0) return ok();
+    MFA_TRY(ensure_device());
+    MFA_TRY(dev_ptr(indptr, "indptr"));
+    MFA_TRY(dev_ptr(csc_ptr, "csc_ptr"));
+    if (nnz > 0) {
+        MFA_TRY(dev_ptr(indices, "indices"));
+        MFA_TRY(dev_ptr(col_kind, "col_kind"));
+        MFA_TRY(dev_ptr(csc_idx, "csc_idx"));
+    }
+    return hip_ok(launch_bsr_prepare(indptr, indices, B, Hkv, nQb, nKb, nnz, q_block, kv_block, Sq, Skv, causal ? 1 : 0,
+                                     col_kind, csc_ptr, csc_idx, stream),
+                  "bsr prepare launch");
+}
+
+mfa_status mfa_varlen_schedule(const int32_t* len_q, const int32_t* len_k, int nseq, int BM, int BN, int causal,
+                               int win_left, int win_right, int32_t* cu_q, int32_t* cu_k, int32_t* max_len,
+                               int32_t* work, int work_cap, int32_t* n_work, hipStream_t stream) {
+    if (nseq < 0 || work_cap < 0) return fail(MFA_E_SHAPE, "negative size");
+    if (BM != 128 || BN != 64) return fail(MFA_E_UNSUPPORTED, "varlen tiles are built for BM=128, BN=64");
+    if (win_left < -1 || win_right < -1) return fail(MFA_E_ARG, "window sides must be >= -1");
+    MFA_TRY(ensure_device());
+    MFA_TRY(dev_ptr(cu_q, "cu_q"));
+    MFA_TRY(dev_ptr(cu_k, "cu_k"));
+    MFA_TRY(dev_ptr(max_len, "max_len"));
+    MFA_TRY(dev_ptr(n_work, "n_work"));
+    if (nseq > 0) {
+        MFA_TRY(dev_ptr(len_q, "len_q"));
+        MFA_TRY(dev_ptr(len_k, "len_k"));
+    }
+    if (work_cap > 0) MFA_TRY(dev_ptr(work, "work"));
+    return hip_ok(launch_varlen_schedule(len_q, len_k, nseq, BM, BN, causal ? 1 : 0, win_left, win_right, cu_q, cu_k,
+                                         max_len, work, work_cap, n_work, stream),
+                  "varlen schedule launch");
+}
+
+static mfa_status check_attn_shapes(const mfa_attn_args* a) {
+    if (a->dtype != MFA_BF16 && a->dtype != MFA_F32) return fail(MFA_E_DTYPE, "unknown dtype code %d", a->dtype);
+    if (a->B < 0 || a->Sq < 0 || a->Sk < 0 || a->Hq < 1 || a->Hkv < 1)
+        return fail(MFA_E_SHAPE, "bad sizes B=%d Sq=%d Sk=%d Hq=%d Hkv=%d", a->B, a->Sq, a->Sk, a->Hq, a->Hkv);
+    if (a->Hq % a->Hkv != 0) return fail(MFA_E_SHAPE, "Hq=%d is not a multiple of Hkv=%d", a->Hq, a->Hkv);
+    if (a->D != 64 && a->D != 128) return fail(MFA_E_UNSUPPORTED, "head dim %d not built (64, 128 are)", a->D);
+    return ok();
+}
+
+static mfa_status fill_mask(const mfa_attn_args* a, const mfa_mask* mk, MaskDev& m, int& BM) {
+    std::memset(&m, 0, sizeof(m));
+    m.kind = mk->kind;
+    m.fine_words = cdiv(a->Sk, 32);
+    m.kv_words = cdiv(a->Sk, 32);
+    BM = 128;
+    switch (mk->kind) {
+        case MFA_MASK_NONE: break;
+        case MFA_MASK_BLOCKID:
+            m.q_blk = mk->q_blk;
+            m.k_blk = mk->k_blk;
+            m.q_valid = mk->q_valid;
+            m.qsum = mk->qsum;
+            m.ksum = mk->ksum;
+            m.kv_bits = mk->kv_bits;
+            break;
+        case MFA_MASK_TILES:
+            m.fine_bits = mk->fine_bits;
+            m.row_ptr = mk->row_ptr;
+            m.col_idx = mk->col_idx;
+            m.col_kind = mk->col_kind;
+            break;
+        case MFA_MASK_BSR:
+            if (mk->q_block != 64 || mk->kv_block != 64)
+                return fail(MFA_E_UNSUPPORTED, "BSR block sizes %d x %d not built (64 x 64 is)", mk->q_block,
+                            mk->kv_block);
+            BM = 64;
+            m.indptr = mk->indptr;
+            m.indices = mk->indices;
+            m.bsr_kind = mk->bsr_kind;
+            m.csc_ptr = mk->csc_ptr;
+            m.csc_idx = mk->csc_idx;
+            m.causal = mk->causal ? 1 : 0;
+            m.nQb = cdiv(a->Sq, 64);
+            break;
+        case MFA_MASK_VARLEN:
+            if (a->B != 1) return fail(MFA_E_SHAPE, "varlen attention takes packed (T, H, D) tensors with B = 1");
+            if (mk->work_cap < 0 || mk->max_q < 0 || mk->max_k < 0)
+                return fail(MFA_E_ARG, "negative work_cap / max_q / max_k");
+            if (mk->win_left < -1 || mk->win_right < -1) return fail(MFA_E_ARG, "window sides must be >= -1");
+            m.cu_q = mk->cu_q;
+            m.cu_k = mk->cu_k;
+            m.work = mk->work;
+            m.work_cap = mk->work_cap;
+            m.max_q = mk->max_q;
+            m.max_k = mk->max_k;
+            m.err = mk->err;
+            m.causal = mk->causal ? 1 : 0;
+            m.win_left = mk->win_left;
+            m.win_right = mk->win_right;
+            break;
+        default: return fail(MFA_E_ARG, "unknown mask kind %d", mk->kind);
+    }
+    return ok();
+}
+
+static mfa_status check_mask_ptrs(const mfa_mask* mk) {
+    switch (mk->kind) {
+        case MFA_MASK_BLOCKID:
+            MFA_TRY(dev_ptr(mk->q_blk, "q_blk"));
+            MFA_TRY(dev_ptr(mk->k_blk, "k_blk"));
+            MFA_TRY(dev_ptr(mk->q_valid, "q_valid"));
+            MFA_TRY(dev_ptr(mk->qsum, "qsum"));
+            MFA_TRY(dev_ptr(mk->ksum, "ksum"));
+            MFA_TRY(dev_ptr(mk->kv_bits, "kv_bits"));
+            break;
+        case MFA_MASK_TILES:
+            MFA_TRY(dev_ptr(mk->row_ptr, "row_ptr"));
+            MFA_TRY(dev_ptr(mk->fine_bits, "fine_bits"));
+            MFA_TRY(dev_ptr(mk->col_idx, "col_idx"));
+            MFA_TRY(dev_ptr(mk->col_kind, "col_kind"));
+            break;
+        case MFA_MASK_BSR:
+            MFA_TRY(dev_ptr(mk->indptr, "indptr"));
+            MFA_TRY(dev_ptr(mk->indices, "indices"));
+            MFA_TRY(dev_ptr(mk->bsr_kind, "bsr_kind"));
+            break;
+        case MFA_MASK_VARLEN:
+            MFA_TRY(dev_ptr(mk->cu_q, "cu_q"));
+            MFA_TRY(dev_ptr(mk->cu_k, "cu_k"));
+            if (mk->work_cap > 0) MFA_TRY(dev_ptr(mk->work, "work"));
+            MFA_TRY(dev_ptr(mk->err, "err", true));
+            break;
+        default: break;
+    }
+    return ok();
+}
+
+static void fill_fwd(const mfa_attn_args* a, float scale, FwdDev& p) {
+    std::memset(&p, 0, sizeof(p));
+    p.q = a->q;
+    p.k = a->k;
+    p.v = a->v;
+    p.o = a->out;
+    p.lse = a->lse;
+    p.qs0 = a->q_stride[0]; p.qs1 = a->q_stride[1]; p.qs2 = a->q_stride[2];
+    p.ks0 = a->k_stride[0]; p.ks1 = a->k_stride[1]; p.ks2 = a->k_stride[2];
+    p.vs0 = a->v_stride[0]; p.vs1 = a->v_stride[1]; p.vs2 = a->v_stride[2];
+    p.os0 = a->o_stride[0]; p.os1 = a->o_stride[1]; p.os2 = a->o_stride[2];
+    p.B = a->B; p.Sq = a->Sq; p.Sk = a->Sk; p.Hq = a->Hq; p.Hkv = a->Hkv; p.G = a->Hq / a->Hkv;
+    p.scale = scale;
+    p.c2 = scale * kLog2e;
+}
+
+static mfa_status check_strides(const char* name, const void* ptr, const int64_t* st, int dtype) {
+    if (dtype == MFA_BF16) {
+        if (!aligned16(ptr)) return fail(MFA_E_ARG, "%s must be 16-byte aligned", name);
+        for (int i = 0; i < 3; ++i)
+            if (st[i] % 8 != 0) return fail(MFA_E_ARG, "%s strides must be multiples of 8 elements", name);
+    }
+    for (int i = 0; i < 3; ++i)
+        if (st[i] < 0) return fail(MFA_E_ARG, "%s strides must be non-negative", name);
+    return ok();
+}
+
+mfa_status mfa_attn_fwd(const mfa_attn_args* a, const mfa_mask* mk, float scale, hipStream_t stream) {
+    if (!a || !mk) return fail(MFA_E_ARG, "args or mask is NULL");
+    MFA_TRY(check_attn_shapes(a));
+    if (!(scale == scale) || scale == 0.f) return fail(MFA_E_ARG, "scale must be a nonzero number");
+    MaskDev m;
+    int BM = 128;
+    MFA_TRY(fill_mask(a, mk, m, BM));
+    if (a->B == 0 || a->Sq == 0) return ok();
+    MFA_TRY(ensure_device());
+    MFA_TRY(dev_ptr(a->q, "q"));
+    MFA_TRY(dev_ptr(a->out, "out"));
+    MFA_TRY(dev_ptr(a->lse, "lse", true));
+    if (a->Sk > 0) {
+        MFA_TRY(dev_ptr(a->k, "k"));
+        MFA_TRY(dev_ptr(a->v, "v"));
+    }
+    MFA_TRY(check_strides("q", a->q, a->q_stride, a->dtype));
+    MFA_TRY(check_strides("k", a->k, a->k_stride, a->dtype));
+    MFA_TRY(check_strides("v", a->v, a->v_stride, a->dtype));
+    MFA_TRY(check_strides("out", a->out, a->o_stride, a->dtype));
+    MFA_TRY(check_mask_ptrs(mk));
+    FwdDev p;
+    fill_fwd(a, scale, p);
+    p.nQt = cdiv(a->Sq, BM);
+    p.nKt = cdiv(a->Sk, 64);  // key-tile width of the forward kernels
+    if (mk->kind == MFA_MASK_VARLEN) {
+        p.total = mk->work_cap * a->Hq;
+        p.nQt = 0;
+    } else {
+        p.total = a->B * a->Hq * p.nQt;
+    }
+    if (p.total == 0) return ok();
+    p.xcd_remap = (a->dtype == MFA_BF16) && (p.total % 8 == 0) ? 1 : 0;
+    return hip_ok(launch_attn_fwd(a->dtype, a->D, BM, p, m, stream), "attention forward launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,400 @@
+// Fused masked attention forward for gfx950.
+//
+// out = softmax(scale * q k^T restricted to allowed keys) v, with the mask
+// applied per 64-key tile and never materialised as a dense score matrix
+// (the shared method of the opentau flash_attn_cuda, BinFlash, flashinfer
+// block_sparse_attention and tensorplay varlen pages). Empty tiles are never
+// visited, full tiles run with no mask work, partial tiles evaluate the
+// representation's predicate per element.
+//
+// bf16 kernel, one workgroup = NW waves = BM = 32*NW query rows of one
+// (batch, query head):
+//  * Each wave owns 32 queries. Scores are computed transposed,
+//    S^T (64 keys x 32 queries) = K Q^T, with v_mfma_f32_32x32x16_bf16: the
+//    accumulator then holds one query per lane (lane & 31) and 16 of its keys
+//    per 32-key block, so the row max needs one cross-half exchange
+//    (v_permlane32_swap) and the probabilities are already laid out as the
+//    B operand of O^T (D x 32 queries) += V^T P^T. Both contractions run over
+//    the same permutation of keys, which is free since keys are summed over.
+//  * K and V tiles (64 x D bf16) are double-buffered in LDS, XOR-swizzled so
+//    that the K operand reads (ds_read_b128) and the transposed V operand
+//    reads (ds_read_b64_tr_b16) are bank-conflict free.
+//  * Online softmax in fp32 with exp2: c = scale*log2(e) is applied to the
+//    fp32 scores after the matmul. The running max is only moved when the
+//    tile max exceeds it by more than kTau (log2 units), which bounds P by
+//    2^kTau and removes nearly all O rescales. The row sum adds the fp32 P
+//    (the bf16 rounding of a dominant P, up to 2^-8 relative, would otherwise
+//    show up in the log-sum-exp); P.V uses P rounded to bf16.
+//  * Epilogue: O / l rounded to bf16 (RNE), LSE = scale*m + ln l in fp32;
+//    rows with no allowed key write +0 and -inf.
+//  * Workgroup ids are remapped so that the query tiles of one (batch, head)
+//    run on one XCD (its L2 holds that head's K/V), heaviest tiles first.
+//
+// fp32 test-mode kernel: same schedule and predicates, one thread per query
+// row, fp32 arithmetic with libm exp/log, used to check the tiling and masking
+// logic at tight tolerance.
+
+#include "sched.hpp"
+
+namespace mfa {
+
+constexpr float kTau = 8.0f;
+
+template <int D>
+struct KV {
+    static constexpr int ROWB = D * 2;
+    static constexpr int CPR = D / 8;  // 16-byte chunks per row
+    static constexpr int TILEB = kBN * ROWB;
+    // Physical 16-byte chunk of logical chunk lc in row r.
+    __device__ static __forceinline__ int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+    __device__ static __forceinline__ int v_swz(int r) { return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
+};
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ bf16x4 ds_read_tr(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(__attribute__((address_space(3))) char*)(p));
+}
+
+template <int D, int NW, int KIND>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, MaskDev m) {
+    constexpr int BM = NW * 32;
+    constexpr int NT = NW * 64;
+    constexpr int ROWB = KV<D>::ROWB;
+    constexpr int CPR = KV<D>::CPR;
+    constexpr int TILEB = KV<D>::TILEB;
+    constexpr int NKC = D / 16;              // 16-wide d chunks of q.k
+    constexpr int NDB = D / 32;              // 32-wide d blocks of O^T
+    constexpr int LOADS = kBN * CPR / NT;    // 16-byte chunks per thread per tile
+    static_assert(LOADS * NT == kBN * CPR, "tile must split evenly over the workgroup");
+
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    char* sK = smem;
+    char* sV = smem + 2 * TILEB;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int hh = lane >> 5;
+    const int c = lane & 31;
+
+    const int logical = xcd_logical(blockIdx.x, p.total, p.xcd_remap);
+    const TileRange t = make_range<KIND, BM>(p, m, logical);
+    if (!t.active) return;
+
+    const int row = t.q_row0 + wave * 32 + c;
+    RowMask<KIND> rm;
+    rm.init(p, m, t, row);
+
+    const bf16* Q = (const bf16*)p.q;
+    const bf16* K = (const bf16*)p.k;
+    const bf16* V = (const bf16*)p.v;
+
+    bf16x8 qf[NKC];
+    {
+        const bf16* qp = Q + (int64_t)t.b * p.qs0 + (int64_t)row * p.qs1 + (int64_t)t.hq * p.qs2 + hh * 8;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+            if (rm.row_ok) qf[kc] = *(const bf16x8*)(qp + kc * 16);
+            else qf[kc] = bf16x8{};
+        }
+    }
+
+    f32x16 o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+    float m_used = -INFINITY;
+    float l_part = 0.f;
+
+    // ---- staging of K/V tiles: thread tid moves chunks id = i*NT + tid ----
+    const bf16* Kbh = K + (int64_t)t.b * p.ks0 + (int64_t)t.hk * p.ks2 + (int64_t)t.k_base * p.ks1;
+    const bf16* Vbh = V + (int64_t)t.b * p.vs0 + (int64_t)t.hk * p.vs2 + (int64_t)t.k_base * p.vs1;
+    u32x4 kr[LOADS], vr[LOADS];
+    auto load_tile = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int id = i * NT + tid;
+            const int r = id / CPR, lc = id % CPR;
+            const int key = kt * kBN + r;
+            if (key < t.k_len) {
+                kr[i] = *(const u32x4*)(Kbh + (int64_t)key * p.ks1 + lc * 8);
+                vr[i] = *(const u32x4*)(Vbh + (int64_t)key * p.vs1 + lc * 8);
+            } else {
+                kr[i] = u32x4{0, 0, 0, 0};
+                vr[i] = u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int id = i * NT + tid;
+            const int r = id / CPR, lc = id % CPR;
+            *(u32x4*)(sK + buf * TILEB + r * ROWB + ((lc ^ KV<D>::k_swz(r)) << 4)) = kr[i];
+            *(u32x4*)(sV + buf * TILEB + r * ROWB + ((lc ^ KV<D>::v_swz(r)) << 4)) = vr[i];
+        }
+    };
+
+    // Per-lane LDS offsets of the operand reads.
+    // K operand: row kb*32 + c, logical chunk kc*2 + hh.
+    int koff[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) koff[kc] = c * ROWB + (((kc * 2 + hh) ^ KV<D>::k_swz(c)) << 4);
+    // V operand (transposed read): row kc2*16 + 8j + 4hh + rq, column
+    // db*32 + 16*((lane>>4)&1) + 4*(lane&3).
+    const int rq = (lane & 15) >> 2;
+    int voff[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const int col = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const int vr0 = 4 * hh + rq;
+        voff[db] = vr0 * ROWB + (((col >> 3) ^ KV<D>::v_swz(vr0)) << 4) + ((col >> 2) & 1) * 8;
+    }
+
+    auto advance = [&](int& it, int& kt, int& kind) {
+        while (it < t.end) {
+            tile_at<KIND, BM>(p, m, t, it, kt, kind);
+            if (kind != kTileEmpty) return;
+            ++it;
+        }
+    };
+
+    int it = t.begin, kt = 0, kind = 0;
+    advance(it, kt, kind);
+    if (it < t.end) {
+        load_tile(kt);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    const float c2 = p.c2;
+    int buf = 0;
+    while (it < t.end) {
+        int it_n = it + 1, kt_n = 0, kind_n = 0;
+        advance(it_n, kt_n, kind_n);
+        const bool has_next = it_n < t.end;
+        if (has_next) load_tile(kt_n);
+
+        // ---- S^T = K Q^T ----
+        f32x16 s[2];
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+        const char* kb_ = sK + buf * TILEB;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 a = *(const bf16x8*)(kb_ + kb * 32 * ROWB + koff[kc]);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[kb], 0, 0, 0);
+            }
+        }
+
+        // ---- mask on partial or ragged tiles ----
+        const bool ragged = (kt + 1) * kBN > t.k_len;
+        if (kind == kTilePartial || ragged) {
+            uint32_t w0 = 0, w1 = 0;
+            if constexpr (KIND == MFA_MASK_TILES) {
+                if (rm.row_ok) {
+                    const uint32_t* fb = m.fine_bits + (int64_t)row * m.fine_words + 2 * kt;
+                    w0 = fb[0];
+                    if (2 * kt + 1 < m.fine_words) w1 = fb[1];
+                }
+            } else if constexpr (KIND == MFA_MASK_BLOCKID) {
+                const uint32_t* kw = m.kv_bits + (int64_t)t.b * m.kv_words + 2 * kt;
+                w0 = kw[0];
+                if (2 * kt + 1 < m.kv_words) w1 = kw[1];
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int off = kb * 32 + (r >> 2) * 8 + 4 * hh + (r & 3);
+                    const int key = kt * kBN + off;
+                    bool ok = rm.row_ok && key < t.k_len;
+                    if constexpr (KIND == MFA_MASK_TILES) {
+                        ok = ok && (((kb ? w1 : w0) >> (off & 31)) & 1u);
+                    } else if constexpr (KIND == MFA_MASK_BLOCKID) {
+                        if (ok) {
+                            const int kbk = m.k_blk[(int64_t)t.b * p.Sk + key];
+                            ok = rm.qvalid && (((kb ? w1 : w0) >> (off & 31)) & 1u) && kbk <= rm.qblk;
+                        }
+                    } else if constexpr (KIND == MFA_MASK_BSR) {
+                        ok = ok && (!m.causal || key <= row);
+                    } else if constexpr (KIND == MFA_MASK_VARLEN) {
+                        const int i = rm.qi_local;
+                        if (m.causal) ok = ok && key <= i;
+                        if (m.win_left >= 0) ok = ok && (i - key) <= m.win_left;
+                        if (m.win_right >= 0) ok = ok && (key - i) <= m.win_right;
+                    }
+                    if (!ok) s[kb][r] = -INFINITY;
+                }
+            }
+        }
+
+        // ---- online softmax ----
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = max_both_halves(mx);
+        const float m_new = fmaxf(m_used, mx);
+        const bool need = (m_new - m_used) * c2 > kTau;  // false when both are -inf
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            const float alpha = need ? fast_exp2((m_used - m_new) * c2) : 1.f;
+            m_used = need ? m_new : m_used;
+            l_part *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        }
+        const float mb = (m_used == -INFINITY) ? 0.f : m_used * c2;
+        bf16x8 pb[4];
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int gp = 0; gp < 2; ++gp)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float pv = fast_exp2(fmaf(s[kb][gp * 8 + e], c2, -mb));
+                    rs += pv;
+                    pb[kb * 2 + gp][e] = (bf16)pv;
+                }
+        l_part += rs;
+
+        // ---- O^T += V^T P^T ----
+        const char* vb_ = sV + buf * TILEB;
+#pragma unroll
+        for (int kc2 = 0; kc2 < 4; ++kc2) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const bf16x4 lo = ds_read_tr(vb_ + kc2 * 16 * ROWB + voff[db]);
+                const bf16x4 hi = ds_read_tr(vb_ + (kc2 * 16 + 8) * ROWB + voff[db]);
+                const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc2], o[db], 0, 0, 0);
+            }
+        }
+
+        if (has_next) store_tile(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+        it = it_n;
+        kt = kt_n;
+        kind = kind_n;
+    }
+
+    // ---- epilogue ----
+    const float l_tot = sum_both_halves(l_part);
+    if (!rm.row_ok) return;
+    const bool empty = !(l_tot > 0.f);
+    float inv = empty ? 0.f : 1.f / l_tot;
+    if (t.len_error) inv = __builtin_nanf("");
+    bf16* op = (bf16*)p.o + (int64_t)t.b * p.os0 + (int64_t)row * p.os1 + (int64_t)t.hq * p.os2;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            bf16x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = empty && !t.len_error ? (bf16)0.f : (bf16)(o[db][g * 4 + e] * inv);
+            *(bf16x4*)(op + db * 32 + g * 8 + 4 * hh) = w;
+        }
+    }
+    if (p.lse && hh == 0) {
+        float L = empty ? -INFINITY : (m_used * c2 + fast_log2(l_tot)) * kLn2;
+        if (t.len_error) L = __builtin_nanf("");
+        p.lse[((int64_t)t.b * p.Hq + t.hq) * p.Sq + row] = L;
+    }
+}
+
+// fp32 test mode: one thread per query row, scalar fp32 arithmetic.
+template <int D, int BM, int KIND>
+__global__ __launch_bounds__(BM) void attn_fwd_f32_kernel(FwdDev p, MaskDev m) {
+    const TileRange t = make_range<KIND, BM>(p, m, blockIdx.x);
+    if (!t.active) return;
+    const int row = t.q_row0 + threadIdx.x;
+    RowMask<KIND> rm;
+    rm.init(p, m, t, row);
+    const float* Q = (const float*)p.q;
+    const float* K = (const float*)p.k + (int64_t)t.b * p.ks0 + (int64_t)t.hk * p.ks2 + (int64_t)t.k_base * p.ks1;
+    const float* V = (const float*)p.v + (int64_t)t.b * p.vs0 + (int64_t)t.hk * p.vs2 + (int64_t)t.k_base * p.vs1;
+    float q[D], o[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        q[d] = rm.row_ok ? Q[(int64_t)t.b * p.qs0 + (int64_t)row * p.qs1 + (int64_t)t.hq * p.qs2 + d] : 0.f;
+        o[d] = 0.f;
+    }
+    float mrun = -INFINITY, l = 0.f;
+    for (int it = t.begin; it < t.end; ++it) {
+        int kt, kind;
+        tile_at<KIND, BM>(p, m, t, it, kt, kind);
+        if (kind == kTileEmpty || !rm.row_ok) continue;
+        for (int j = 0; j < kBN; ++j) {
+            const int key = kt * kBN + j;
+            if (key >= t.k_len) break;
+            if (kind == kTilePartial && !allowed<KIND>(p, m, t, rm, key)) continue;
+            const float* kp = K + (int64_t)key * p.ks1;
+            float s = 0.f;
+#pragma unroll
+            for (int d = 0; d < D; ++d) s = fmaf(q[d], kp[d], s);
+            s *= p.scale;
+            const float mn = fmaxf(mrun, s);
+            const float corr = expf(mrun - mn);
+            const float pe = expf(s - mn);
+            l = l * corr + pe;
+            const float* vp = V + (int64_t)key * p.vs1;
+#pragma unroll
+            for (int d = 0; d < D; ++d) o[d] = fmaf(pe, vp[d], o[d] * corr);
+            mrun = mn;
+        }
+    }
+    if (!rm.row_ok) return;
+    const bool empty = !(l > 0.f);
+    float* op = (float*)p.o + (int64_t)t.b * p.os0 + (int64_t)row * p.os1 + (int64_t)t.hq * p.os2;
+#pragma unroll
+    for (int d = 0; d < D; ++d) op[d] = t.len_error ? __builtin_nanf("") : (empty ? 0.f : o[d] / l);
+    if (p.lse) p.lse[((int64_t)t.b * p.Hq + t.hq) * p.Sq + row] =
+        t.len_error ? __builtin_nanf("") : (empty ? -INFINITY : mrun + logf(l));
+}
+
+// ---------------------------------------------------------------------------
+// Host launch
+// ---------------------------------------------------------------------------
+
+template <int D, int NW, int KIND>
+static hipError_t launch_bf16(const FwdDev& p, const MaskDev& m, hipStream_t s) {
+    const size_t lds = 4 * KV<D>::TILEB;
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, KIND>), dim3(p.total), dim3(NW * 64), lds, s, p, m);
+    return hipGetLastError();
+}
+
+template <int D, int BM, int KIND>
+static hipError_t launch_f32(const FwdDev& p, const MaskDev& m, hipStream_t s) {
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<D, BM, KIND>), dim3(p.total), dim3(BM), 0, s, p, m);
+    return hipGetLastError();
+}
+
+template <int KIND>
+static hipError_t dispatch_kind(int dtype, int D, int BM, const FwdDev& p, const MaskDev& m, hipStream_t s) {
+    if (dtype == MFA_BF16) {
+        if (BM == 128) return D == 128 ? launch_bf16<128, 4, KIND>(p, m, s) : launch_bf16<64, 4, KIND>(p, m, s);
+        return D == 128 ? launch_bf16<128, 2, KIND>(p, m, s) : launch_bf16<64, 2, KIND>(p, m, s);
+    }
+    if (BM == 128) return D == 128 ? launch_f32<128, 128, KIND>(p, m, s) : launch_f32<64, 128, KIND>(p, m, s);
+    return D == 128 ? launch_f32<128, 64, KIND>(p, m, s) : launch_f32<64, 64, KIND>(p, m, s);
+}
+
+hipError_t launch_attn_fwd(int dtype, int D, int BM, const FwdDev& p, const MaskDev& m, hipStream_t s) {
+    switch (m.kind) {
+        case MFA_MASK_NONE: return dispatch_kind<MFA_MASK_NONE>(dtype, D, BM, p, m, s);
+        case MFA_MASK_BLOCKID: return dispatch_kind<MFA_MASK_BLOCKID>(dtype, D, BM, p, m, s);
+        case MFA_MASK_TILES: return dispatch_kind<MFA_MASK_TILES>(dtype, D, BM, p, m, s);
+        case MFA_MASK_BSR: return dispatch_kind<MFA_MASK_BSR>(dtype, D, BM, p, m, s);
+        case MFA_MASK_VARLEN: return dispatch_kind<MFA_MASK_VARLEN>(dtype, D, BM, p, m, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mfa

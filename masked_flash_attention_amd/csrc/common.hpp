@@ -1,0 +1,99 @@
+// Shared device/host helpers for libmfa (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mfa.h"
+
+namespace mfa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kTileEmpty = MFA_TILE_EMPTY;
+constexpr int kTilePartial = MFA_TILE_PARTIAL;
+constexpr int kTileFull = MFA_TILE_FULL;
+
+// Device copy of mfa_mask plus derived sizes. Passed by value to kernels.
+struct MaskDev {
+    int kind;
+    const int32_t* q_blk;
+    const int32_t* k_blk;
+    const uint8_t* q_valid;
+    const int32_t* qsum;
+    const int32_t* ksum;
+    const uint32_t* kv_bits;
+    const uint32_t* fine_bits;
+    const int32_t* row_ptr;
+    const int32_t* col_idx;
+    const uint8_t* col_kind;
+    const int32_t* indptr;
+    const int32_t* indices;
+    const uint8_t* bsr_kind;
+    const int32_t* csc_ptr;
+    const int32_t* csc_idx;
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    const int32_t* work;
+    int32_t* err;
+    int work_cap;
+    int max_q, max_k;
+    int causal, win_left, win_right;
+    int fine_words;   // ceil(Sk / 32)
+    int kv_words;     // ceil(Sk / 32)
+    int nQb;          // BSR query-block rows per (b, h)
+};
+
+// Problem description shared by the forward kernels.
+struct FwdDev {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int64_t qs0, qs1, qs2;
+    int64_t ks0, ks1, ks2;
+    int64_t vs0, vs1, vs2;
+    int64_t os0, os1, os2;
+    int B, Sq, Sk, Hq, Hkv, G;
+    int nQt, nKt;
+    float scale, c2;  // c2 = scale * log2(e)
+    int total;        // workgroups launched
+    int xcd_remap;    // 1: logical id = (w % 8) * (total / 8) + w / 8
+};
+
+__device__ __forceinline__ int xcd_logical(int w, int total, int remap) {
+    if (!remap) return w;
+    return (w & 7) * (total >> 3) + (w >> 3);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value of `x` held by lane (lane ^ 32), via the gfx950 cross-half swap.
+__device__ __forceinline__ float other_half(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    // lanes 0..31: r[1] holds lane+32's value; lanes 32..63: r[0] holds lane-32's value
+    return __int_as_float((__lane_id() < 32) ? r[1] : r[0]);
+}
+
+__device__ __forceinline__ float max_both_halves(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_both_halves(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
+}  // namespace mfa

@@ -1,0 +1,504 @@
+// Mask-representation kernels for gfx950: block ids, block-id tile
+// summaries, dense-mask compaction, BSR kinds and CSC, varlen schedule.
+// All outputs are deterministic (no order-dependent atomics): prefix counts
+// come from wave ballots (v_mbcnt) and LDS block scans.
+
+#include "common.hpp"
+
+namespace mfa {
+
+// ---------------------------------------------------------------------------
+// Block-wide helpers (blockDim.x multiple of 64, <= 1024)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int lane_prefix(uint64_t ballot) {
+    // number of set bits in lanes below this one
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(ballot >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ballot, 0));
+}
+
+// Exclusive prefix count of `flag` over the block; returns the block total in *total.
+__device__ __forceinline__ int block_exclusive_count(bool flag, int* total, int* lds16) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const uint64_t b = __builtin_amdgcn_ballot_w64(flag);
+    const int in_wave = lane_prefix(b);
+    if (lane == 0) lds16[wave] = __builtin_popcountll(b);
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int w = 0; w < nw; ++w) {
+        const int cnt = lds16[w];
+        before += (w < wave) ? cnt : 0;
+        tot += cnt;
+    }
+    __syncthreads();
+    *total = tot;
+    return before + in_wave;
+}
+
+// Exclusive prefix sum of small non-negative ints over the block.
+__device__ __forceinline__ int block_exclusive_sum(int v, int* total, int* lds1024) {
+    const int t = threadIdx.x, n = blockDim.x;
+    lds1024[t] = v;
+    __syncthreads();
+    // Hillis-Steele inclusive scan in LDS
+    for (int off = 1; off < n; off <<= 1) {
+        const int x = (t >= off) ? lds1024[t - off] : 0;
+        __syncthreads();
+        lds1024[t] += x;
+        __syncthreads();
+    }
+    const int incl = lds1024[t];
+    *total = lds1024[n - 1];
+    __syncthreads();
+    return incl - v;
+}
+
+// ---------------------------------------------------------------------------
+// Block ids ("opentau.policies.flash_attn_cuda", make_att_block_ids)
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void block_ids_kernel(const uint8_t* pad, const int32_t* att, int N, int nc,
+                                                        const uint8_t* cross_pad, int32_t* q_blk, int32_t* k_blk,
+                                                        uint8_t* q_valid, uint8_t* k_valid) {
+    __shared__ int lds[16];
+    const int b = blockIdx.x;
+    const int Sk = nc + N;
+    for (int c = threadIdx.x; c < nc; c += blockDim.x) {
+        k_blk[(int64_t)b * Sk + c] = MFA_BLK_CROSS;
+        k_valid[(int64_t)b * Sk + c] = cross_pad[(int64_t)b * nc + c] != 0;
+    }
+    int carry = 0;
+    for (int base = 0; base < N; base += blockDim.x) {
+        const int i = base + threadIdx.x;
+        const bool in = i < N;
+        const bool open = in && att[(int64_t)b * N + i] != 0;
+        int total;
+        const int before = block_exclusive_count(open, &total, lds);
+        if (in) {
+            const int id = carry + before + (open ? 1 : 0);  // inclusive running count
+            const uint8_t v = pad[(int64_t)b * N + i] != 0;
+            q_blk[(int64_t)b * N + i] = id;
+            q_valid[(int64_t)b * N + i] = v;
+            k_blk[(int64_t)b * Sk + nc + i] = id;
+            k_valid[(int64_t)b * Sk + nc + i] = v;
+        }
+        carry += total;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Block-id tile summaries: one wave per tile
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(64) void blockid_summary_kernel(const int32_t* q_blk, const int32_t* k_blk,
+                                                             const uint8_t* q_valid, const uint8_t* k_valid,
+                                                             int Sq, int Sk, int BM, int BN, int nQt, int nKt,
+                                                             int32_t* qsum, int32_t* ksum, uint32_t* kv_bits) {
+    const int b = blockIdx.y;
+    const int tile = blockIdx.x;
+    const bool isq = tile < nQt;
+    const int T = isq ? BM : BN;
+    const int S = isq ? Sq : Sk;
+    const int t0 = (isq ? tile : tile - nQt) * T;
+    const int32_t* ids = isq ? q_blk + (int64_t)b * Sq : k_blk + (int64_t)b * Sk;
+    const uint8_t* val = isq ? q_valid + (int64_t)b * Sq : k_valid + (int64_t)b * Sk;
+    int mn = INT32_MAX, mx = INT32_MIN;
+    bool any = false, all = true;
+    for (int j = threadIdx.x; j < T; j += 64) {
+        const int pos = t0 + j;
+        const bool in = pos < S;
+        const bool v = in && val[pos] != 0;
+        if (v) {
+            const int id = ids[pos];
+            mn = min(mn, id);
+            mx = max(mx, id);
+        }
+        any = any || v;
+        all = all && v;
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+        mn = min(mn, __shfl_xor(mn, off));
+        mx = max(mx, __shfl_xor(mx, off));
+    }
+    const bool any_w = __builtin_amdgcn_ballot_w64(any) != 0;
+    const bool all_w = __builtin_amdgcn_ballot_w64(!all) == 0;
+    if (threadIdx.x == 0) {
+        int32_t* out = isq ? qsum + ((int64_t)b * nQt + tile) * 4 : ksum + ((int64_t)b * nKt + tile - nQt) * 4;
+        out[0] = mn;
+        out[1] = mx;
+        out[2] = any_w;
+        out[3] = all_w;
+    }
+    if (!isq) {
+        // key validity bits of this BN = 64 key tile: words 2*kt, 2*kt+1
+        const int pos = t0 + threadIdx.x;
+        const bool v = pos < Sk && val[pos] != 0;
+        const uint64_t bits = __builtin_amdgcn_ballot_w64(v);
+        const int W = (Sk + 31) / 32;
+        const int w0 = t0 / 32;
+        if (threadIdx.x == 0 && w0 < W) kv_bits[(int64_t)b * W + w0] = (uint32_t)bits;
+        if (threadIdx.x == 0 && w0 + 1 < W) kv_bits[(int64_t)b * W + w0 + 1] = (uint32_t)(bits >> 32);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dense (Nq, Nk) bool mask -> tile kinds + packed fine bits
+// (BinFlash, "Efficiently Dispatching ..."). HBM-bound: each thread reads
+// 16 mask bytes of a row per step (dwordx4), packs them into 16 bits and
+// folds them into its key tile's any/all flags.
+// Workgroup = 256 threads = 128 rows x 256 columns (4 key tiles of 64).
+// ---------------------------------------------------------------------------
+
+constexpr int kCmpRows = 128;   // BM
+constexpr int kCmpCols = 256;   // 4 key tiles of 64 per workgroup
+constexpr int kCmpPasses = kCmpRows / 16;
+
+__device__ __forceinline__ uint32_t pack4(uint32_t w) {
+    // 4 mask bytes -> 4 bits (bit k = byte k != 0)
+    const uint32_t nz = (((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w) & 0x80808080u;
+    return (((nz >> 7) * 0x01020408u) >> 24) & 0xFu;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void compact_tiles_kernel(const uint8_t* mask, int Nq, int Nk, int nKt,
+                                                            uint8_t* tile_kind, uint32_t* fine_bits) {
+    __shared__ uint32_t s_any[4], s_all[4];
+    const int qt = blockIdx.y;
+    const int col0 = blockIdx.x * kCmpCols;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int seg = t & 15;            // 16-column segment in the 256-column strip
+    const int rsub = t >> 4;           // row within a 16-row pass
+    const int col = col0 + seg * 16;
+    const int W = (Nk + 31) / 32;
+    if (t < 4) {
+        s_any[t] = 0;
+        s_all[t] = 1;
+    }
+    uint32_t words[kCmpPasses];
+    // issue every load of the strip first
+#pragma unroll
+    for (int ps = 0; ps < kCmpPasses; ++ps) {
+        const int r = qt * kCmpRows + ps * 16 + rsub;
+        uint32_t bits = 0;
+        if (r < Nq) {
+            const uint8_t* rp = mask + (int64_t)r * Nk;
+            if (VEC && col + 16 <= Nk) {
+                const u32x4 v = *(const u32x4*)(rp + col);
+                bits = pack4(v[0]) | (pack4(v[1]) << 4) | (pack4(v[2]) << 8) | (pack4(v[3]) << 12);
+            } else {
+                for (int e = 0; e < 16; ++e)
+                    if (col + e < Nk && rp[col + e] != 0) bits |= 1u << e;
+            }
+        }
+        words[ps] = bits;
+    }
+    bool any = false, all = true;
+    // columns of this thread that exist
+    const int ncol = max(0, min(16, Nk - col));
+    const uint32_t full16 = ncol >= 16 ? 0xFFFFu : ((1u << ncol) - 1u);
+#pragma unroll
+    for (int ps = 0; ps < kCmpPasses; ++ps) {
+        const int r = qt * kCmpRows + ps * 16 + rsub;
+        const uint32_t bits = words[ps];
+        any = any || bits != 0;
+        all = all && (r < Nq) && ncol == 16 && bits == full16;
+        // pair lanes (even, odd) form one 32-bit word of the row
+        const uint32_t hi = __shfl_xor(bits, 1);
+        if (r < Nq && (seg & 1) == 0) {
+            const int wi = col / 32;
+            if (wi < W) fine_bits[(int64_t)r * W + wi] = bits | (hi << 16);
+        }
+    }
+    // key tile of this thread: seg / 4; fold any/all over the wave, then the block
+    const uint64_t ba = __builtin_amdgcn_ballot_w64(any);
+    const uint64_t bl = __builtin_amdgcn_ballot_w64(all);
+    __syncthreads();
+    if (lane < 4) {
+        const uint64_t sel = 0x000F000F000F000Full << (4 * lane);
+        if (ba & sel) atomicOr(&s_any[lane], 1u);
+        if ((bl & sel) != sel) atomicAnd(&s_all[lane], 0u);
+    }
+    (void)wave;
+    __syncthreads();
+    if (t < 4) {
+        const int kt = col0 / 64 + t;
+        if (kt < nKt) {
+            const uint8_t k = s_all[t] ? kTileFull : (s_any[t] ? kTilePartial : kTileEmpty);
+            tile_kind[(int64_t)qt * nKt + kt] = k;
+        }
+    }
+}
+
+// CSR of non-empty tiles: one workgroup per query-tile row. The row offset is
+// the count of non-empty tiles in all earlier rows (recounted here, so no
+// workspace and no inter-workgroup ordering is needed).
+__global__ __launch_bounds__(256) void compact_csr_kernel(const uint8_t* tile_kind, int nQt, int nKt,
+                                                          int32_t* row_ptr, int32_t* col_idx, uint8_t* col_kind) {
+    __shared__ int lds[1024];
+    const int qt = blockIdx.x;
+    const int64_t before_n = (int64_t)qt * nKt;
+    int cnt = 0;
+    for (int64_t i = threadIdx.x; i < before_n; i += blockDim.x) cnt += tile_kind[i] != 0;
+    int tot;
+    block_exclusive_sum(cnt, &tot, lds);
+    const int base = tot;
+    if (threadIdx.x == 0) row_ptr[qt] = base;
+    int carry = 0;
+    const uint8_t* rowk = tile_kind + before_n;
+    for (int k0 = 0; k0 < nKt; k0 += blockDim.x) {
+        const int kt = k0 + threadIdx.x;
+        const uint8_t k = kt < nKt ? rowk[kt] : 0;
+        int n;
+        const int pos = block_exclusive_count(k != 0, &n, lds);
+        if (k != 0) {
+            col_idx[base + carry + pos] = kt;
+            col_kind[base + carry + pos] = k;
+        }
+        carry += n;
+    }
+    if (qt == nQt - 1 && threadIdx.x == 0) row_ptr[nQt] = base + carry;
+}
+
+// ---------------------------------------------------------------------------
+// BSR (flashinfer block_sparse_attention): entry kinds and CSC. One workgroup
+// per (b, h); rows are visited in ascending order, the entries of one row in
+// parallel (a canonical row has distinct columns), so the CSC lists come out
+// ascending without atomics on the output.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint8_t bsr_kind_of(int r, int c, int qb, int kb, int Sq, int Skv, int causal) {
+    const int i0 = r * qb, i1 = min((r + 1) * qb, Sq) - 1;
+    const int j0 = c * kb, j1 = min((c + 1) * kb, Skv) - 1;
+    if (i1 < i0 || j1 < j0) return kTileEmpty;
+    const bool ragged = (i1 - i0 + 1 != qb) || (j1 - j0 + 1 != kb);
+    if (!causal) return ragged ? kTilePartial : kTileFull;
+    if (j0 > i1) return kTileEmpty;
+    if (j1 <= i0 && !ragged) return kTileFull;
+    return kTilePartial;
+}
+
+__global__ __launch_bounds__(256) void bsr_prepare_kernel(const int32_t* indptr, const int32_t* indices, int nQb,
+                                                          int nKb, int64_t nnz, int qb, int kb, int Sq, int Skv, int causal,
+                                                          uint8_t* col_kind, int32_t* csc_ptr, int32_t* csc_idx) {
+    extern __shared__ int cnt[];  // nKb ints, then 1024 scan scratch
+    int* scan = cnt + nKb;
+    const int bh = blockIdx.x;
+    const int* ip = indptr + (int64_t)bh * (nQb + 1);
+    int32_t* cp = csc_ptr + (int64_t)bh * (nKb + 1);
+    for (int c = threadIdx.x; c < nKb; c += blockDim.x) cnt[c] = 0;
+    __syncthreads();
+    // Rows are expected canonical (mfa_bsr_validate); out-of-range offsets or
+    // ids are skipped here so that malformed input cannot write out of bounds.
+    for (int r = 0; r < nQb; ++r) {
+        const int e0 = max(ip[r], 0), e1 = (int)min((int64_t)ip[r + 1], nnz);
+        for (int e = e0 + threadIdx.x; e < e1; e += blockDim.x) {
+            const int c = indices[e];
+            if (c < 0 || c >= nKb) continue;
+            col_kind[e] = bsr_kind_of(r, c, qb, kb, Sq, Skv, causal);
+            cnt[c] += 1;  // distinct columns within one row
+        }
+        __syncthreads();
+    }
+    // exclusive scan of column counts, in chunks of blockDim
+    int carry = ip[0];
+    for (int c0 = 0; c0 < nKb; c0 += blockDim.x) {
+        const int c = c0 + threadIdx.x;
+        const int v = c < nKb ? cnt[c] : 0;
+        int tot;
+        const int ex = block_exclusive_sum(v, &tot, scan);
+        if (c < nKb) {
+            cp[c] = carry + ex;
+            cnt[c] = carry + ex;  // becomes the write cursor
+        }
+        carry += tot;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) cp[nKb] = carry;
+    __syncthreads();
+    for (int r = 0; r < nQb; ++r) {
+        const int e0 = max(ip[r], 0), e1 = (int)min((int64_t)ip[r + 1], nnz);
+        for (int e = e0 + threadIdx.x; e < e1; e += blockDim.x) {
+            const int c = indices[e];
+            if (c < 0 || c >= nKb) continue;
+            const int dst = cnt[c];
+            if (dst >= 0 && dst < nnz) csc_idx[dst] = r;
+            cnt[c] = dst + 1;
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Varlen packing and schedule ("tensorplay.nn.attention.varlen", Packed
+// layout). One workgroup of 1024 threads. Tiles are ordered by descending
+// number of visited key tiles (a counting sort over costs capped at
+// kMaxCost), ties by ascending (seq, q0).
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxCost = 4095;
+
+__device__ __forceinline__ int varlen_cost(int Lq, int Lk, int q0, int BM, int BN, int causal, int left, int right) {
+    const int q1 = min(q0 + BM, Lq) - 1;
+    int lo = left >= 0 ? max(0, q0 - left) : 0;
+    int hi = Lk - 1;
+    if (right >= 0) hi = min(hi, q1 + right);
+    if (causal) hi = min(hi, q1);
+    if (hi < lo) return 0;
+    return min(hi / BN - lo / BN + 1, kMaxCost);
+}
+
+__global__ __launch_bounds__(1024) void varlen_schedule_kernel(const int32_t* len_q, const int32_t* len_k, int nseq,
+                                                               int BM, int BN, int causal, int left, int right,
+                                                               int32_t* cu_q, int32_t* cu_k, int32_t* max_len,
+                                                               int32_t* work, int work_cap, int32_t* n_work) {
+    __shared__ int scan[1024];
+    __shared__ int hist[kMaxCost + 1];
+    __shared__ int s_max[2];
+    __shared__ int s_cost[1024];
+    const int t = threadIdx.x, n = blockDim.x;
+    for (int i = t; i <= kMaxCost; i += n) hist[i] = 0;
+    if (t == 0) {
+        s_max[0] = 0;
+        s_max[1] = 0;
+    }
+    __syncthreads();
+    // cumulative lengths and tile counts
+    int cq = 0, ck = 0, ctile = 0;
+    if (t == 0) {
+        cu_q[0] = 0;
+        cu_k[0] = 0;
+    }
+    for (int s0 = 0; s0 < nseq; s0 += n) {
+        const int s = s0 + t;
+        const int lq = s < nseq ? len_q[s] : 0;
+        const int lk = s < nseq ? len_k[s] : 0;
+        int tq, tk, tt;
+        const int eq = block_exclusive_sum(lq, &tq, scan);
+        const int ek = block_exclusive_sum(lk, &tk, scan);
+        if (s < nseq) {
+            cu_q[s + 1] = cq + eq + lq;
+            cu_k[s + 1] = ck + ek + lk;
+            atomicMax(&s_max[0], lq);
+            atomicMax(&s_max[1], lk);
+        }
+        const int nt = (lq + BM - 1) / BM;
+        block_exclusive_sum(nt, &tt, scan);
+        cq += tq;
+        ck += tk;
+        ctile += tt;
+    }
+    __syncthreads();
+    if (t == 0) {
+        max_len[0] = s_max[0];
+        max_len[1] = s_max[1];
+        n_work[0] = ctile <= work_cap ? ctile : -1;
+    }
+    for (int i = t; i < work_cap; i += n) {
+        work[2 * i] = -1;
+        work[2 * i + 1] = -1;
+    }
+    if (ctile > work_cap) return;
+    __syncthreads();
+    // Enumerate tiles in (seq, q0) order: a thread walks sequences, tiles of a
+    // sequence are handled in chunks by the whole block.
+    // Pass 1: histogram of costs.
+    for (int s = 0; s < nseq; ++s) {
+        const int lq = len_q[s], lk = len_k[s];
+        const int nt = (lq + BM - 1) / BM;
+        for (int i = t; i < nt; i += n) atomicAdd(&hist[varlen_cost(lq, lk, i * BM, BM, BN, causal, left, right)], 1);
+    }
+    __syncthreads();
+    // start[cost] = number of tiles with a larger cost (descending order)
+    if (t == 0) {
+        int acc = 0;
+        for (int c = kMaxCost; c >= 0; --c) {
+            const int h = hist[c];
+            hist[c] = acc;
+            acc += h;
+        }
+    }
+    __syncthreads();
+    // Pass 2: stable placement in (seq, q0) order, chunk by chunk.
+    for (int s = 0; s < nseq; ++s) {
+        const int lq = len_q[s], lk = len_k[s];
+        const int nt = (lq + BM - 1) / BM;
+        for (int i0 = 0; i0 < nt; i0 += n) {
+            const int i = i0 + t;
+            const int cost = i < nt ? varlen_cost(lq, lk, i * BM, BM, BN, causal, left, right) : -1;
+            s_cost[t] = cost;
+            __syncthreads();
+            int rank = 0;
+            if (cost >= 0)
+                for (int u = 0; u < t; ++u) rank += (s_cost[u] == cost);
+            const int pos = cost >= 0 ? hist[cost] + rank : 0;
+            __syncthreads();
+            if (cost >= 0) {
+                work[2 * pos] = s;
+                work[2 * pos + 1] = i * BM;
+                atomicAdd(&hist[cost], 1);
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+
+hipError_t launch_block_ids(const uint8_t* pad, const int32_t* att, int B, int N, int nc, const uint8_t* cross_pad,
+                            int32_t* q_blk, int32_t* k_blk, uint8_t* q_valid, uint8_t* k_valid, hipStream_t s) {
+    hipLaunchKernelGGL(block_ids_kernel, dim3(B), dim3(256), 0, s, pad, att, N, nc, cross_pad, q_blk, k_blk, q_valid,
+                       k_valid);
+    return hipGetLastError();
+}
+
+hipError_t launch_blockid_summary(const int32_t* q_blk, const int32_t* k_blk, const uint8_t* q_valid,
+                                  const uint8_t* k_valid, int B, int Sq, int Sk, int BM, int BN, int32_t* qsum,
+                                  int32_t* ksum, uint32_t* kv_bits, hipStream_t s) {
+    const int nQt = (Sq + BM - 1) / BM, nKt = (Sk + BN - 1) / BN;
+    if (nQt + nKt == 0) return hipSuccess;
+    hipLaunchKernelGGL(blockid_summary_kernel, dim3(nQt + nKt, B), dim3(64), 0, s, q_blk, k_blk, q_valid, k_valid, Sq,
+                       Sk, BM, BN, nQt, nKt, qsum, ksum, kv_bits);
+    return hipGetLastError();
+}
+
+hipError_t launch_compact(const uint8_t* mask, int Nq, int Nk, uint8_t* tile_kind, uint32_t* fine_bits,
+                          int32_t* row_ptr, int32_t* col_idx, uint8_t* col_kind, hipStream_t s) {
+    const int nQt = (Nq + kCmpRows - 1) / kCmpRows, nKt = (Nk + 63) / 64;
+    if (nQt == 0) {
+        return hipMemsetAsync(row_ptr, 0, sizeof(int32_t), s);
+    }
+    if (nKt > 0) {
+        const dim3 grid((Nk + kCmpCols - 1) / kCmpCols, nQt);
+        const bool vec = (Nk % 16 == 0) && (((uintptr_t)mask & 15) == 0);
+        if (vec)
+            hipLaunchKernelGGL(compact_tiles_kernel<true>, grid, dim3(256), 0, s, mask, Nq, Nk, nKt, tile_kind,
+                               fine_bits);
+        else
+            hipLaunchKernelGGL(compact_tiles_kernel<false>, grid, dim3(256), 0, s, mask, Nq, Nk, nKt, tile_kind,
+                               fine_bits);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(compact_csr_kernel, dim3(nQt), dim3(256), 0, s, tile_kind, nQt, nKt, row_ptr, col_idx, col_kind);
+    return hipGetLastError();
+}
+
+hipError_t launch_bsr_prepare(const int32_t* indptr, const int32_t* indices, int B, int Hkv, int nQb, int nKb,
+                              int64_t nnz, int qb, int kb, int Sq, int Skv, int causal, uint8_t* col_kind, int32_t* csc_ptr,
+                              int32_t* csc_idx, hipStream_t s) {
+    const size_t lds = (size_t)(nKb + 256) * sizeof(int);
+    hipLaunchKernelGGL(bsr_prepare_kernel, dim3(B * Hkv), dim3(256), lds, s, indptr, indices, nQb, nKb, nnz, qb, kb, Sq, Skv,
+                       causal, col_kind, csc_ptr, csc_idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_varlen_schedule(const int32_t* len_q, const int32_t* len_k, int nseq, int BM, int BN, int causal,
+                                  int left, int right, int32_t* cu_q, int32_t* cu_k, int32_t* max_len,
+                                  int32_t* work, int work_cap, int32_t* n_work, hipStream_t s) {
+    hipLaunchKernelGGL(varlen_schedule_kernel, dim3(1), dim3(1024), 0, s, len_q, len_k, nseq, BM, BN, causal, left,
+                       right, cu_q, cu_k, max_len, work, work_cap, n_work);
+    return hipGetLastError();
+}
+
+}  // namespace mfa

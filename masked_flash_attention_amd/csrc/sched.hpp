@@ -1,0 +1,201 @@
+// Per-workgroup tile schedule and per-element mask predicates, shared by the
+// bf16 MFMA forward kernel and the fp32 test-mode kernel.
+//
+// A workgroup owns one query tile of BM rows of one (batch, query head) (or of
+// one varlen sequence). It walks only the key tiles that can hold an allowed
+// entry: the CSR list of non-empty tiles (dense-mask tiles, as in the BinFlash
+// method's "pre-sorted list of non-empty K-blocks per Q-row"), the BSR row
+// (flashinfer block_sparse_attention), the key-tile range of the sliding
+// window (varlen), or every key tile classified from block-id summaries
+// (opentau block ids). Full tiles skip the mask entirely; partial tiles
+// evaluate the predicate per element.
+#pragma once
+
+#include "common.hpp"
+
+namespace mfa {
+
+constexpr int kBN = 64;  // key-tile width of every forward kernel
+
+struct TileRange {
+    int b, hq, hk;
+    int qt;         // query-tile index in the representation's tile grid
+    int q_row0;     // first query row of the tile (row index along Sq)
+    int q_rows;     // rows of the tile that exist (<= BM)
+    int q_base;     // varlen: cu_q[seq]; local query index = row - q_base
+    int k_base;     // varlen: cu_k[seq]; key rows are k_base + local key index
+    int k_len;      // keys that exist (Sk or the sequence's key length)
+    int begin, end; // iteration range
+    int seq;        // varlen sequence (-1 otherwise)
+    bool active;
+    bool len_error; // varlen: sequence longer than the stated max_q / max_k
+};
+
+template <int KIND, int BM>
+__device__ __forceinline__ TileRange make_range(const FwdDev& p, const MaskDev& m, int logical) {
+    TileRange t;
+    t.seq = -1;
+    t.active = true;
+    t.len_error = false;
+    t.q_base = 0;
+    t.k_base = 0;
+    t.k_len = p.Sk;
+    if constexpr (KIND == MFA_MASK_VARLEN) {
+        const int wi = logical / p.Hq;
+        t.hq = logical - wi * p.Hq;
+        t.b = 0;
+        t.hk = t.hq / p.G;
+        int s = -1, q0 = 0;
+        if (wi < m.work_cap) {
+            s = m.work[2 * wi];
+            q0 = m.work[2 * wi + 1];
+        }
+        if (s < 0) {
+            t.active = false;
+            t.begin = t.end = 0;
+            t.q_rows = 0;
+            t.q_row0 = 0;
+            t.qt = 0;
+            return t;
+        }
+        t.seq = s;
+        const int cq0 = m.cu_q[s], cq1 = m.cu_q[s + 1];
+        const int ck0 = m.cu_k[s], ck1 = m.cu_k[s + 1];
+        const int Lq = cq1 - cq0, Lk = ck1 - ck0;
+        t.q_base = cq0;
+        t.k_base = ck0;
+        t.k_len = Lk;
+        t.qt = q0 / BM;
+        t.q_row0 = cq0 + q0;
+        t.q_rows = min(BM, Lq - q0);
+        const int i1 = q0 + t.q_rows - 1;
+        int lo = 0, hi = Lk - 1;
+        if (m.win_left >= 0) lo = max(0, q0 - m.win_left);
+        if (m.win_right >= 0) hi = min(hi, i1 + m.win_right);
+        if (m.causal) hi = min(hi, i1);
+        if (hi < lo) {
+            t.begin = t.end = 0;
+        } else {
+            t.begin = lo / kBN;
+            t.end = hi / kBN + 1;
+        }
+        if (Lq > m.max_q || Lk > m.max_k) {
+            t.len_error = true;
+            if (m.err) *m.err = 1;
+        }
+        return t;
+    } else {
+        const int bh = logical / p.nQt;
+        t.qt = p.nQt - 1 - (logical - bh * p.nQt);  // heaviest (last) query tiles first
+        t.b = bh / p.Hq;
+        t.hq = bh - t.b * p.Hq;
+        t.hk = t.hq / p.G;
+        t.q_row0 = t.qt * BM;
+        t.q_rows = min(BM, p.Sq - t.q_row0);
+        if constexpr (KIND == MFA_MASK_TILES) {
+            t.begin = m.row_ptr[t.qt];
+            t.end = m.row_ptr[t.qt + 1];
+        } else if constexpr (KIND == MFA_MASK_BSR) {
+            const int* ip = m.indptr + ((int64_t)t.b * p.Hkv + t.hk) * (m.nQb + 1);
+            t.begin = ip[t.qt];
+            t.end = ip[t.qt + 1];
+        } else {
+            t.begin = 0;
+            t.end = p.nKt;
+        }
+        return t;
+    }
+}
+
+// Block-id tile classification from the per-tile summaries {min, max, any, all}.
+__device__ __forceinline__ int classify_blockid(const int32_t* qs, const int32_t* ks) {
+    const int qmin = qs[0], qmax = qs[1], qany = qs[2], qall = qs[3];
+    const int kmin = ks[0], kmax = ks[1], kany = ks[2], kall = ks[3];
+    if (!qany || !kany || kmin > qmax) return kTileEmpty;
+    if (qall && kall && kmax <= qmin) return kTileFull;
+    return kTilePartial;
+}
+
+// Key tile and kind of iteration `it`. Kind 0 means skip.
+template <int KIND, int BM>
+__device__ __forceinline__ void tile_at(const FwdDev& p, const MaskDev& m, const TileRange& t, int it,
+                                        int& kt, int& kind) {
+    if constexpr (KIND == MFA_MASK_TILES) {
+        kt = m.col_idx[it];
+        kind = m.col_kind[it];
+    } else if constexpr (KIND == MFA_MASK_BSR) {
+        kt = m.indices[it];
+        kind = m.bsr_kind[it];
+    } else if constexpr (KIND == MFA_MASK_BLOCKID) {
+        kt = it;
+        const int nQt = p.nQt, nKt = p.nKt;
+        kind = classify_blockid(m.qsum + ((int64_t)t.b * nQt + t.qt) * 4,
+                                m.ksum + ((int64_t)t.b * nKt + kt) * 4);
+    } else if constexpr (KIND == MFA_MASK_VARLEN) {
+        kt = it;
+        const int i0 = t.q_row0 - t.q_base, i1 = i0 + t.q_rows - 1;
+        const int j0 = kt * kBN, j1 = min(j0 + kBN, t.k_len) - 1;
+        bool full = (j1 - j0 + 1 == kBN);
+        if (m.causal) full = full && (j1 <= i0);
+        if (m.win_left >= 0) full = full && (i1 - j0 <= m.win_left);
+        if (m.win_right >= 0) full = full && (j1 - i0 <= m.win_right);
+        kind = full ? kTileFull : kTilePartial;
+    } else {
+        kt = it;
+        kind = kTileFull;
+    }
+}
+
+// Per-row mask state for one query row (one lane's query in the MFMA kernel).
+template <int KIND>
+struct RowMask {
+    int qi;        // query row along Sq (global packed row for varlen)
+    int qi_local;  // varlen local index; otherwise == qi
+    int qblk;      // BLOCKID
+    int qvalid;    // BLOCKID
+    int row_ok;    // the row exists (inside Sq, or inside its varlen sequence)
+    __device__ __forceinline__ void init(const FwdDev& p, const MaskDev& m, const TileRange& t, int row) {
+        qi = row;
+        qi_local = row - t.q_base;
+        qblk = 0;
+        qvalid = 1;
+        row_ok = (row - t.q_row0) < t.q_rows;
+        if constexpr (KIND == MFA_MASK_BLOCKID) {
+            if (row < p.Sq) {
+                qblk = m.q_blk[(int64_t)t.b * p.Sq + row];
+                qvalid = m.q_valid[(int64_t)t.b * p.Sq + row] != 0;
+            } else {
+                qvalid = 0;
+            }
+        }
+    }
+};
+
+// Generic per-element predicate (used by the fp32 test kernel and for
+// reference reasoning; the MFMA kernel has a vectorised version of each).
+// key is the sequence-local key index.
+template <int KIND>
+__device__ __forceinline__ bool allowed(const FwdDev& p, const MaskDev& m, const TileRange& t,
+                                        const RowMask<KIND>& r, int key) {
+    if (key >= t.k_len || !r.row_ok) return false;
+    if constexpr (KIND == MFA_MASK_TILES) {
+        const uint32_t w = m.fine_bits[(int64_t)r.qi * m.fine_words + (key >> 5)];
+        return (w >> (key & 31)) & 1u;
+    } else if constexpr (KIND == MFA_MASK_BLOCKID) {
+        const uint32_t w = m.kv_bits[(int64_t)t.b * m.kv_words + (key >> 5)];
+        const int kb = m.k_blk[(int64_t)t.b * p.Sk + key];
+        return r.qvalid && ((w >> (key & 31)) & 1u) && kb <= r.qblk;
+    } else if constexpr (KIND == MFA_MASK_BSR) {
+        return !m.causal || key <= r.qi;
+    } else if constexpr (KIND == MFA_MASK_VARLEN) {
+        const int i = r.qi_local, j = key;
+        if (m.causal && j > i) return false;
+        if (m.win_left >= 0 && i - j > m.win_left) return false;
+        if (m.win_right >= 0 && j - i > m.win_right) return false;
+        return true;
+    } else {
+        return true;
+    }
+}
+
+}  // namespace mfa

@@ -1,0 +1,48 @@
+"""Helpers shared by the GPU parity tests: device setup, oracle comparison."""
+
+import sys
+
+import numpy as np
+import torch
+
+DEV = "cuda:0"
+BF16_OUT_TOL = 2e-2   # max-abs error of attention outputs, bf16 in/out, fp32 accumulate
+F32_OUT_TOL = 1e-4    # max-abs error in fp32 test mode
+LSE_TOL = 1e-3        # max-abs error of the log-sum-exp
+
+
+def note(msg):
+    """Name the case before each GPU step, flushed, so a fault names it."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x, dtype=None):
+    if isinstance(x, np.ndarray):
+        x = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype is not None:
+        x = x.to(dtype)
+    return x.to(DEV)
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def compare_attention(out, lse, ref_out, ref_lse, out_tol, lse_tol=LSE_TOL, rows_axis_lse=-1):
+    """Max-abs check of out and lse; empty rows (ref lse = -inf) must be exactly 0 / -inf.
+
+    out / ref_out: same-shaped arrays with the query axis matching lse's last axis
+    after transposition by the caller; returns (max out error, max lse error).
+    """
+    out = np.asarray(out, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    assert np.all(np.isfinite(out)), "non-finite output"
+    err_o = float(np.max(np.abs(out - ref_out))) if out.size else 0.0
+    empty = np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(lse), empty), "empty-row pattern of lse differs"
+    fin = ~empty
+    err_l = float(np.max(np.abs(lse[fin] - ref_lse[fin]))) if fin.any() else 0.0
+    assert err_o <= out_tol, f"out max-abs error {err_o:.3e} > {out_tol}"
+    assert err_l <= lse_tol, f"lse max-abs error {err_l:.3e} > {lse_tol}"
+    return err_o, err_l

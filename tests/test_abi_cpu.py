@@ -1,0 +1,157 @@
+"""C ABI checks that need no GPU: exports, struct layout, host-side validation.
+
+On a machine without a GPU every call that passes validation stops at the
+device check with MFA_E_NO_DEVICE; nothing is launched.
+"""
+
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from masked_flash_attention_amd import _ffi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mfa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_ffi.LIB_PATH):
+        from masked_flash_attention_amd import build
+        build.build(verbose=False)
+    return _ffi.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mfa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) >= 13
+    out = subprocess.run(["nm", "-D", "--defined-only", _ffi.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (mfa_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert set(names) == set(_ffi.SIGNATURES), "binding signatures and header disagree"
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.cpp"
+    src.write_text(r'''
+#include <cstdio>
+#include <cstddef>
+#include "mfa.h"
+#define P(s, f) printf(#s "." #f " %zu\n", offsetof(s, f))
+int main() {
+  printf("mfa_attn_args %zu\nmfa_mask %zu\nmfa_attn_bwd_args %zu\n",
+         sizeof(mfa_attn_args), sizeof(mfa_mask), sizeof(mfa_attn_bwd_args));
+  P(mfa_attn_args, q); P(mfa_attn_args, lse); P(mfa_attn_args, o_stride);
+  P(mfa_mask, tile_kind); P(mfa_mask, q_block); P(mfa_mask, cu_q); P(mfa_mask, err); P(mfa_mask, win_right);
+  P(mfa_attn_bwd_args, dout); P(mfa_attn_bwd_args, dv_stride);
+  return 0;
+}''')
+    exe = tmp_path / "layout"
+    subprocess.run(["g++", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                    str(src), "-o", str(exe)], check=True)
+    got = dict(line.rsplit(" ", 1) for line in subprocess.run([str(exe)], capture_output=True,
+                                                               text=True).stdout.split("\n") if line)
+    got = {k: int(v) for k, v in got.items()}
+    assert got["mfa_attn_args"] == C.sizeof(_ffi.AttnArgs)
+    assert got["mfa_mask"] == C.sizeof(_ffi.Mask)
+    assert got["mfa_attn_bwd_args"] == C.sizeof(_ffi.BwdArgs)
+    for cls, cname in ((_ffi.AttnArgs, "mfa_attn_args"), (_ffi.Mask, "mfa_mask"), (_ffi.BwdArgs, "mfa_attn_bwd_args")):
+        for key, off in got.items():
+            if key.startswith(cname + "."):
+                assert getattr(cls, key.split(".", 1)[1]).offset == off, key
+
+
+def _args(**kw):
+    a = _ffi.AttnArgs()
+    a.dtype, a.B, a.Sq, a.Sk, a.Hq, a.Hkv, a.D = 0, 1, 128, 128, 4, 2, 128
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _status(lib, code):
+    return lib.mfa_status_name(code).decode()
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(Hq=3, Hkv=2), "MFA_E_SHAPE"),
+    (dict(Hkv=0), "MFA_E_SHAPE"),
+    (dict(Sq=-1), "MFA_E_SHAPE"),
+    (dict(D=96), "MFA_E_UNSUPPORTED"),
+    (dict(dtype=7), "MFA_E_DTYPE"),
+])
+def test_attn_fwd_rejects_before_any_device_call(lib, kw, want):
+    m = _ffi.Mask()
+    s = lib.mfa_attn_fwd(C.byref(_args(**kw)), C.byref(m), 0.125, None)
+    assert _status(lib, s) == want
+    assert lib.mfa_last_error().decode()
+
+
+def test_attn_fwd_null_and_mask_errors(lib):
+    assert _status(lib, lib.mfa_attn_fwd(None, None, 0.1, None)) == "MFA_E_ARG"
+    m = _ffi.Mask()
+    m.kind = 9
+    assert _status(lib, lib.mfa_attn_fwd(C.byref(_args()), C.byref(m), 0.1, None)) == "MFA_E_ARG"
+    m = _ffi.Mask()
+    m.kind, m.q_block, m.kv_block = _ffi.MASK_BSR, 32, 64
+    assert _status(lib, lib.mfa_attn_fwd(C.byref(_args()), C.byref(m), 0.1, None)) == "MFA_E_UNSUPPORTED"
+    m = _ffi.Mask()
+    m.kind = _ffi.MASK_VARLEN
+    assert _status(lib, lib.mfa_attn_fwd(C.byref(_args(B=2)), C.byref(m), 0.1, None)) == "MFA_E_SHAPE"
+    assert _status(lib, lib.mfa_attn_fwd(C.byref(_args()), C.byref(_ffi.Mask()), float("nan"), None)) == "MFA_E_ARG"
+
+
+def test_maskrep_validation(lib):
+    st = lib.mfa_make_block_ids(None, None, 1, 8, 2, None, None, None, None, None, None)
+    assert _status(lib, st) == "MFA_E_ARG" and "cross_pad" in lib.mfa_last_error().decode()
+    st = lib.mfa_compact_dense_mask(None, 10, 10, 64, 64, None, None, None, None, None, None)
+    assert _status(lib, st) == "MFA_E_UNSUPPORTED"
+    st = lib.mfa_varlen_schedule(None, None, 2, 64, 64, 1, -1, -1, None, None, None, None, 4, None, None)
+    assert _status(lib, st) == "MFA_E_UNSUPPORTED"
+    st = lib.mfa_varlen_schedule(None, None, 2, 128, 64, 1, -2, -1, None, None, None, None, 4, None, None)
+    assert _status(lib, st) == "MFA_E_ARG"
+    st = lib.mfa_bsr_validate(None, None, 1, 1, 4, 4, 0, None, None)
+    assert _status(lib, st) == "MFA_E_ARG"
+    st = lib.mfa_bsr_prepare(None, None, 1, 1, 3, 4, 0, 64, 64, 256, 256, 1, None, None, None, None)
+    assert _status(lib, st) == "MFA_E_SHAPE"
+    st = lib.mfa_blockid_tile_summary(None, None, None, None, 1, 8, 8, 128, 32, None, None, None, None)
+    assert _status(lib, st) == "MFA_E_UNSUPPORTED"
+
+
+def test_empty_problems_are_noops(lib):
+    m = _ffi.Mask()
+    assert _status(lib, lib.mfa_attn_fwd(C.byref(_args(Sq=0)), C.byref(m), 0.1, None)) == "MFA_OK"
+    assert _status(lib, lib.mfa_attn_fwd(C.byref(_args(B=0)), C.byref(m), 0.1, None)) == "MFA_OK"
+    st = lib.mfa_make_block_ids(None, None, 0, 8, 0, None, None, None, None, None, None)
+    assert _status(lib, st) == "MFA_OK"
+
+
+def test_no_device_here_is_reported(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert lib.mfa_is_available() == 0
+    assert "device" in lib.mfa_last_error().decode().lower()
+    m = _ffi.Mask()
+    st = lib.mfa_attn_fwd(C.byref(_args()), C.byref(m), 0.1, None)
+    assert _status(lib, st) == "MFA_E_NO_DEVICE"
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_ffi, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_ffi, "_lib", None)
+    with pytest.raises(ImportError, match="not built"):
+        _ffi.load()
+    import masked_flash_attention_amd as mfa
+    assert mfa.is_available() is False
+    assert "not built" in mfa.load_error()
