@@ -1,0 +1,252 @@
+"""Benchmark: causal dense-mask masked attention forward on one MI355X.
+
+Workload (the BinFlash "Use" example shape): B=4, H=32, N=8192, D=128 bf16
+q/k/v ~ N(0,1) in (B, H, N, D), an (N, N) lower-triangular bool mask (True =
+attend). One step is the whole tensor->tensor call: compaction of the dense
+mask into 128x64 tiles + packed fine bits + CSR list, then the fused masked
+attention forward writing out (bf16) and LSE (fp32). Inputs are resident in
+HBM before timing starts.
+
+Metric: forward effective TFLOP/s counting 4*BM*BN*D FLOPs per attended
+(non-empty) tile per (batch, head), over the step time; also reported: the
+same over attention-kernel time only, FLOPs over allowed (i, j) entries, % of
+the bf16 dense MFMA peak (2516.6 TFLOP/s), and the skip criterion (causal vs
+all-True vs all-False masks of the same shape).
+
+Prints ONE JSON line. --gpus N > 1 is not supported (single-GPU path).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (AMD published figure)
+PEAK_HBM_GBS = 8000.0
+BM, BN = 128, 64
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("attn_fwd.hip", "sched.hpp", "common.hpp"):
+        with open(os.path.join(ROOT, "masked_flash_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(bytes_algo_per_launch):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "attn_fwd_bf16_causal8192_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, tile_flops_per_bh, seconds):
+    """Time the fp64 oracle on whole (batch, head) slices until `seconds` pass."""
+    from oracle import attention as A
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    mask = w["mask"][None, None]
+    done = 0
+    t0 = time.perf_counter()
+    pairs = [(b, h) for b in range(w["q"].shape[0]) for h in range(w["q"].shape[1])]
+    for b, h in pairs:
+        q = w["q"][b:b + 1, h:h + 1].double().numpy().transpose(0, 2, 1, 3)
+        k = w["k"][b:b + 1, h:h + 1].double().numpy().transpose(0, 2, 1, 3)
+        v = w["v"][b:b + 1, h:h + 1].double().numpy().transpose(0, 2, 1, 3)
+        A.attention_fwd(q, k, v, mask, w["scale"], chunk=2048)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(tile_flops_per_bh * done / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{done} of {len(pairs)} (batch, head) slices, all 8192 query rows each, fp64 NumPy "
+                      f"dense masked softmax ({dt:.1f} s); attended-tile FLOPs of the sample over that time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-skip-check", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of q (268 MB) for HBM counter calibration")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures the single-GPU path only; --gpus must be 1 (no multi-GPU path is built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import masked_flash_attention_amd as mfa
+    import workloads as W
+
+    if not mfa.is_available():
+        raise SystemExit(f"libmfa unavailable: {mfa.load_error()}")
+    dev = "cuda:0"
+    log("generating inputs")
+    w = W.causal_dense()
+    B, H, N, D = w["q"].shape
+    q, k, v = (w[x].to(dev) for x in "qkv")
+    mask = torch.from_numpy(w["mask"]).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    scale = w["scale"]
+
+    def step():
+        comp = mfa.compact_dense_mask(mask)
+        mfa.attn_fwd(q, k, v, mfa.MaskRep.tiles(comp), scale, "bhsd", out=out, lse=lse)
+        return comp
+
+    log("warmup")
+    for _ in range(a.warmup):
+        comp = step()
+    torch.cuda.synchronize()
+    nnz = int(comp["row_ptr"][-1].item())
+    tile_flops = 4.0 * BM * BN * D * nnz * B * H
+    allowed = int(w["mask"].sum())
+    allowed_flops = 4.0 * D * allowed * B * H
+
+    log(f"timing {a.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / a.steps
+
+    # per-kernel durations with events on the stream the kernels run on
+    rep = mfa.MaskRep.tiles(comp)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    for e0, e1 in ev:
+        e0.record()
+        mfa.attn_fwd(q, k, v, rep, scale, "bhsd", out=out, lse=lse)
+        e1.record()
+    torch.cuda.synchronize()
+    attn_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    for e0, e1 in evc:
+        e0.record()
+        mfa.compact_dense_mask(mask)
+        e1.record()
+    torch.cuda.synchronize()
+    compact_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evc]))
+
+    # skip criterion: all-True and all-False masks of the same shape
+    skip = None
+    if not a.no_skip_check:
+        res = {}
+        for name, mk in (("all_true", torch.ones_like(mask)), ("all_false", torch.zeros_like(mask))):
+            r = mfa.MaskRep.tiles(mfa.compact_dense_mask(mk))
+            for _ in range(2):
+                mfa.attn_fwd(q, k, v, r, scale, "bhsd", out=out, lse=lse)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(max(3, a.steps // 2))]
+            for e0, e1 in evs:
+                e0.record()
+                mfa.attn_fwd(q, k, v, r, scale, "bhsd", out=out, lse=lse)
+                e1.record()
+            torch.cuda.synchronize()
+            res[name] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+        frac_tiles = nnz / ((N // BM) * (N // BN))
+        skip = {"t_causal_ms": round(attn_ms, 4), "t_all_true_ms": round(res["all_true"], 4),
+                "t_all_false_ms": round(res["all_false"], 4),
+                "causal_over_all_true": round(attn_ms / res["all_true"], 4),
+                "causal_bound": round(frac_tiles + 0.05, 4),
+                "all_false_over_all_true": round(res["all_false"] / res["all_true"], 4),
+                "all_true_tflops": round(4.0 * D * N * N * B * H / res["all_true"] / 1e9, 1)}
+        # restore the causal output for the parity check below
+        mfa.attn_fwd(q, k, v, rep, scale, "bhsd", out=out, lse=lse)
+
+    if a.copy_calibration:
+        dst = torch.empty_like(q)
+        for _ in range(3):
+            dst.copy_(q)
+        torch.cuda.synchronize()
+
+    # sampled parity of this very launch against the oracle
+    from oracle import attention as A
+    rows = np.array([0, 127, 128, 4095, 8191])
+    tri = w["mask"]
+    errs = []
+    for b, h in ((0, 0), (3, 31)):
+        def allowed_rows(bb, hm, rr):
+            return tri[rr]
+        allowed_rows.heads = 1
+        qq = w["q"][b:b + 1, h:h + 1].double().numpy().transpose(0, 2, 1, 3)
+        kk = w["k"][b:b + 1, h:h + 1].double().numpy().transpose(0, 2, 1, 3)
+        vv = w["v"][b:b + 1, h:h + 1].double().numpy().transpose(0, 2, 1, 3)
+        ro, rl = A.attention_fwd(qq, kk, vv, allowed_rows, scale, rows=rows)
+        go = out[b, h, rows].double().cpu().numpy()
+        errs.append(float(np.abs(go - ro[0, :, 0]).max()))
+    parity = {"rows_checked": int(2 * rows.size), "max_abs_err": max(errs), "tol": 2e-2}
+
+    attn_tflops = tile_flops / (attn_ms * 1e-3) / 1e12
+    value = tile_flops / (step_ms * 1e-3) / 1e12
+    traffic = read_traffic(None)
+    result = {
+        "metric": "fwd effective TFLOP/s on attended tiles (bf16)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal dense-mask attention forward (mask compaction + fused kernel)",
+                   "B": B, "H": H, "N": N, "D": D, "layout": "BHND", "tile": f"{BM}x{BN}",
+                   "attended_tiles_per_bh": nnz, "global_batch": B, "seq_len": N},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "attn_kernel_ms": round(attn_ms, 4),
+        "compact_ms": round(compact_ms, 4),
+        "attn_kernel_tflops": round(attn_tflops, 2),
+        "allowed_entry_tflops": round(allowed_flops / (attn_ms * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "skip": skip,
+        "parity": parity,
+        "kernel_source_sha": kernel_source_hash(),
+    }
+    if not a.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(w, tile_flops / (B * H), a.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

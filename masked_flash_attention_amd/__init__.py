@@ -61,7 +61,11 @@ def _stream():
 
 
 def _u8(t):
-    return t if t.dtype == torch.uint8 else t.to(torch.uint8)
+    if t.dtype == torch.uint8:
+        return t
+    if t.dtype == torch.bool:
+        return t.view(torch.uint8)  # same bytes (0/1), no copy
+    return t.to(torch.uint8)
 
 
 def _i32(t):

@@ -58,6 +58,11 @@ def build(jobs=None, debug=False, verbose=True):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"linking libmfa.so failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
+    missing = [ln.split()[-1] for ln in nm.splitlines() if "__device_stub__" in ln]
+    if missing:
+        raise RuntimeError(f"libmfa.so has undefined kernel stubs (kernel templates dropped by the host pass): "
+                           f"{missing[:3]}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -23,6 +23,9 @@ hipError_t launch_bsr_prepare(const int32_t*, const int32_t*, int, int, int, int
                               uint8_t*, int32_t*, int32_t*, hipStream_t);
 hipError_t launch_varlen_schedule(const int32_t*, const int32_t*, int, int, int, int, int, int, int32_t*, int32_t*,
                                   int32_t*, int32_t*, int, int32_t*, hipStream_t);
+hipError_t launch_bwd_preprocess(const BwdDev& p, int D, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdDev& p, const MaskDev& m, int D, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdDev& p, const MaskDev& m, int D, hipStream_t s);
 }  // namespace mfa
 
 using namespace mfa;
@@ -420,6 +423,99 @@ mfa_status mfa_attn_fwd(const mfa_attn_args* a, const mfa_mask* mk, float scale,
     if (p.total == 0) return ok();
     p.xcd_remap = (a->dtype == MFA_BF16) && (p.total % 8 == 0) ? 1 : 0;
     return hip_ok(launch_attn_fwd(a->dtype, a->D, BM, p, m, stream), "attention forward launch");
+}
+
+// ---- backward ----
+
+static mfa_status check_bwd(const mfa_attn_bwd_args* a, bool need_tensors) {
+    if (!a) return fail(MFA_E_ARG, "args is NULL");
+    MFA_TRY(check_attn_shapes(&a->fwd));
+    if (a->fwd.dtype != MFA_BF16) return fail(MFA_E_UNSUPPORTED, "the backward is built for bf16 only");
+    if (a->fwd.B == 0 || a->fwd.Sq == 0 || !need_tensors) return ok();
+    MFA_TRY(ensure_device());
+    MFA_TRY(dev_ptr(a->fwd.out, "out"));
+    MFA_TRY(dev_ptr(a->dout, "dout"));
+    MFA_TRY(dev_ptr(a->delta, "delta"));
+    MFA_TRY(check_strides("out", a->fwd.out, a->fwd.o_stride, MFA_BF16));
+    MFA_TRY(check_strides("dout", a->dout, a->do_stride, MFA_BF16));
+    return ok();
+}
+
+static void fill_bwd(const mfa_attn_bwd_args* a, float scale, BwdDev& p) {
+    std::memset(&p, 0, sizeof(p));
+    fill_fwd(&a->fwd, scale, p.f);
+    p.dout = a->dout;
+    p.dq = a->dq;
+    p.dk = a->dk;
+    p.dv = a->dv;
+    p.delta = a->delta;
+    p.dos0 = a->do_stride[0]; p.dos1 = a->do_stride[1]; p.dos2 = a->do_stride[2];
+    p.dqs0 = a->dq_stride[0]; p.dqs1 = a->dq_stride[1]; p.dqs2 = a->dq_stride[2];
+    p.dks0 = a->dk_stride[0]; p.dks1 = a->dk_stride[1]; p.dks2 = a->dk_stride[2];
+    p.dvs0 = a->dv_stride[0]; p.dvs1 = a->dv_stride[1]; p.dvs2 = a->dv_stride[2];
+}
+
+static mfa_status check_bwd_mask(const mfa_attn_bwd_args* a, const mfa_mask* mk, bool csc, MaskDev& m) {
+    if (!mk) return fail(MFA_E_ARG, "mask is NULL");
+    if (mk->kind != MFA_MASK_BSR)
+        return fail(MFA_E_UNSUPPORTED, "the backward is built for BSR masks (kind %d given)", mk->kind);
+    int BM = 0;
+    MFA_TRY(fill_mask(&a->fwd, mk, m, BM));
+    MFA_TRY(dev_ptr(mk->indptr, "indptr"));
+    MFA_TRY(dev_ptr(mk->indices, "indices"));
+    MFA_TRY(dev_ptr(mk->bsr_kind, "bsr_kind"));
+    if (csc) {
+        MFA_TRY(dev_ptr(mk->csc_ptr, "csc_ptr"));
+        MFA_TRY(dev_ptr(mk->csc_idx, "csc_idx"));
+    }
+    return ok();
+}
+
+mfa_status mfa_attn_bwd_preprocess(const mfa_attn_bwd_args* a, hipStream_t stream) {
+    MFA_TRY(check_bwd(a, true));
+    if (a->fwd.B == 0 || a->fwd.Sq == 0) return ok();
+    BwdDev p;
+    fill_bwd(a, 1.f, p);
+    return hip_ok(launch_bwd_preprocess(p, a->fwd.D, stream), "backward preprocess launch");
+}
+
+static mfa_status bwd_common(const mfa_attn_bwd_args* a, const mfa_mask* mk, float scale, bool csc, BwdDev& p,
+                             MaskDev& m) {
+    MFA_TRY(check_bwd(a, true));
+    if (!(scale == scale) || scale == 0.f) return fail(MFA_E_ARG, "scale must be a nonzero number");
+    if (a->fwd.B == 0 || a->fwd.Sq == 0) return ok();
+    MFA_TRY(dev_ptr(a->fwd.q, "q"));
+    MFA_TRY(dev_ptr(a->fwd.k, "k"));
+    MFA_TRY(dev_ptr(a->fwd.v, "v"));
+    MFA_TRY(dev_ptr(a->fwd.lse, "lse"));
+    MFA_TRY(check_strides("q", a->fwd.q, a->fwd.q_stride, MFA_BF16));
+    MFA_TRY(check_strides("k", a->fwd.k, a->fwd.k_stride, MFA_BF16));
+    MFA_TRY(check_strides("v", a->fwd.v, a->fwd.v_stride, MFA_BF16));
+    MFA_TRY(check_bwd_mask(a, mk, csc, m));
+    fill_bwd(a, scale, p);
+    return ok();
+}
+
+mfa_status mfa_attn_bwd_dkdv(const mfa_attn_bwd_args* a, const mfa_mask* mk, float scale, hipStream_t stream) {
+    BwdDev p;
+    MaskDev m;
+    MFA_TRY(bwd_common(a, mk, scale, true, p, m));
+    if (a->fwd.B == 0 || a->fwd.Sq == 0) return ok();
+    MFA_TRY(dev_ptr(a->dk, "dk"));
+    MFA_TRY(dev_ptr(a->dv, "dv"));
+    MFA_TRY(check_strides("dk", a->dk, a->dk_stride, MFA_BF16));
+    MFA_TRY(check_strides("dv", a->dv, a->dv_stride, MFA_BF16));
+    return hip_ok(launch_bwd_dkdv(p, m, a->fwd.D, stream), "backward dK/dV launch");
+}
+
+mfa_status mfa_attn_bwd_dq(const mfa_attn_bwd_args* a, const mfa_mask* mk, float scale, hipStream_t stream) {
+    BwdDev p;
+    MaskDev m;
+    MFA_TRY(bwd_common(a, mk, scale, false, p, m));
+    if (a->fwd.B == 0 || a->fwd.Sq == 0) return ok();
+    MFA_TRY(dev_ptr(a->dq, "dq"));
+    MFA_TRY(check_strides("dq", a->dq, a->dq_stride, MFA_BF16));
+    return hip_ok(launch_bwd_dq(p, m, a->fwd.D, stream), "backward dQ launch");
 }
 
 }  // extern "C"

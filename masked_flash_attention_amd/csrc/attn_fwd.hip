@@ -51,6 +51,14 @@ struct KV {
 };
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Bits [0, n) set (n clamped to [0, 32]).
+__device__ __forceinline__ uint32_t below(int n) {
+    return n <= 0 ? 0u : (n >= 32 ? 0xFFFFFFFFu : ((1u << n) - 1u));
+}
 
 __device__ __forceinline__ bf16x4 ds_read_tr(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(__attribute__((address_space(3))) char*)(p));
@@ -65,8 +73,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
     constexpr int TILEB = KV<D>::TILEB;
     constexpr int NKC = D / 16;              // 16-wide d chunks of q.k
     constexpr int NDB = D / 32;              // 32-wide d blocks of O^T
-    constexpr int LOADS = kBN * CPR / NT;    // 16-byte chunks per thread per tile
-    static_assert(LOADS * NT == kBN * CPR, "tile must split evenly over the workgroup");
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* sK = smem;
@@ -106,33 +112,41 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
     float m_used = -INFINITY;
     float l_part = 0.f;
 
-    // ---- staging of K/V tiles: thread tid moves chunks id = i*NT + tid ----
-    const bf16* Kbh = K + (int64_t)t.b * p.ks0 + (int64_t)t.hk * p.ks2 + (int64_t)t.k_base * p.ks1;
-    const bf16* Vbh = V + (int64_t)t.b * p.vs0 + (int64_t)t.hk * p.vs2 + (int64_t)t.k_base * p.vs1;
-    u32x4 kr[LOADS], vr[LOADS];
-    auto load_tile = [&](int kt) {
+    // ---- staging of K/V tiles: direct global->LDS buffer loads ----
+    // One wave instruction moves 1 KB = RPI rows into a contiguous LDS block;
+    // lane l lands at byte 16*l of it, i.e. row RPI*i + l/CPR, physical chunk
+    // l%CPR, so it fetches the logical chunk that the swizzle puts there.
+    // Rows past the key length read as zeros (buffer range check).
+    constexpr int RPI = 1024 / ROWB;             // rows per wave instruction
+    constexpr int NI = kBN / RPI / NW;           // instructions per wave per tile (each of K, V)
+    static_assert(NI * RPI * NW == kBN, "tile rows must split evenly over the waves");
+    const char* Kbh = (const char*)K + 2 * ((int64_t)t.b * p.ks0 + (int64_t)t.hk * p.ks2 + (int64_t)t.k_base * p.ks1);
+    const char* Vbh = (const char*)V + 2 * ((int64_t)t.b * p.vs0 + (int64_t)t.hk * p.vs2 + (int64_t)t.k_base * p.vs1);
+    const int64_t krow = 2 * p.ks1, vrow = 2 * p.vs1;
+    const int64_t knrec = t.k_len > 0 ? (int64_t)(t.k_len - 1) * krow + ROWB : 0;
+    const int64_t vnrec = t.k_len > 0 ? (int64_t)(t.k_len - 1) * vrow + ROWB : 0;
+    int kgo[NI], vgo[NI];
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int id = i * NT + tid;
-            const int r = id / CPR, lc = id % CPR;
-            const int key = kt * kBN + r;
-            if (key < t.k_len) {
-                kr[i] = *(const u32x4*)(Kbh + (int64_t)key * p.ks1 + lc * 8);
-                vr[i] = *(const u32x4*)(Vbh + (int64_t)key * p.vs1 + lc * 8);
-            } else {
-                kr[i] = u32x4{0, 0, 0, 0};
-                vr[i] = u32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
+    for (int i = 0; i < NI; ++i) {
+        const int r = (wave * NI + i) * RPI + lane / CPR;
+        const int pc = lane % CPR;
+        kgo[i] = (int)(r * krow) + ((pc ^ KV<D>::k_swz(r)) << 4);
+        vgo[i] = (int)(r * vrow) + ((pc ^ KV<D>::v_swz(r)) << 4);
+    }
+    auto load_tile = [&](int kt, int buf) {
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer-resource builtins exist only in the device pass
+        const int64_t k0 = (int64_t)kt * kBN * krow, v0 = (int64_t)kt * kBN * vrow;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Kbh + k0), 0, (int)(knrec > k0 ? knrec - k0 : 0), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Vbh + v0), 0, (int)(vnrec > v0 ? vnrec - v0 : 0), 0x00020000);
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int id = i * NT + tid;
-            const int r = id / CPR, lc = id % CPR;
-            *(u32x4*)(sK + buf * TILEB + r * ROWB + ((lc ^ KV<D>::k_swz(r)) << 4)) = kr[i];
-            *(u32x4*)(sV + buf * TILEB + r * ROWB + ((lc ^ KV<D>::v_swz(r)) << 4)) = vr[i];
+        for (int i = 0; i < NI; ++i) {
+            const int blk = (wave * NI + i) * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sK + buf * TILEB + blk), 16, kgo[i], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sV + buf * TILEB + blk), 16, vgo[i], 0, 0, 0);
         }
+#endif
     };
 
     // Per-lane LDS offsets of the operand reads.
@@ -161,10 +175,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
 
     int it = t.begin, kt = 0, kind = 0;
     advance(it, kt, kind);
-    if (it < t.end) {
-        load_tile(kt);
-        store_tile(0);
-    }
+    if (it < t.end) load_tile(kt, 0);
+    wait_vmem();
     __syncthreads();
 
     const float c2 = p.c2;
@@ -173,7 +185,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
         int it_n = it + 1, kt_n = 0, kind_n = 0;
         advance(it_n, kt_n, kind_n);
         const bool has_next = it_n < t.end;
-        if (has_next) load_tile(kt_n);
+        if (has_next) load_tile(kt_n, buf ^ 1);  // buf^1 was released by the last barrier
 
         // ---- S^T = K Q^T ----
         f32x16 s[2];
@@ -190,45 +202,65 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
         }
 
         // ---- mask on partial or ragged tiles ----
+        // okw[kb] holds, at bit (r>>2)*8 + (r&3), whether score s[kb][r] (key
+        // offset kb*32 + (r>>2)*8 + 4*hh + (r&3) in the tile) is allowed.
         const bool ragged = (kt + 1) * kBN > t.k_len;
         if (kind == kTilePartial || ragged) {
-            uint32_t w0 = 0, w1 = 0;
+            uint32_t okw[2];
+            const int base_off = kt * kBN + 4 * hh;  // tile key index of bit 0 of okw[0]
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) okw[kb] = below(t.k_len - base_off - kb * 32);
             if constexpr (KIND == MFA_MASK_TILES) {
+                uint32_t w0 = 0, w1 = 0;
                 if (rm.row_ok) {
                     const uint32_t* fb = m.fine_bits + (int64_t)row * m.fine_words + 2 * kt;
                     w0 = fb[0];
                     if (2 * kt + 1 < m.fine_words) w1 = fb[1];
                 }
+                okw[0] &= w0 >> (4 * hh);
+                okw[1] &= w1 >> (4 * hh);
             } else if constexpr (KIND == MFA_MASK_BLOCKID) {
                 const uint32_t* kw = m.kv_bits + (int64_t)t.b * m.kv_words + 2 * kt;
-                w0 = kw[0];
-                if (2 * kt + 1 < m.kv_words) w1 = kw[1];
-            }
+                const uint32_t w0 = kw[0];
+                const uint32_t w1 = (2 * kt + 1 < m.kv_words) ? kw[1] : 0u;
+                okw[0] &= w0 >> (4 * hh);
+                okw[1] &= w1 >> (4 * hh);
+                const int32_t* kbp = m.k_blk + (int64_t)t.b * p.Sk;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+                for (int kb = 0; kb < 2; ++kb) {
+                    uint32_t cmp = 0;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int off = kb * 32 + (r >> 2) * 8 + 4 * hh + (r & 3);
-                    const int key = kt * kBN + off;
-                    bool ok = rm.row_ok && key < t.k_len;
-                    if constexpr (KIND == MFA_MASK_TILES) {
-                        ok = ok && (((kb ? w1 : w0) >> (off & 31)) & 1u);
-                    } else if constexpr (KIND == MFA_MASK_BLOCKID) {
-                        if (ok) {
-                            const int kbk = m.k_blk[(int64_t)t.b * p.Sk + key];
-                            ok = rm.qvalid && (((kb ? w1 : w0) >> (off & 31)) & 1u) && kbk <= rm.qblk;
+                    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int key = base_off + kb * 32 + g * 8 + e;
+                            const int kbk = key < t.k_len ? kbp[key] : INT32_MAX;
+                            cmp |= (kbk <= rm.qblk ? 1u : 0u) << (g * 8 + e);
                         }
-                    } else if constexpr (KIND == MFA_MASK_BSR) {
-                        ok = ok && (!m.causal || key <= row);
-                    } else if constexpr (KIND == MFA_MASK_VARLEN) {
-                        const int i = rm.qi_local;
-                        if (m.causal) ok = ok && key <= i;
-                        if (m.win_left >= 0) ok = ok && (i - key) <= m.win_left;
-                        if (m.win_right >= 0) ok = ok && (key - i) <= m.win_right;
                     }
-                    if (!ok) s[kb][r] = -INFINITY;
+                    okw[kb] &= rm.qvalid ? cmp : 0u;
+                }
+            } else if constexpr (KIND == MFA_MASK_BSR) {
+                if (m.causal) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) okw[kb] &= below(row - base_off - kb * 32 + 1);
+                }
+            } else if constexpr (KIND == MFA_MASK_VARLEN) {
+                const int i = rm.qi_local;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const int o = base_off + kb * 32;
+                    if (m.causal) okw[kb] &= below(i - o + 1);
+                    if (m.win_left >= 0) okw[kb] &= ~below(i - m.win_left - o);
+                    if (m.win_right >= 0) okw[kb] &= below(i + m.win_right - o + 1);
                 }
             }
+            if (!rm.row_ok) okw[0] = okw[1] = 0u;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    s[kb][r] = ((okw[kb] >> ((r >> 2) * 8 + (r & 3))) & 1u) ? s[kb][r] : -INFINITY;
         }
 
         // ---- online softmax ----
@@ -277,7 +309,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
             }
         }
 
-        if (has_next) store_tile(buf ^ 1);
+        wait_vmem();  // this wave's tile loads have landed in LDS
         __syncthreads();
         buf ^= 1;
         it = it_n;

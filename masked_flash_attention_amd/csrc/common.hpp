@@ -71,6 +71,20 @@ struct FwdDev {
     int xcd_remap;    // 1: logical id = (w % 8) * (total / 8) + w / 8
 };
 
+// Backward problem: the forward's tensors plus dO, dQ, dK, dV and delta.
+struct BwdDev {
+    FwdDev f;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* delta;
+    int64_t dos0, dos1, dos2;
+    int64_t dqs0, dqs1, dqs2;
+    int64_t dks0, dks1, dks2;
+    int64_t dvs0, dvs1, dvs2;
+};
+
 __device__ __forceinline__ int xcd_logical(int w, int total, int remap) {
     if (!remap) return w;
     return (w & 7) * (total >> 3) + (w >> 3);

@@ -3,7 +3,7 @@
 // All outputs are deterministic (no order-dependent atomics): prefix counts
 // come from wave ballots (v_mbcnt) and LDS block scans.
 
-#include "common.hpp"
+#include "sched.hpp"
 
 namespace mfa {
 
@@ -229,21 +229,46 @@ __global__ __launch_bounds__(256) void compact_tiles_kernel(const uint8_t* mask,
 }
 
 // CSR of non-empty tiles: one workgroup per query-tile row. The row offset is
-// the count of non-empty tiles in all earlier rows (recounted here, so no
-// workspace and no inter-workgroup ordering is needed).
+// the count of non-empty tiles in all earlier rows, recounted here from the
+// tile map (16 kinds per load), so no workspace and no inter-workgroup
+// ordering is needed.
+__device__ __forceinline__ int nonzero_bytes(uint32_t w) {
+    return __builtin_popcount((((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w) & 0x80808080u);
+}
+
+__device__ __forceinline__ int block_sum(int v, int* lds16) {
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    if (lane == 0) lds16[wave] = v;
+    __syncthreads();
+    int tot = 0;
+    for (int w = 0; w < nw; ++w) tot += lds16[w];
+    __syncthreads();
+    return tot;
+}
+
 __global__ __launch_bounds__(256) void compact_csr_kernel(const uint8_t* tile_kind, int nQt, int nKt,
                                                           int32_t* row_ptr, int32_t* col_idx, uint8_t* col_kind) {
-    __shared__ int lds[1024];
+    __shared__ int lds[16];
     const int qt = blockIdx.x;
-    const int64_t before_n = (int64_t)qt * nKt;
+    const int64_t nbytes = (int64_t)qt * nKt;
     int cnt = 0;
-    for (int64_t i = threadIdx.x; i < before_n; i += blockDim.x) cnt += tile_kind[i] != 0;
-    int tot;
-    block_exclusive_sum(cnt, &tot, lds);
-    const int base = tot;
+    const bool vec = (((uintptr_t)tile_kind) & 15) == 0;
+    int64_t done = 0;
+    if (vec) {
+        const int64_t nvec = nbytes >> 4;
+        const u32x4* p4 = (const u32x4*)tile_kind;
+        for (int64_t i = threadIdx.x; i < nvec; i += blockDim.x) {
+            const u32x4 w = p4[i];
+            cnt += nonzero_bytes(w[0]) + nonzero_bytes(w[1]) + nonzero_bytes(w[2]) + nonzero_bytes(w[3]);
+        }
+        done = nvec << 4;
+    }
+    for (int64_t i = done + threadIdx.x; i < nbytes; i += blockDim.x) cnt += tile_kind[i] != 0;
+    const int base = block_sum(cnt, lds);
     if (threadIdx.x == 0) row_ptr[qt] = base;
     int carry = 0;
-    const uint8_t* rowk = tile_kind + before_n;
+    const uint8_t* rowk = tile_kind + nbytes;
     for (int k0 = 0; k0 < nKt; k0 += blockDim.x) {
         const int kt = k0 + threadIdx.x;
         const uint8_t k = kt < nKt ? rowk[kt] : 0;
@@ -264,17 +289,6 @@ __global__ __launch_bounds__(256) void compact_csr_kernel(const uint8_t* tile_ki
 // parallel (a canonical row has distinct columns), so the CSC lists come out
 // ascending without atomics on the output.
 // ---------------------------------------------------------------------------
-
-__device__ __forceinline__ uint8_t bsr_kind_of(int r, int c, int qb, int kb, int Sq, int Skv, int causal) {
-    const int i0 = r * qb, i1 = min((r + 1) * qb, Sq) - 1;
-    const int j0 = c * kb, j1 = min((c + 1) * kb, Skv) - 1;
-    if (i1 < i0 || j1 < j0) return kTileEmpty;
-    const bool ragged = (i1 - i0 + 1 != qb) || (j1 - j0 + 1 != kb);
-    if (!causal) return ragged ? kTilePartial : kTileFull;
-    if (j0 > i1) return kTileEmpty;
-    if (j1 <= i0 && !ragged) return kTileFull;
-    return kTilePartial;
-}
 
 __global__ __launch_bounds__(256) void bsr_prepare_kernel(const int32_t* indptr, const int32_t* indices, int nQb,
                                                           int nKb, int64_t nnz, int qb, int kb, int Sq, int Skv, int causal,

@@ -107,6 +107,21 @@ __device__ __forceinline__ TileRange make_range(const FwdDev& p, const MaskDev& 
     }
 }
 
+// Kind of a listed BSR block (r, c) with qb x kb blocks: token-level causal
+// j <= i on global positions inside the block when `causal` (mask_type
+// "causal" of flashinfer block_sparse_attention); out-of-range positions are
+// not allowed, so a ragged block is never full.
+__host__ __device__ __forceinline__ int bsr_kind_of(int r, int c, int qb, int kb, int Sq, int Skv, int causal) {
+    const int i0 = r * qb, i1 = min((r + 1) * qb, Sq) - 1;
+    const int j0 = c * kb, j1 = min((c + 1) * kb, Skv) - 1;
+    if (i1 < i0 || j1 < j0) return kTileEmpty;
+    const bool ragged = (i1 - i0 + 1 != qb) || (j1 - j0 + 1 != kb);
+    if (!causal) return ragged ? kTilePartial : kTileFull;
+    if (j0 > i1) return kTileEmpty;
+    if (j1 <= i0 && !ragged) return kTileFull;
+    return kTilePartial;
+}
+
 // Block-id tile classification from the per-tile summaries {min, max, any, all}.
 __device__ __forceinline__ int classify_blockid(const int32_t* qs, const int32_t* ks) {
     const int qmin = qs[0], qmax = qs[1], qany = qs[2], qall = qs[3];
