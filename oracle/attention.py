@@ -158,3 +158,55 @@ def varlen_attention_fwd(q, k, v, cu_q, cu_k, scale, causal, left, right, rows=N
     allowed.heads = 1
     out, lse = attention_fwd(_f64(q)[None], _f64(k)[None], _f64(v)[None], allowed, scale, rows=rows)
     return out[0], lse[0]
+
+
+def attention_bwd_sampled(q, k, v, dout, allowed, scale, b, hk, rows, cols, chunk=1024):
+    """Selected rows of dQ and columns of dK/dV for one (batch, kv head), fp64.
+
+    Same formulas as ``attention_bwd`` evaluated without the dense (Sq, Sk)
+    matrices: the forward (O, LSE) of every query row of the group's heads is
+    computed in row chunks, then dQ_i (for i in ``rows``) uses row i's
+    P, dP and Delta, and dK_j / dV_j (for j in ``cols``) sum column j over all
+    query rows and all query heads of the group. ``allowed`` is a callable
+    ``allowed(b, hm, rows) -> (len(rows), Sk)`` (as for ``attention_fwd``).
+    Returns dq (G, len(rows), D) for the group's heads, dk (len(cols), D),
+    dv (len(cols), D).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    Hm = _mask_heads(allowed, Hq)
+    rows = np.asarray(rows)
+    cols = np.asarray(cols)
+    kk, vv = k[b, :, hk, :], v[b, :, hk, :]
+    dq = np.zeros((G, rows.size, D))
+    dk = np.zeros((cols.size, D))
+    dv = np.zeros((cols.size, D))
+    for g in range(G):
+        hq = hk * G + g
+        hm = hq * Hm // Hq
+        out, lse = attention_fwd(q[b:b + 1, :, hq:hq + 1], k[b:b + 1, :, hk:hk + 1], v[b:b + 1, :, hk:hk + 1],
+                                 lambda bb, h_, rr: allowed(b, hm, rr), scale, chunk=chunk)
+        L = lse[0, 0]
+        delta = (do[b, :, hq, :] * out[0, :, 0, :]).sum(axis=1)
+        qq, dd = q[b, :, hq, :], do[b, :, hq, :]
+        # dQ rows
+        a = np.asarray(allowed(b, hm, rows), dtype=bool)
+        s = scale * (qq[rows] @ kk.T)
+        fin = np.isfinite(L[rows])
+        P = np.where(a & fin[:, None], np.exp(s - np.where(fin, L[rows], 0.0)[:, None]), 0.0)
+        dP = dd[rows] @ vv.T
+        dq[g] = scale * ((P * (dP - delta[rows][:, None])) @ kk)
+        # dK / dV columns, all query rows in chunks
+        for c0 in range(0, Sq, chunk):
+            rr = np.arange(c0, min(c0 + chunk, Sq))
+            a = np.asarray(allowed(b, hm, rr), dtype=bool)[:, cols]
+            s = scale * (qq[rr] @ kk[cols].T)
+            fin = np.isfinite(L[rr])
+            P = np.where(a & fin[:, None], np.exp(s - np.where(fin, L[rr], 0.0)[:, None]), 0.0)
+            dP = dd[rr] @ vv[cols].T
+            dS = P * (dP - delta[rr][:, None])
+            dv += P.T @ dd[rr]
+            dk += scale * (dS.T @ qq[rr])
+    return dq, dk, dv

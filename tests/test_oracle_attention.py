@@ -183,3 +183,24 @@ def test_backward_equals_torch_autograd_sdpa():
     o.backward(torch.from_numpy(do.transpose(0, 2, 1, 3).copy()))
     for g, tt in zip((dq, dk, dv), t):
         np.testing.assert_allclose(g, tt.grad.numpy().transpose(0, 2, 1, 3), rtol=1e-11, atol=1e-12)
+
+
+def test_sampled_backward_equals_dense_backward():
+    rng = np.random.default_rng(50)
+    B, Sq, Sk, Hq, Hkv, D = 2, 40, 36, 4, 2, 8
+    q, k, v = _rand((B, Sq, Hq, D), 51), _rand((B, Sk, Hkv, D), 52), _rand((B, Sk, Hkv, D), 53)
+    do = _rand((B, Sq, Hq, D), 54)
+    mask = rng.random((B, Hkv, Sq, Sk)) < 0.5
+    mask[:, :, 7] = False  # empty rows
+    dq, dk, dv, *_ = A.attention_bwd(q, k, v, do, mask, 0.3)
+
+    def allowed(b, hm, rr):
+        return mask[b, hm][rr]
+    allowed.heads = Hkv
+    rows, cols = np.array([0, 7, 39]), np.array([1, 17, 35])
+    for b in range(B):
+        for hk in range(Hkv):
+            sq, sk, sv = A.attention_bwd_sampled(q, k, v, do, allowed, 0.3, b, hk, rows, cols, chunk=16)
+            np.testing.assert_allclose(sq, dq[b][rows][:, hk * 2:hk * 2 + 2].transpose(1, 0, 2), rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(sk, dk[b, cols, hk], rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(sv, dv[b, cols, hk], rtol=1e-10, atol=1e-12)
