@@ -189,10 +189,13 @@ def main():
         mfa.attn_fwd(q, k, v, rep, scale, "bhsd", out=out, lse=lse)
 
     if a.copy_calibration:
+        # a plain device copy of exactly q.nbytes (268 MB) read + written, so that
+        # rocprofv3 FETCH_SIZE / WRITE_SIZE of the attention kernel can be scaled
         dst = torch.empty_like(q)
         for _ in range(3):
             dst.copy_(q)
         torch.cuda.synchronize()
+        log(f"copy calibration: {q.numel() * q.element_size()} bytes per copy")
 
     # sampled parity of this very launch against the oracle
     from oracle import attention as A

@@ -287,3 +287,63 @@ def test_error_paths_on_device():
     with pytest.raises(mfa.MfaError) as e:
         mfa.attn_fwd(q.half(), q.half(), q.half(), mfa.MaskRep.none())
     assert e.value.status_name == "MFA_E_DTYPE"
+
+
+# --- edge cases ----------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_no_keys_gives_empty_rows(dtype):
+    note(f"edge Sk=0 {dtype}")
+    q = to_dev(W.tensors(60, [(2, 5, 2, 64)])[0], dtype)
+    k = torch.zeros(2, 0, 2, 64, dtype=dtype, device=DEV)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((2, 2, 5), float("nan"), device=DEV)
+    mfa.attn_fwd(q, k, k, mfa.MaskRep.none(), 0.125, "bshd", out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 0) and torch.isneginf(lse).all()
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1), (1, 1, 1, 65), (3, 129, 2, 1), (1, 63, 1, 64), (2, 200, 3, 300)])
+def test_odd_sizes_none_and_tiles(shape):
+    B, Sq, H, Sk = shape
+    note(f"edge odd sizes {shape}")
+    D = 128
+    q, k, v = _inputs((B, Sq, H, D), (B, Sk, H, D), 61 + Sq, torch.bfloat16)
+    for rep, m in ((mfa.MaskRep.none(), np.ones((Sq, Sk), bool)),
+                   (None, W.random_dense_mask(Sq, Sk, 0.5, seed=Sq))):
+        if rep is None:
+            rep = mfa.MaskRep.tiles(mfa.compact_dense_mask(to_dev(m)))
+        out, lse = _run(q, k, v, rep, 0.09, "bshd", torch.bfloat16)
+        ro, rl = A.attention_fwd(f64(q), f64(k), f64(v), m[None, None], 0.09)
+        compare_attention(f64(out), f64(lse), ro, rl, BF16_OUT_TOL)
+
+
+def test_strided_views():
+    """q/k/v/out as non-contiguous views (head-dim contiguous): a slice of a
+    larger head axis and a permuted (B, H, S, D) tensor read as (B, S, H, D)."""
+    note("edge strided views")
+    B, S, H, D = 2, 190, 3, 64
+    big = W.tensors(62, [(B, S, 2 * H, D)])[0].to(DEV)
+    q = big[:, :, 1::2]  # every other head
+    k, v = (W.tensors(63, [(B, H, S, D)])[0].to(DEV).permute(0, 2, 1, 3) for _ in range(2))
+    out = torch.full((B, S, 2 * H, D), float("nan"), dtype=torch.bfloat16, device=DEV)[:, :, ::2]
+    lse = torch.empty(B, H, S, device=DEV)
+    m = np.tri(S, S, dtype=bool)
+    rep = mfa.MaskRep.tiles(mfa.compact_dense_mask(to_dev(m)))
+    mfa.attn_fwd(q, k, v, rep, 0.125, "bshd", out=out, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = A.attention_fwd(f64(q), f64(k), f64(v), m[None, None], 0.125)
+    compare_attention(f64(out), f64(lse), ro, rl, BF16_OUT_TOL)
+
+
+def test_varlen_all_empty_sequences_and_single_tokens():
+    note("edge varlen zeros and ones")
+    L = np.array([0, 1, 0, 1, 2, 0], np.int32)
+    T = int(L.sum())
+    q, k, v = _inputs((T, 2, 64), (T, 2, 64), 64, torch.bfloat16)
+    s = mfa.varlen_schedule(to_dev(L), causal=True, window=(-1, -1), work_cap=T // 128 + L.size)
+    rep = mfa.MaskRep.varlen(s, 2, 2, causal=True)
+    out, lse = _run(q, k, v, rep, 0.125, "thd", torch.bfloat16)
+    cu = M.cu_seqlens(L)
+    ro, rl = A.varlen_attention_fwd(f64(q), f64(k), f64(v), cu, cu, 0.125, True, -1, -1)
+    compare_attention(f64(out), f64(lse), ro, rl, BF16_OUT_TOL)
