@@ -92,6 +92,91 @@ def cpu_baseline(w, tile_flops_per_bh, seconds):
                       f"dense masked softmax ({dt:.1f} s); attended-tile FLOPs of the sample over that time"}
 
 
+def _time(fn, reps=10, warm=2):
+    for _ in range(warm):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+
+def _tiles_blockid(qsum, ksum):
+    """Non-empty 128x64 tiles per batch entry from the GPU's block-id summaries."""
+    q = qsum.cpu().numpy().astype(np.int64)
+    k = ksum.cpu().numpy().astype(np.int64)
+    empty = (q[:, :, None, 2] == 0) | (k[:, None, :, 2] == 0) | (k[:, None, :, 0] > q[:, :, None, 1])
+    return int((~empty).sum())
+
+
+def rows_section(dev):
+    """Time each scope row's kernels on its own workload (ms/call, TFLOP/s over attended tiles)."""
+    import masked_flash_attention_amd as mfa
+    import workloads as W
+    out = {}
+    # a1/a2 + a6 on the block-causal tiny and the GQA + cross workloads
+    for name, w, nc in (("blockcausal_tiny_N256", W.blockcausal_tiny(), None),
+                        ("blockcausal_gqa_cross_N1024", W.blockcausal_gqa_cross(), 256)):
+        pad = torch.from_numpy(w["pad"]).to(dev)
+        att = torch.from_numpy(w["att"]).to(dev)
+        cross = None if nc is None else torch.from_numpy(w["cross_pad"]).to(dev)
+        ids_ms = _time(lambda: mfa.make_block_ids(pad, att, nc, cross))
+        ids = mfa.make_block_ids(pad, att, nc, cross)
+        sum_ms = _time(lambda: mfa.blockid_tile_summary(*ids))
+        summ = mfa.blockid_tile_summary(*ids)
+        rep = mfa.MaskRep.blockid(*ids, summary=summ)
+        q, k, v = (w[x].to(dev) for x in "qkv")
+        o = torch.empty_like(q)
+        fwd_ms = _time(lambda: mfa.attn_fwd(q, k, v, rep, w["scale"], "bshd", out=o))
+        B, Sq, Hq, D = q.shape
+        tiles = _tiles_blockid(summ[0], summ[1]) * Hq
+        out[name] = {"block_ids_ms": round(ids_ms, 4), "tile_summary_ms": round(sum_ms, 4),
+                     "fwd_ms": round(fwd_ms, 4),
+                     "fwd_tflops_attended_tiles": round(4.0 * 128 * 64 * D * tiles / fwd_ms / 1e9, 1)}
+    # a5 + a6 on varlen
+    w = W.varlen_window()
+    L = torch.from_numpy(w["lengths"]).to(dev)
+    T = int(w["lengths"].sum())
+    cap = T // 128 + len(w["lengths"])
+    sched_ms = _time(lambda: mfa.varlen_schedule(L, causal=True, window=(511, 0), work_cap=cap))
+    sch = mfa.varlen_schedule(L, causal=True, window=(511, 0), work_cap=cap)
+    Lmax = int(w["lengths"].max())
+    rep = mfa.MaskRep.varlen(sch, Lmax, Lmax, causal=True, window=(511, 0))
+    q, k, v = (w[x].to(dev) for x in "qkv")
+    o = torch.empty_like(q)
+    fwd_ms = _time(lambda: mfa.attn_fwd(q, k, v, rep, w["scale"], "thd", out=o))
+    tiles = 0
+    for Ls in w["lengths"].tolist():
+        for q0 in range(0, Ls, 128):
+            q1 = min(q0 + 128, Ls) - 1
+            tiles += q1 // 64 - max(0, q0 - 511) // 64 + 1
+    out["varlen_window_32seq"] = {"schedule_ms": round(sched_ms, 4), "fwd_ms": round(fwd_ms, 4),
+                                  "fwd_tflops_attended_tiles": round(4.0 * 128 * 64 * 64 * tiles * 16 / fwd_ms / 1e9, 1)}
+    # a4 + a6 + a9 on BSR
+    w = W.bsr_random()
+    N = 16384
+    ip, ix = torch.from_numpy(w["indptr"]).to(dev), torch.from_numpy(w["indices"]).to(dev)
+    prep_ms = _time(lambda: mfa.bsr_prepare(ip, ix, 64, 64, N, N, True))
+    kind, cp, ci = mfa.bsr_prepare(ip, ix, 64, 64, N, N, True)
+    rep = mfa.MaskRep.bsr(ip, ix, kind, causal=True, csc_ptr=cp, csc_idx=ci)
+    q, k, v, do = (w[x].to(dev) for x in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty(2, 16, N, device=dev)
+    fwd_ms = _time(lambda: mfa.attn_fwd(q, k, v, rep, w["scale"], "bshd", out=o, lse=lse))
+    bwd_ms = _time(lambda: mfa.attn_bwd(q, k, v, o, lse, do, rep, w["scale"], "bshd"), reps=5)
+    tiles = int((kind != 0).sum().item())
+    f = 4.0 * 64 * 64 * 128 * tiles
+    out["bsr_causal_N16384"] = {"bsr_prepare_ms": round(prep_ms, 4), "fwd_ms": round(fwd_ms, 4),
+                                "fwd_tflops_attended_tiles": round(f / fwd_ms / 1e9, 1),
+                                "bwd_ms": round(bwd_ms, 4),
+                                "bwd_tflops_algorithmic": round(2.5 * f / bwd_ms / 1e9, 1),
+                                "bwd_tflops_executed": round(3.5 * f / bwd_ms / 1e9, 1)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +185,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-skip-check", action="store_true")
+    ap.add_argument("--rows", action="store_true",
+                    help="also time every scope row on its own workload (adds a 'rows' object)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of q (268 MB) for HBM counter calibration")
     a = ap.parse_args()
@@ -245,6 +332,9 @@ def main():
         "parity": parity,
         "kernel_source_sha": kernel_source_hash(),
     }
+    if a.rows:
+        log("per-row timings")
+        result["rows"] = rows_section(dev)
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(w, tile_flops / (B * H), a.cpu_seconds)
