@@ -53,6 +53,8 @@ struct KV {
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Wait for every vector-memory operation of this wave (the K/V tile loads
+// into LDS included).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Bits [0, n) set (n clamped to [0, 32]).
@@ -62,6 +64,64 @@ __device__ __forceinline__ uint32_t below(int n) {
 
 __device__ __forceinline__ bf16x4 ds_read_tr(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(__attribute__((address_space(3))) char*)(p));
+}
+
+// Sets the scores of disallowed keys of key tile kt to -inf. Register r of
+// s[kb] holds key kb*32 + (r>>2)*8 + 4*hh + (r&3) of the tile (query = this
+// lane's row); okw[kb] collects, at bit (r>>2)*8 + (r&3), whether that key is
+// allowed. fw: the row's two fine-bit words of the tile (dense-tile masks).
+template <int KIND>
+__device__ __forceinline__ void mask_scores(const FwdDev& p, const MaskDev& m, const TileRange& t,
+                                            const RowMask<KIND>& rm, int row, int hh, int kt,
+                                            const uint32_t (&fw)[2], f32x16 (&s)[2]) {
+    uint32_t okw[2];
+    const int base_off = kt * kBN + 4 * hh;  // tile key index of bit 0 of okw[0]
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) okw[kb] = below(t.k_len - base_off - kb * 32);
+    if constexpr (KIND == MFA_MASK_TILES) {
+        okw[0] &= fw[0] >> (4 * hh);
+        okw[1] &= fw[1] >> (4 * hh);
+    } else if constexpr (KIND == MFA_MASK_BLOCKID) {
+        const uint32_t* kw = m.kv_bits + (int64_t)t.b * m.kv_words + 2 * kt;
+        const uint32_t w0 = kw[0];
+        const uint32_t w1 = (2 * kt + 1 < m.kv_words) ? kw[1] : 0u;
+        okw[0] &= w0 >> (4 * hh);
+        okw[1] &= w1 >> (4 * hh);
+        const int32_t* kbp = m.k_blk + (int64_t)t.b * p.Sk;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            uint32_t cmp = 0;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int key = base_off + kb * 32 + g * 8 + e;
+                    const int kbk = key < t.k_len ? kbp[key] : INT32_MAX;
+                    cmp |= (kbk <= rm.qblk ? 1u : 0u) << (g * 8 + e);
+                }
+            }
+            okw[kb] &= rm.qvalid ? cmp : 0u;
+        }
+    } else if constexpr (KIND == MFA_MASK_BSR) {
+        if (m.causal) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) okw[kb] &= below(row - base_off - kb * 32 + 1);
+        }
+    } else if constexpr (KIND == MFA_MASK_VARLEN) {
+        const int i = rm.qi_local;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int o = base_off + kb * 32;
+            if (m.causal) okw[kb] &= below(i - o + 1);
+            if (m.win_left >= 0) okw[kb] &= ~below(i - m.win_left - o);
+            if (m.win_right >= 0) okw[kb] &= below(i + m.win_right - o + 1);
+        }
+    }
+    if (!rm.row_ok) okw[0] = okw[1] = 0u;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = ((okw[kb] >> ((r >> 2) * 8 + (r & 3))) & 1u) ? s[kb][r] : -INFINITY;
 }
 
 template <int D, int NW, int KIND>
@@ -133,13 +193,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
         kgo[i] = (int)(r * krow) + ((pc ^ KV<D>::k_swz(r)) << 4);
         vgo[i] = (int)(r * vrow) + ((pc ^ KV<D>::v_swz(r)) << 4);
     }
-    auto load_tile = [&](int kt, int buf) {
+    // `live` false issues the same loads with an empty range (they write
+    // zeros into the free buffer), which keeps the loop free of a branch.
+    auto load_tile = [&](int kt, int buf, bool live) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer-resource builtins exist only in the device pass
         const int64_t k0 = (int64_t)kt * kBN * krow, v0 = (int64_t)kt * kBN * vrow;
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(Kbh + k0), 0, (int)(knrec > k0 ? knrec - k0 : 0), 0x00020000);
+            (void*)(Kbh + k0), 0, (int)(live && knrec > k0 ? knrec - k0 : 0), 0x00020000);
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(Vbh + v0), 0, (int)(vnrec > v0 ? vnrec - v0 : 0), 0x00020000);
+            (void*)(Vbh + v0), 0, (int)(live && vnrec > v0 ? vnrec - v0 : 0), 0x00020000);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int blk = (wave * NI + i) * 1024;
@@ -165,27 +227,42 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
         voff[db] = vr0 * ROWB + (((col >> 3) ^ KV<D>::v_swz(vr0)) << 4) + ((col >> 2) & 1) * 8;
     }
 
-    auto advance = [&](int& it, int& kt, int& kind) {
-        while (it < t.end) {
-            tile_at<KIND, BM>(p, m, t, it, kt, kind);
-            if (kind != kTileEmpty) return;
-            ++it;
+    TileCursor<KIND, BM> cursor;
+    cursor.init(p, m, t, lane);
+    auto advance = [&](int& it, int& kt, int& kind) { cursor.seek(p, m, t, lane, it, kt, kind); };
+
+    // Dense-tile masks: the two fine-bit words of this lane's row for a
+    // partial (or ragged) tile, loaded one tile ahead together with that
+    // tile's K/V, so that the mask never waits on a load of its own.
+    auto fine_words = [&](int kt_, int kind_, uint32_t (&w)[2]) {
+        w[0] = w[1] = 0u;
+        if constexpr (KIND == MFA_MASK_TILES) {
+            if (__builtin_expect(rm.row_ok && (kind_ == kTilePartial || (kt_ + 1) * kBN > t.k_len), 0)) {
+                const uint32_t* fb = m.fine_bits + (int64_t)row * m.fine_words + 2 * kt_;
+                w[0] = fb[0];
+                if (2 * kt_ + 1 < m.fine_words) w[1] = fb[1];
+            }
         }
     };
 
     int it = t.begin, kt = 0, kind = 0;
     advance(it, kt, kind);
-    if (it < t.end) load_tile(kt, 0);
+    uint32_t fw[2];
+    fine_words(kt, kind, fw);
+    if (it < t.end) load_tile(kt, 0, true);
     wait_vmem();
     __syncthreads();
 
     const float c2 = p.c2;
     int buf = 0;
-    while (it < t.end) {
-        int it_n = it + 1, kt_n = 0, kind_n = 0;
+    if (it < t.end) do {
+        int it_n = it + 1, kt_n = kt, kind_n = kTileEmpty;
         advance(it_n, kt_n, kind_n);
         const bool has_next = it_n < t.end;
-        if (has_next) load_tile(kt_n, buf ^ 1);  // buf^1 was released by the last barrier
+        if (!has_next) kt_n = kt, kind_n = kTileEmpty;
+        uint32_t fw_n[2];
+        fine_words(kt_n, kind_n, fw_n);
+        load_tile(kt_n, buf ^ 1, has_next);  // buf^1 was released by the last barrier
 
         // ---- S^T = K Q^T ----
         f32x16 s[2];
@@ -202,77 +279,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
         }
 
         // ---- mask on partial or ragged tiles ----
-        // okw[kb] holds, at bit (r>>2)*8 + (r&3), whether score s[kb][r] (key
-        // offset kb*32 + (r>>2)*8 + 4*hh + (r&3) in the tile) is allowed.
-        const bool ragged = (kt + 1) * kBN > t.k_len;
-        if (kind == kTilePartial || ragged) {
-            uint32_t okw[2];
-            const int base_off = kt * kBN + 4 * hh;  // tile key index of bit 0 of okw[0]
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) okw[kb] = below(t.k_len - base_off - kb * 32);
-            if constexpr (KIND == MFA_MASK_TILES) {
-                uint32_t w0 = 0, w1 = 0;
-                if (rm.row_ok) {
-                    const uint32_t* fb = m.fine_bits + (int64_t)row * m.fine_words + 2 * kt;
-                    w0 = fb[0];
-                    if (2 * kt + 1 < m.fine_words) w1 = fb[1];
-                }
-                okw[0] &= w0 >> (4 * hh);
-                okw[1] &= w1 >> (4 * hh);
-            } else if constexpr (KIND == MFA_MASK_BLOCKID) {
-                const uint32_t* kw = m.kv_bits + (int64_t)t.b * m.kv_words + 2 * kt;
-                const uint32_t w0 = kw[0];
-                const uint32_t w1 = (2 * kt + 1 < m.kv_words) ? kw[1] : 0u;
-                okw[0] &= w0 >> (4 * hh);
-                okw[1] &= w1 >> (4 * hh);
-                const int32_t* kbp = m.k_blk + (int64_t)t.b * p.Sk;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    uint32_t cmp = 0;
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int key = base_off + kb * 32 + g * 8 + e;
-                            const int kbk = key < t.k_len ? kbp[key] : INT32_MAX;
-                            cmp |= (kbk <= rm.qblk ? 1u : 0u) << (g * 8 + e);
-                        }
-                    }
-                    okw[kb] &= rm.qvalid ? cmp : 0u;
-                }
-            } else if constexpr (KIND == MFA_MASK_BSR) {
-                if (m.causal) {
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) okw[kb] &= below(row - base_off - kb * 32 + 1);
-                }
-            } else if constexpr (KIND == MFA_MASK_VARLEN) {
-                const int i = rm.qi_local;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const int o = base_off + kb * 32;
-                    if (m.causal) okw[kb] &= below(i - o + 1);
-                    if (m.win_left >= 0) okw[kb] &= ~below(i - m.win_left - o);
-                    if (m.win_right >= 0) okw[kb] &= below(i + m.win_right - o + 1);
-                }
-            }
-            if (!rm.row_ok) okw[0] = okw[1] = 0u;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    s[kb][r] = ((okw[kb] >> ((r >> 2) * 8 + (r & 3))) & 1u) ? s[kb][r] : -INFINITY;
-        }
+        if (__builtin_expect(kind == kTilePartial || (kt + 1) * kBN > t.k_len, 0))
+            mask_scores<KIND>(p, m, t, rm, row, hh, kt, fw, s);
 
         // ---- online softmax ----
-        float mx = -INFINITY;
+        // Row max and row sum as 4 independent chains each (short dependency
+        // chains: a single wave issues them back to back).
+        float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], s[kb][r]);
+        float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
         mx = max_both_halves(mx);
         const float m_new = fmaxf(m_used, mx);
         const bool need = (m_new - m_used) * c2 > kTau;  // false when both are -inf
-        if (__builtin_amdgcn_ballot_w64(need)) {
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
             const float alpha = need ? fast_exp2((m_used - m_new) * c2) : 1.f;
             m_used = need ? m_new : m_used;
             l_part *= alpha;
@@ -283,7 +305,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
         }
         const float mb = (m_used == -INFINITY) ? 0.f : m_used * c2;
         bf16x8 pb[4];
-        float rs = 0.f;
+        float rs4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -291,10 +313,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float pv = fast_exp2(fmaf(s[kb][gp * 8 + e], c2, -mb));
-                    rs += pv;
+                    rs4[e & 3] += pv;
                     pb[kb * 2 + gp][e] = (bf16)pv;
                 }
-        l_part += rs;
+        l_part += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
 
         // ---- O^T += V^T P^T ----
         const char* vb_ = sV + buf * TILEB;
@@ -315,7 +337,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
         it = it_n;
         kt = kt_n;
         kind = kind_n;
-    }
+        fw[0] = fw_n[0];
+        fw[1] = fw_n[1];
+    } while (it < t.end);
 
     // ---- epilogue ----
     const float l_tot = sum_both_halves(l_part);

@@ -161,6 +161,76 @@ __device__ __forceinline__ void tile_at(const FwdDev& p, const MaskDev& m, const
     }
 }
 
+// Walks the non-empty key tiles of a query tile 64 list entries at a time.
+// Lane l of the wave holds entry (base + l) packed as kt | kind << 28, and a
+// ballot marks the non-empty lanes, so stepping to the next tile is a bit
+// scan plus v_readlane rather than a dependent global load per tile. The
+// window after the current one is requested when the current one is entered,
+// so its latency overlaps at least one tile of work. All members are
+// wave-uniform except the two packed entry registers.
+template <int KIND, int BM>
+struct TileCursor {
+    int base;       // list position held by lane 0 of `cur`
+    uint32_t cur;   // this lane's entry of the current window
+    uint32_t nxt;   // this lane's entry of the following window
+    uint64_t nz;    // lanes of `cur` holding a non-empty tile
+
+    __device__ static __forceinline__ uint32_t fetch(const FwdDev& p, const MaskDev& m, const TileRange& t,
+                                                     int pos) {
+        if (pos >= t.end) return 0u;
+        int kt, kind;
+        tile_at<KIND, BM>(p, m, t, pos, kt, kind);
+        return (uint32_t)kt | ((uint32_t)kind << 28);
+    }
+
+    __device__ __forceinline__ void init(const FwdDev& p, const MaskDev& m, const TileRange& t, int lane) {
+        base = t.begin;
+        cur = fetch(p, m, t, base + lane);
+        nxt = fetch(p, m, t, base + 64 + lane);
+        nz = __builtin_amdgcn_ballot_w64((cur >> 28) != 0u);
+    }
+
+    // First non-empty tile at list position >= it; it >= t.end when none.
+    // The common case, a later entry of the current window, takes one
+    // (rarely taken) branch.
+    __device__ __forceinline__ void seek(const FwdDev& p, const MaskDev& m, const TileRange& t, int lane, int& it,
+                                         int& kt, int& kind) {
+        const int idx = it - base;
+        const uint64_t rest = idx < 64 ? (nz >> idx) : 0ull;
+        if (__builtin_expect(rest != 0ull, 1)) {
+            it += (int)__builtin_ctzll(rest);
+            const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)cur, it - base);
+            kt = (int)(e & 0x0FFFFFFFu);
+            kind = (int)(e >> 28);
+            return;
+        }
+        seek_slow(p, m, t, lane, it, kt, kind);
+    }
+
+    __device__ void seek_slow(const FwdDev& p, const MaskDev& m, const TileRange& t, int lane, int& it, int& kt,
+                              int& kind) {
+        while (it < t.end) {
+            const int idx = it - base;
+            if (idx < 64) {
+                const uint64_t rest = nz >> idx;
+                if (rest) {
+                    it += (int)__builtin_ctzll(rest);
+                    const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)cur, it - base);
+                    kt = (int)(e & 0x0FFFFFFFu);
+                    kind = (int)(e >> 28);
+                    return;
+                }
+                it = base + 64;
+                continue;
+            }
+            base += 64;
+            cur = nxt;
+            nxt = fetch(p, m, t, base + 64 + lane);
+            nz = __builtin_amdgcn_ballot_w64((cur >> 28) != 0u);
+        }
+    }
+};
+
 // Per-row mask state for one query row (one lane's query in the MFMA kernel).
 template <int KIND>
 struct RowMask {
