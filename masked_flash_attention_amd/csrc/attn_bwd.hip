@@ -185,10 +185,14 @@ __global__ __launch_bounds__(128, 1) void bwd_dkdv_kernel(BwdDev p, MaskDev m) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) trq[j][db] = tr_off<D>(8 * j + 4 * hh, db, lane);
 
+    // CSC entries of this key block, read through a register window
+    auto fetch_r = [&](int i) { return i < len ? (uint32_t)m.csc_idx[e0 + i] : 0u; };
+    ListWindow win;
+    win.init(fetch_r, 0, lane);
     auto item = [&](int it, int& hq, int& r) {
         const int g = it / len;
         hq = hk * f.G + g;
-        r = m.csc_idx[e0 + (it - g * len)];
+        r = (int)win.get(fetch_r, it - g * len, lane);
     };
     auto stage = [&](int it, int buf) {
         int hq, r;
@@ -344,12 +348,18 @@ __global__ __launch_bounds__(128, 2) void bwd_dq_kernel(BwdDev p, MaskDev m) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) trk[j][db] = tr_off<D>(8 * j + 4 * hh, db, lane);
 
+    // BSR row entries (block index | kind << 28), read through a register window
+    auto fetch_e = [&](int e) {
+        return e < end ? (uint32_t)m.indices[e] | ((uint32_t)m.bsr_kind[e] << 28) : 0u;
+    };
+    ListWindow win;
+    win.init(fetch_e, beg, lane);
     auto next = [&](int e) {
-        while (e < end && m.bsr_kind[e] == kTileEmpty) ++e;
+        while (e < end && (win.get(fetch_e, e, lane) >> 28) == (uint32_t)kTileEmpty) ++e;
         return e;
     };
     auto stage = [&](int e, int buf) {
-        const int kb = m.indices[e];
+        const int kb = (int)(win.get(fetch_e, e, lane) & 0x0FFFFFFFu);
         stage_tile<D>(kbase, 2 * f.ks1, kb * 64, f.Sk, sK + buf * TILEB, wave, 2, lane);
         stage_tile<D>(vbase, 2 * f.vs1, kb * 64, f.Sk, sV + buf * TILEB, wave, 2, lane);
     };
@@ -360,10 +370,11 @@ __global__ __launch_bounds__(128, 2) void bwd_dq_kernel(BwdDev p, MaskDev m) {
     __syncthreads();
     int buf = 0;
     while (e < end) {
+        const uint32_t ent = win.get(fetch_e, e, lane);  // before next() moves the window on
+        const int kb = (int)(ent & 0x0FFFFFFFu);
+        const bool diag = m.causal && (int)(ent >> 28) == kTilePartial;
         const int en = next(e + 1);
         if (en < end) stage(en, buf ^ 1);
-        const int kb = m.indices[e];
-        const bool diag = m.causal && m.bsr_kind[e] == kTilePartial;
         const char* k_ = sK + buf * TILEB;
         const char* v_ = sV + buf * TILEB;
         f32x16 s[2], dp[2];

@@ -90,6 +90,37 @@ __device__ __forceinline__ int xcd_logical(int w, int total, int remap) {
     return (w & 7) * (total >> 3) + (w >> 3);
 }
 
+// 64 consecutive entries of a device list held one per lane of the wave,
+// with the following 64 already requested: get(pos) for a non-decreasing
+// wave-uniform pos is a v_readlane instead of a dependent global load.
+// fetch(pos) loads entry pos (or returns 0 past the end); moving backwards
+// or past the requested window reloads.
+struct ListWindow {
+    int base;
+    uint32_t cur, nxt;
+
+    template <class F>
+    __device__ __forceinline__ void init(const F& fetch, int pos, int lane) {
+        base = pos;
+        cur = fetch(pos + lane);
+        nxt = fetch(pos + 64 + lane);
+    }
+
+    template <class F>
+    __device__ __forceinline__ uint32_t get(const F& fetch, int pos, int lane) {
+        if (__builtin_expect(pos < base || pos - base >= 64, 0)) {
+            if (pos - base >= 64 && pos - base < 128) {
+                base += 64;
+                cur = nxt;
+                nxt = fetch(base + 64 + lane);
+            } else {
+                init(fetch, pos, lane);
+            }
+        }
+        return (uint32_t)__builtin_amdgcn_readlane((int)cur, pos - base);
+    }
+};
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
