@@ -265,6 +265,8 @@ typedef struct mfa_mask {
     int causal;
     int win_left;          /* VARLEN only; -1 = open */
     int win_right;         /* VARLEN only; -1 = open */
+    int nseq;              /* VARLEN: number of sequences (cu_q holds nseq + 1
+                              entries); read by the dK/dV backward pass */
 } mfa_mask;
 
 /* Fused masked attention forward: out = softmax(scale q k^T + mask) v per
@@ -273,12 +275,24 @@ typedef struct mfa_mask {
 mfa_status mfa_attn_fwd(const mfa_attn_args* args, const mfa_mask* mask, float scale,
                         hipStream_t stream);
 
-/* Backward, split as in the BinFlash method: a preprocessing pass, dK/dV over
- * key blocks, then dQ over query blocks. fwd holds q, k, v, out and lse (the
- * forward's outputs; lse required). dout/dq/dk/dv use the same stride
- * convention as fwd. delta (B, Hq, Sq) fp32 contiguous is written by the
+/* Backward, split as in the BinFlash method ("Efficiently Dispatching ...":
+ * dK/dV over key blocks, dQ over query blocks, with the same dispatch as the
+ * forward): a preprocessing pass, dK/dV over 64-key blocks, then dQ over
+ * query tiles. fwd holds q, k, v, out and lse (the forward's outputs; lse
+ * required). dout/dq/dk/dv use the same stride convention as fwd. delta
+ * (B, Hq, Sq) fp32 contiguous ((Hq, T) for VARLEN) is written by the
  * preprocess pass (delta_i = sum_d dout_id * out_id) and read by the others.
- * Built for BSR masks with q_block = kv_block = 64, bf16, D = 128 or 64. */
+ * bf16, D = 128 or 64, every mask kind. Per kind the passes read:
+ *   NONE     nothing;
+ *   TILES    dQ: row_ptr, col_idx, col_kind, fine_bits; dK/dV: tile_kind,
+ *            fine_bits;
+ *   BLOCKID  q_blk, k_blk, q_valid, qsum, ksum, kv_bits (summaries at
+ *            BM = 128, BN = 64);
+ *   BSR      dQ: indptr, indices, bsr_kind; dK/dV: csc_ptr, csc_idx
+ *            (q_block = kv_block = 64);
+ *   VARLEN   dQ: cu_q, cu_k, work; dK/dV: cu_q, cu_k and nseq. Key blocks
+ *            past max_k are not visited: a sequence longer than max_k or
+ *            max_q gets NaN gradients in the blocks that are and sets *err. */
 typedef struct mfa_attn_bwd_args {
     mfa_attn_args fwd;
     const void* dout;

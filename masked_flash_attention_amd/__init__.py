@@ -233,7 +233,8 @@ class MaskRep:
             t["err"] = err
         return MaskRep(_ffi.MASK_VARLEN, t, {"work_cap": sched["work_cap"], "max_q": int(max_q),
                                              "max_k": int(max_k), "causal": int(bool(causal)),
-                                             "win_left": int(window[0]), "win_right": int(window[1])})
+                                             "win_left": int(window[0]), "win_right": int(window[1]),
+                                             "nseq": int(sched["cu_q"].numel()) - 1})
 
     def to_c(self):
         m = _ffi.Mask()
@@ -348,7 +349,8 @@ def attn_bwd_dq(args, mask: MaskRep, scale):
 
 
 def attn_bwd(q, k, v, out, lse, dout, mask: MaskRep, scale=None, layout="bshd"):
-    """Two-pass backward: preprocess, dK/dV over key blocks, dQ over query blocks."""
+    """Two-pass backward (any mask kind): preprocess, dK/dV over key blocks,
+    dQ over query tiles. Returns (dq, dk, dv) shaped like q, k, v."""
     B, Sq, Sk, Hq, Hkv, D = _dims(q, k, layout)
     if scale is None:
         scale = D ** -0.5
@@ -359,3 +361,33 @@ def attn_bwd(q, k, v, out, lse, dout, mask: MaskRep, scale=None, layout="bshd"):
     attn_bwd_dkdv(a, mask, scale)
     attn_bwd_dq(a, mask, scale)
     return dq, dk, dv
+
+
+class _MaskedAttention(torch.autograd.Function):
+    """Forward and backward both run the library's kernels; the mask
+    representation and scale are constants of the graph."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, mask, scale, layout):
+        out, lse = attn_fwd(q, k, v, mask, scale, layout)
+        ctx.save_for_backward(q, k, v, out, lse)
+        ctx.mask, ctx.scale, ctx.layout = mask, scale, layout
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse = ctx.saved_tensors
+        if dout.stride(-1) != 1 or dout.data_ptr() % 16:
+            dout = dout.contiguous()
+        dq, dk, dv = attn_bwd(q, k, v, out, lse, dout, ctx.mask, ctx.scale, ctx.layout)
+        return dq, dk, dv, None, None, None
+
+
+def masked_attention(q, k, v, mask: MaskRep, scale=None, layout="bshd"):
+    """Differentiable masked attention: out = softmax(scale q k^T + mask) v.
+
+    bf16 q, k, v with requires_grad as needed; gradients come from the
+    two-pass backward (mfa_attn_bwd_*). layout as for attn_fwd."""
+    if scale is None:
+        scale = q.shape[-1] ** -0.5
+    return _MaskedAttention.apply(q, k, v, mask, float(scale), layout)

@@ -33,7 +33,7 @@ class Mask(C.Structure):
                 ("q_block", C.c_int), ("kv_block", C.c_int),
                 ("cu_q", vp), ("cu_k", vp), ("work", vp), ("work_cap", C.c_int), ("max_q", C.c_int),
                 ("max_k", C.c_int), ("err", vp),
-                ("causal", C.c_int), ("win_left", C.c_int), ("win_right", C.c_int)]
+                ("causal", C.c_int), ("win_left", C.c_int), ("win_right", C.c_int), ("nseq", C.c_int)]
 
 
 class BwdArgs(C.Structure):

@@ -455,18 +455,54 @@ static void fill_bwd(const mfa_attn_bwd_args* a, float scale, BwdDev& p) {
     p.dvs0 = a->dv_stride[0]; p.dvs1 = a->dv_stride[1]; p.dvs2 = a->dv_stride[2];
 }
 
-static mfa_status check_bwd_mask(const mfa_attn_bwd_args* a, const mfa_mask* mk, bool csc, MaskDev& m) {
+// Mask fields each backward pass reads (see mfa.h) and the derived sizes.
+static mfa_status check_bwd_mask(const mfa_attn_bwd_args* a, const mfa_mask* mk, bool dkdv, MaskDev& m,
+                                 int& BM) {
     if (!mk) return fail(MFA_E_ARG, "mask is NULL");
-    if (mk->kind != MFA_MASK_BSR)
-        return fail(MFA_E_UNSUPPORTED, "the backward is built for BSR masks (kind %d given)", mk->kind);
-    int BM = 0;
     MFA_TRY(fill_mask(&a->fwd, mk, m, BM));
-    MFA_TRY(dev_ptr(mk->indptr, "indptr"));
-    MFA_TRY(dev_ptr(mk->indices, "indices"));
-    MFA_TRY(dev_ptr(mk->bsr_kind, "bsr_kind"));
-    if (csc) {
-        MFA_TRY(dev_ptr(mk->csc_ptr, "csc_ptr"));
-        MFA_TRY(dev_ptr(mk->csc_idx, "csc_idx"));
+    m.tile_kind = mk->tile_kind;
+    m.nseq = mk->nseq;
+    switch (mk->kind) {
+        case MFA_MASK_NONE: break;
+        case MFA_MASK_BLOCKID:
+            MFA_TRY(dev_ptr(mk->q_blk, "q_blk"));
+            MFA_TRY(dev_ptr(mk->k_blk, "k_blk"));
+            MFA_TRY(dev_ptr(mk->q_valid, "q_valid"));
+            MFA_TRY(dev_ptr(mk->qsum, "qsum"));
+            MFA_TRY(dev_ptr(mk->ksum, "ksum"));
+            MFA_TRY(dev_ptr(mk->kv_bits, "kv_bits"));
+            break;
+        case MFA_MASK_TILES:
+            MFA_TRY(dev_ptr(mk->fine_bits, "fine_bits"));
+            if (dkdv) {
+                MFA_TRY(dev_ptr(mk->tile_kind, "tile_kind"));
+            } else {
+                MFA_TRY(dev_ptr(mk->row_ptr, "row_ptr"));
+                MFA_TRY(dev_ptr(mk->col_idx, "col_idx"));
+                MFA_TRY(dev_ptr(mk->col_kind, "col_kind"));
+            }
+            break;
+        case MFA_MASK_BSR:
+            if (dkdv) {
+                MFA_TRY(dev_ptr(mk->csc_ptr, "csc_ptr"));
+                MFA_TRY(dev_ptr(mk->csc_idx, "csc_idx"));
+            } else {
+                MFA_TRY(dev_ptr(mk->indptr, "indptr"));
+                MFA_TRY(dev_ptr(mk->indices, "indices"));
+                MFA_TRY(dev_ptr(mk->bsr_kind, "bsr_kind"));
+            }
+            break;
+        case MFA_MASK_VARLEN:
+            MFA_TRY(dev_ptr(mk->cu_q, "cu_q"));
+            MFA_TRY(dev_ptr(mk->cu_k, "cu_k"));
+            MFA_TRY(dev_ptr(mk->err, "err", true));
+            if (dkdv) {
+                if (mk->nseq < 0) return fail(MFA_E_ARG, "negative nseq");
+            } else if (mk->work_cap > 0) {
+                MFA_TRY(dev_ptr(mk->work, "work"));
+            }
+            break;
+        default: return fail(MFA_E_ARG, "unknown mask kind %d", mk->kind);
     }
     return ok();
 }
@@ -479,20 +515,34 @@ mfa_status mfa_attn_bwd_preprocess(const mfa_attn_bwd_args* a, hipStream_t strea
     return hip_ok(launch_bwd_preprocess(p, a->fwd.D, stream), "backward preprocess launch");
 }
 
-static mfa_status bwd_common(const mfa_attn_bwd_args* a, const mfa_mask* mk, float scale, bool csc, BwdDev& p,
+static mfa_status bwd_common(const mfa_attn_bwd_args* a, const mfa_mask* mk, float scale, bool dkdv, BwdDev& p,
                              MaskDev& m) {
     MFA_TRY(check_bwd(a, true));
     if (!(scale == scale) || scale == 0.f) return fail(MFA_E_ARG, "scale must be a nonzero number");
     if (a->fwd.B == 0 || a->fwd.Sq == 0) return ok();
     MFA_TRY(dev_ptr(a->fwd.q, "q"));
-    MFA_TRY(dev_ptr(a->fwd.k, "k"));
-    MFA_TRY(dev_ptr(a->fwd.v, "v"));
     MFA_TRY(dev_ptr(a->fwd.lse, "lse"));
+    if (a->fwd.Sk > 0) {
+        MFA_TRY(dev_ptr(a->fwd.k, "k"));
+        MFA_TRY(dev_ptr(a->fwd.v, "v"));
+    }
     MFA_TRY(check_strides("q", a->fwd.q, a->fwd.q_stride, MFA_BF16));
     MFA_TRY(check_strides("k", a->fwd.k, a->fwd.k_stride, MFA_BF16));
     MFA_TRY(check_strides("v", a->fwd.v, a->fwd.v_stride, MFA_BF16));
-    MFA_TRY(check_bwd_mask(a, mk, csc, m));
+    int BM = 128;
+    MFA_TRY(check_bwd_mask(a, mk, dkdv, m, BM));
     fill_bwd(a, scale, p);
+    // the dQ pass runs the forward's grid; the dK/dV pass reads nQt / nKt of
+    // the 128 x 64 tile map and summaries
+    p.f.nQt = cdiv(a->fwd.Sq, BM);
+    p.f.nKt = cdiv(a->fwd.Sk, 64);
+    if (mk->kind == MFA_MASK_VARLEN) {
+        p.f.total = mk->work_cap * a->fwd.Hq;
+        p.f.nQt = 0;
+    } else {
+        p.f.total = a->fwd.B * a->fwd.Hq * p.f.nQt;
+    }
+    p.f.xcd_remap = (p.f.total % 8 == 0) ? 1 : 0;
     return ok();
 }
 
@@ -500,7 +550,7 @@ mfa_status mfa_attn_bwd_dkdv(const mfa_attn_bwd_args* a, const mfa_mask* mk, flo
     BwdDev p;
     MaskDev m;
     MFA_TRY(bwd_common(a, mk, scale, true, p, m));
-    if (a->fwd.B == 0 || a->fwd.Sq == 0) return ok();
+    if (a->fwd.B == 0 || a->fwd.Sq == 0 || a->fwd.Sk == 0) return ok();
     MFA_TRY(dev_ptr(a->dk, "dk"));
     MFA_TRY(dev_ptr(a->dv, "dv"));
     MFA_TRY(check_strides("dk", a->dk, a->dk_stride, MFA_BF16));

@@ -1,18 +1,19 @@
-// Backward of masked attention for BSR block-sparse masks on gfx950.
+// Backward of masked attention on gfx950, for every mask representation.
 //
-// The split follows the BinFlash method ("Backward uses two passes: dKdV over
-// K-blocks, dQ over Q-blocks, with the same gathered dispatch"), here over the
-// flashinfer-style BSR rows and their column-major copy:
+// The split follows the BinFlash method (two passes with the forward's
+// dispatch: dK/dV over key blocks, dQ over query blocks):
 //   preprocess  delta_i = sum_d dO_id * O_id                       (fp32)
-//   dK/dV pass  one workgroup per (batch, kv head, 64-key block); it walks
-//               the query blocks that list this key block (CSC), for every
-//               query head of the GQA group, and accumulates
-//               dV += P^T dO and dK += scale * dS^T Q in registers;
-//   dQ pass     one workgroup per (batch, query head, 64-query block); it walks
-//               the row's key blocks (CSR) and accumulates dQ += scale * dS K.
+//   dK/dV pass  one workgroup per (batch or varlen sequence, kv head, 64-key
+//               block); it walks the query blocks that can attend to the
+//               block, for every query head of the GQA group, and
+//               accumulates dV += P^T dO and dK += scale * dS^T Q in
+//               registers;
+//   dQ pass     one workgroup per forward query tile; it walks the forward's
+//               key tiles and accumulates dQ += scale * dS K.
 // P = exp2(s * scale*log2e - LSE*log2e) is recomputed from the forward's LSE,
-// dS = P o (dP - delta), dP = dO V^T. No atomics: every output element is
-// written by exactly one workgroup, so results are deterministic.
+// dS = P o (dP - delta), dP = dO V^T; disallowed entries have P = 0. No
+// atomics: every output element is written by exactly one workgroup, so
+// results are deterministic.
 //
 // MFMA layouts (v_mfma_f32_32x32x16_bf16): in the dK/dV pass scores are
 // computed as S = Q K^T so that a lane owns one key and 16 of the queries; the
@@ -132,7 +133,43 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdDev p) {
 // dK / dV pass
 // ---------------------------------------------------------------------------
 
-template <int D>
+// Allowed bits of one 32-query half in the dK/dV layout: bit rr says whether
+// query qi0 + (rr>>2)*8 + 4*hh + (rr&3) (index within the batch entry or the
+// varlen sequence) may attend to this lane's key key_l. Used on partial
+// blocks only; full blocks need none, empty blocks are never visited.
+template <int KIND>
+__device__ __forceinline__ uint32_t allowed_bits_T(const FwdDev& f, const MaskDev& m, int b, int q_len, int k_len,
+                                                   int key_l, int qi0, int hh, int kblk, bool kval) {
+    uint32_t bits = 0;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+        const int i = qi0 + (rr >> 2) * 8 + 4 * hh + (rr & 3);
+        bool ok = i < q_len && key_l < k_len;
+        if constexpr (KIND == MFA_MASK_BSR) {
+            ok = ok && (!m.causal || key_l <= i);
+        } else if constexpr (KIND == MFA_MASK_TILES) {
+            if (ok) ok = (m.fine_bits[(int64_t)i * m.fine_words + (key_l >> 5)] >> (key_l & 31)) & 1u;
+        } else if constexpr (KIND == MFA_MASK_BLOCKID) {
+            if (ok) {
+                const int64_t qi = (int64_t)b * f.Sq + i;
+                ok = kval && m.q_valid[qi] && kblk <= m.q_blk[qi];
+            }
+        } else if constexpr (KIND == MFA_MASK_VARLEN) {
+            ok = ok && (!m.causal || key_l <= i) && (m.win_left < 0 || i - key_l <= m.win_left) &&
+                 (m.win_right < 0 || key_l - i <= m.win_right);
+        }
+        bits |= (ok ? 1u : 0u) << rr;
+    }
+    return bits;
+}
+
+// One workgroup (2 waves, 64 keys) per (batch or varlen sequence, kv head,
+// 64-key block). The query blocks that can attend to the key block come from
+// the CSC list (BSR), the dense tile map or the block-id summaries (both at
+// 128-row granularity: a 64-row block takes its tile's kind), the window
+// arithmetic (varlen) or all blocks (no mask); they are walked through a
+// ScanWindow, once per query head of the GQA group.
+template <int D, int KIND>
 __global__ __launch_bounds__(128, 1) void bwd_dkdv_kernel(BwdDev p, MaskDev m) {
     constexpr int ROWB = 2 * D, TILEB = 64 * ROWB, NKC = D / 16, NDB = D / 32;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -142,14 +179,38 @@ __global__ __launch_bounds__(128, 1) void bwd_dkdv_kernel(BwdDev p, MaskDev m) {
     float* sDl = sL + 128;                             // [2][64] delta
 
     const FwdDev& f = p.f;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hh = lane >> 5, c = lane & 31;
-    const int nKb = (f.Sk + 63) / 64;
-    const int bh = blockIdx.x / nKb;
-    const int kbk = blockIdx.x - bh * nKb;
-    const int b = bh / f.Hkv, hk = bh - b * f.Hkv;
-    const int key = kbk * 64 + wave * 32 + c;
-    const bool key_ok = key < f.Sk;
+
+    int b = 0, hk = 0, kbk = 0;
+    int q_base = 0, q_len = f.Sq, k_base = 0, k_len = f.Sk;
+    bool len_error = false;
+    if constexpr (KIND == MFA_MASK_VARLEN) {
+        const int nKbm = (m.max_k + 63) / 64;
+        kbk = blockIdx.x % nKbm;
+        const int sh = blockIdx.x / nKbm;
+        hk = sh % f.Hkv;
+        const int seq = sh / f.Hkv;
+        q_base = m.cu_q[seq];
+        q_len = m.cu_q[seq + 1] - q_base;
+        k_base = m.cu_k[seq];
+        k_len = m.cu_k[seq + 1] - k_base;
+        if (kbk * 64 >= k_len) return;
+        if (q_len > m.max_q || k_len > m.max_k) {
+            len_error = true;
+            if (m.err && threadIdx.x == 0) *m.err = 1;
+        }
+    } else {
+        const int nKb = (f.Sk + 63) / 64;
+        const int bh = blockIdx.x / nKb;
+        kbk = blockIdx.x - bh * nKb;
+        b = bh / f.Hkv;
+        hk = bh - b * f.Hkv;
+    }
+    const int key_l = kbk * 64 + wave * 32 + c;  // key within the batch entry / sequence
+    const bool key_ok = key_l < k_len;
+    const int key = k_base + key_l;              // row of k, v, dk, dv
 
     // stationary K and V fragments (B operands: K^T, V^T with lane = key)
     bf16x8 kf[NKC], vf[NKC];
@@ -168,52 +229,102 @@ __global__ __launch_bounds__(128, 1) void bwd_dkdv_kernel(BwdDev p, MaskDev m) {
         dk[db] = f32x16{};
         dv[db] = f32x16{};
     }
+    // key-side mask values
+    int kblk = INT32_MAX;
+    bool kval = false;
+    if constexpr (KIND == MFA_MASK_BLOCKID) {
+        if (key_ok) {
+            kblk = m.k_blk[(int64_t)b * f.Sk + key_l];
+            kval = (m.kv_bits[(int64_t)b * m.kv_words + (key_l >> 5)] >> (key_l & 31)) & 1u;
+        }
+    }
 
-    const int* cp = m.csc_ptr + (int64_t)bh * (nKb + 1);
-    const int e0 = cp[kbk], len = cp[kbk + 1] - e0;
-    const int total = len * f.G;
+    // ---- the query blocks of this key block ----
+    const int nQb = (q_len + 63) / 64;
+    int pbeg = 0, pend = nQb, e0 = 0;
+    if constexpr (KIND == MFA_MASK_BSR) {
+        const int nKb = (f.Sk + 63) / 64;
+        const int* cp = m.csc_ptr + ((int64_t)b * f.Hkv + hk) * (nKb + 1);
+        e0 = cp[kbk];
+        pend = cp[kbk + 1] - e0;
+    } else if constexpr (KIND == MFA_MASK_VARLEN) {
+        const int j0 = kbk * 64, j1 = min(j0 + 63, k_len - 1);
+        int lo = 0, hi = q_len - 1;
+        if (m.causal) lo = max(lo, j0);
+        if (m.win_right >= 0) lo = max(lo, j0 - m.win_right);
+        if (m.win_left >= 0) hi = min(hi, j1 + m.win_left);
+        pbeg = lo / 64;
+        pend = hi >= lo ? hi / 64 + 1 : pbeg;
+    }
+    auto fetch = [&](int pos) -> uint32_t {
+        if (pos >= pend) return 0u;
+        int qb = pos, kind = kTileFull;
+        if constexpr (KIND == MFA_MASK_BSR) {
+            qb = m.csc_idx[e0 + pos];
+            kind = bsr_kind_of(qb, kbk, 64, 64, f.Sq, f.Sk, m.causal);
+        } else if constexpr (KIND == MFA_MASK_TILES) {
+            kind = m.tile_kind[(int64_t)(qb >> 1) * f.nKt + kbk];
+        } else if constexpr (KIND == MFA_MASK_BLOCKID) {
+            kind = classify_blockid(m.qsum + ((int64_t)b * f.nQt + (qb >> 1)) * 4,
+                                    m.ksum + ((int64_t)b * f.nKt + kbk) * 4);
+        } else if constexpr (KIND == MFA_MASK_VARLEN) {
+            const int i0 = qb * 64, i1 = min(i0 + 63, q_len - 1);
+            const int j0 = kbk * 64, j1 = min(j0 + 63, k_len - 1);
+            bool full = (i1 - i0 == 63) && (j1 - j0 == 63);
+            if (m.causal) full = full && j1 <= i0;
+            if (m.win_left >= 0) full = full && i1 - j0 <= m.win_left;
+            if (m.win_right >= 0) full = full && j1 - i0 <= m.win_right;
+            kind = full ? kTileFull : kTilePartial;
+        }
+        return (uint32_t)qb | ((uint32_t)kind << 28);
+    };
+    ScanWindow win;
+    win.init(fetch, pbeg, lane);
+    int g = 0, pos = pbeg;
+    uint32_t ent = 0;
+    bool have = win.seek(fetch, pos, pend, lane, ent);
+    auto next_step = [&](int& g_, int& pos_, uint32_t& ent_) -> bool {
+        ++pos_;
+        if (win.seek(fetch, pos_, pend, lane, ent_)) return true;
+        if (++g_ >= f.G) return false;
+        pos_ = pbeg;
+        return win.seek(fetch, pos_, pend, lane, ent_);
+    };
+
     const float c2 = f.c2;
-
-    // per-lane operand offsets
     int qrow_off[NKC];  // A operand rows of S / dP for query block 0: row c, chunk kc*2 + hh
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) qrow_off[kc] = row_off<D>(c, kc * 2 + hh);
-    // transposed reads: rows kq*16 + 8j + 4hh + (lane&15)/4; the swizzle depends on (8j + 4hh) & 15
     int trq[2][NDB];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) trq[j][db] = tr_off<D>(8 * j + 4 * hh, db, lane);
 
-    // CSC entries of this key block, read through a register window
-    auto fetch_r = [&](int i) { return i < len ? (uint32_t)m.csc_idx[e0 + i] : 0u; };
-    ListWindow win;
-    win.init(fetch_r, 0, lane);
-    auto item = [&](int it, int& hq, int& r) {
-        const int g = it / len;
-        hq = hk * f.G + g;
-        r = (int)win.get(fetch_r, it - g * len, lane);
-    };
-    auto stage = [&](int it, int buf) {
-        int hq, r;
-        item(it, hq, r);
-        const char* qb = (const char*)f.q + 2 * ((int64_t)b * f.qs0 + (int64_t)hq * f.qs2);
-        const char* ob = (const char*)p.dout + 2 * ((int64_t)b * p.dos0 + (int64_t)hq * p.dos2);
-        stage_tile<D>(qb, 2 * f.qs1, r * 64, f.Sq, sQ + buf * TILEB, wave, 2, lane);
-        stage_tile<D>(ob, 2 * p.dos1, r * 64, f.Sq, sO + buf * TILEB, wave, 2, lane);
-        const int64_t row = ((int64_t)b * f.Hq + hq) * f.Sq;
-        if (wave == 0) stage_vec64(f.lse + row, r * 64, f.Sq, sL + buf * 64, lane);
-        else stage_vec64(p.delta + row, r * 64, f.Sq, sDl + buf * 64, lane);
+    auto stage = [&](int g_, uint32_t ent_, int buf) {
+        const int hq = hk * f.G + g_;
+        const int qb = (int)(ent_ & 0x0FFFFFFFu);
+        const char* qbp = (const char*)f.q + 2 * ((int64_t)b * f.qs0 + (int64_t)hq * f.qs2);
+        const char* obp = (const char*)p.dout + 2 * ((int64_t)b * p.dos0 + (int64_t)hq * p.dos2);
+        const int r0 = q_base + qb * 64, rend = q_base + q_len;
+        stage_tile<D>(qbp, 2 * f.qs1, r0, rend, sQ + buf * TILEB, wave, 2, lane);
+        stage_tile<D>(obp, 2 * p.dos1, r0, rend, sO + buf * TILEB, wave, 2, lane);
+        const int64_t lrow = ((int64_t)b * f.Hq + hq) * f.Sq;
+        if (wave == 0) stage_vec64(f.lse + lrow, r0, rend, sL + buf * 64, lane);
+        else stage_vec64(p.delta + lrow, r0, rend, sDl + buf * 64, lane);
     };
 
-    if (total > 0) stage(0, 0);
+    if (have) stage(g, ent, 0);
     vm_wait();
     __syncthreads();
     int buf = 0;
-    for (int it = 0; it < total; ++it) {
-        int hq, r;
-        item(it, hq, r);
-        if (it + 1 < total) stage(it + 1, buf ^ 1);
+    while (have) {
+        const int qb = (int)(ent & 0x0FFFFFFFu);
+        const int kind = (int)(ent >> 28);
+        int g_n = g, pos_n = pos;
+        uint32_t ent_n = 0;
+        const bool have_n = next_step(g_n, pos_n, ent_n);
+        if (have_n) stage(g_n, ent_n, buf ^ 1);
         const char* q_ = sQ + buf * TILEB;
         const char* o_ = sO + buf * TILEB;
         const float* l_ = sL + buf * 64;
@@ -222,36 +333,39 @@ __global__ __launch_bounds__(128, 1) void bwd_dkdv_kernel(BwdDev p, MaskDev m) {
         // S = Q K^T and dP = dO V^T for the two 32-query halves
         f32x16 s[2], dp[2];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            s[qb] = f32x16{};
-            dp[qb] = f32x16{};
+        for (int qh = 0; qh < 2; ++qh) {
+            s[qh] = f32x16{};
+            dp[qh] = f32x16{};
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
-                const bf16x8 aq = *(const bf16x8*)(q_ + qb * 32 * ROWB + qrow_off[kc]);
-                const bf16x8 ao = *(const bf16x8*)(o_ + qb * 32 * ROWB + qrow_off[kc]);
-                s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kc], s[qb], 0, 0, 0);
-                dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[kc], dp[qb], 0, 0, 0);
+                const bf16x8 aq = *(const bf16x8*)(q_ + qh * 32 * ROWB + qrow_off[kc]);
+                const bf16x8 ao = *(const bf16x8*)(o_ + qh * 32 * ROWB + qrow_off[kc]);
+                s[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kc], s[qh], 0, 0, 0);
+                dp[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[kc], dp[qh], 0, 0, 0);
             }
         }
-        // P and dS; register r of half qb is query qb*32 + (r>>2)*8 + 4*hh + (r&3)
-        const int kind = bsr_kind_of(r, kbk, 64, 64, f.Sq, f.Sk, m.causal);
-        const bool diag = m.causal && kind == kTilePartial;
+        // allowed bits on partial blocks; register r of half qh is query qh*32 + (r>>2)*8 + 4*hh + (r&3)
+        uint32_t okb[2] = {0xFFFFu, 0xFFFFu};
+        if (__builtin_expect(kind == kTilePartial, 0)) {
+#pragma unroll
+            for (int qh = 0; qh < 2; ++qh)
+                okb[qh] = allowed_bits_T<KIND>(f, m, b, q_len, k_len, key_l, qb * 64 + qh * 32, hh, kblk, kval);
+        }
         bf16x8 pb[4], sb[4];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qh = 0; qh < 2; ++qh) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 L = *(const f32x4*)(l_ + qb * 32 + g * 8 + 4 * hh);
-                const f32x4 Dl = *(const f32x4*)(d_ + qb * 32 + g * 8 + 4 * hh);
+            for (int gq = 0; gq < 4; ++gq) {
+                const f32x4 L = *(const f32x4*)(l_ + qh * 32 + gq * 8 + 4 * hh);
+                const f32x4 Dl = *(const f32x4*)(d_ + qh * 32 + gq * 8 + 4 * hh);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int rr = g * 4 + e;
-                    const int qi = r * 64 + qb * 32 + g * 8 + 4 * hh + e;
-                    float pv = fast_exp2(fmaf(s[qb][rr], c2, -lse_log2(L[e])));
-                    if (diag && key > qi) pv = 0.f;
-                    const float ds = pv * (dp[qb][rr] - Dl[e]);
-                    pb[qb * 2 + (g >> 1)][(g & 1) * 4 + e] = (bf16)pv;
-                    sb[qb * 2 + (g >> 1)][(g & 1) * 4 + e] = (bf16)ds;
+                    const int rr = gq * 4 + e;
+                    float pv = fast_exp2(fmaf(s[qh][rr], c2, -lse_log2(L[e])));
+                    if (!((okb[qh] >> rr) & 1u)) pv = 0.f;
+                    const float ds = pv * (dp[qh][rr] - Dl[e]);
+                    pb[qh * 2 + (gq >> 1)][(gq & 1) * 4 + e] = (bf16)pv;
+                    sb[qh * 2 + (gq >> 1)][(gq & 1) * 4 + e] = (bf16)ds;
                 }
             }
         }
@@ -274,69 +388,78 @@ __global__ __launch_bounds__(128, 1) void bwd_dkdv_kernel(BwdDev p, MaskDev m) {
         vm_wait();
         __syncthreads();
         buf ^= 1;
+        have = have_n;
+        g = g_n;
+        pos = pos_n;
+        ent = ent_n;
     }
 
     if (!key_ok) return;
+    const float nanv = __builtin_nanf("");
     bf16* dkp = (bf16*)p.dk + (int64_t)b * p.dks0 + (int64_t)key * p.dks1 + (int64_t)hk * p.dks2;
     bf16* dvp = (bf16*)p.dv + (int64_t)b * p.dvs0 + (int64_t)key * p.dvs1 + (int64_t)hk * p.dvs2;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int gq = 0; gq < 4; ++gq) {
             bf16x4 wk, wv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                wk[e] = (bf16)(dk[db][g * 4 + e] * f.scale);
-                wv[e] = (bf16)dv[db][g * 4 + e];
+                wk[e] = (bf16)(len_error ? nanv : dk[db][gq * 4 + e] * f.scale);
+                wv[e] = (bf16)(len_error ? nanv : dv[db][gq * 4 + e]);
             }
-            *(bf16x4*)(dkp + db * 32 + g * 8 + 4 * hh) = wk;
-            *(bf16x4*)(dvp + db * 32 + g * 8 + 4 * hh) = wv;
+            *(bf16x4*)(dkp + db * 32 + gq * 8 + 4 * hh) = wk;
+            *(bf16x4*)(dvp + db * 32 + gq * 8 + 4 * hh) = wv;
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// dQ pass
+// dQ pass: one workgroup per forward query tile (BM = 32 * NW rows; 64 for
+// BSR, 128 otherwise), walking the forward's key tiles with the same tile
+// cursor and the same per-element masks.
 // ---------------------------------------------------------------------------
 
-template <int D>
-__global__ __launch_bounds__(128, 2) void bwd_dq_kernel(BwdDev p, MaskDev m) {
+template <int D, int NW, int KIND>
+__global__ __launch_bounds__(NW * 64, (NW == 2 || KIND == MFA_MASK_BLOCKID) ? 1 : 2) void bwd_dq_kernel(BwdDev p, MaskDev m) {
+    constexpr int BM = NW * 32;
     constexpr int ROWB = 2 * D, TILEB = 64 * ROWB, NKC = D / 16, NDB = D / 32;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* sK = smem;                 // [2][64 x D]
     char* sV = smem + 2 * TILEB;     // [2][64 x D]
 
     const FwdDev& f = p.f;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hh = lane >> 5, c = lane & 31;
-    const int nQb = m.nQb;
-    const int bh = blockIdx.x / nQb;
-    const int r = nQb - 1 - (blockIdx.x - bh * nQb);  // longest rows first
-    const int b = bh / f.Hq, hq = bh - b * f.Hq, hk = hq / f.G;
-    const int qi = r * 64 + wave * 32 + c;
-    const bool q_ok = qi < f.Sq;
+
+    const int logical = xcd_logical(blockIdx.x, f.total, f.xcd_remap);
+    const TileRange t = make_range<KIND, BM>(f, m, logical);
+    if (!t.active) return;
+    const int row = t.q_row0 + wave * 32 + c;
+    RowMask<KIND> rm;
+    rm.init(f, m, t, row);
 
     bf16x8 qf[NKC], of[NKC];
     {
-        const bf16* qp = (const bf16*)f.q + (int64_t)b * f.qs0 + (int64_t)qi * f.qs1 + (int64_t)hq * f.qs2 + hh * 8;
-        const bf16* op = (const bf16*)p.dout + (int64_t)b * p.dos0 + (int64_t)qi * p.dos1 + (int64_t)hq * p.dos2 + hh * 8;
+        const bf16* qp = (const bf16*)f.q + (int64_t)t.b * f.qs0 + (int64_t)row * f.qs1 + (int64_t)t.hq * f.qs2 + hh * 8;
+        const bf16* op = (const bf16*)p.dout + (int64_t)t.b * p.dos0 + (int64_t)row * p.dos1 +
+                         (int64_t)t.hq * p.dos2 + hh * 8;
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
-            qf[kc] = q_ok ? *(const bf16x8*)(qp + kc * 16) : bf16x8{};
-            of[kc] = q_ok ? *(const bf16x8*)(op + kc * 16) : bf16x8{};
+            qf[kc] = rm.row_ok ? *(const bf16x8*)(qp + kc * 16) : bf16x8{};
+            of[kc] = rm.row_ok ? *(const bf16x8*)(op + kc * 16) : bf16x8{};
         }
     }
-    const int64_t lrow = ((int64_t)b * f.Hq + hq) * f.Sq + qi;
-    const float l2 = q_ok ? lse_log2(f.lse[lrow]) : INFINITY;
-    const float dl = q_ok ? p.delta[lrow] : 0.f;
+    const int64_t lrow = ((int64_t)t.b * f.Hq + t.hq) * f.Sq + row;
+    const float l2 = rm.row_ok ? lse_log2(f.lse[lrow]) : INFINITY;
+    const float dl = rm.row_ok ? p.delta[lrow] : 0.f;
     f32x16 dq[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dq[db] = f32x16{};
 
-    const int* ip = m.indptr + ((int64_t)b * f.Hkv + hk) * (nQb + 1);
-    const int beg = ip[r], end = ip[r + 1];
-    const char* kbase = (const char*)f.k + 2 * ((int64_t)b * f.ks0 + (int64_t)hk * f.ks2);
-    const char* vbase = (const char*)f.v + 2 * ((int64_t)b * f.vs0 + (int64_t)hk * f.vs2);
+    const char* kbase = (const char*)f.k + 2 * ((int64_t)t.b * f.ks0 + (int64_t)t.hk * f.ks2 + (int64_t)t.k_base * f.ks1);
+    const char* vbase = (const char*)f.v + 2 * ((int64_t)t.b * f.vs0 + (int64_t)t.hk * f.vs2 + (int64_t)t.k_base * f.vs1);
     const float c2 = f.c2;
 
     int krow_off[NKC];
@@ -348,35 +471,42 @@ __global__ __launch_bounds__(128, 2) void bwd_dq_kernel(BwdDev p, MaskDev m) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) trk[j][db] = tr_off<D>(8 * j + 4 * hh, db, lane);
 
-    // BSR row entries (block index | kind << 28), read through a register window
-    auto fetch_e = [&](int e) {
-        return e < end ? (uint32_t)m.indices[e] | ((uint32_t)m.bsr_kind[e] << 28) : 0u;
+    TileCursor<KIND, BM> cursor;
+    cursor.init(f, m, t, lane);
+    auto fine_words = [&](int kt_, int kind_, uint32_t (&w)[2]) {
+        w[0] = w[1] = 0u;
+        if constexpr (KIND == MFA_MASK_TILES) {
+            if (rm.row_ok && (kind_ == kTilePartial || (kt_ + 1) * kBN > t.k_len)) {
+                const uint32_t* fb = m.fine_bits + (int64_t)row * m.fine_words + 2 * kt_;
+                w[0] = fb[0];
+                if (2 * kt_ + 1 < m.fine_words) w[1] = fb[1];
+            }
+        }
     };
-    ListWindow win;
-    win.init(fetch_e, beg, lane);
-    auto next = [&](int e) {
-        while (e < end && (win.get(fetch_e, e, lane) >> 28) == (uint32_t)kTileEmpty) ++e;
-        return e;
-    };
-    auto stage = [&](int e, int buf) {
-        const int kb = (int)(win.get(fetch_e, e, lane) & 0x0FFFFFFFu);
-        stage_tile<D>(kbase, 2 * f.ks1, kb * 64, f.Sk, sK + buf * TILEB, wave, 2, lane);
-        stage_tile<D>(vbase, 2 * f.vs1, kb * 64, f.Sk, sV + buf * TILEB, wave, 2, lane);
+    auto stage = [&](int kt_, int buf) {
+        stage_tile<D>(kbase, 2 * f.ks1, kt_ * 64, t.k_len, sK + buf * TILEB, wave, NW, lane);
+        stage_tile<D>(vbase, 2 * f.vs1, kt_ * 64, t.k_len, sV + buf * TILEB, wave, NW, lane);
     };
 
-    int e = next(beg);
-    if (e < end) stage(e, 0);
+    int it = t.begin, kt = 0, kind = kTileEmpty;
+    cursor.seek(f, m, t, lane, it, kt, kind);
+    uint32_t fw[2];
+    fine_words(kt, kind, fw);
+    if (it < t.end) stage(kt, 0);
     vm_wait();
     __syncthreads();
     int buf = 0;
-    while (e < end) {
-        const uint32_t ent = win.get(fetch_e, e, lane);  // before next() moves the window on
-        const int kb = (int)(ent & 0x0FFFFFFFu);
-        const bool diag = m.causal && (int)(ent >> 28) == kTilePartial;
-        const int en = next(e + 1);
-        if (en < end) stage(en, buf ^ 1);
+    while (it < t.end) {
+        int it_n = it + 1, kt_n = kt, kind_n = kTileEmpty;
+        cursor.seek(f, m, t, lane, it_n, kt_n, kind_n);
+        const bool has_next = it_n < t.end;
+        uint32_t fw_n[2];
+        fine_words(kt_n, has_next ? kind_n : kTileEmpty, fw_n);
+        if (has_next) stage(kt_n, buf ^ 1);
         const char* k_ = sK + buf * TILEB;
         const char* v_ = sV + buf * TILEB;
+
+        // S^T = K Q^T and dP^T = V dO^T (64 keys x 32 queries per wave)
         f32x16 s[2], dp[2];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
@@ -390,15 +520,15 @@ __global__ __launch_bounds__(128, 2) void bwd_dq_kernel(BwdDev p, MaskDev m) {
                 dp[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[kc], dp[h2], 0, 0, 0);
             }
         }
-        // register r of key half h2 is key kb*64 + h2*32 + (r>>2)*8 + 4*hh + (r&3)
+        if (__builtin_expect(kind == kTilePartial || (kt + 1) * kBN > t.k_len, 0))
+            mask_scores<KIND>(f, m, t, rm, row, hh, kt, fw, s);
+        // register r of key half h2 is key kt*64 + h2*32 + (r>>2)*8 + 4*hh + (r&3)
         bf16x8 sb[4];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
-                const int key = kb * 64 + h2 * 32 + (rr >> 2) * 8 + 4 * hh + (rr & 3);
-                float pv = fast_exp2(fmaf(s[h2][rr], c2, -l2));
-                if (diag && key > qi) pv = 0.f;
+                const float pv = fast_exp2(fmaf(s[h2][rr], c2, -l2));
                 sb[h2 * 2 + (rr >> 3)][rr & 7] = (bf16)(pv * (dp[h2][rr] - dl));
             }
         // dQ^T += K^T dS^T
@@ -416,19 +546,24 @@ __global__ __launch_bounds__(128, 2) void bwd_dq_kernel(BwdDev p, MaskDev m) {
         vm_wait();
         __syncthreads();
         buf ^= 1;
-        e = en;
+        it = it_n;
+        kt = kt_n;
+        kind = kind_n;
+        fw[0] = fw_n[0];
+        fw[1] = fw_n[1];
     }
 
-    if (!q_ok) return;
-    bf16* dqp = (bf16*)p.dq + (int64_t)b * p.dqs0 + (int64_t)qi * p.dqs1 + (int64_t)hq * p.dqs2;
+    if (!rm.row_ok) return;
+    const float nanv = __builtin_nanf("");
+    bf16* dqp = (bf16*)p.dq + (int64_t)t.b * p.dqs0 + (int64_t)row * p.dqs1 + (int64_t)t.hq * p.dqs2;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int gq = 0; gq < 4; ++gq) {
             bf16x4 w;
 #pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) w[e4] = (bf16)(dq[db][g * 4 + e4] * f.scale);
-            *(bf16x4*)(dqp + db * 32 + g * 8 + 4 * hh) = w;
+            for (int e4 = 0; e4 < 4; ++e4) w[e4] = (bf16)(t.len_error ? nanv : dq[db][gq * 4 + e4] * f.scale);
+            *(bf16x4*)(dqp + db * 32 + gq * 8 + 4 * hh) = w;
         }
 }
 
@@ -446,33 +581,59 @@ hipError_t launch_bwd_preprocess(const BwdDev& p, int D, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, int KIND>
 static hipError_t dkdv_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) {
     const size_t lds = 4 * 64 * 2 * D + 4 * 64 * sizeof(float);
-    hipError_t e = hipFuncSetAttribute((const void*)&bwd_dkdv_kernel<D>,
+    hipError_t e = hipFuncSetAttribute((const void*)&bwd_dkdv_kernel<D, KIND>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    const int grid = p.f.B * p.f.Hkv * ((p.f.Sk + 63) / 64);
+    const int64_t grid = KIND == MFA_MASK_VARLEN
+                             ? (int64_t)m.nseq * p.f.Hkv * ((m.max_k + 63) / 64)
+                             : (int64_t)p.f.B * p.f.Hkv * ((p.f.Sk + 63) / 64);
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(grid), dim3(128), lds, s, p, m);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, KIND>), dim3((unsigned)grid), dim3(128), lds, s, p, m);
+    return hipGetLastError();
+}
+
+template <int D, int KIND>
+static hipError_t dq_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) {
+    constexpr int NW = KIND == MFA_MASK_BSR ? 2 : 4;
+    const size_t lds = 4 * 64 * 2 * D;
+    if (p.f.total == 0) return hipSuccess;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, KIND>), dim3(p.f.total), dim3(NW * 64), lds, s, p, m);
     return hipGetLastError();
 }
 
 template <int D>
-static hipError_t dq_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) {
-    const size_t lds = 4 * 64 * 2 * D;
-    const int grid = p.f.B * p.f.Hq * m.nQb;
-    if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(grid), dim3(128), lds, s, p, m);
-    return hipGetLastError();
+static hipError_t dkdv_kind(const BwdDev& p, const MaskDev& m, hipStream_t s) {
+    switch (m.kind) {
+        case MFA_MASK_NONE: return dkdv_launch<D, MFA_MASK_NONE>(p, m, s);
+        case MFA_MASK_BLOCKID: return dkdv_launch<D, MFA_MASK_BLOCKID>(p, m, s);
+        case MFA_MASK_TILES: return dkdv_launch<D, MFA_MASK_TILES>(p, m, s);
+        case MFA_MASK_BSR: return dkdv_launch<D, MFA_MASK_BSR>(p, m, s);
+        case MFA_MASK_VARLEN: return dkdv_launch<D, MFA_MASK_VARLEN>(p, m, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int D>
+static hipError_t dq_kind(const BwdDev& p, const MaskDev& m, hipStream_t s) {
+    switch (m.kind) {
+        case MFA_MASK_NONE: return dq_launch<D, MFA_MASK_NONE>(p, m, s);
+        case MFA_MASK_BLOCKID: return dq_launch<D, MFA_MASK_BLOCKID>(p, m, s);
+        case MFA_MASK_TILES: return dq_launch<D, MFA_MASK_TILES>(p, m, s);
+        case MFA_MASK_BSR: return dq_launch<D, MFA_MASK_BSR>(p, m, s);
+        case MFA_MASK_VARLEN: return dq_launch<D, MFA_MASK_VARLEN>(p, m, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dkdv(const BwdDev& p, const MaskDev& m, int D, hipStream_t s) {
-    return D == 128 ? dkdv_launch<128>(p, m, s) : dkdv_launch<64>(p, m, s);
+    return D == 128 ? dkdv_kind<128>(p, m, s) : dkdv_kind<64>(p, m, s);
 }
 
 hipError_t launch_bwd_dq(const BwdDev& p, const MaskDev& m, int D, hipStream_t s) {
-    return D == 128 ? dq_launch<128>(p, m, s) : dq_launch<64>(p, m, s);
+    return D == 128 ? dq_kind<128>(p, m, s) : dq_kind<64>(p, m, s);
 }
 
 }  // namespace mfa

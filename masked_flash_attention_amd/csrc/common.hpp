@@ -48,9 +48,11 @@ struct MaskDev {
     int work_cap;
     int max_q, max_k;
     int causal, win_left, win_right;
+    const uint8_t* tile_kind;  // TILES: (ceil(Sq/128), ceil(Sk/64)) kinds (dK/dV pass)
     int fine_words;   // ceil(Sk / 32)
     int kv_words;     // ceil(Sk / 32)
     int nQb;          // BSR query-block rows per (b, h)
+    int nseq;         // VARLEN sequences
 };
 
 // Problem description shared by the forward kernels.
@@ -118,6 +120,48 @@ struct ListWindow {
             }
         }
         return (uint32_t)__builtin_amdgcn_readlane((int)cur, pos - base);
+    }
+};
+
+// As ListWindow, for entries packed as value | kind << 28 where kind 0 means
+// "skip": seek() moves to the next entry with a nonzero kind using a ballot
+// of the window, so runs of skipped entries cost a bit scan, not a load each.
+struct ScanWindow {
+    int base;
+    uint32_t cur, nxt;
+    uint64_t nz;
+
+    template <class F>
+    __device__ __forceinline__ void init(const F& fetch, int pos, int lane) {
+        base = pos;
+        cur = fetch(pos + lane);
+        nxt = fetch(pos + 64 + lane);
+        nz = __builtin_amdgcn_ballot_w64((cur >> 28) != 0u);
+    }
+
+    // First position >= pos (and < end) whose entry has a nonzero kind;
+    // false when there is none. A pos before the window restarts it.
+    template <class F>
+    __device__ bool seek(const F& fetch, int& pos, int end, int lane, uint32_t& entry) {
+        while (pos < end) {
+            if (pos < base) init(fetch, pos, lane);
+            const int idx = pos - base;
+            if (idx < 64) {
+                const uint64_t rest = nz >> idx;
+                if (rest) {
+                    pos += (int)__builtin_ctzll(rest);
+                    entry = (uint32_t)__builtin_amdgcn_readlane((int)cur, pos - base);
+                    return true;
+                }
+                pos = base + 64;
+                continue;
+            }
+            base += 64;
+            cur = nxt;
+            nxt = fetch(base + 64 + lane);
+            nz = __builtin_amdgcn_ballot_w64((cur >> 28) != 0u);
+        }
+        return false;
     }
 };
 

@@ -1,5 +1,6 @@
 // Per-workgroup tile schedule and per-element mask predicates, shared by the
-// bf16 MFMA forward kernel and the fp32 test-mode kernel.
+// bf16 MFMA forward kernel, the fp32 test-mode kernel and the backward dQ
+// pass (which walks the same key tiles as the forward).
 //
 // A workgroup owns one query tile of BM rows of one (batch, query head) (or of
 // one varlen sequence). It walks only the key tiles that can hold an allowed
@@ -281,6 +282,69 @@ __device__ __forceinline__ bool allowed(const FwdDev& p, const MaskDev& m, const
     } else {
         return true;
     }
+}
+
+// Bits [0, n) set (n clamped to [0, 32]).
+__device__ __forceinline__ uint32_t below(int n) {
+    return n <= 0 ? 0u : (n >= 32 ? 0xFFFFFFFFu : ((1u << n) - 1u));
+}
+
+// Sets the scores of disallowed keys of key tile kt to -inf. Register r of
+// s[kb] holds key kb*32 + (r>>2)*8 + 4*hh + (r&3) of the tile (query = this
+// lane's row); okw[kb] collects, at bit (r>>2)*8 + (r&3), whether that key is
+// allowed. fw: the row's two fine-bit words of the tile (dense-tile masks).
+template <int KIND>
+__device__ __forceinline__ void mask_scores(const FwdDev& p, const MaskDev& m, const TileRange& t,
+                                            const RowMask<KIND>& rm, int row, int hh, int kt,
+                                            const uint32_t (&fw)[2], f32x16 (&s)[2]) {
+    uint32_t okw[2];
+    const int base_off = kt * kBN + 4 * hh;  // tile key index of bit 0 of okw[0]
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) okw[kb] = below(t.k_len - base_off - kb * 32);
+    if constexpr (KIND == MFA_MASK_TILES) {
+        okw[0] &= fw[0] >> (4 * hh);
+        okw[1] &= fw[1] >> (4 * hh);
+    } else if constexpr (KIND == MFA_MASK_BLOCKID) {
+        const uint32_t* kw = m.kv_bits + (int64_t)t.b * m.kv_words + 2 * kt;
+        const uint32_t w0 = kw[0];
+        const uint32_t w1 = (2 * kt + 1 < m.kv_words) ? kw[1] : 0u;
+        okw[0] &= w0 >> (4 * hh);
+        okw[1] &= w1 >> (4 * hh);
+        const int32_t* kbp = m.k_blk + (int64_t)t.b * p.Sk;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            uint32_t cmp = 0;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int key = base_off + kb * 32 + g * 8 + e;
+                    const int kbk = key < t.k_len ? kbp[key] : INT32_MAX;
+                    cmp |= (kbk <= rm.qblk ? 1u : 0u) << (g * 8 + e);
+                }
+            }
+            okw[kb] &= rm.qvalid ? cmp : 0u;
+        }
+    } else if constexpr (KIND == MFA_MASK_BSR) {
+        if (m.causal) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) okw[kb] &= below(row - base_off - kb * 32 + 1);
+        }
+    } else if constexpr (KIND == MFA_MASK_VARLEN) {
+        const int i = rm.qi_local;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int o = base_off + kb * 32;
+            if (m.causal) okw[kb] &= below(i - o + 1);
+            if (m.win_left >= 0) okw[kb] &= ~below(i - m.win_left - o);
+            if (m.win_right >= 0) okw[kb] &= below(i + m.win_right - o + 1);
+        }
+    }
+    if (!rm.row_ok) okw[0] = okw[1] = 0u;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = ((okw[kb] >> ((r >> 2) * 8 + (r & 3))) & 1u) ? s[kb][r] : -INFINITY;
 }
 
 }  // namespace mfa

@@ -9,6 +9,14 @@ DEV = "cuda:0"
 BF16_OUT_TOL = 2e-2   # max-abs error of attention outputs, bf16 in/out, fp32 accumulate
 F32_OUT_TOL = 1e-4    # max-abs error in fp32 test mode
 LSE_TOL = 1e-3        # max-abs error of the log-sum-exp
+GRAD_ULP = 2.0 ** -7  # one bf16 unit in the last place, relative to the value
+
+
+def grad_tolerance(ref):
+    """Per-element bound for bf16-stored gradients: the output tolerance plus
+    one bf16 ULP of the exact value (gradients above ~2.5 in magnitude cannot
+    meet 2e-2 once rounded to bf16)."""
+    return BF16_OUT_TOL + GRAD_ULP * np.abs(ref)
 
 
 def note(msg):

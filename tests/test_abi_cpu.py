@@ -52,7 +52,7 @@ int main() {
   printf("mfa_attn_args %zu\nmfa_mask %zu\nmfa_attn_bwd_args %zu\n",
          sizeof(mfa_attn_args), sizeof(mfa_mask), sizeof(mfa_attn_bwd_args));
   P(mfa_attn_args, q); P(mfa_attn_args, lse); P(mfa_attn_args, o_stride);
-  P(mfa_mask, tile_kind); P(mfa_mask, q_block); P(mfa_mask, cu_q); P(mfa_mask, err); P(mfa_mask, win_right);
+  P(mfa_mask, tile_kind); P(mfa_mask, q_block); P(mfa_mask, cu_q); P(mfa_mask, err); P(mfa_mask, win_right); P(mfa_mask, nseq);
   P(mfa_attn_bwd_args, dout); P(mfa_attn_bwd_args, dv_stride);
   return 0;
 }''')

@@ -1,0 +1,168 @@
+"""Backward for the dense-tile, block-id, varlen and unmasked representations
+(the BSR backward has its own file), and the autograd wrapper, on the GPU
+against the fp64 oracle's dense gradients. Bound per element: 2e-2 plus one
+bf16 ULP of the exact gradient (2^-7 |ref|): these cases have few keys per
+row, gradients reach |g| ~ 5-6, where one bf16 step is already 0.03."""
+
+import numpy as np
+import pytest
+import torch
+
+import masked_flash_attention_amd as mfa
+from oracle import attention as A
+from oracle import masks as M
+import workloads as W
+from tests.gpu_util import BF16_OUT_TOL, DEV, f64, grad_tolerance, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_grads(got, ref, tag=""):
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        g = f64(g)
+        assert np.all(np.isfinite(g)), f"{tag} {name}: non-finite gradient"
+        if not g.size:
+            continue
+        excess = np.abs(g - r) - grad_tolerance(r)
+        i = np.unravel_index(int(np.argmax(excess)), excess.shape)
+        assert excess[i] <= 0, f"{tag} {name}: |{g[i]:.5f} - {r[i]:.5f}| over the bound at {i}"
+
+
+def _run(q, k, v, do, rep, scale, layout):
+    qd, kd, vd, dod = (to_dev(t) for t in (q, k, v, do))
+    out, lse = mfa.attn_fwd(qd, kd, vd, rep, scale, layout)
+    grads = mfa.attn_bwd(qd, kd, vd, out, lse, dod, rep, scale, layout)
+    torch.cuda.synchronize()
+    return grads
+
+
+# --- dense mask -> tiles (BinFlash) ---------------------------------------------------
+
+def _tiles_case(kind, Sq, Sk, seed):
+    if kind == "causal":
+        return np.tril(np.ones((Sq, Sk), bool), k=Sk - Sq)
+    return W.random_dense_mask(Sq, Sk, 0.3, seed)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kind", ["causal", "random"])
+@pytest.mark.parametrize("gqa", [False, True])
+def test_tiles_backward(D, kind, gqa):
+    note(f"tiles bwd D={D} {kind} gqa={gqa}")
+    Sq, Sk = (300, 300) if kind == "causal" else (300, 333)
+    Hq, Hkv = (4, 2) if gqa else (3, 3)
+    mask = _tiles_case(kind, Sq, Sk, seed=D + gqa)
+    q, k, v, do = W.tensors(50 + D + gqa, [(2, Sq, Hq, D), (2, Sk, Hkv, D), (2, Sk, Hkv, D), (2, Sq, Hq, D)])
+    rep = mfa.MaskRep.tiles(mfa.compact_dense_mask(to_dev(mask)))
+    scale = D ** -0.5
+    got = _run(q, k, v, do, rep, scale, "bshd")
+    ref = A.attention_bwd(q, k, v, do, mask[None, None], scale)[:3]
+    _check_grads(got, ref, tag=f"tiles {kind}")
+
+
+def test_tiles_backward_bhsd_layout_and_determinism():
+    note("tiles bwd bhsd + determinism")
+    B, H, N, D = 1, 2, 260, 128
+    mask = W.random_dense_mask(N, N, 0.5, 7) | np.eye(N, dtype=bool)
+    q, k, v, do = W.tensors(71, [(B, H, N, D)] * 4)
+    rep = mfa.MaskRep.tiles(mfa.compact_dense_mask(to_dev(mask)))
+    a = _run(q, k, v, do, rep, 0.1, "bhsd")
+    b = _run(q, k, v, do, rep, 0.1, "bhsd")
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    t = lambda x: x.transpose(1, 2).contiguous()  # noqa: E731  (B, H, S, D) -> (B, S, H, D)
+    ref = A.attention_bwd(t(q), t(k), t(v), t(do), mask[None, None], 0.1)[:3]
+    _check_grads([x.transpose(1, 2) for x in a], ref, tag="tiles bhsd")
+
+
+# --- block ids (opentau) ---------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["cfg1", "small_gqa_cross"])
+def test_blockid_backward(name):
+    note(f"blockid bwd {name}")
+    if name == "cfg1":
+        w = W.blockcausal_tiny()
+        nc, cross = None, None
+        do = W.tensors(901, [tuple(w["q"].shape)])[0]
+    else:
+        w = W.blockcausal_gqa_cross(B=3, N=333, Hq=4, Hkv=2, D=128, Nc=37, prefix=100, blk_lo=5, blk_hi=40,
+                                    pad_hi=60, seed=21)
+        nc, cross = w["n_cross"], w["cross_pad"]
+        do = W.tensors(902, [tuple(w["q"].shape)])[0]
+    ids = mfa.make_block_ids(to_dev(w["pad"]), to_dev(w["att"]), nc, None if cross is None else to_dev(cross))
+    rep = mfa.MaskRep.blockid(*ids)
+    got = _run(w["q"], w["k"], w["v"], do, rep, w["scale"], "bshd")
+    allowed = M.blockid_mask(*M.make_att_block_ids(w["pad"], w["att"], nc, cross))[:, None]
+    ref = A.attention_bwd(w["q"], w["k"], w["v"], do, allowed, w["scale"])[:3]
+    _check_grads(got, ref, tag=name)
+    # padded query rows have no allowed key: their dQ is exactly zero
+    dq = f64(got[0])
+    pad_rows = ~w["pad"]
+    assert np.all(dq[pad_rows] == 0.0)
+
+
+# --- varlen (tensorplay varlen) --------------------------------------------------------
+
+@pytest.mark.parametrize("causal,win", [(True, (100, 0)), (True, (-1, -1)), (False, (50, 30))])
+def test_varlen_backward(causal, win):
+    note(f"varlen bwd causal={causal} win={win}")
+    L = np.array([1, 128, 129, 0, 300, 7, 64, 200], np.int32)
+    T = int(L.sum())
+    Hq, Hkv, D = 4, 2, 64
+    q, k, v, do = W.tensors(33, [(T, Hq, D), (T, Hkv, D), (T, Hkv, D), (T, Hq, D)])
+    s = mfa.varlen_schedule(to_dev(L), causal=causal, window=win, work_cap=T // 128 + L.size)
+    rep = mfa.MaskRep.varlen(s, int(L.max()), int(L.max()), causal=causal, window=win)
+    got = _run(q, k, v, do, rep, D ** -0.5, "thd")
+    cu = M.cu_seqlens(L)
+    allowed = M.varlen_mask(cu, cu, causal, win[0], win[1])[None, None]
+    ref = A.attention_bwd(q[None], k[None], v[None], do[None], allowed, D ** -0.5)[:3]
+    _check_grads(got, [r[0] for r in ref], tag="varlen")
+
+
+def test_varlen_backward_understated_max_is_an_error():
+    note("varlen bwd understated max")
+    L = np.array([300, 100], np.int32)
+    T = int(L.sum())
+    q, k, v, do = (to_dev(t) for t in W.tensors(5, [(T, 2, 64)] * 4))
+    s = mfa.varlen_schedule(to_dev(L), causal=True, window=(-1, -1), work_cap=T // 128 + 2)
+    good = mfa.MaskRep.varlen(s, 300, 300, causal=True)
+    out, lse = mfa.attn_fwd(q, k, v, good, None, "thd")
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bad = mfa.MaskRep.varlen(s, 200, 200, causal=True, err=err)
+    dq, dk, dv = mfa.attn_bwd(q, k, v, out, lse, do, bad, None, "thd")
+    torch.cuda.synchronize()
+    assert int(err.item()) == 1
+    # the over-long sequence's visited key blocks and its query rows are NaN;
+    # the other sequence is computed normally
+    assert torch.isnan(dk[:200].float()).all() and torch.isnan(dq[:300].float()).all()
+    assert torch.isfinite(dk[300:].float()).all() and torch.isfinite(dq[300:].float()).all()
+
+
+# --- no mask, cross-attention shapes -----------------------------------------------------
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_unmasked_backward_ragged(D):
+    note(f"none bwd D={D}")
+    Sq, Sk = 200, 333
+    q, k, v, do = W.tensors(44 + D, [(2, Sq, 4, D), (2, Sk, 2, D), (2, Sk, 2, D), (2, Sq, 4, D)])
+    got = _run(q, k, v, do, mfa.MaskRep.none(), D ** -0.5, "bshd")
+    ref = A.attention_bwd(q, k, v, do, np.ones((1, 1, Sq, Sk), bool), D ** -0.5)[:3]
+    _check_grads(got, ref, tag="none")
+
+
+# --- autograd ---------------------------------------------------------------------------
+
+def test_autograd_wrapper_matches_oracle():
+    note("autograd wrapper")
+    B, N, H, D = 2, 190, 2, 128
+    mask = np.tril(np.ones((N, N), bool))
+    q, k, v, do = W.tensors(61, [(B, N, H, D)] * 4)
+    rep = mfa.MaskRep.tiles(mfa.compact_dense_mask(to_dev(mask)))
+    qd, kd, vd = (to_dev(t).requires_grad_() for t in (q, k, v))
+    out = mfa.masked_attention(qd, kd, vd, rep, 0.1)
+    out.backward(to_dev(do))
+    torch.cuda.synchronize()
+    ro = A.attention_fwd(q, k, v, mask[None, None], 0.1)[0]
+    assert float(np.abs(f64(out) - ro).max()) <= BF16_OUT_TOL
+    ref = A.attention_bwd(q, k, v, do, mask[None, None], 0.1)[:3]
+    _check_grads([qd.grad, kd.grad, vd.grad], ref, tag="autograd")
