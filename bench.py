@@ -112,11 +112,23 @@ def _tiles_blockid(qsum, ksum):
     return int((~empty).sum())
 
 
-def rows_section(dev):
-    """Time each scope row's kernels on its own workload (ms/call, TFLOP/s over attended tiles)."""
+def rows_section(dev, causal=None):
+    """Time each scope row's kernels on its own workload (ms/call, TFLOP/s over attended tiles).
+
+    causal: (q, k, v, rep, scale, fwd_tile_flops) of the causal N=8192 step, whose
+    backward (all three passes) is timed here too."""
     import masked_flash_attention_amd as mfa
     import workloads as W
     out = {}
+    if causal is not None:
+        q, k, v, rep, scale, f = causal
+        do = torch.randn_like(q)
+        o, lse = mfa.attn_fwd(q, k, v, rep, scale, "bhsd")
+        bwd_ms = _time(lambda: mfa.attn_bwd(q, k, v, o, lse, do, rep, scale, "bhsd"), reps=5)
+        del do, o, lse
+        out["causal_dense_N8192_backward"] = {"bwd_ms": round(bwd_ms, 4),
+                                              "bwd_tflops_algorithmic": round(2.5 * f / bwd_ms / 1e9, 1),
+                                              "bwd_tflops_executed": round(3.5 * f / bwd_ms / 1e9, 1)}
     # a1/a2 + a6 on the block-causal tiny and the GQA + cross workloads
     for name, w, nc in (("blockcausal_tiny_N256", W.blockcausal_tiny(), None),
                         ("blockcausal_gqa_cross_N1024", W.blockcausal_gqa_cross(), 256)):
@@ -133,9 +145,13 @@ def rows_section(dev):
         fwd_ms = _time(lambda: mfa.attn_fwd(q, k, v, rep, w["scale"], "bshd", out=o))
         B, Sq, Hq, D = q.shape
         tiles = _tiles_blockid(summ[0], summ[1]) * Hq
+        o, lse = mfa.attn_fwd(q, k, v, rep, w["scale"], "bshd")
+        do = torch.randn_like(q)
+        bwd_ms = _time(lambda: mfa.attn_bwd(q, k, v, o, lse, do, rep, w["scale"], "bshd"), reps=5)
         out[name] = {"block_ids_ms": round(ids_ms, 4), "tile_summary_ms": round(sum_ms, 4),
                      "fwd_ms": round(fwd_ms, 4),
-                     "fwd_tflops_attended_tiles": round(4.0 * 128 * 64 * D * tiles / fwd_ms / 1e9, 1)}
+                     "fwd_tflops_attended_tiles": round(4.0 * 128 * 64 * D * tiles / fwd_ms / 1e9, 1),
+                     "bwd_ms": round(bwd_ms, 4)}
     # a5 + a6 on varlen
     w = W.varlen_window()
     L = torch.from_numpy(w["lengths"]).to(dev)
@@ -148,13 +164,17 @@ def rows_section(dev):
     q, k, v = (w[x].to(dev) for x in "qkv")
     o = torch.empty_like(q)
     fwd_ms = _time(lambda: mfa.attn_fwd(q, k, v, rep, w["scale"], "thd", out=o))
+    o, lse = mfa.attn_fwd(q, k, v, rep, w["scale"], "thd")
+    do = torch.randn_like(q)
+    vbwd_ms = _time(lambda: mfa.attn_bwd(q, k, v, o, lse, do, rep, w["scale"], "thd"), reps=5)
     tiles = 0
     for Ls in w["lengths"].tolist():
         for q0 in range(0, Ls, 128):
             q1 = min(q0 + 128, Ls) - 1
             tiles += q1 // 64 - max(0, q0 - 511) // 64 + 1
     out["varlen_window_32seq"] = {"schedule_ms": round(sched_ms, 4), "fwd_ms": round(fwd_ms, 4),
-                                  "fwd_tflops_attended_tiles": round(4.0 * 128 * 64 * 64 * tiles * 16 / fwd_ms / 1e9, 1)}
+                                  "fwd_tflops_attended_tiles": round(4.0 * 128 * 64 * 64 * tiles * 16 / fwd_ms / 1e9, 1),
+                                  "bwd_ms": round(vbwd_ms, 4)}
     # a4 + a6 + a9 on BSR
     w = W.bsr_random()
     N = 16384
@@ -334,7 +354,7 @@ def main():
     }
     if a.rows:
         log("per-row timings")
-        result["rows"] = rows_section(dev)
+        result["rows"] = rows_section(dev, (q, k, v, rep, scale, tile_flops))
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(w, tile_flops / (B * H), a.cpu_seconds)

@@ -170,7 +170,7 @@ __device__ __forceinline__ uint32_t allowed_bits_T(const FwdDev& f, const MaskDe
 // arithmetic (varlen) or all blocks (no mask); they are walked through a
 // ScanWindow, once per query head of the GQA group.
 template <int D, int KIND>
-__global__ __launch_bounds__(128, 1) void bwd_dkdv_kernel(BwdDev p, MaskDev m) {
+__global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p, MaskDev m) {
     constexpr int ROWB = 2 * D, TILEB = 64 * ROWB, NKC = D / 16, NDB = D / 32;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* sQ = smem;                                   // [2][64 x D] Q

@@ -166,3 +166,34 @@ def test_autograd_wrapper_matches_oracle():
     assert float(np.abs(f64(out) - ro).max()) <= BF16_OUT_TOL
     ref = A.attention_bwd(q, k, v, do, mask[None, None], 0.1)[:3]
     _check_grads([qd.grad, kd.grad, vd.grad], ref, tag="autograd")
+
+
+# --- full size: causal dense mask, B=4, H=32, N=8192, D=128 -------------------------------
+
+def test_cfg2_causal_backward_sampled():
+    """The benchmark's causal workload through the dense-tile backward at full
+    size; dQ rows and dK/dV columns of two (batch, head) slices against the
+    oracle's sampled gradients."""
+    note("cfg2 causal bwd full size")
+    w = W.causal_dense()
+    B, H, N, D = w["q"].shape
+    do = W.tensors(2002, [(B, H, N, D)])[0]
+    mask = w["mask"]
+    rep = mfa.MaskRep.tiles(mfa.compact_dense_mask(to_dev(mask)))
+    qd, kd, vd, dod = (to_dev(t) for t in (w["q"], w["k"], w["v"], do))
+    out, lse = mfa.attn_fwd(qd, kd, vd, rep, w["scale"], "bhsd")
+    dq, dk, dv = mfa.attn_bwd(qd, kd, vd, out, lse, dod, rep, w["scale"], "bhsd")
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 4095, 8191])
+    cols = np.array([0, 63, 64, 4095, 8190, 8191])
+
+    def allowed(bb, hm, rr):
+        return mask[np.asarray(rr)]
+    allowed.heads = 1
+    sl = lambda t, b, h: t[b:b + 1, h:h + 1].transpose(1, 2)  # noqa: E731  -> (1, N, 1, D)
+    for b, h in ((0, 0), (3, 31)):
+        rq, rk, rv = A.attention_bwd_sampled(sl(w["q"], b, h), sl(w["k"], b, h), sl(w["v"], b, h), sl(do, b, h),
+                                             allowed, w["scale"], 0, 0, rows, cols, chunk=2048)
+        _check_grads([dq[b, h, rows], dk[b, h, cols], dv[b, h, cols]], [rq[0], rk, rv], tag=f"cfg2 b={b} h={h}")
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
