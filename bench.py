@@ -126,6 +126,12 @@ def rows_section(dev, causal=None):
         o, lse = mfa.attn_fwd(q, k, v, rep, scale, "bhsd")
         bwd_ms = _time(lambda: mfa.attn_bwd(q, k, v, o, lse, do, rep, scale, "bhsd"), reps=5)
         del do, o, lse
+        # the same causal mask from a predicate (no dense mask) vs compacting the dense one
+        N = q.shape[2]
+        pred_ms = _time(lambda: mfa.predicate_tiles(mfa.Pred.causal(), N, N))
+        pred_bytes = N * ((N + 31) // 32) * 4 + (N // 128) * (N // 64)
+        out["causal_predicate_N8192"] = {"predicate_tiles_ms": round(pred_ms, 4),
+                                         "written_GBps": round(pred_bytes / pred_ms / 1e6, 1)}
         out["causal_dense_N8192_backward"] = {"bwd_ms": round(bwd_ms, 4),
                                               "bwd_tflops_algorithmic": round(2.5 * f / bwd_ms / 1e9, 1),
                                               "bwd_tflops_executed": round(3.5 * f / bwd_ms / 1e9, 1)}

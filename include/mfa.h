@@ -132,6 +132,38 @@ mfa_status mfa_compact_dense_mask(const uint8_t* mask, int Nq, int Nk, int BM, i
                                   int32_t* row_ptr, int32_t* col_idx, uint8_t* col_kind,
                                   hipStream_t stream);
 
+/* Predicate masks (tensorplay omni_attention, "Block masks": a mask_mod
+ * predicate of (b, h, q_idx, kv_idx), composed with and_masks / or_masks;
+ * noop_mask allows everything). Here a predicate is an OR of up to
+ * MFA_PRED_MAX_TERMS conjunctions, each an AND of up to MFA_PRED_MAX_ATOMS
+ * linear atoms   a*q_idx + b*kv_idx + c >= 0   (int64 arithmetic, 0-based
+ * positions, the same for every batch entry and head). Examples:
+ *   causal (q_idx >= kv_idx)             {1, -1, 0}
+ *   at most W past keys (q - kv < W)     {-1, 1, W - 1}
+ *   a prefix of P keys (kv < P)          {0, -1, P - 1}
+ * A conjunction with no atoms is always true (noop_mask); a predicate with
+ * no conjunctions allows nothing. */
+#define MFA_PRED_MAX_TERMS 4
+#define MFA_PRED_MAX_ATOMS 4
+typedef struct mfa_pred_atom {
+    int64_t a, b, c;
+} mfa_pred_atom;
+typedef struct mfa_predicate {
+    int n_terms;
+    int n_atoms[MFA_PRED_MAX_TERMS];
+    mfa_pred_atom atoms[MFA_PRED_MAX_TERMS][MFA_PRED_MAX_ATOMS];
+} mfa_predicate;
+
+/* The tile representation of a predicate mask over an (Nq, Nk) grid: the
+ * same outputs, layout and meaning as mfa_compact_dense_mask (BM = 128,
+ * BN = 64), computed by evaluating the predicate per element on the GPU, so
+ * that no dense mask exists in memory. pred is a host pointer, read before
+ * the call returns. Errors: MFA_E_ARG for counts outside [0, max] or
+ * negative sizes, MFA_E_NO_DEVICE / MFA_E_HIP as elsewhere. */
+mfa_status mfa_predicate_tiles(const mfa_predicate* pred, int Nq, int Nk, uint8_t* tile_kind,
+                               uint32_t* fine_bits, int32_t* row_ptr, int32_t* col_idx,
+                               uint8_t* col_kind, hipStream_t stream);
+
 /* Synchronous inspection of BSR routing arrays ("flashinfer ...
  * block_sparse_attention": "BSR inputs are synchronously inspected to
  * validate canonical rows and derive their maximum width").

@@ -140,6 +140,74 @@ def compact_dense_mask(mask, BM=TILE_M, BN=TILE_N):
     return out
 
 
+class Pred:
+    """A mask predicate of (q_idx, kv_idx) in disjunctive form: a tuple of
+    conjunctions, each a tuple of linear atoms (a, b, c) meaning
+    a*q_idx + b*kv_idx + c >= 0. and_/or_ compose like and_masks / or_masks;
+    noop() allows everything (one empty conjunction), never() nothing."""
+
+    def __init__(self, terms):
+        self.terms = tuple(tuple(tuple(int(x) for x in atom) for atom in term) for term in terms)
+
+    @staticmethod
+    def atom(a, b, c):
+        return Pred(((((a, b, c),),)))
+
+    @staticmethod
+    def causal():
+        return Pred.atom(1, -1, 0)                 # q_idx >= kv_idx
+
+    @staticmethod
+    def past_window(w):
+        return Pred.atom(-1, 1, int(w) - 1)        # q_idx - kv_idx < w
+
+    @staticmethod
+    def prefix(p):
+        return Pred.atom(0, -1, int(p) - 1)        # kv_idx < p
+
+    @staticmethod
+    def noop():
+        return Pred(((),))
+
+    @staticmethod
+    def never():
+        return Pred(())
+
+    def and_(self, other):
+        return Pred(tuple(x + y for x in self.terms for y in other.terms))
+
+    def or_(self, other):
+        return Pred(self.terms + other.terms)
+
+    def to_c(self):
+        if len(self.terms) > _ffi.PRED_MAX_TERMS or any(len(t) > _ffi.PRED_MAX_ATOMS for t in self.terms):
+            raise ValueError(f"at most {_ffi.PRED_MAX_TERMS} conjunctions of {_ffi.PRED_MAX_ATOMS} atoms")
+        p = _ffi.Predicate()
+        p.n_terms = len(self.terms)
+        for i, term in enumerate(self.terms):
+            p.n_atoms[i] = len(term)
+            for j, (a, b, c) in enumerate(term):
+                p.atoms[i][j].a, p.atoms[i][j].b, p.atoms[i][j].c = a, b, c
+        return p
+
+
+def predicate_tiles(pred: Pred, Nq, Nk, device="cuda", BM=TILE_M, BN=TILE_N):
+    """Tile map, packed fine bits and CSR of a predicate mask (mfa_predicate_tiles);
+    the same outputs as compact_dense_mask, with no dense mask built."""
+    nQt, nKt = _cdiv(Nq, BM), _cdiv(Nk, BN)
+    out = {
+        "tile_kind": torch.empty(nQt, nKt, dtype=torch.uint8, device=device),
+        "fine_bits": torch.empty(Nq, _cdiv(Nk, 32), dtype=torch.int32, device=device),
+        "row_ptr": torch.empty(nQt + 1, dtype=torch.int32, device=device),
+        "col_idx": torch.empty(max(1, nQt * nKt), dtype=torch.int32, device=device),
+        "col_kind": torch.empty(max(1, nQt * nKt), dtype=torch.uint8, device=device),
+    }
+    cp = pred.to_c()
+    _ffi.check(_lib().mfa_predicate_tiles(C.byref(cp), Nq, Nk, _p(out["tile_kind"]), _p(out["fine_bits"]),
+                                          _p(out["row_ptr"]), _p(out["col_idx"]), _p(out["col_kind"]), _stream()))
+    return out
+
+
 def bsr_validate(block_indptr, block_indices, n_kv_blocks):
     """Synchronously check canonical BSR rows; return the widest row (mfa_bsr_validate)."""
     ip, ix = _i32(block_indptr).contiguous(), _i32(block_indices).contiguous()

@@ -41,6 +41,19 @@ class BwdArgs(C.Structure):
                 ("do_stride", i64x3), ("dq_stride", i64x3), ("dk_stride", i64x3), ("dv_stride", i64x3)]
 
 
+PRED_MAX_TERMS = 4
+PRED_MAX_ATOMS = 4
+
+
+class PredAtom(C.Structure):
+    _fields_ = [("a", C.c_int64), ("b", C.c_int64), ("c", C.c_int64)]
+
+
+class Predicate(C.Structure):
+    _fields_ = [("n_terms", C.c_int), ("n_atoms", C.c_int * PRED_MAX_TERMS),
+                ("atoms", (PredAtom * PRED_MAX_ATOMS) * PRED_MAX_TERMS)]
+
+
 # name -> argument types (restype is int status except where noted)
 SIGNATURES = {
     "mfa_is_available": ([], C.c_int),
@@ -50,6 +63,7 @@ SIGNATURES = {
     "mfa_blockid_tile_summary": ([vp, vp, vp, vp, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, vp, vp, vp, vp],
                                  C.c_int),
     "mfa_compact_dense_mask": ([vp, C.c_int, C.c_int, C.c_int, C.c_int, vp, vp, vp, vp, vp, vp], C.c_int),
+    "mfa_predicate_tiles": ([C.POINTER(Predicate), C.c_int, C.c_int, vp, vp, vp, vp, vp, vp], C.c_int),
     "mfa_bsr_validate": ([vp, vp, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64, C.POINTER(C.c_int), vp], C.c_int),
     "mfa_bsr_prepare": ([vp, vp, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int, C.c_int, C.c_int,
                          C.c_int, C.c_int, vp, vp, vp, vp], C.c_int),

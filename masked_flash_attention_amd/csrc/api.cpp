@@ -19,6 +19,8 @@ hipError_t launch_block_ids(const uint8_t*, const int32_t*, int, int, int, const
 hipError_t launch_blockid_summary(const int32_t*, const int32_t*, const uint8_t*, const uint8_t*, int, int, int, int,
                                   int, int32_t*, int32_t*, uint32_t*, hipStream_t);
 hipError_t launch_compact(const uint8_t*, int, int, uint8_t*, uint32_t*, int32_t*, int32_t*, uint8_t*, hipStream_t);
+hipError_t launch_predicate_tiles(const mfa_predicate&, int, int, uint8_t*, uint32_t*, int32_t*, int32_t*, uint8_t*,
+                                  hipStream_t);
 hipError_t launch_bsr_prepare(const int32_t*, const int32_t*, int, int, int, int, int64_t, int, int, int, int, int,
                               uint8_t*, int32_t*, int32_t*, hipStream_t);
 hipError_t launch_varlen_schedule(const int32_t*, const int32_t*, int, int, int, int, int, int, int32_t*, int32_t*,
@@ -178,6 +180,29 @@ mfa_status mfa_compact_dense_mask(const uint8_t* mask, int Nq, int Nk, int BM, i
     }
     return hip_ok(launch_compact(mask, Nq, Nk, tile_kind, fine_bits, row_ptr, col_idx, col_kind, stream),
                   "compaction launch");
+}
+
+mfa_status mfa_predicate_tiles(const mfa_predicate* pred, int Nq, int Nk, uint8_t* tile_kind, uint32_t* fine_bits,
+                               int32_t* row_ptr, int32_t* col_idx, uint8_t* col_kind, hipStream_t stream) {
+    if (!pred) return fail(MFA_E_ARG, "pred is NULL");
+    if (Nq < 0 || Nk < 0) return fail(MFA_E_SHAPE, "negative size (Nq=%d, Nk=%d)", Nq, Nk);
+    if (pred->n_terms < 0 || pred->n_terms > MFA_PRED_MAX_TERMS)
+        return fail(MFA_E_ARG, "n_terms=%d outside [0, %d]", pred->n_terms, MFA_PRED_MAX_TERMS);
+    for (int t = 0; t < pred->n_terms; ++t)
+        if (pred->n_atoms[t] < 0 || pred->n_atoms[t] > MFA_PRED_MAX_ATOMS)
+            return fail(MFA_E_ARG, "n_atoms[%d]=%d outside [0, %d]", t, pred->n_atoms[t], MFA_PRED_MAX_ATOMS);
+    MFA_TRY(ensure_device());
+    MFA_TRY(dev_ptr(row_ptr, "row_ptr"));
+    if (Nq > 0 && Nk > 0) {
+        MFA_TRY(dev_ptr(tile_kind, "tile_kind"));
+        MFA_TRY(dev_ptr(fine_bits, "fine_bits"));
+        MFA_TRY(dev_ptr(col_idx, "col_idx"));
+        MFA_TRY(dev_ptr(col_kind, "col_kind"));
+    }
+    mfa_predicate p = *pred;
+    for (int t = p.n_terms; t < MFA_PRED_MAX_TERMS; ++t) p.n_atoms[t] = 0;
+    return hip_ok(launch_predicate_tiles(p, Nq, Nk, tile_kind, fine_bits, row_ptr, col_idx, col_kind, stream),
+                  "predicate tiles launch");
 }
 
 mfa_status mfa_bsr_validate(const int32_t* indptr, const int32_t* indices, int B, int Hkv, int nQb, int nKb,

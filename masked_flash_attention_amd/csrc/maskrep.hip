@@ -158,13 +158,17 @@ __device__ __forceinline__ uint32_t pack4(uint32_t w) {
     return (((nz >> 7) * 0x01020408u) >> 24) & 0xFu;
 }
 
-template <bool VEC>
-__global__ __launch_bounds__(256) void compact_tiles_kernel(const uint8_t* mask, int Nq, int Nk, int nKt,
-                                                            uint8_t* tile_kind, uint32_t* fine_bits) {
+// Body shared by the dense-mask and the predicate tile builders: one
+// workgroup = 128 rows x 256 columns (4 key tiles); thread t covers a 16-column
+// segment (t & 15) of row (t >> 4) + 16*pass. bits16(r, col) returns the
+// allowed bits of row r, columns [col, col + 16) (0 past Nk).
+template <class Bits16>
+__device__ __forceinline__ void tile_strip(const Bits16& bits16, int Nq, int Nk, int nKt, uint8_t* tile_kind,
+                                           uint32_t* fine_bits) {
     __shared__ uint32_t s_any[4], s_all[4];
     const int qt = blockIdx.y;
     const int col0 = blockIdx.x * kCmpCols;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63;
     const int seg = t & 15;            // 16-column segment in the 256-column strip
     const int rsub = t >> 4;           // row within a 16-row pass
     const int col = col0 + seg * 16;
@@ -174,22 +178,11 @@ __global__ __launch_bounds__(256) void compact_tiles_kernel(const uint8_t* mask,
         s_all[t] = 1;
     }
     uint32_t words[kCmpPasses];
-    // issue every load of the strip first
+    // every load (or evaluation) of the strip first
 #pragma unroll
     for (int ps = 0; ps < kCmpPasses; ++ps) {
         const int r = qt * kCmpRows + ps * 16 + rsub;
-        uint32_t bits = 0;
-        if (r < Nq) {
-            const uint8_t* rp = mask + (int64_t)r * Nk;
-            if (VEC && col + 16 <= Nk) {
-                const u32x4 v = *(const u32x4*)(rp + col);
-                bits = pack4(v[0]) | (pack4(v[1]) << 4) | (pack4(v[2]) << 8) | (pack4(v[3]) << 12);
-            } else {
-                for (int e = 0; e < 16; ++e)
-                    if (col + e < Nk && rp[col + e] != 0) bits |= 1u << e;
-            }
-        }
-        words[ps] = bits;
+        words[ps] = r < Nq ? bits16(r, col) : 0u;
     }
     bool any = false, all = true;
     // columns of this thread that exist
@@ -217,7 +210,6 @@ __global__ __launch_bounds__(256) void compact_tiles_kernel(const uint8_t* mask,
         if (ba & sel) atomicOr(&s_any[lane], 1u);
         if ((bl & sel) != sel) atomicAnd(&s_all[lane], 0u);
     }
-    (void)wave;
     __syncthreads();
     if (t < 4) {
         const int kt = col0 / 64 + t;
@@ -226,6 +218,61 @@ __global__ __launch_bounds__(256) void compact_tiles_kernel(const uint8_t* mask,
             tile_kind[(int64_t)qt * nKt + kt] = k;
         }
     }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void compact_tiles_kernel(const uint8_t* mask, int Nq, int Nk, int nKt,
+                                                            uint8_t* tile_kind, uint32_t* fine_bits) {
+    auto bits16 = [&](int r, int col) -> uint32_t {
+        const uint8_t* rp = mask + (int64_t)r * Nk;
+        uint32_t bits = 0;
+        if (VEC && col + 16 <= Nk) {
+            const u32x4 v = *(const u32x4*)(rp + col);
+            bits = pack4(v[0]) | (pack4(v[1]) << 4) | (pack4(v[2]) << 8) | (pack4(v[3]) << 12);
+        } else {
+            for (int e = 0; e < 16; ++e)
+                if (col + e < Nk && rp[col + e] != 0) bits |= 1u << e;
+        }
+        return bits;
+    };
+    tile_strip(bits16, Nq, Nk, nKt, tile_kind, fine_bits);
+}
+
+// floor(n / d) and ceil(n / d) for d > 0
+__device__ __forceinline__ int64_t floor_div(int64_t n, int64_t d) { return n >= 0 ? n / d : -((-n + d - 1) / d); }
+__device__ __forceinline__ int64_t ceil_div(int64_t n, int64_t d) { return -floor_div(-n, d); }
+
+// Bits e in [0, 16) with e >= d, and with e <= d.
+__device__ __forceinline__ uint32_t ge16(int64_t d) { return d <= 0 ? 0xFFFFu : (d >= 16 ? 0u : (0xFFFFu & ~((1u << d) - 1u))); }
+__device__ __forceinline__ uint32_t le16(int64_t d) { return d < 0 ? 0u : (d >= 15 ? 0xFFFFu : ((2u << d) - 1u)); }
+
+// Allowed bits of row i, columns [j0, j0 + 16): OR over the conjunctions of
+// the AND of their linear atoms a*i + b*j + c >= 0. Along a row each atom is
+// monotone in j, so it contributes a prefix or suffix of the 16 columns.
+__device__ __forceinline__ uint32_t predicate_bits16(const mfa_predicate& P, int64_t i, int64_t j0) {
+    uint32_t out = 0;
+    for (int tm = 0; tm < P.n_terms; ++tm) {
+        uint32_t m = 0xFFFFu;
+        for (int at = 0; at < P.n_atoms[tm]; ++at) {
+            const mfa_pred_atom A = P.atoms[tm][at];
+            const int64_t base = A.a * i + A.c;  // value at kv_idx = 0
+            if (A.b == 0) m &= base >= 0 ? 0xFFFFu : 0u;
+            else if (A.b > 0) m &= ge16(ceil_div(-base, A.b) - j0);   // j >= ceil(-base / b)
+            else m &= le16(floor_div(base, -A.b) - j0);                // j <= floor(base / -b)
+        }
+        out |= m;
+    }
+    return out;
+}
+
+__global__ __launch_bounds__(256) void predicate_tiles_kernel(mfa_predicate P, int Nq, int Nk, int nKt,
+                                                              uint8_t* tile_kind, uint32_t* fine_bits) {
+    auto bits16 = [&](int r, int col) -> uint32_t {
+        const int ncol = max(0, min(16, Nk - col));
+        const uint32_t exist = ncol >= 16 ? 0xFFFFu : ((1u << ncol) - 1u);
+        return predicate_bits16(P, r, col) & exist;
+    };
+    tile_strip(bits16, Nq, Nk, nKt, tile_kind, fine_bits);
 }
 
 // CSR of non-empty tiles: one workgroup per query-tile row. The row offset is
@@ -495,6 +542,24 @@ hipError_t launch_compact(const uint8_t* mask, int Nq, int Nk, uint8_t* tile_kin
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(compact_csr_kernel, dim3(nQt), dim3(256), 0, s, tile_kind, nQt, nKt, row_ptr, col_idx, col_kind);
+    return hipGetLastError();
+}
+
+hipError_t launch_predicate_tiles(const mfa_predicate& pred, int Nq, int Nk, uint8_t* tile_kind,
+                                  uint32_t* fine_bits, int32_t* row_ptr, int32_t* col_idx, uint8_t* col_kind,
+                                  hipStream_t s) {
+    const int nQt = (Nq + kCmpRows - 1) / kCmpRows, nKt = (Nk + 63) / 64;
+    if (nQt == 0) {
+        return hipMemsetAsync(row_ptr, 0, sizeof(int32_t), s);
+    }
+    if (nKt > 0) {
+        const dim3 grid((Nk + kCmpCols - 1) / kCmpCols, nQt);
+        hipLaunchKernelGGL(predicate_tiles_kernel, grid, dim3(256), 0, s, pred, Nq, Nk, nKt, tile_kind, fine_bits);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(compact_csr_kernel, dim3(nQt), dim3(256), 0, s, tile_kind, nQt, nKt, row_ptr, col_idx,
+                       col_kind);
     return hipGetLastError();
 }
 

@@ -128,6 +128,26 @@ def test_maskrep_validation(lib):
     assert _status(lib, st) == "MFA_E_UNSUPPORTED"
 
 
+def test_predicate_validation_and_composition(lib):
+    p = _ffi.Predicate()
+    p.n_terms = 5
+    assert _status(lib, lib.mfa_predicate_tiles(C.byref(p), 16, 16, None, None, None, None, None, None)) == "MFA_E_ARG"
+    p.n_terms, p.n_atoms[0] = 1, 7
+    assert _status(lib, lib.mfa_predicate_tiles(C.byref(p), 16, 16, None, None, None, None, None, None)) == "MFA_E_ARG"
+    assert _status(lib, lib.mfa_predicate_tiles(None, 16, 16, None, None, None, None, None, None)) == "MFA_E_ARG"
+    p.n_atoms[0] = 0
+    assert _status(lib, lib.mfa_predicate_tiles(C.byref(p), -1, 16, None, None, None, None, None, None)) == "MFA_E_SHAPE"
+    import masked_flash_attention_amd as mfa
+    # and_ distributes over the disjunctions; or_ concatenates them
+    a = mfa.Pred.causal().or_(mfa.Pred.prefix(3))
+    b = a.and_(mfa.Pred.past_window(5))
+    assert b.terms == (((1, -1, 0), (-1, 1, 4)), ((0, -1, 2), (-1, 1, 4)))
+    assert mfa.Pred.noop().and_(a).terms == a.terms
+    assert mfa.Pred.never().or_(a).terms == a.terms and mfa.Pred.never().and_(a).terms == ()
+    with pytest.raises(ValueError):
+        mfa.Pred(tuple(((1, 0, 0),) for _ in range(5))).to_c()
+
+
 def test_empty_problems_are_noops(lib):
     m = _ffi.Mask()
     assert _status(lib, lib.mfa_attn_fwd(C.byref(_args(Sq=0)), C.byref(m), 0.1, None)) == "MFA_OK"
