@@ -4,11 +4,11 @@ TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the benchmark's
 CPU-baseline leg, never by the product path.
 
 This is the plain definition the pages' methods reach exactly (up to rounding
-order): "a drop-in replacement for F.scaled_dot_product_attention ... where an
-(N, N) bool mask is given" (BinFlash, intro) and "matches the hand-written
-masked-softmax computation" (tensorplay omni_attention, intro). No tiles, no
-online softmax: per (batch, query head) the full score rows are formed, masked,
-normalised and applied.
+order): BinFlash (intro) replaces scaled-dot-product attention under a dense
+(N, N) bool mask, and tensorplay omni_attention (intro) states that its result
+equals masked softmax written out by hand. No tiles, no online softmax: per
+(batch, query head) the full score rows are formed, masked, normalised and
+applied.
 
 Conventions (readings where the pages are silent):
 
@@ -23,7 +23,12 @@ Conventions (readings where the pages are silent):
 * masks are given as a bool array (Bm, Hm, Sq, Sk) with Bm in {1, B} and Hm in
   {1, Hkv, Hq} (head index hq * Hm // Hq), or as a callable
   ``allowed(b, hm, rows) -> (len(rows), Sk) bool`` for row-sampled checks at
-  sizes where the dense mask does not fit in memory.
+  sizes where the dense mask does not fit in memory;
+* ``score_mod(score, b, h, q_idx, kv_idx)`` (tensorplay omni_attention,
+  intro: it receives the current score and its coordinates and returns the
+  modified score) is applied to the scaled scores before masking; the
+  backward takes it to be additive (a term that does not depend on the
+  score, as positional biases are), so dS is unchanged by it.
 """
 
 from __future__ import annotations
@@ -57,7 +62,24 @@ def _mask_heads(allowed, Hq):
     return np.asarray(allowed).shape[1]
 
 
-def attention_fwd(q, k, v, allowed, scale, rows=None, chunk=1024):
+def alibi(slopes):
+    """score_mod adding slope[h] * (kv_idx - q_idx); slopes of 1 give the
+    omni_attention intro's example, score - (q_idx - kv_idx)."""
+    sl = np.asarray(slopes, dtype=np.float64)
+
+    def mod(score, b, h, q_idx, kv_idx):
+        return score + sl[h] * (np.asarray(kv_idx, np.float64) - np.asarray(q_idx, np.float64))
+    return mod
+
+
+def _scores(q_rows, k_all, scale, score_mod, b, hq, rr):
+    s = scale * (q_rows @ k_all.T)
+    if score_mod is not None:
+        s = score_mod(s, b, hq, np.asarray(rr)[:, None], np.arange(k_all.shape[0])[None, :])
+    return s
+
+
+def attention_fwd(q, k, v, allowed, scale, rows=None, chunk=1024, score_mod=None):
     """Masked softmax attention. q (B, Sq, Hq, D); k, v (B, Sk, Hkv, D).
 
     Returns (out (B, nrows, Hq, D) fp64, lse (B, Hq, nrows) fp64) for the query
@@ -71,7 +93,7 @@ def attention_fwd(q, k, v, allowed, scale, rows=None, chunk=1024):
     G = Hq // Hkv
     Hm = _mask_heads(allowed, Hq)
     rows = np.arange(Sq) if rows is None else np.asarray(rows)
-    out = np.zeros((B, rows.size, Hq, D))
+    out = np.zeros((B, rows.size, Hq, v.shape[3]))
     lse = np.full((B, Hq, rows.size), -np.inf)
     for b in range(B):
         for hq in range(Hq):
@@ -79,7 +101,7 @@ def attention_fwd(q, k, v, allowed, scale, rows=None, chunk=1024):
             hm = hq * Hm // Hq
             for c0 in range(0, rows.size, chunk):
                 rr = rows[c0:c0 + chunk]
-                s = scale * (q[b, rr, hq, :] @ k[b, :, hk, :].T)
+                s = _scores(q[b, rr, hq, :], k[b, :, hk, :], scale, score_mod, b, hq, rr)
                 a = _mask_rows(allowed, b, hm, rr, Sk)
                 has = a.any(axis=1)
                 sm = np.where(a, s, -np.inf)
@@ -93,7 +115,7 @@ def attention_fwd(q, k, v, allowed, scale, rows=None, chunk=1024):
     return out, lse
 
 
-def attention_bwd(q, k, v, dout, allowed, scale):
+def attention_bwd(q, k, v, dout, allowed, scale, score_mod=None):
     """Gradients of sum(out * dout) with respect to q, k, v (fp64, dense).
 
     P_ij = exp(s_ij - LSE_i) on allowed entries, 0 elsewhere;
@@ -109,7 +131,7 @@ def attention_bwd(q, k, v, dout, allowed, scale):
     Sk, Hkv = k.shape[1], k.shape[2]
     G = Hq // Hkv
     Hm = _mask_heads(allowed, Hq)
-    out, lse = attention_fwd(q, k, v, allowed, scale)
+    out, lse = attention_fwd(q, k, v, allowed, scale, score_mod=score_mod)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -120,7 +142,7 @@ def attention_bwd(q, k, v, dout, allowed, scale):
             hk = hq // G
             hm = hq * Hm // Hq
             a = _mask_rows(allowed, b, hm, rows, Sk)
-            s = scale * (q[b, :, hq, :] @ k[b, :, hk, :].T)
+            s = _scores(q[b, :, hq, :], k[b, :, hk, :], scale, score_mod, b, hq, rows)
             L = lse[b, hq]
             finite = np.isfinite(L)
             P = np.where(a & finite[:, None], np.exp(s - np.where(finite, L, 0.0)[:, None]), 0.0)
@@ -134,11 +156,13 @@ def attention_bwd(q, k, v, dout, allowed, scale):
     return dq, dk, dv, out, lse, delta
 
 
-def varlen_attention_fwd(q, k, v, cu_q, cu_k, scale, causal, left, right, rows=None):
+def varlen_attention_fwd(q, k, v, cu_q, cu_k, scale, causal, left, right, rows=None, score_mod=None):
     """Packed variable-length attention (tensorplay varlen "Packed layout").
 
     q (Tq, Hq, D), k/v (Tk, Hkv, D); query row t of sequence s may see key u
     iff u is in sequence s and the window predicate holds on local positions.
+    ``score_mod`` sees local positions too (q_idx = t - cu_q[s],
+    kv_idx = u - cu_k[s]) and the sequence index as b.
     Returns out (n, Hq, D), lse (Hq, n) for the rows ``rows`` (default all).
     """
     cq = np.asarray(cu_q).astype(np.int64)
@@ -156,11 +180,19 @@ def varlen_attention_fwd(q, k, v, cu_q, cu_k, scale, causal, left, right, rows=N
         return in_seq & window_allows(i[:, None], j, causal, left, right)
 
     allowed.heads = 1
-    out, lse = attention_fwd(_f64(q)[None], _f64(k)[None], _f64(v)[None], allowed, scale, rows=rows)
+    mod = None
+    if score_mod is not None:
+        def mod(score, b, h, q_idx, kv_idx):
+            t = np.asarray(q_idx).reshape(-1)
+            sq = seq_of[t]
+            return score_mod(score, sq[:, None], h, (t - cq[sq])[:, None],
+                             np.asarray(kv_idx).reshape(1, -1) - ck[sq][:, None])
+    out, lse = attention_fwd(_f64(q)[None], _f64(k)[None], _f64(v)[None], allowed, scale, rows=rows,
+                             score_mod=mod)
     return out[0], lse[0]
 
 
-def attention_bwd_sampled(q, k, v, dout, allowed, scale, b, hk, rows, cols, chunk=1024):
+def attention_bwd_sampled(q, k, v, dout, allowed, scale, b, hk, rows, cols, chunk=1024, score_mod=None):
     """Selected rows of dQ and columns of dK/dV for one (batch, kv head), fp64.
 
     Same formulas as ``attention_bwd`` evaluated without the dense (Sq, Sk)
@@ -168,8 +200,8 @@ def attention_bwd_sampled(q, k, v, dout, allowed, scale, b, hk, rows, cols, chun
     computed in row chunks, then dQ_i (for i in ``rows``) uses row i's
     P, dP and Delta, and dK_j / dV_j (for j in ``cols``) sum column j over all
     query rows and all query heads of the group. ``allowed`` is a callable
-    ``allowed(b, hm, rows) -> (len(rows), Sk)`` (as for ``attention_fwd``).
-    Returns dq (G, len(rows), D) for the group's heads, dk (len(cols), D),
+    ``allowed(b, hm, rows) -> (len(rows), Sk)`` (as for ``attention_fwd``);
+    ``score_mod`` as there (additive). Returns dq (G, len(rows), D) for the group's heads, dk (len(cols), D),
     dv (len(cols), D).
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
@@ -186,14 +218,16 @@ def attention_bwd_sampled(q, k, v, dout, allowed, scale, b, hk, rows, cols, chun
     for g in range(G):
         hq = hk * G + g
         hm = hq * Hm // Hq
+        mod = None if score_mod is None else (
+            lambda sc, bb, h_, qi, kj, hq=hq: score_mod(sc, b, hq, qi, kj))
         out, lse = attention_fwd(q[b:b + 1, :, hq:hq + 1], k[b:b + 1, :, hk:hk + 1], v[b:b + 1, :, hk:hk + 1],
-                                 lambda bb, h_, rr: allowed(b, hm, rr), scale, chunk=chunk)
+                                 lambda bb, h_, rr: allowed(b, hm, rr), scale, chunk=chunk, score_mod=mod)
         L = lse[0, 0]
         delta = (do[b, :, hq, :] * out[0, :, 0, :]).sum(axis=1)
         qq, dd = q[b, :, hq, :], do[b, :, hq, :]
         # dQ rows
         a = np.asarray(allowed(b, hm, rows), dtype=bool)
-        s = scale * (qq[rows] @ kk.T)
+        s = _scores(qq[rows], kk, scale, score_mod, b, hq, rows)
         fin = np.isfinite(L[rows])
         P = np.where(a & fin[:, None], np.exp(s - np.where(fin, L[rows], 0.0)[:, None]), 0.0)
         dP = dd[rows] @ vv.T
@@ -203,6 +237,8 @@ def attention_bwd_sampled(q, k, v, dout, allowed, scale, b, hk, rows, cols, chun
             rr = np.arange(c0, min(c0 + chunk, Sq))
             a = np.asarray(allowed(b, hm, rr), dtype=bool)[:, cols]
             s = scale * (qq[rr] @ kk[cols].T)
+            if score_mod is not None:
+                s = score_mod(s, b, hq, rr[:, None], cols[None, :])
             fin = np.isfinite(L[rr])
             P = np.where(a & fin[:, None], np.exp(s - np.where(fin, L[rr], 0.0)[:, None]), 0.0)
             dP = dd[rr] @ vv[cols].T

@@ -204,3 +204,116 @@ def test_sampled_backward_equals_dense_backward():
             np.testing.assert_allclose(sq, dq[b][rows][:, hk * 2:hk * 2 + 2].transpose(1, 0, 2), rtol=1e-10, atol=1e-12)
             np.testing.assert_allclose(sk, dk[b, cols, hk], rtol=1e-10, atol=1e-12)
             np.testing.assert_allclose(sv, dv[b, cols, hk], rtol=1e-10, atol=1e-12)
+
+
+# --- score_mod (tensorplay omni_attention, intro) -------------------------------------
+
+def _small_qkv(seed, B=1, S=40, H=2, D=16):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, S, H, D)), rng.standard_normal((B, S, H, D)),
+            rng.standard_normal((B, S, H, D)), rng.standard_normal((B, S, H, D)))
+
+
+def test_score_mod_row_bias_only_shifts_lse():
+    """A term that depends on the query row only cancels in the softmax: the
+    output is unchanged and the log-sum-exp moves by exactly that term. An
+    implementation that applied the term along the key axis would change the
+    output."""
+    q, k, v, _ = _small_qkv(1)
+    allowed = np.tril(np.ones((40, 40), bool))[None, None]
+    mod = lambda s, b, h, qi, kj: s + 0.37 * qi + 0.0 * kj  # noqa: E731
+    o0, l0 = A.attention_fwd(q, k, v, allowed, 0.25)
+    o1, l1 = A.attention_fwd(q, k, v, allowed, 0.25, score_mod=mod)
+    assert np.allclose(o1, o0, atol=1e-12)
+    assert np.allclose(l1 - l0, 0.37 * np.arange(40)[None, None, :], atol=1e-12)
+
+
+def test_alibi_equals_an_extra_key_feature():
+    """ALiBi by construction without score_mod: slope*(kv - q) = slope*kv - slope*q;
+    the kv part is an extra dimension (q' = [q, slope/scale], k' = [k, kv_idx]) and
+    the q part is a row constant. So outputs and dQ, dK (first D columns), dV
+    equal plain attention on the augmented inputs, and LSE differs by slope*q."""
+    q, k, v, do = _small_qkv(2, S=33)
+    slopes = np.array([0.5, 1.0])
+    scale = 0.3
+    allowed = np.tril(np.ones((33, 33), bool))[None, None]
+    B, S, H, D = q.shape
+    qa = np.concatenate([q, np.broadcast_to((slopes / scale)[None, None, :, None], (B, S, H, 1))], axis=3)
+    ka = np.concatenate([k, np.broadcast_to(np.arange(S, dtype=float)[None, :, None, None], (B, S, H, 1))], axis=3)
+    o_ref, l_ref = A.attention_fwd(qa, ka, v, allowed, scale)
+    o, l = A.attention_fwd(q, k, v, allowed, scale, score_mod=A.alibi(slopes))
+    assert np.allclose(o, o_ref, atol=1e-12)
+    assert np.allclose(l, l_ref - slopes[None, :, None] * np.arange(S)[None, None, :], atol=1e-10)
+    g = A.attention_bwd(q, k, v, do, allowed, scale, score_mod=A.alibi(slopes))
+    ga = A.attention_bwd(qa, ka, v, do, allowed, scale)
+    assert np.allclose(g[0], ga[0][..., :D], atol=1e-10)
+    assert np.allclose(g[1], ga[1][..., :D], atol=1e-10)
+    assert np.allclose(g[2], ga[2], atol=1e-10)
+
+
+def test_alibi_large_slope_picks_the_nearest_allowed_key():
+    """With a large positive slope the latest allowed key dominates: under a
+    causal mask row i attends to key i alone (output -> v_i, LSE -> scale q.k_i)."""
+    q, k, v, _ = _small_qkv(3, S=20)
+    allowed = np.tril(np.ones((20, 20), bool))[None, None]
+    o, l = A.attention_fwd(q, k, v, allowed, 0.2, score_mod=A.alibi([200.0, 200.0]))
+    assert np.allclose(o, v, atol=1e-9)
+    want = 0.2 * np.einsum("bshd,bshd->bhs", q, k)
+    assert np.allclose(l, want, atol=1e-9)
+
+
+def test_alibi_equals_sdpa_with_an_additive_float_mask():
+    """torch's SDPA adds a float attn_mask to the scaled scores; the ALiBi term
+    slope[h] * (j - i) plus -inf on disallowed entries must give the same
+    output and gradients (GQA, ragged Sq != Sk)."""
+    rng = np.random.default_rng(60)
+    B, Sq, Sk, Hq, Hkv, D = 2, 21, 30, 4, 2, 8
+    q, k, v = _rand((B, Sq, Hq, D), 61), _rand((B, Sk, Hkv, D), 62), _rand((B, Sk, Hkv, D), 63)
+    do = _rand((B, Sq, Hq, D), 64)
+    mask = rng.random((B, 1, Sq, Sk)) < 0.5
+    mask[..., 3] = True
+    slopes = np.array([0.25, -0.5, 1.0, 0.0625])
+    mod = A.alibi(slopes)
+    out, _ = A.attention_fwd(q, k, v, mask, 0.4, score_mod=mod)
+    dq, dk, dv, *_ = A.attention_bwd(q, k, v, do, mask, 0.4, score_mod=mod)
+    bias = slopes[None, :, None, None] * (np.arange(Sk)[None, :] - np.arange(Sq)[:, None])[None, None]
+    fmask = np.where(mask, bias, -np.inf)
+    t = [torch.tensor(x.transpose(0, 2, 1, 3), requires_grad=True) for x in (q, k, v)]
+    o = F.scaled_dot_product_attention(*t, attn_mask=torch.from_numpy(fmask), scale=0.4, enable_gqa=True)
+    np.testing.assert_allclose(out, o.detach().numpy().transpose(0, 2, 1, 3), rtol=1e-11, atol=1e-12)
+    o.backward(torch.from_numpy(do.transpose(0, 2, 1, 3).copy()))
+    for g, tt in zip((dq, dk, dv), t):
+        np.testing.assert_allclose(g, tt.grad.numpy().transpose(0, 2, 1, 3), rtol=1e-10, atol=1e-12)
+
+
+def test_score_mod_sampled_and_varlen_agree_with_dense():
+    rng = np.random.default_rng(70)
+    B, S, Hq, Hkv, D = 1, 36, 4, 2, 8
+    q, k, v = _rand((B, S, Hq, D), 71), _rand((B, S, Hkv, D), 72), _rand((B, S, Hkv, D), 73)
+    do = _rand((B, S, Hq, D), 74)
+    mask = np.tril(np.ones((S, S), bool))[None, None] & (rng.random((1, 1, S, S)) < 0.7)
+    mod = A.alibi([0.5, 1.0, 2.0, 0.125])
+    dq, dk, dv, *_ = A.attention_bwd(q, k, v, do, mask, 0.3, score_mod=mod)
+
+    def allowed(b, hm, rr):
+        return mask[0, 0][rr]
+    allowed.heads = 1
+    rows, cols = np.array([0, 9, 35]), np.array([0, 20, 35])
+    for hk in range(Hkv):
+        sq, sk, sv = A.attention_bwd_sampled(q, k, v, do, allowed, 0.3, 0, hk, rows, cols, chunk=8, score_mod=mod)
+        np.testing.assert_allclose(sq, dq[0][rows][:, hk * 2:hk * 2 + 2].transpose(1, 0, 2), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(sk, dk[0, cols, hk], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(sv, dv[0, cols, hk], rtol=1e-10, atol=1e-12)
+    # varlen: the bias uses positions local to each sequence
+    lengths = [7, 1, 12]
+    cu = M.cu_seqlens(lengths)
+    T = int(cu[-1])
+    qv, kv, vv = _rand((T, 2, 4), 75), _rand((T, 2, 4), 76), _rand((T, 2, 4), 77)
+    mod2 = A.alibi([0.75, 1.5])
+    out, lse = A.varlen_attention_fwd(qv, kv, vv, cu, cu, 0.5, True, -1, 0, score_mod=mod2)
+    for s, L in enumerate(lengths):
+        sl = slice(cu[s], cu[s + 1])
+        m = np.tril(np.ones((L, L), bool))
+        o_s, l_s = A.attention_fwd(qv[None, sl], kv[None, sl], vv[None, sl], m[None, None], 0.5, score_mod=mod2)
+        np.testing.assert_allclose(out[sl], o_s[0], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse[:, sl], l_s[0], rtol=1e-12)
