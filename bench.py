@@ -135,6 +135,18 @@ def rows_section(dev, causal=None):
         out["causal_dense_N8192_backward"] = {"bwd_ms": round(bwd_ms, 4),
                                               "bwd_tflops_algorithmic": round(2.5 * f / bwd_ms / 1e9, 1),
                                               "bwd_tflops_executed": round(3.5 * f / bwd_ms / 1e9, 1)}
+        # the same step with the per-head positional bias slope * (kv - q)
+        H = q.shape[1]
+        slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32, device=dev)
+        ob = torch.empty_like(q)
+        afwd_ms = _time(lambda: mfa.attn_fwd(q, k, v, rep, scale, "bhsd", out=ob, alibi_slopes=slopes))
+        do = torch.randn_like(q)
+        ob, lse = mfa.attn_fwd(q, k, v, rep, scale, "bhsd", alibi_slopes=slopes)
+        abwd_ms = _time(lambda: mfa.attn_bwd(q, k, v, ob, lse, do, rep, scale, "bhsd", alibi_slopes=slopes), reps=5)
+        del do, ob, lse
+        out["causal_dense_N8192_alibi"] = {"fwd_ms": round(afwd_ms, 4),
+                                           "fwd_tflops_attended_tiles": round(f / afwd_ms / 1e9, 1),
+                                           "bwd_ms": round(abwd_ms, 4)}
     # a1/a2 + a6 on the block-causal tiny and the GQA + cross workloads
     for name, w, nc in (("blockcausal_tiny_N256", W.blockcausal_tiny(), None),
                         ("blockcausal_gqa_cross_N1024", W.blockcausal_gqa_cross(), 256)):

@@ -249,6 +249,15 @@ typedef struct mfa_attn_args {
     int64_t k_stride[3];
     int64_t v_stride[3];
     int64_t o_stride[3];
+    /* Optional (Hq) fp32 device array, or NULL: adds slope[h] * (kv_idx -
+     * q_idx) to every scaled score of query head h before the mask and the
+     * softmax, the distance-decay score_mod of tensorplay omni_attention
+     * (intro) with a slope per head (slopes of 1 give that example exactly).
+     * Positions are indices along Sq and Sk (local to the sequence for
+     * VARLEN). The log-sum-exp includes the bias. Read by the forward and
+     * both backward passes, which must get the forward's slopes. Slopes must
+     * be finite. */
+    const float* alibi_slopes;
 } mfa_attn_args;
 
 /* Mask representation for one attention call. Only the fields of `kind` are
@@ -301,9 +310,10 @@ typedef struct mfa_mask {
                               entries); read by the dK/dV backward pass */
 } mfa_mask;
 
-/* Fused masked attention forward: out = softmax(scale q k^T + mask) v per
- * (batch, head), with log-sum-exp. scale is explicit (callers usually pass
- * D^-0.5). Head dims 64 and 128 are built; others give MFA_E_UNSUPPORTED. */
+/* Fused masked attention forward: out = softmax(scale q k^T + bias + mask) v
+ * per (batch, head), with log-sum-exp. scale is explicit (callers usually
+ * pass D^-0.5) and must be finite and positive (MFA_E_ARG otherwise). Head
+ * dims 64 and 128 are built; others give MFA_E_UNSUPPORTED. */
 mfa_status mfa_attn_fwd(const mfa_attn_args* args, const mfa_mask* mask, float scale,
                         hipStream_t stream);
 

@@ -355,11 +355,26 @@ def _dtype_code(t):
     raise MfaError(3, f"dtype {t.dtype} not supported (bfloat16, or float32 test mode)")
 
 
-def attn_fwd(q, k, v, mask: MaskRep, scale=None, layout="bshd", out=None, return_lse=True, lse=None):
+def _slopes_ptr(alibi_slopes, Hq, device):
+    """Device pointer of a (Hq,) fp32 slope vector for the positional bias
+    slope[h] * (kv_idx - q_idx), or None."""
+    if alibi_slopes is None:
+        return None
+    t = alibi_slopes
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.device != device \
+            or t.shape != (Hq,) or not t.is_contiguous():
+        raise ValueError(f"alibi_slopes must be a contiguous float32 tensor of shape ({Hq},) on {device}")
+    return t.data_ptr()
+
+
+def attn_fwd(q, k, v, mask: MaskRep, scale=None, layout="bshd", out=None, return_lse=True, lse=None,
+             alibi_slopes=None):
     """Masked attention forward (mfa_attn_fwd). Returns (out, lse or None).
 
     layout: "bshd" (B, S, H, D), "bhsd" (B, H, S, D) or "thd" (packed varlen).
-    lse is fp32 (B, Hq, Sq) ((Hq, T) for "thd").
+    lse is fp32 (B, Hq, Sq) ((Hq, T) for "thd"). alibi_slopes: optional
+    (Hq,) fp32 tensor; adds slope[h] * (kv_idx - q_idx) to the scaled scores
+    (positions local to the sequence for "thd").
     """
     B, Sq, Sk, Hq, Hkv, D = _dims(q, k, layout)
     if scale is None:
@@ -377,12 +392,13 @@ def attn_fwd(q, k, v, mask: MaskRep, scale=None, layout="bshd", out=None, return
     a.k_stride = _ffi.i64x3(*_bsh_strides(k, layout))
     a.v_stride = _ffi.i64x3(*_bsh_strides(v, layout))
     a.o_stride = _ffi.i64x3(*_bsh_strides(out, layout))
+    a.alibi_slopes = _slopes_ptr(alibi_slopes, Hq, q.device)
     m = mask.to_c()
     _ffi.check(_lib().mfa_attn_fwd(C.byref(a), C.byref(m), float(scale), _stream()))
     return out, (lse if return_lse else None)
 
 
-def _bwd_args(q, k, v, out, lse, dout, dq, dk, dv, delta, layout):
+def _bwd_args(q, k, v, out, lse, dout, dq, dk, dv, delta, layout, alibi_slopes=None):
     B, Sq, Sk, Hq, Hkv, D = _dims(q, k, layout)
     a = _ffi.BwdArgs()
     f = a.fwd
@@ -393,6 +409,7 @@ def _bwd_args(q, k, v, out, lse, dout, dq, dk, dv, delta, layout):
     f.k_stride = _ffi.i64x3(*_bsh_strides(k, layout))
     f.v_stride = _ffi.i64x3(*_bsh_strides(v, layout))
     f.o_stride = _ffi.i64x3(*_bsh_strides(out, layout))
+    f.alibi_slopes = _slopes_ptr(alibi_slopes, Hq, q.device)
     a.dout, a.dq, a.dk, a.dv, a.delta = dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), \
         delta.data_ptr()
     a.do_stride = _ffi.i64x3(*_bsh_strides(dout, layout))
@@ -416,15 +433,16 @@ def attn_bwd_dq(args, mask: MaskRep, scale):
     _ffi.check(_lib().mfa_attn_bwd_dq(C.byref(args), C.byref(m), float(scale), _stream()))
 
 
-def attn_bwd(q, k, v, out, lse, dout, mask: MaskRep, scale=None, layout="bshd"):
+def attn_bwd(q, k, v, out, lse, dout, mask: MaskRep, scale=None, layout="bshd", alibi_slopes=None):
     """Two-pass backward (any mask kind): preprocess, dK/dV over key blocks,
-    dQ over query tiles. Returns (dq, dk, dv) shaped like q, k, v."""
+    dQ over query tiles. Returns (dq, dk, dv) shaped like q, k, v. The
+    slopes must be the forward's."""
     B, Sq, Sk, Hq, Hkv, D = _dims(q, k, layout)
     if scale is None:
         scale = D ** -0.5
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty(B, Hq, Sq, dtype=torch.float32, device=q.device)
-    a = _bwd_args(q, k, v, out, lse, dout, dq, dk, dv, delta, layout)
+    a = _bwd_args(q, k, v, out, lse, dout, dq, dk, dv, delta, layout, alibi_slopes)
     attn_bwd_preprocess(a)
     attn_bwd_dkdv(a, mask, scale)
     attn_bwd_dq(a, mask, scale)
@@ -433,13 +451,13 @@ def attn_bwd(q, k, v, out, lse, dout, mask: MaskRep, scale=None, layout="bshd"):
 
 class _MaskedAttention(torch.autograd.Function):
     """Forward and backward both run the library's kernels; the mask
-    representation and scale are constants of the graph."""
+    representation, scale and bias slopes are constants of the graph."""
 
     @staticmethod
-    def forward(ctx, q, k, v, mask, scale, layout):
-        out, lse = attn_fwd(q, k, v, mask, scale, layout)
+    def forward(ctx, q, k, v, mask, scale, layout, alibi_slopes):
+        out, lse = attn_fwd(q, k, v, mask, scale, layout, alibi_slopes=alibi_slopes)
         ctx.save_for_backward(q, k, v, out, lse)
-        ctx.mask, ctx.scale, ctx.layout = mask, scale, layout
+        ctx.mask, ctx.scale, ctx.layout, ctx.slopes = mask, scale, layout, alibi_slopes
         return out
 
     @staticmethod
@@ -447,15 +465,16 @@ class _MaskedAttention(torch.autograd.Function):
         q, k, v, out, lse = ctx.saved_tensors
         if dout.stride(-1) != 1 or dout.data_ptr() % 16:
             dout = dout.contiguous()
-        dq, dk, dv = attn_bwd(q, k, v, out, lse, dout, ctx.mask, ctx.scale, ctx.layout)
-        return dq, dk, dv, None, None, None
+        dq, dk, dv = attn_bwd(q, k, v, out, lse, dout, ctx.mask, ctx.scale, ctx.layout, ctx.slopes)
+        return dq, dk, dv, None, None, None, None
 
 
-def masked_attention(q, k, v, mask: MaskRep, scale=None, layout="bshd"):
-    """Differentiable masked attention: out = softmax(scale q k^T + mask) v.
+def masked_attention(q, k, v, mask: MaskRep, scale=None, layout="bshd", alibi_slopes=None):
+    """Differentiable masked attention: out = softmax(scale q k^T + bias + mask) v.
 
     bf16 q, k, v with requires_grad as needed; gradients come from the
-    two-pass backward (mfa_attn_bwd_*). layout as for attn_fwd."""
+    two-pass backward (mfa_attn_bwd_*). layout and alibi_slopes as for
+    attn_fwd (the slopes get no gradient)."""
     if scale is None:
         scale = q.shape[-1] ** -0.5
-    return _MaskedAttention.apply(q, k, v, mask, float(scale), layout)
+    return _MaskedAttention.apply(q, k, v, mask, float(scale), layout, alibi_slopes)

@@ -21,7 +21,8 @@ i64x3 = C.c_int64 * 3
 class AttnArgs(C.Structure):
     _fields_ = [("dtype", C.c_int), ("B", C.c_int), ("Sq", C.c_int), ("Sk", C.c_int), ("Hq", C.c_int),
                 ("Hkv", C.c_int), ("D", C.c_int), ("q", vp), ("k", vp), ("v", vp), ("out", vp), ("lse", vp),
-                ("q_stride", i64x3), ("k_stride", i64x3), ("v_stride", i64x3), ("o_stride", i64x3)]
+                ("q_stride", i64x3), ("k_stride", i64x3), ("v_stride", i64x3), ("o_stride", i64x3),
+                ("alibi_slopes", vp)]
 
 
 class Mask(C.Structure):

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -401,6 +402,7 @@ static void fill_fwd(const mfa_attn_args* a, float scale, FwdDev& p) {
     p.B = a->B; p.Sq = a->Sq; p.Sk = a->Sk; p.Hq = a->Hq; p.Hkv = a->Hkv; p.G = a->Hq / a->Hkv;
     p.scale = scale;
     p.c2 = scale * kLog2e;
+    p.alibi = a->alibi_slopes;
 }
 
 static mfa_status check_strides(const char* name, const void* ptr, const int64_t* st, int dtype) {
@@ -417,7 +419,7 @@ static mfa_status check_strides(const char* name, const void* ptr, const int64_t
 mfa_status mfa_attn_fwd(const mfa_attn_args* a, const mfa_mask* mk, float scale, hipStream_t stream) {
     if (!a || !mk) return fail(MFA_E_ARG, "args or mask is NULL");
     MFA_TRY(check_attn_shapes(a));
-    if (!(scale == scale) || scale == 0.f) return fail(MFA_E_ARG, "scale must be a nonzero number");
+    if (!(scale > 0.f && scale <= FLT_MAX)) return fail(MFA_E_ARG, "scale must be finite and positive");
     MaskDev m;
     int BM = 128;
     MFA_TRY(fill_mask(a, mk, m, BM));
@@ -426,6 +428,7 @@ mfa_status mfa_attn_fwd(const mfa_attn_args* a, const mfa_mask* mk, float scale,
     MFA_TRY(dev_ptr(a->q, "q"));
     MFA_TRY(dev_ptr(a->out, "out"));
     MFA_TRY(dev_ptr(a->lse, "lse", true));
+    MFA_TRY(dev_ptr(a->alibi_slopes, "alibi_slopes", true));
     if (a->Sk > 0) {
         MFA_TRY(dev_ptr(a->k, "k"));
         MFA_TRY(dev_ptr(a->v, "v"));
@@ -543,10 +546,11 @@ mfa_status mfa_attn_bwd_preprocess(const mfa_attn_bwd_args* a, hipStream_t strea
 static mfa_status bwd_common(const mfa_attn_bwd_args* a, const mfa_mask* mk, float scale, bool dkdv, BwdDev& p,
                              MaskDev& m) {
     MFA_TRY(check_bwd(a, true));
-    if (!(scale == scale) || scale == 0.f) return fail(MFA_E_ARG, "scale must be a nonzero number");
+    if (!(scale > 0.f && scale <= FLT_MAX)) return fail(MFA_E_ARG, "scale must be finite and positive");
     if (a->fwd.B == 0 || a->fwd.Sq == 0) return ok();
     MFA_TRY(dev_ptr(a->fwd.q, "q"));
     MFA_TRY(dev_ptr(a->fwd.lse, "lse"));
+    MFA_TRY(dev_ptr(a->fwd.alibi_slopes, "alibi_slopes", true));
     if (a->fwd.Sk > 0) {
         MFA_TRY(dev_ptr(a->fwd.k, "k"));
         MFA_TRY(dev_ptr(a->fwd.v, "v"));

@@ -169,7 +169,7 @@ __device__ __forceinline__ uint32_t allowed_bits_T(const FwdDev& f, const MaskDe
 // 128-row granularity: a 64-row block takes its tile's kind), the window
 // arithmetic (varlen) or all blocks (no mask); they are walked through a
 // ScanWindow, once per query head of the GQA group.
-template <int D, int KIND>
+template <int D, int KIND, bool BIAS>
 __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p, MaskDev m) {
     constexpr int ROWB = 2 * D, TILEB = 64 * ROWB, NKC = D / 16, NDB = D / 32;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -332,9 +332,15 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
 
         // S = Q K^T and dP = dO V^T for the two 32-query halves
         f32x16 s[2], dp[2];
+        if constexpr (BIAS) {
+            const float sl = f.alibi[hk * f.G + g] / f.scale;
+            alibi_fill(s, sl, key_l - qb * 64 - 4 * hh, -sl);
+        } else {
+            s[0] = f32x16{};
+            s[1] = f32x16{};
+        }
 #pragma unroll
         for (int qh = 0; qh < 2; ++qh) {
-            s[qh] = f32x16{};
             dp[qh] = f32x16{};
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
@@ -420,7 +426,7 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
 // cursor and the same per-element masks.
 // ---------------------------------------------------------------------------
 
-template <int D, int NW, int KIND>
+template <int D, int NW, int KIND, bool BIAS>
 __global__ __launch_bounds__(NW * 64, (NW == 2 || KIND == MFA_MASK_BLOCKID) ? 1 : 2) void bwd_dq_kernel(BwdDev p, MaskDev m) {
     constexpr int BM = NW * 32;
     constexpr int ROWB = 2 * D, TILEB = 64 * ROWB, NKC = D / 16, NDB = D / 32;
@@ -488,6 +494,13 @@ __global__ __launch_bounds__(NW * 64, (NW == 2 || KIND == MFA_MASK_BLOCKID) ? 1 
         stage_tile<D>(vbase, 2 * f.vs1, kt_ * 64, t.k_len, sV + buf * TILEB, wave, NW, lane);
     };
 
+    float sl = 0.f;  // bias slope in raw score units
+    int d_row = 0;   // 4*hh - this lane's query position (local to the sequence)
+    if constexpr (BIAS) {
+        sl = f.alibi[t.hq] / f.scale;
+        d_row = 4 * hh - (row - t.q_base);
+    }
+
     int it = t.begin, kt = 0, kind = kTileEmpty;
     cursor.seek(f, m, t, lane, it, kt, kind);
     uint32_t fw[2];
@@ -508,9 +521,14 @@ __global__ __launch_bounds__(NW * 64, (NW == 2 || KIND == MFA_MASK_BLOCKID) ? 1 
 
         // S^T = K Q^T and dP^T = V dO^T (64 keys x 32 queries per wave)
         f32x16 s[2], dp[2];
+        if constexpr (BIAS) {
+            alibi_fill(s, sl, kt * kBN + d_row, sl);
+        } else {
+            s[0] = f32x16{};
+            s[1] = f32x16{};
+        }
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-            s[h2] = f32x16{};
             dp[h2] = f32x16{};
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
@@ -581,27 +599,37 @@ hipError_t launch_bwd_preprocess(const BwdDev& p, int D, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int D, int KIND>
+template <int D, int KIND, bool BIAS>
 static hipError_t dkdv_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) {
     const size_t lds = 4 * 64 * 2 * D + 4 * 64 * sizeof(float);
-    hipError_t e = hipFuncSetAttribute((const void*)&bwd_dkdv_kernel<D, KIND>,
+    hipError_t e = hipFuncSetAttribute((const void*)&bwd_dkdv_kernel<D, KIND, BIAS>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int64_t grid = KIND == MFA_MASK_VARLEN
                              ? (int64_t)m.nseq * p.f.Hkv * ((m.max_k + 63) / 64)
                              : (int64_t)p.f.B * p.f.Hkv * ((p.f.Sk + 63) / 64);
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, KIND>), dim3((unsigned)grid), dim3(128), lds, s, p, m);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, KIND, BIAS>), dim3((unsigned)grid), dim3(128), lds, s, p, m);
+    return hipGetLastError();
+}
+
+template <int D, int KIND>
+static hipError_t dkdv_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) {
+    return p.f.alibi ? dkdv_launch<D, KIND, true>(p, m, s) : dkdv_launch<D, KIND, false>(p, m, s);
+}
+
+template <int D, int KIND, bool BIAS>
+static hipError_t dq_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) {
+    constexpr int NW = KIND == MFA_MASK_BSR ? 2 : 4;
+    const size_t lds = 4 * 64 * 2 * D;
+    if (p.f.total == 0) return hipSuccess;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, KIND, BIAS>), dim3(p.f.total), dim3(NW * 64), lds, s, p, m);
     return hipGetLastError();
 }
 
 template <int D, int KIND>
 static hipError_t dq_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) {
-    constexpr int NW = KIND == MFA_MASK_BSR ? 2 : 4;
-    const size_t lds = 4 * 64 * 2 * D;
-    if (p.f.total == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, KIND>), dim3(p.f.total), dim3(NW * 64), lds, s, p, m);
-    return hipGetLastError();
+    return p.f.alibi ? dq_launch<D, KIND, true>(p, m, s) : dq_launch<D, KIND, false>(p, m, s);
 }
 
 template <int D>

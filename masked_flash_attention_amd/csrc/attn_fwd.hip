@@ -61,7 +61,7 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(__attribute__((address_space(3))) char*)(p));
 }
 
-template <int D, int NW, int KIND>
+template <int D, int NW, int KIND, bool BIAS>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, MaskDev m) {
     constexpr int BM = NW * 32;
     constexpr int NT = NW * 64;
@@ -191,6 +191,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
     __syncthreads();
 
     const float c2 = p.c2;
+    float sl = 0.f;  // bias slope in raw score units
+    int d_row = 0;   // 4*hh - this lane's query position (local to the sequence)
+    if constexpr (BIAS) {
+        sl = p.alibi[t.hq] / p.scale;
+        d_row = 4 * hh - (row - t.q_base);
+    }
     int buf = 0;
     if (it < t.end) do {
         int it_n = it + 1, kt_n = kt, kind_n = kTileEmpty;
@@ -203,8 +209,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
 
         // ---- S^T = K Q^T ----
         f32x16 s[2];
-        s[0] = f32x16{};
-        s[1] = f32x16{};
+        if constexpr (BIAS) {
+            alibi_fill(s, sl, kt * kBN + d_row, sl);
+        } else {
+            s[0] = f32x16{};
+            s[1] = f32x16{};
+        }
         const char* kb_ = sK + buf * TILEB;
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
@@ -333,6 +343,7 @@ __global__ __launch_bounds__(BM) void attn_fwd_f32_kernel(FwdDev p, MaskDev m) {
 #pragma unroll
             for (int d = 0; d < D; ++d) s = fmaf(q[d], kp[d], s);
             s *= p.scale;
+            if (p.alibi) s += p.alibi[t.hq] * (float)(key - (row - t.q_base));
             const float mn = fmaxf(mrun, s);
             const float corr = expf(mrun - mn);
             const float pe = expf(s - mn);
@@ -359,7 +370,10 @@ __global__ __launch_bounds__(BM) void attn_fwd_f32_kernel(FwdDev p, MaskDev m) {
 template <int D, int NW, int KIND>
 static hipError_t launch_bf16(const FwdDev& p, const MaskDev& m, hipStream_t s) {
     const size_t lds = 4 * KV<D>::TILEB;
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, KIND>), dim3(p.total), dim3(NW * 64), lds, s, p, m);
+    if (p.alibi)
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, KIND, true>), dim3(p.total), dim3(NW * 64), lds, s, p, m);
+    else
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, KIND, false>), dim3(p.total), dim3(NW * 64), lds, s, p, m);
     return hipGetLastError();
 }
 

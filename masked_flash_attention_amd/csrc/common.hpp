@@ -69,6 +69,7 @@ struct FwdDev {
     int B, Sq, Sk, Hq, Hkv, G;
     int nQt, nKt;
     float scale, c2;  // c2 = scale * log2(e)
+    const float* alibi;  // per query head slopes of the bias slope * (kv - q), or null
     int total;        // workgroups launched
     int xcd_remap;    // 1: logical id = (w % 8) * (total / 8) + w / 8
 };

@@ -108,6 +108,21 @@ __device__ __forceinline__ TileRange make_range(const FwdDev& p, const MaskDev& 
     }
 }
 
+// Positional bias slope * (kv_idx - q_idx) (the distance-decay score_mod of
+// tensorplay omni_attention, intro, with a slope per query head) in raw score
+// units, sl = slope / scale, written into a pair of score accumulators before
+// the q.k contraction adds onto them. Register r of half h holds the element at
+// offset h*32 + (r>>2)*8 + (r&3) along the accumulator's row axis; d0 is
+// kv_idx - q_idx of offset 0 and `step` the bias change per unit offset (sl
+// when the row axis runs over keys, -sl when it runs over queries).
+__device__ __forceinline__ void alibi_fill(f32x16 (&s)[2], float sl, int d0, float step) {
+    const float base = sl * (float)d0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[h][r] = fmaf(step, (float)(h * 32 + (r >> 2) * 8 + (r & 3)), base);
+}
+
 // Kind of a listed BSR block (r, c) with qb x kb blocks: token-level causal
 // j <= i on global positions inside the block when `causal` (mask_type
 // "causal" of flashinfer block_sparse_attention); out-of-range positions are

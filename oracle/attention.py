@@ -115,7 +115,7 @@ def attention_fwd(q, k, v, allowed, scale, rows=None, chunk=1024, score_mod=None
     return out, lse
 
 
-def attention_bwd(q, k, v, dout, allowed, scale, score_mod=None):
+def attention_bwd(q, k, v, dout, allowed, scale, score_mod=None, term_sums=False):
     """Gradients of sum(out * dout) with respect to q, k, v (fp64, dense).
 
     P_ij = exp(s_ij - LSE_i) on allowed entries, 0 elsewhere;
@@ -124,7 +124,17 @@ def attention_bwd(q, k, v, dout, allowed, scale, score_mod=None):
     dK_j = scale sum_i dS_ij q_i; dK/dV sum over the query heads of a group.
     The two-pass split (dK/dV over key blocks, dQ over query blocks) of the
     BinFlash method is a schedule of these same sums.
-    Returns dq, dk, dv, out, lse, delta (delta (B, Hq, Sq)).
+    Returns dq, dk, dv, out, lse, delta (delta (B, Hq, Sq)); with
+    ``term_sums`` also (tq, tk, tv), magnitudes that bound how far a kernel
+    storing P, dS and O in bf16 (unit roundoff u = 2^-9) can move each
+    gradient, to first order in u:
+      tv_j = sum_i P_ij |dO_i|                (P rounded for dV);
+      E_ij = P_ij (|dP_ij| + |Delta_i| + B_i), with
+      B_i  = sum_d |dO_id| |O_id| + sum_j P_ij |dP_ij|, which bounds the
+             error of a Delta taken from the rounded O (output rounding plus
+             the rounding of each P_ij, which scales a whole row v_j);
+      tq_i = scale sum_j E_ij |k_j|, tk_j = scale sum_i E_ij |q_i|
+    so that |error| <= u * t plus the fp32 accumulation error.
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, Sq, Hq, D = q.shape
@@ -136,6 +146,8 @@ def attention_bwd(q, k, v, dout, allowed, scale, score_mod=None):
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     delta = np.zeros((B, Hq, Sq))
+    if term_sums:
+        tq, tk, tv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     rows = np.arange(Sq)
     for b in range(B):
         for hq in range(Hq):
@@ -153,6 +165,14 @@ def attention_bwd(q, k, v, dout, allowed, scale, score_mod=None):
             dS = P * (dP - dl[:, None])
             dq[b, :, hq, :] = scale * (dS @ k[b, :, hk, :])
             dk[b, :, hk, :] += scale * (dS.T @ q[b, :, hq, :])
+            if term_sums:
+                Bi = (np.abs(do[b, :, hq, :]) * np.abs(out[b, :, hq, :])).sum(axis=1) + (P * np.abs(dP)).sum(axis=1)
+                E = P * (np.abs(dP) + np.abs(dl)[:, None] + Bi[:, None])
+                tq[b, :, hq, :] = scale * (E @ np.abs(k[b, :, hk, :]))
+                tk[b, :, hk, :] += scale * (E.T @ np.abs(q[b, :, hq, :]))
+                tv[b, :, hk, :] += P.T @ np.abs(do[b, :, hq, :])
+    if term_sums:
+        return dq, dk, dv, out, lse, delta, (tq, tk, tv)
     return dq, dk, dv, out, lse, delta
 
 

@@ -19,6 +19,15 @@ def grad_tolerance(ref):
     return BF16_OUT_TOL + GRAD_ULP * np.abs(ref)
 
 
+def grad_tolerance_terms(ref, term_sum):
+    """grad_tolerance plus the first-order bound of the bf16 storage of P, dS
+    and O (unit roundoff 2^-9) that the oracle's term_sums give. It matters
+    where rows put nearly all their weight on one key (a strong positional
+    bias): then |O| ~ |v|, so Delta = dO.O taken from the rounded O moves by
+    ~0.1, and dV_j is a small difference of large terms."""
+    return grad_tolerance(ref) + 2.0 ** -9 * np.abs(term_sum)
+
+
 def note(msg):
     """Name the case before each GPU step, flushed, so a fault names it."""
     print(f"[gpu-case] {msg}", flush=True)

@@ -51,7 +51,7 @@ def test_struct_layout_matches_header(tmp_path):
 int main() {
   printf("mfa_attn_args %zu\nmfa_mask %zu\nmfa_attn_bwd_args %zu\n",
          sizeof(mfa_attn_args), sizeof(mfa_mask), sizeof(mfa_attn_bwd_args));
-  P(mfa_attn_args, q); P(mfa_attn_args, lse); P(mfa_attn_args, o_stride);
+  P(mfa_attn_args, q); P(mfa_attn_args, lse); P(mfa_attn_args, o_stride); P(mfa_attn_args, alibi_slopes);
   P(mfa_mask, tile_kind); P(mfa_mask, q_block); P(mfa_mask, cu_q); P(mfa_mask, err); P(mfa_mask, win_right); P(mfa_mask, nseq);
   P(mfa_attn_bwd_args, dout); P(mfa_attn_bwd_args, dv_stride);
   return 0;
@@ -95,6 +95,13 @@ def test_attn_fwd_rejects_before_any_device_call(lib, kw, want):
     s = lib.mfa_attn_fwd(C.byref(_args(**kw)), C.byref(m), 0.125, None)
     assert _status(lib, s) == want
     assert lib.mfa_last_error().decode()
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("nan"), float("inf")])
+def test_scale_must_be_finite_and_positive(lib, scale):
+    m = _ffi.Mask()
+    assert _status(lib, lib.mfa_attn_fwd(C.byref(_args()), C.byref(m), scale, None)) == "MFA_E_ARG"
+    assert "scale" in lib.mfa_last_error().decode()
 
 
 def test_attn_fwd_null_and_mask_errors(lib):

@@ -317,3 +317,27 @@ def test_score_mod_sampled_and_varlen_agree_with_dense():
         o_s, l_s = A.attention_fwd(qv[None, sl], kv[None, sl], vv[None, sl], m[None, None], 0.5, score_mod=mod2)
         np.testing.assert_allclose(out[sl], o_s[0], rtol=1e-12, atol=1e-14)
         np.testing.assert_allclose(lse[:, sl], l_s[0], rtol=1e-12)
+
+
+def test_term_sums_bound_the_gradients():
+    """The rounding magnitudes bound each gradient (|sum| <= sum |.|, and
+    |dS_ij| <= E_ij), with equality for dV where every term has one sign (a
+    single allowed key per row makes dS zero and dV_j = sum_i |dO_i| when
+    dO > 0)."""
+    q, k, v = _rand((1, 12, 2, 4), 80), _rand((1, 12, 2, 4), 81), _rand((1, 12, 2, 4), 82)
+    do = _rand((1, 12, 2, 4), 83)
+    mask = np.random.default_rng(84).random((1, 1, 12, 12)) < 0.5
+    r = A.attention_bwd(q, k, v, do, mask, 0.5, score_mod=A.alibi([0.5, 2.0]), term_sums=True)
+    for g, t in zip(r[:3], r[6]):
+        assert np.all(np.abs(g) <= t + 1e-12)
+    eye = np.eye(12, dtype=bool)[None, None]
+    pos = np.abs(do)
+    dq, dk, dv, *_, (tq, tk, tv) = A.attention_bwd(q, k, v, pos, eye, 0.5, term_sums=True)
+    np.testing.assert_allclose(dv, tv, rtol=1e-13)
+    np.testing.assert_allclose(dv, pos, rtol=1e-13)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    # E_ii = |dP_ii| + |Delta_i| + B_i with B_i = sum|dO_i||v_i| + |dP_ii|
+    dP = np.einsum("bshd,bshd->bsh", pos, v)
+    B_ = np.einsum("bshd,bshd->bsh", pos, np.abs(v)) + np.abs(dP)
+    E = 2 * np.abs(dP) + B_
+    np.testing.assert_allclose(tq, 0.5 * E[..., None] * np.abs(k), rtol=1e-12)
