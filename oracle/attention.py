@@ -176,13 +176,15 @@ def attention_bwd(q, k, v, dout, allowed, scale, score_mod=None, term_sums=False
     return dq, dk, dv, out, lse, delta
 
 
-def varlen_attention_fwd(q, k, v, cu_q, cu_k, scale, causal, left, right, rows=None, score_mod=None):
+def varlen_attention_fwd(q, k, v, cu_q, cu_k, scale, causal, left, right, rows=None, score_mod=None,
+                         seqused_k=None):
     """Packed variable-length attention (tensorplay varlen "Packed layout").
 
     q (Tq, Hq, D), k/v (Tk, Hkv, D); query row t of sequence s may see key u
     iff u is in sequence s and the window predicate holds on local positions.
     ``score_mod`` sees local positions too (q_idx = t - cu_q[s],
-    kv_idx = u - cu_k[s]) and the sequence index as b.
+    kv_idx = u - cu_k[s]) and the sequence index as b. ``seqused_k`` keeps
+    only the first seqused_k[s] keys of each sequence.
     Returns out (n, Hq, D), lse (Hq, n) for the rows ``rows`` (default all).
     """
     cq = np.asarray(cu_q).astype(np.int64)
@@ -195,7 +197,10 @@ def varlen_attention_fwd(q, k, v, cu_q, cu_k, scale, causal, left, right, rows=N
         s = seq_of[rr]
         i = rr - cq[s]
         j = kidx[None, :] - ck[s][:, None]
-        in_seq = (j >= 0) & (j < (ck[s + 1] - ck[s])[:, None])
+        klen = ck[s + 1] - ck[s]
+        if seqused_k is not None:
+            klen = np.minimum(klen, np.asarray(seqused_k).astype(np.int64)[s])
+        in_seq = (j >= 0) & (j < klen[:, None])
         from .masks import window_allows
         return in_seq & window_allows(i[:, None], j, causal, left, right)
 

@@ -277,7 +277,33 @@ def bsr_entry_kind(r, c, q_block, kv_block, Sq, Skv, causal):
     return PARTIAL
 
 
-def bsr_col_kind(block_indptr, block_indices, q_block, kv_block, Sq, Skv, causal):
+def kv_valid_from_bits(kv_valid_bits, Skv):
+    """(B, Skv) bool from the (B, ceil(Skv/32)) u32 token-validity bitmap
+    (flashinfer block_sparse_attention, Parameters: kv_valid_bits), LSB-first."""
+    w = np.asarray(kv_valid_bits).astype(np.uint64)
+    out = np.zeros((w.shape[0], Skv), dtype=bool)
+    for b in range(w.shape[0]):
+        for j in range(Skv):
+            out[b, j] = (int(w[b, j // 32]) >> (j % 32)) & 1 == 1
+    return out
+
+
+def bsr_entry_kind_valid(r, c, q_block, kv_block, Sq, Skv, causal, kv_valid_row):
+    """Kind of listed block (r, c) when only the keys with kv_valid_row[j] may be
+    attended: no valid key in the block makes it empty, an invalid key makes a
+    full block partial."""
+    kind = bsr_entry_kind(r, c, q_block, kv_block, Sq, Skv, causal)
+    if kind == EMPTY or kv_valid_row is None:
+        return kind
+    seg = np.asarray(kv_valid_row)[c * kv_block:min((c + 1) * kv_block, Skv)]
+    if not seg.any():
+        return EMPTY
+    if kind == FULL and not seg.all():
+        return PARTIAL
+    return kind
+
+
+def bsr_col_kind(block_indptr, block_indices, q_block, kv_block, Sq, Skv, causal, kv_valid=None):
     ip = np.asarray(block_indptr).astype(np.int64)
     ix = np.asarray(block_indices).astype(np.int64)
     kind = np.zeros(ix.size, dtype=np.uint8)
@@ -285,7 +311,8 @@ def bsr_col_kind(block_indptr, block_indices, q_block, kv_block, Sq, Skv, causal
         for h in range(ip.shape[1]):
             for r in range(ip.shape[2] - 1):
                 for e in range(ip[b, h, r], ip[b, h, r + 1]):
-                    kind[e] = bsr_entry_kind(r, int(ix[e]), q_block, kv_block, Sq, Skv, causal)
+                    kind[e] = bsr_entry_kind_valid(r, int(ix[e]), q_block, kv_block, Sq, Skv, causal,
+                                                   None if kv_valid is None else kv_valid[b])
     return kind
 
 
@@ -317,8 +344,9 @@ def bsr_to_csc(block_indptr, block_indices, n_kv_blocks):
     return csc_ptr, csc_idx
 
 
-def bsr_mask(block_indptr, block_indices, q_block, kv_block, Sq, Skv, causal):
-    """Dense (B, Hkv, Sq, Skv) mask: listed blocks, intersected with j <= i if causal."""
+def bsr_mask(block_indptr, block_indices, q_block, kv_block, Sq, Skv, causal, kv_valid=None):
+    """Dense (B, Hkv, Sq, Skv) mask: listed blocks, intersected with j <= i if
+    causal and with the valid keys (kv_valid (B, Skv) bool) if given."""
     ip = np.asarray(block_indptr).astype(np.int64)
     ix = np.asarray(block_indices).astype(np.int64)
     B, H, R1 = ip.shape
@@ -331,7 +359,32 @@ def bsr_mask(block_indptr, block_indices, q_block, kv_block, Sq, Skv, causal):
                     m[b, h, r * q_block:(r + 1) * q_block, c * kv_block:(c + 1) * kv_block] = True
     if causal:
         m &= np.tri(Sq, Skv, dtype=bool)[None, None]
+    if kv_valid is not None:
+        m &= np.asarray(kv_valid, dtype=bool)[:, None, None, :]
     return m
+
+
+def bsr_from_bitmask(bits, n_kv_blocks):
+    """BSR rows from the exact-block bitmap of the bitmask sparse format
+    (flashinfer block_sparse_attention, Parameters: exact_block_bits,
+    sparse_format): bits (B, Hkv, nQb, ceil(nKb/32)) u32, LSB-first; bit c of
+    row r selects KV block c. Returns indptr (B, Hkv, nQb+1) with one running
+    offset over all rows, and the ascending block ids."""
+    w = np.asarray(bits).astype(np.uint64)
+    B, H, R = w.shape[:3]
+    indptr = np.zeros((B, H, R + 1), dtype=np.int64)
+    ids = []
+    run = 0
+    for b in range(B):
+        for h in range(H):
+            indptr[b, h, 0] = run
+            for r in range(R):
+                for c in range(n_kv_blocks):
+                    if (int(w[b, h, r, c // 32]) >> (c % 32)) & 1:
+                        ids.append(c)
+                        run += 1
+                indptr[b, h, r + 1] = run
+    return indptr.astype(np.int32), np.asarray(ids, dtype=np.int32)
 
 
 # ---------------------------------------------------------------------------
@@ -365,8 +418,11 @@ def window_allows(i, j, causal, left, right):
     return ok
 
 
-def varlen_mask(cu_q, cu_k, causal, left, right):
-    """Packed (Tq, Tk) mask: same sequence and window predicate on local positions."""
+def varlen_mask(cu_q, cu_k, causal, left, right, seqused_k=None):
+    """Packed (Tq, Tk) mask: same sequence and window predicate on local
+    positions; with ``seqused_k`` only the first seqused_k[s] keys of sequence s
+    may be attended (tensorplay varlen, intro: seqused_k bounds the usable key
+    length)."""
     cq = np.asarray(cu_q).astype(np.int64)
     ck = np.asarray(cu_k).astype(np.int64)
     Tq, Tk = int(cq[-1]), int(ck[-1])
@@ -374,8 +430,26 @@ def varlen_mask(cu_q, cu_k, causal, left, right):
     for s in range(cq.size - 1):
         qi = np.arange(cq[s + 1] - cq[s])
         kj = np.arange(ck[s + 1] - ck[s])
-        m[cq[s]:cq[s + 1], ck[s]:ck[s + 1]] = window_allows(qi[:, None], kj[None, :], causal, left, right)
+        ok = window_allows(qi[:, None], kj[None, :], causal, left, right)
+        if seqused_k is not None:
+            ok &= kj[None, :] < int(seqused_k[s])
+        m[cq[s]:cq[s + 1], ck[s]:ck[s + 1]] = ok
     return m
+
+
+def paged_to_packed(pages, block_table, lengths, page_size):
+    """Gather paged key/value storage into the packed layout (tensorplay
+    varlen, intro: block_table points at paged key/value blocks). pages
+    (n_pages, page_size, H, D); block_table (nseq, max_pages) page ids; key j
+    of sequence s sits at row j % page_size of page block_table[s, j //
+    page_size]. Returns (sum(lengths), H, D)."""
+    out = []
+    for s, L in enumerate(np.asarray(lengths).astype(np.int64)):
+        for j in range(int(L)):
+            out.append(np.asarray(pages[int(block_table[s][j // page_size]), j % page_size]))
+    if not out:
+        return np.zeros((0,) + tuple(np.asarray(pages).shape[2:]))
+    return np.stack(out)
 
 
 def varlen_tile_cost(Lq, Lk, q0, BM, BN, causal, left, right):

@@ -249,6 +249,60 @@ def test_bsr_csc_roundtrip():
                 assert rebuilt[r] == ix[ip[b, h, r]:ip[b, h, r + 1]].tolist()
 
 
+def _valid_keys(B, Skv, seed):
+    rng = np.random.default_rng(seed)
+    v = rng.random((B, Skv)) < 0.7
+    v[0, 64:128] = False     # one whole 64-key block invalid in batch entry 0
+    return v
+
+
+def test_kv_valid_bits_roundtrip_and_kinds_against_bruteforce():
+    """kv_valid_bits (flashinfer, Parameters): bits decode to the packing of
+    pack_bits_rows; the per-entry kinds equal a brute-force classification of
+    the dense mask, which is itself checked element by element against the
+    definition (listed block, j <= i, valid key)."""
+    ip, ix, nb = _small_bsr(seed=4, N=320, block=32)
+    blk, N = 32, 320
+    valid = _valid_keys(ip.shape[0], N, 5)
+    bits = M.pack_bits_rows(valid)
+    assert np.array_equal(M.kv_valid_from_bits(bits, N), valid)
+    m = M.bsr_mask(ip, ix, blk, blk, N, N, causal=True, kv_valid=valid)
+    kinds = M.bsr_col_kind(ip, ix, blk, blk, N, N, causal=True, kv_valid=valid)
+    for b in range(ip.shape[0]):
+        for h in range(ip.shape[1]):
+            tk = M.tile_kinds(m[b, h], blk, blk)
+            for r in range(nb):
+                listed = set(ix[ip[b, h, r]:ip[b, h, r + 1]].tolist())
+                for e in range(ip[b, h, r], ip[b, h, r + 1]):
+                    assert kinds[e] == tk[r, ix[e]]
+                for i in range(r * blk, (r + 1) * blk, 7):
+                    for j in range(0, N, 5):
+                        want = (j // blk) in listed and j <= i and bool(valid[b, j])
+                        assert m[b, h, i, j] == want
+    # the all-invalid block is never kept as partial or full
+    sel = [e for e in range(ip[0, 0, -1]) if ix[e] in (2, 3)]
+    assert sel and all(kinds[e] == M.EMPTY for e in range(ip[0, 0, 0], ip[0, 0, -1]) if ix[e] in (2, 3))
+
+
+def test_bitmask_format_to_bsr_against_selection():
+    """exact_block_bits (flashinfer, Parameters; sparse_format "bitmask"): a
+    random block selection written as LSB-first words comes back as canonical
+    BSR rows whose expansion at block size 1 is the selection itself."""
+    rng = np.random.default_rng(11)
+    B, H, R, nKb = 2, 3, 9, 70
+    sel = rng.random((B, H, R, nKb)) < 0.2
+    sel[0, 0, 0] = False
+    sel[1, 2, 8] = True
+    W_ = (nKb + 31) // 32
+    bits = np.zeros((B, H, R, W_), np.uint32)
+    for b, h, r, c in zip(*np.nonzero(sel)):
+        bits[b, h, r, c // 32] |= np.uint32(1 << (c % 32))
+    ip, ix = M.bsr_from_bitmask(bits, nKb)
+    assert M.bsr_validate(ip, ix, nKb) == sel.sum(axis=3).max()
+    assert np.array_equal(M.bsr_mask(ip, ix, 1, 1, R, nKb, causal=False), sel)
+    assert ip[0, 0, 0] == 0 and ip[-1, -1, -1] == sel.sum()
+
+
 # --- varlen packing (tensorplay varlen "Packed layout") ---------------------------
 
 def test_cu_seqlens_worked_example():
@@ -304,3 +358,51 @@ def test_varlen_schedule_costs_and_order():
         costs.append(touched)
         assert touched == M.varlen_tile_cost(L, L, q0, BM, BN, True, left, 0)
     assert costs == sorted(costs, reverse=True)
+
+
+def test_seqused_k_equals_dropping_the_unused_keys():
+    """seqused_k (tensorplay varlen, intro): attention with the first
+    seqused_k[s] keys of each sequence equals attention on a packed K/V from
+    which the other keys were removed."""
+    from oracle import attention as A
+    rng = np.random.default_rng(12)
+    Lq = np.array([5, 0, 17, 9])
+    Lk = np.array([8, 3, 20, 9])
+    used = np.array([3, 0, 20, 1])
+    cq, ck = M.cu_seqlens(Lq), M.cu_seqlens(Lk)
+    q = rng.standard_normal((int(cq[-1]), 2, 4))
+    k = rng.standard_normal((int(ck[-1]), 2, 4))
+    v = rng.standard_normal((int(ck[-1]), 2, 4))
+    for causal, win in ((False, (-1, -1)), (True, (-1, -1)), (False, (2, 1))):
+        out, lse = A.varlen_attention_fwd(q, k, v, cq, ck, 0.5, causal, win[0], win[1], seqused_k=used)
+        keep = np.concatenate([np.arange(ck[s], ck[s] + used[s]) for s in range(4)])
+        o2, l2 = A.varlen_attention_fwd(q, k[keep], v[keep], cq, M.cu_seqlens(used), 0.5, causal, win[0], win[1])
+        np.testing.assert_allclose(out, o2, rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(lse, l2, rtol=1e-13)
+        m = M.varlen_mask(cq, ck, causal, win[0], win[1], seqused_k=used)
+        m2 = M.varlen_mask(cq, M.cu_seqlens(used), causal, win[0], win[1])
+        assert np.array_equal(m[:, keep], m2) and not m[:, np.setdiff1d(np.arange(int(ck[-1])), keep)].any()
+
+
+def test_paged_gather_inverts_a_scatter_into_shuffled_pages():
+    """block_table (tensorplay varlen, intro): scattering a packed K into pages
+    in a random order and gathering through the table gives K back."""
+    rng = np.random.default_rng(13)
+    lengths = np.array([130, 1, 0, 64, 200])
+    page, H, D = 64, 2, 3
+    T = int(lengths.sum())
+    k = rng.standard_normal((T, H, D))
+    npg = [(int(L) + page - 1) // page for L in lengths]
+    n_pages = sum(npg) + 3
+    perm = rng.permutation(n_pages)
+    pages = np.full((n_pages, page, H, D), np.nan)
+    table = np.full((lengths.size, max(npg)), -1, np.int32)
+    nxt, off = 0, 0
+    for s, L in enumerate(lengths):
+        for pi in range(npg[s]):
+            table[s, pi] = perm[nxt]
+            nxt += 1
+        for j in range(int(L)):
+            pages[table[s, j // page], j % page] = k[off + j]
+        off += int(L)
+    assert np.array_equal(M.paged_to_packed(pages, table, lengths, page), k)
