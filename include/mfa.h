@@ -164,9 +164,9 @@ mfa_status mfa_predicate_tiles(const mfa_predicate* pred, int Nq, int Nk, uint8_
                                uint32_t* fine_bits, int32_t* row_ptr, int32_t* col_idx,
                                uint8_t* col_kind, hipStream_t stream);
 
-/* Synchronous inspection of BSR routing arrays ("flashinfer ...
- * block_sparse_attention": "BSR inputs are synchronously inspected to
- * validate canonical rows and derive their maximum width").
+/* Synchronous inspection of BSR routing arrays (flashinfer
+ * block_sparse_attention, description: the BSR inputs are checked on the
+ * host for canonical rows, and the widest row is found).
  *   indptr   (B, Hkv, nQb + 1) i32: row (b, h, r) lists
  *            indices[indptr[b,h,r] : indptr[b,h,r+1]] (offsets into one flat
  *            array)
@@ -180,7 +180,12 @@ mfa_status mfa_bsr_validate(const int32_t* indptr, const int32_t* indices, int B
 
 /* Kinds of the listed blocks and the column-major copy used by the dK/dV
  * pass. Rows must be canonical (see mfa_bsr_validate).
- *   causal     1 = token-level j <= i inside the blocks (mask_type "causal")
+ *   causal     1 = token-level j <= i inside the blocks (mask_type causal)
+ *   kv_valid_bits  optional (B, ceil(Skv/32)) u32 token-validity bitmap
+ *              (flashinfer block_sparse_attention, Parameters), LSB-first;
+ *              NULL = every key valid. A block with no valid key becomes
+ *              empty and a full block with an invalid key partial; pass the
+ *              same bitmap as mfa_mask.kv_bits to the attention calls.
  *   col_kind   (nnz) u8: kind of entry e given Sq, Skv, block sizes, causal
  *   csc_ptr    (B, Hkv, nKb + 1) i32: for (b, h) the segment starts at
  *              indptr[b,h,0]; csc_idx[csc_ptr[b,h,c] : csc_ptr[b,h,c+1]] lists
@@ -188,9 +193,23 @@ mfa_status mfa_bsr_validate(const int32_t* indptr, const int32_t* indices, int B
  *   csc_idx    (nnz) i32 */
 mfa_status mfa_bsr_prepare(const int32_t* indptr, const int32_t* indices, int B, int Hkv,
                            int nQb, int nKb, int64_t nnz, int q_block, int kv_block,
-                           int Sq, int Skv, int causal,
+                           int Sq, int Skv, int causal, const uint32_t* kv_valid_bits,
                            uint8_t* col_kind, int32_t* csc_ptr, int32_t* csc_idx,
                            hipStream_t stream);
+
+/* BSR rows from the bitmask sparse format (flashinfer
+ * block_sparse_attention, Parameters: exact_block_bits with sparse_format
+ * bitmask): bit c (LSB-first) of row (b, h, r) selects KV block c.
+ *   bits     (B, Hkv, nQb, ceil(nKb/32)) u32 device
+ *   indptr   (B, Hkv, nQb + 1) i32 device out: one running offset over all
+ *            rows, as mfa_bsr_validate expects
+ *   indices  (cap) i32 device out: ascending block ids per row; entries
+ *            past cap are not written (cap >= B*Hkv*nQb*nKb always holds
+ *            them; indptr[B,Hkv,nQb] is the count either way)
+ * Asynchronous; bits past nKb in a row's last word are ignored. */
+mfa_status mfa_bsr_from_bitmask(const uint32_t* bits, int B, int Hkv, int nQb, int nKb,
+                                int32_t* indptr, int32_t* indices, int64_t cap,
+                                hipStream_t stream);
 
 /* Variable-length packing and schedule ("tensorplay.nn.attention.varlen",
  * Packed layout).
@@ -273,6 +292,9 @@ typedef struct mfa_mask {
     const uint8_t* k_valid;
     const int32_t* qsum;
     const int32_t* ksum;
+    /* BLOCKID: key validity bits from the summary call. BSR: the optional
+     * kv_valid_bits token bitmap (B, ceil(Sk/32)) u32 (NULL = all valid),
+     * the same one given to mfa_bsr_prepare. */
     const uint32_t* kv_bits;
     /* TILES: outputs of mfa_compact_dense_mask for an (Sq, Sk) mask shared
      * by every batch entry and head. */
@@ -308,6 +330,25 @@ typedef struct mfa_mask {
     int win_right;         /* VARLEN only; -1 = open */
     int nseq;              /* VARLEN: number of sequences (cu_q holds nseq + 1
                               entries); read by the dK/dV backward pass */
+    /* VARLEN options (tensorplay varlen, intro), NULL / 0 when unused:
+     * seqused_k    (nseq) i32: only the first min(seqused_k[s], len_k[s])
+     *              keys of sequence s are attended (values < 0 count as 0);
+     *              the other keys' dK/dV rows are written as zeros.
+     * block_table  (nseq, max_pages) i32: paged k / v. k and v are then page
+     *              pools (n_pages, page_size, Hkv, D) addressed through
+     *              k_stride / v_stride = (page, row, head) element strides,
+     *              and key j of sequence s sits at row j % page_size of page
+     *              block_table[s, j / page_size]. page_size must be a
+     *              positive multiple of 64. cu_k still gives the key lengths.
+     *              A sequence needing more than max_pages pages, or whose
+     *              pages include an id outside [0, n_pages), gets NaN rows
+     *              and sets *err. Forward only (the backward passes return
+     *              MFA_E_UNSUPPORTED). */
+    const int32_t* seqused_k;
+    const int32_t* block_table;
+    int max_pages;
+    int page_size;
+    int n_pages;
 } mfa_mask;
 
 /* Fused masked attention forward: out = softmax(scale q k^T + bias + mask) v

@@ -217,8 +217,11 @@ def bsr_validate(block_indptr, block_indices, n_kv_blocks):
     return w.value
 
 
-def bsr_prepare(block_indptr, block_indices, q_block, kv_block, Sq, Skv, causal):
-    """(col_kind (nnz,) u8, csc_ptr (B, H, nKb+1), csc_idx (nnz,)) (mfa_bsr_prepare)."""
+def bsr_prepare(block_indptr, block_indices, q_block, kv_block, Sq, Skv, causal, kv_valid_bits=None):
+    """(col_kind (nnz,) u8, csc_ptr (B, H, nKb+1), csc_idx (nnz,)) (mfa_bsr_prepare).
+
+    kv_valid_bits: optional (B, ceil(Skv/32)) int32/uint32 token-validity
+    bitmap; give the same one to MaskRep.bsr."""
     ip, ix = _i32(block_indptr).contiguous(), _i32(block_indices).contiguous()
     B, H, R1 = ip.shape
     nKb = _cdiv(Skv, kv_block)
@@ -227,9 +230,36 @@ def bsr_prepare(block_indptr, block_indices, q_block, kv_block, Sq, Skv, causal)
     col_kind = torch.empty(max(1, nnz), dtype=torch.uint8, device=dev)
     csc_ptr = torch.empty(B, H, nKb + 1, dtype=torch.int32, device=dev)
     csc_idx = torch.empty(max(1, nnz), dtype=torch.int32, device=dev)
+    kvb = None if kv_valid_bits is None else _kv_bits(kv_valid_bits, B, Skv)
     _ffi.check(_lib().mfa_bsr_prepare(_p(ip), _p(ix), B, H, R1 - 1, nKb, nnz, q_block, kv_block, Sq, Skv,
-                                      int(bool(causal)), _p(col_kind), _p(csc_ptr), _p(csc_idx), _stream()))
+                                      int(bool(causal)), None if kvb is None else _p(kvb), _p(col_kind),
+                                      _p(csc_ptr), _p(csc_idx), _stream()))
     return col_kind[:nnz], csc_ptr, csc_idx[:nnz]
+
+
+def _kv_bits(bits, B, Skv):
+    t = bits.contiguous()
+    if t.dtype not in (torch.int32, torch.uint32) or tuple(t.shape) != (B, _cdiv(Skv, 32)):
+        raise ValueError(f"kv_valid_bits must be a 32-bit ({B}, {_cdiv(Skv, 32)}) tensor")
+    return t
+
+
+def bsr_from_bitmask(bits, n_kv_blocks, cap=None):
+    """BSR rows from the bitmask sparse format (mfa_bsr_from_bitmask).
+
+    bits: (B, Hkv, nQb, ceil(nKb/32)) 32-bit words, bit c of a row selects KV
+    block c. Returns (indptr (B, Hkv, nQb+1) i32, indices (cap,) i32), no
+    host sync: cap defaults to the largest possible count, and only
+    indices[:indptr[-1,-1,-1]] is meaningful."""
+    t = bits.contiguous()
+    B, H, R, W = t.shape
+    if W != _cdiv(n_kv_blocks, 32):
+        raise ValueError(f"last axis must hold ceil({n_kv_blocks}/32) words")
+    cap = B * H * R * n_kv_blocks if cap is None else int(cap)
+    indptr = torch.empty(B, H, R + 1, dtype=torch.int32, device=t.device)
+    indices = torch.empty(max(1, cap), dtype=torch.int32, device=t.device)
+    _ffi.check(_lib().mfa_bsr_from_bitmask(_p(t), B, H, R, n_kv_blocks, _p(indptr), _p(indices), cap, _stream()))
+    return indptr, indices[:cap]
 
 
 def varlen_schedule(len_q, len_k=None, causal=True, window=(-1, -1), BM=TILE_M, BN=TILE_N, work_cap=None):
@@ -287,22 +317,35 @@ class MaskRep:
 
     @staticmethod
     def bsr(block_indptr, block_indices, bsr_kind, q_block=64, kv_block=64, causal=True, csc_ptr=None,
-            csc_idx=None):
+            csc_idx=None, kv_valid_bits=None):
         t = {"indptr": _i32(block_indptr).contiguous(), "indices": _i32(block_indices).contiguous(),
              "bsr_kind": bsr_kind}
         if csc_ptr is not None:
             t["csc_ptr"], t["csc_idx"] = csc_ptr, csc_idx
+        if kv_valid_bits is not None:
+            t["kv_bits"] = kv_valid_bits.contiguous()
         return MaskRep(_ffi.MASK_BSR, t, {"q_block": q_block, "kv_block": kv_block, "causal": int(bool(causal))})
 
     @staticmethod
-    def varlen(sched, max_q, max_k, causal=True, window=(-1, -1), err=None):
+    def varlen(sched, max_q, max_k, causal=True, window=(-1, -1), err=None, seqused_k=None, block_table=None,
+               page_size=None, n_pages=None):
+        """Packed variable-length mask. seqused_k: optional (nseq,) int32 keys
+        used per sequence. block_table (nseq, max_pages) int32 with page_size
+        and n_pages: k / v are page pools (n_pages, page_size, Hkv, D)
+        (forward only)."""
         t = {"cu_q": sched["cu_q"], "cu_k": sched["cu_k"], "work": sched["work"]}
+        ints = {"work_cap": sched["work_cap"], "max_q": int(max_q), "max_k": int(max_k),
+                "causal": int(bool(causal)), "win_left": int(window[0]), "win_right": int(window[1]),
+                "nseq": int(sched["cu_q"].numel()) - 1}
         if err is not None:
             t["err"] = err
-        return MaskRep(_ffi.MASK_VARLEN, t, {"work_cap": sched["work_cap"], "max_q": int(max_q),
-                                             "max_k": int(max_k), "causal": int(bool(causal)),
-                                             "win_left": int(window[0]), "win_right": int(window[1]),
-                                             "nseq": int(sched["cu_q"].numel()) - 1})
+        if seqused_k is not None:
+            t["seqused_k"] = _i32(seqused_k).contiguous()
+        if block_table is not None:
+            bt = _i32(block_table).contiguous()
+            t["block_table"] = bt
+            ints.update(max_pages=int(bt.shape[1]), page_size=int(page_size), n_pages=int(n_pages))
+        return MaskRep(_ffi.MASK_VARLEN, t, ints)
 
     def to_c(self):
         m = _ffi.Mask()
@@ -329,11 +372,16 @@ def _bsh_strides(t, layout):
     if layout == "bhsd":
         return (t.stride(0), t.stride(2), t.stride(1))
     if layout == "thd":
+        if t.dim() == 4:  # paged k / v: (page, row, head) strides
+            return (t.stride(0), t.stride(1), t.stride(2))
         return (0, t.stride(0), t.stride(1))
     raise ValueError(f"unknown layout {layout!r}")
 
 
 def _dims(q, k, layout):
+    if layout == "thd" and k.dim() == 4:  # paged k / v: (n_pages, page_size, Hkv, D)
+        Sq, Hq, D = q.shape
+        return 1, Sq, k.shape[0] * k.shape[1], Hq, k.shape[2], D
     if layout == "bshd":
         B, Sq, Hq, D = q.shape
         Sk, Hkv = k.shape[1], k.shape[2]

@@ -34,7 +34,9 @@ class Mask(C.Structure):
                 ("q_block", C.c_int), ("kv_block", C.c_int),
                 ("cu_q", vp), ("cu_k", vp), ("work", vp), ("work_cap", C.c_int), ("max_q", C.c_int),
                 ("max_k", C.c_int), ("err", vp),
-                ("causal", C.c_int), ("win_left", C.c_int), ("win_right", C.c_int), ("nseq", C.c_int)]
+                ("causal", C.c_int), ("win_left", C.c_int), ("win_right", C.c_int), ("nseq", C.c_int),
+                ("seqused_k", vp), ("block_table", vp), ("max_pages", C.c_int), ("page_size", C.c_int),
+                ("n_pages", C.c_int)]
 
 
 class BwdArgs(C.Structure):
@@ -67,7 +69,8 @@ SIGNATURES = {
     "mfa_predicate_tiles": ([C.POINTER(Predicate), C.c_int, C.c_int, vp, vp, vp, vp, vp, vp], C.c_int),
     "mfa_bsr_validate": ([vp, vp, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64, C.POINTER(C.c_int), vp], C.c_int),
     "mfa_bsr_prepare": ([vp, vp, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int, C.c_int, C.c_int,
-                         C.c_int, C.c_int, vp, vp, vp, vp], C.c_int),
+                         C.c_int, C.c_int, vp, vp, vp, vp, vp], C.c_int),
+    "mfa_bsr_from_bitmask": ([vp, C.c_int, C.c_int, C.c_int, C.c_int, vp, vp, C.c_int64, vp], C.c_int),
     "mfa_varlen_schedule": ([vp, vp, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, vp, vp, vp, vp,
                              C.c_int, vp, vp], C.c_int),
     "mfa_attn_fwd": ([C.POINTER(AttnArgs), C.POINTER(Mask), C.c_float, vp], C.c_int),

@@ -23,7 +23,8 @@ hipError_t launch_compact(const uint8_t*, int, int, uint8_t*, uint32_t*, int32_t
 hipError_t launch_predicate_tiles(const mfa_predicate&, int, int, uint8_t*, uint32_t*, int32_t*, int32_t*, uint8_t*,
                                   hipStream_t);
 hipError_t launch_bsr_prepare(const int32_t*, const int32_t*, int, int, int, int, int64_t, int, int, int, int, int,
-                              uint8_t*, int32_t*, int32_t*, hipStream_t);
+                              const uint32_t*, uint8_t*, int32_t*, int32_t*, hipStream_t);
+hipError_t launch_bsr_from_bitmask(const uint32_t*, int, int, int, int, int32_t*, int32_t*, int64_t, hipStream_t);
 hipError_t launch_varlen_schedule(const int32_t*, const int32_t*, int, int, int, int, int, int, int32_t*, int32_t*,
                                   int32_t*, int32_t*, int, int32_t*, hipStream_t);
 hipError_t launch_bwd_preprocess(const BwdDev& p, int D, hipStream_t s);
@@ -247,8 +248,9 @@ mfa_status mfa_bsr_validate(const int32_t* indptr, const int32_t* indices, int B
 }
 
 mfa_status mfa_bsr_prepare(const int32_t* indptr, const int32_t* indices, int B, int Hkv, int nQb, int nKb,
-                           int64_t nnz, int q_block, int kv_block, int Sq, int Skv, int causal, uint8_t* col_kind,
-                           int32_t* csc_ptr, int32_t* csc_idx, hipStream_t stream) {
+                           int64_t nnz, int q_block, int kv_block, int Sq, int Skv, int causal,
+                           const uint32_t* kv_valid_bits, uint8_t* col_kind, int32_t* csc_ptr, int32_t* csc_idx,
+                           hipStream_t stream) {
     if (B < 0 || Hkv < 0 || nQb < 0 || nKb < 0 || nnz < 0 || Sq < 0 || Skv < 0)
         return fail(MFA_E_SHAPE, "negative size");
     if (q_block <= 0 || kv_block <= 0) return fail(MFA_E_ARG, "block sizes must be positive");
@@ -260,14 +262,29 @@ mfa_status mfa_bsr_prepare(const int32_t* indptr, const int32_t* indices, int B,
     MFA_TRY(ensure_device());
     MFA_TRY(dev_ptr(indptr, "indptr"));
     MFA_TRY(dev_ptr(csc_ptr, "csc_ptr"));
+    MFA_TRY(dev_ptr(kv_valid_bits, "kv_valid_bits", true));
     if (nnz > 0) {
         MFA_TRY(dev_ptr(indices, "indices"));
         MFA_TRY(dev_ptr(col_kind, "col_kind"));
         MFA_TRY(dev_ptr(csc_idx, "csc_idx"));
     }
     return hip_ok(launch_bsr_prepare(indptr, indices, B, Hkv, nQb, nKb, nnz, q_block, kv_block, Sq, Skv, causal ? 1 : 0,
-                                     col_kind, csc_ptr, csc_idx, stream),
+                                     kv_valid_bits, col_kind, csc_ptr, csc_idx, stream),
                   "bsr prepare launch");
+}
+
+mfa_status mfa_bsr_from_bitmask(const uint32_t* bits, int B, int Hkv, int nQb, int nKb, int32_t* indptr,
+                                int32_t* indices, int64_t cap, hipStream_t stream) {
+    if (B < 0 || Hkv < 0 || nQb < 0 || nKb < 0 || cap < 0) return fail(MFA_E_SHAPE, "negative size");
+    const int64_t rows = (int64_t)B * Hkv * nQb;
+    if (rows * nKb > INT32_MAX) return fail(MFA_E_UNSUPPORTED, "more than 2^31 - 1 possible blocks");
+    if ((int64_t)B * Hkv == 0) return ok();
+    MFA_TRY(ensure_device());
+    MFA_TRY(dev_ptr(indptr, "indptr"));
+    if (rows > 0 && nKb > 0) MFA_TRY(dev_ptr(bits, "bits"));
+    if (cap > 0) MFA_TRY(dev_ptr(indices, "indices"));
+    return hip_ok(launch_bsr_from_bitmask(bits, B, Hkv, nQb, nKb, indptr, indices, cap, stream),
+                  "bsr from bitmask launch");
 }
 
 mfa_status mfa_varlen_schedule(const int32_t* len_q, const int32_t* len_k, int nseq, int BM, int BN, int causal,
@@ -334,6 +351,7 @@ static mfa_status fill_mask(const mfa_attn_args* a, const mfa_mask* mk, MaskDev&
             m.csc_idx = mk->csc_idx;
             m.causal = mk->causal ? 1 : 0;
             m.nQb = cdiv(a->Sq, 64);
+            m.kv_bits = mk->kv_bits;  // optional kv_valid_bits
             break;
         case MFA_MASK_VARLEN:
             if (a->B != 1) return fail(MFA_E_SHAPE, "varlen attention takes packed (T, H, D) tensors with B = 1");
@@ -350,6 +368,17 @@ static mfa_status fill_mask(const mfa_attn_args* a, const mfa_mask* mk, MaskDev&
             m.causal = mk->causal ? 1 : 0;
             m.win_left = mk->win_left;
             m.win_right = mk->win_right;
+            m.seqused_k = mk->seqused_k;
+            m.block_table = mk->block_table;
+            if (mk->block_table) {
+                if (mk->page_size <= 0 || mk->page_size % 64 != 0)
+                    return fail(MFA_E_ARG, "page_size must be a positive multiple of 64 (got %d)", mk->page_size);
+                if (mk->max_pages <= 0 || mk->n_pages <= 0)
+                    return fail(MFA_E_ARG, "max_pages and n_pages must be positive with a block table");
+                m.max_pages = mk->max_pages;
+                m.page_size = mk->page_size;
+                m.n_pages = mk->n_pages;
+            }
             break;
         default: return fail(MFA_E_ARG, "unknown mask kind %d", mk->kind);
     }
@@ -376,12 +405,15 @@ static mfa_status check_mask_ptrs(const mfa_mask* mk) {
             MFA_TRY(dev_ptr(mk->indptr, "indptr"));
             MFA_TRY(dev_ptr(mk->indices, "indices"));
             MFA_TRY(dev_ptr(mk->bsr_kind, "bsr_kind"));
+            MFA_TRY(dev_ptr(mk->kv_bits, "kv_bits", true));
             break;
         case MFA_MASK_VARLEN:
             MFA_TRY(dev_ptr(mk->cu_q, "cu_q"));
             MFA_TRY(dev_ptr(mk->cu_k, "cu_k"));
             if (mk->work_cap > 0) MFA_TRY(dev_ptr(mk->work, "work"));
             MFA_TRY(dev_ptr(mk->err, "err", true));
+            MFA_TRY(dev_ptr(mk->seqused_k, "seqused_k", true));
+            MFA_TRY(dev_ptr(mk->block_table, "block_table", true));
             break;
         default: break;
     }
@@ -511,6 +543,7 @@ static mfa_status check_bwd_mask(const mfa_attn_bwd_args* a, const mfa_mask* mk,
             }
             break;
         case MFA_MASK_BSR:
+            MFA_TRY(dev_ptr(mk->kv_bits, "kv_bits", true));
             if (dkdv) {
                 MFA_TRY(dev_ptr(mk->csc_ptr, "csc_ptr"));
                 MFA_TRY(dev_ptr(mk->csc_idx, "csc_idx"));
@@ -521,9 +554,12 @@ static mfa_status check_bwd_mask(const mfa_attn_bwd_args* a, const mfa_mask* mk,
             }
             break;
         case MFA_MASK_VARLEN:
+            if (mk->block_table)
+                return fail(MFA_E_UNSUPPORTED, "paged k / v (block_table) is supported by the forward only");
             MFA_TRY(dev_ptr(mk->cu_q, "cu_q"));
             MFA_TRY(dev_ptr(mk->cu_k, "cu_k"));
             MFA_TRY(dev_ptr(mk->err, "err", true));
+            MFA_TRY(dev_ptr(mk->seqused_k, "seqused_k", true));
             if (dkdv) {
                 if (mk->nseq < 0) return fail(MFA_E_ARG, "negative nseq");
             } else if (mk->work_cap > 0) {

@@ -146,7 +146,7 @@ __device__ __forceinline__ uint32_t allowed_bits_T(const FwdDev& f, const MaskDe
         const int i = qi0 + (rr >> 2) * 8 + 4 * hh + (rr & 3);
         bool ok = i < q_len && key_l < k_len;
         if constexpr (KIND == MFA_MASK_BSR) {
-            ok = ok && (!m.causal || key_l <= i);
+            ok = ok && kval && (!m.causal || key_l <= i);
         } else if constexpr (KIND == MFA_MASK_TILES) {
             if (ok) ok = (m.fine_bits[(int64_t)i * m.fine_words + (key_l >> 5)] >> (key_l & 31)) & 1u;
         } else if constexpr (KIND == MFA_MASK_BLOCKID) {
@@ -185,6 +185,7 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
 
     int b = 0, hk = 0, kbk = 0;
     int q_base = 0, q_len = f.Sq, k_base = 0, k_len = f.Sk;
+    int k_alloc = f.Sk;  // keys whose gradient rows are written (k_len of them are attended)
     bool len_error = false;
     if constexpr (KIND == MFA_MASK_VARLEN) {
         const int nKbm = (m.max_k + 63) / 64;
@@ -195,9 +196,10 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
         q_base = m.cu_q[seq];
         q_len = m.cu_q[seq + 1] - q_base;
         k_base = m.cu_k[seq];
-        k_len = m.cu_k[seq + 1] - k_base;
-        if (kbk * 64 >= k_len) return;
-        if (q_len > m.max_q || k_len > m.max_k) {
+        k_alloc = m.cu_k[seq + 1] - k_base;
+        k_len = m.seqused_k ? min(k_alloc, max(m.seqused_k[seq], 0)) : k_alloc;
+        if (kbk * 64 >= k_alloc) return;
+        if (q_len > m.max_q || k_alloc > m.max_k) {
             len_error = true;
             if (m.err && threadIdx.x == 0) *m.err = 1;
         }
@@ -238,6 +240,18 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
             kval = (m.kv_bits[(int64_t)b * m.kv_words + (key_l >> 5)] >> (key_l & 31)) & 1u;
         }
     }
+    // BSR token validity: whole-block state from the block's two words
+    bool blk_all_valid = true, blk_any_valid = true;
+    if constexpr (KIND == MFA_MASK_BSR) {
+        kval = true;
+        if (m.kv_bits) {
+            const uint32_t* kw = m.kv_bits + (int64_t)b * m.kv_words + 2 * kbk;
+            const uint32_t w0 = kw[0], w1 = (2 * kbk + 1 < m.kv_words) ? kw[1] : 0u;
+            blk_all_valid = w0 == 0xFFFFFFFFu && w1 == 0xFFFFFFFFu;
+            blk_any_valid = (w0 | w1) != 0u;
+            kval = key_ok && (((key_l < 32 + kbk * 64 ? w0 : w1) >> (key_l & 31)) & 1u);
+        }
+    }
 
     // ---- the query blocks of this key block ----
     const int nQb = (q_len + 63) / 64;
@@ -246,10 +260,10 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
         const int nKb = (f.Sk + 63) / 64;
         const int* cp = m.csc_ptr + ((int64_t)b * f.Hkv + hk) * (nKb + 1);
         e0 = cp[kbk];
-        pend = cp[kbk + 1] - e0;
+        pend = blk_any_valid ? cp[kbk + 1] - e0 : 0;
     } else if constexpr (KIND == MFA_MASK_VARLEN) {
         const int j0 = kbk * 64, j1 = min(j0 + 63, k_len - 1);
-        int lo = 0, hi = q_len - 1;
+        int lo = 0, hi = j1 >= j0 ? q_len - 1 : -1;  // no used key in the block: no query block
         if (m.causal) lo = max(lo, j0);
         if (m.win_right >= 0) lo = max(lo, j0 - m.win_right);
         if (m.win_left >= 0) hi = min(hi, j1 + m.win_left);
@@ -262,6 +276,7 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
         if constexpr (KIND == MFA_MASK_BSR) {
             qb = m.csc_idx[e0 + pos];
             kind = bsr_kind_of(qb, kbk, 64, 64, f.Sq, f.Sk, m.causal);
+            if (kind == kTileFull && !blk_all_valid) kind = kTilePartial;
         } else if constexpr (KIND == MFA_MASK_TILES) {
             kind = m.tile_kind[(int64_t)(qb >> 1) * f.nKt + kbk];
         } else if constexpr (KIND == MFA_MASK_BLOCKID) {
@@ -400,7 +415,7 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
         ent = ent_n;
     }
 
-    if (!key_ok) return;
+    if (key_l >= k_alloc) return;  // keys past the used length get zero gradients
     const float nanv = __builtin_nanf("");
     bf16* dkp = (bf16*)p.dk + (int64_t)b * p.dks0 + (int64_t)key * p.dks1 + (int64_t)hk * p.dks2;
     bf16* dvp = (bf16*)p.dv + (int64_t)b * p.dvs0 + (int64_t)key * p.dvs1 + (int64_t)hk * p.dvs2;

@@ -132,13 +132,35 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
     }
     // `live` false issues the same loads with an empty range (they write
     // zeros into the free buffer), which keeps the loop free of a branch.
+    // Paged keys (varlen with a block table): each tile lies inside one page,
+    // found through the table (the tile range checked every page id; a bad
+    // one turned the rows into NaN, and its tiles read as zeros here).
+    auto tile_base = [&](int kt, bool live, const char*& kp, const char*& vp, int& kn, int& vn) {
+        const int64_t k0 = (int64_t)kt * kBN * krow, v0 = (int64_t)kt * kBN * vrow;
+        kp = Kbh + k0;
+        vp = Vbh + v0;
+        kn = (int)(live && knrec > k0 ? knrec - k0 : 0);
+        vn = (int)(live && vnrec > v0 ? vnrec - v0 : 0);
+        if constexpr (KIND == MFA_MASK_VARLEN) {
+            if (m.block_table) {
+                int r = 0;
+                const int pg = page_of(m, t.seq, kt * kBN, r);
+                const bool ok = pg >= 0;
+                const int rows = min(kBN, t.k_len - kt * kBN);
+                kp = Kbh + 2 * ((int64_t)max(pg, 0) * p.ks0 + (int64_t)r * p.ks1);
+                vp = Vbh + 2 * ((int64_t)max(pg, 0) * p.vs0 + (int64_t)r * p.vs1);
+                kn = (live && ok && rows > 0) ? (int)((rows - 1) * krow + ROWB) : 0;
+                vn = (live && ok && rows > 0) ? (int)((rows - 1) * vrow + ROWB) : 0;
+            }
+        }
+    };
     auto load_tile = [&](int kt, int buf, bool live) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer-resource builtins exist only in the device pass
-        const int64_t k0 = (int64_t)kt * kBN * krow, v0 = (int64_t)kt * kBN * vrow;
-        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(Kbh + k0), 0, (int)(live && knrec > k0 ? knrec - k0 : 0), 0x00020000);
-        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(Vbh + v0), 0, (int)(live && vnrec > v0 ? vnrec - v0 : 0), 0x00020000);
+        const char *kp, *vp;
+        int kn, vn;
+        tile_base(kt, live, kp, vp, kn, vn);
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, kn, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, vn, 0x00020000);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int blk = (wave * NI + i) * 1024;
@@ -339,6 +361,16 @@ __global__ __launch_bounds__(BM) void attn_fwd_f32_kernel(FwdDev p, MaskDev m) {
             if (key >= t.k_len) break;
             if (kind == kTilePartial && !allowed<KIND>(p, m, t, rm, key)) continue;
             const float* kp = K + (int64_t)key * p.ks1;
+            const float* vp = V + (int64_t)key * p.vs1;
+            if constexpr (KIND == MFA_MASK_VARLEN) {
+                if (m.block_table) {
+                    int r = 0;
+                    const int pg = page_of(m, t.seq, key, r);
+                    if (pg < 0) continue;  // the tile range flagged this sequence
+                    kp = K + (int64_t)pg * p.ks0 + (int64_t)r * p.ks1;
+                    vp = V + (int64_t)pg * p.vs0 + (int64_t)r * p.vs1;
+                }
+            }
             float s = 0.f;
 #pragma unroll
             for (int d = 0; d < D; ++d) s = fmaf(q[d], kp[d], s);
@@ -348,7 +380,6 @@ __global__ __launch_bounds__(BM) void attn_fwd_f32_kernel(FwdDev p, MaskDev m) {
             const float corr = expf(mrun - mn);
             const float pe = expf(s - mn);
             l = l * corr + pe;
-            const float* vp = V + (int64_t)key * p.vs1;
 #pragma unroll
             for (int d = 0; d < D; ++d) o[d] = fmaf(pe, vp[d], o[d] * corr);
             mrun = mn;

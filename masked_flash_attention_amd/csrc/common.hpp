@@ -53,6 +53,9 @@ struct MaskDev {
     int kv_words;     // ceil(Sk / 32)
     int nQb;          // BSR query-block rows per (b, h)
     int nseq;         // VARLEN sequences
+    const int32_t* seqused_k;    // VARLEN: keys used per sequence, or null
+    const int32_t* block_table;  // VARLEN: (nseq, max_pages) pages of k / v, or null
+    int max_pages, page_size, n_pages;
 };
 
 // Problem description shared by the forward kernels.

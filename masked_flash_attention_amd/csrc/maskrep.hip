@@ -337,9 +337,24 @@ __global__ __launch_bounds__(256) void compact_csr_kernel(const uint8_t* tile_ki
 // ascending without atomics on the output.
 // ---------------------------------------------------------------------------
 
+// Validity of keys [j0, j1] in one batch entry's LSB-first bitmap: bit 0 =
+// some key valid, bit 1 = every key valid.
+__device__ __forceinline__ int key_range_validity(const uint32_t* words, int j0, int j1) {
+    bool any = false, all = true;
+    for (int w = j0 >> 5; w <= (j1 >> 5); ++w) {
+        const int lo = max(j0 - w * 32, 0), hi = min(j1 - w * 32, 31);
+        const uint32_t span = (hi == 31 ? 0xFFFFFFFFu : ((1u << (hi + 1)) - 1u)) & ~((1u << lo) - 1u);
+        const uint32_t v = words[w] & span;
+        any = any || v != 0u;
+        all = all && v == span;
+    }
+    return (any ? 1 : 0) | (all ? 2 : 0);
+}
+
 __global__ __launch_bounds__(256) void bsr_prepare_kernel(const int32_t* indptr, const int32_t* indices, int nQb,
                                                           int nKb, int64_t nnz, int qb, int kb, int Sq, int Skv, int causal,
-                                                          uint8_t* col_kind, int32_t* csc_ptr, int32_t* csc_idx) {
+                                                          const uint32_t* kv_valid, int Hkv, uint8_t* col_kind,
+                                                          int32_t* csc_ptr, int32_t* csc_idx) {
     extern __shared__ int cnt[];  // nKb ints, then 1024 scan scratch
     int* scan = cnt + nKb;
     const int bh = blockIdx.x;
@@ -354,7 +369,15 @@ __global__ __launch_bounds__(256) void bsr_prepare_kernel(const int32_t* indptr,
         for (int e = e0 + threadIdx.x; e < e1; e += blockDim.x) {
             const int c = indices[e];
             if (c < 0 || c >= nKb) continue;
-            col_kind[e] = bsr_kind_of(r, c, qb, kb, Sq, Skv, causal);
+            int kind = bsr_kind_of(r, c, qb, kb, Sq, Skv, causal);
+            if (kv_valid && kind != kTileEmpty) {
+                // token validity (kv_valid_bits): no valid key -> empty, an invalid key -> not full
+                const int v = key_range_validity(kv_valid + (int64_t)(bh / Hkv) * ((Skv + 31) >> 5), c * kb,
+                                                 min((c + 1) * kb, Skv) - 1);
+                if (!(v & 1)) kind = kTileEmpty;
+                else if (kind == kTileFull && !(v & 2)) kind = kTilePartial;
+            }
+            col_kind[e] = (uint8_t)kind;
             cnt[c] += 1;  // distinct columns within one row
         }
         __syncthreads();
@@ -385,6 +408,58 @@ __global__ __launch_bounds__(256) void bsr_prepare_kernel(const int32_t* indptr,
             cnt[c] = dst + 1;
         }
         __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Bitmask sparse format -> BSR rows (flashinfer block_sparse_attention,
+// Parameters: exact_block_bits). One workgroup scans the per-row counts into
+// the running offsets; then one thread per row writes its ascending ids.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t row_word(const uint32_t* bits, int64_t row, int W, int w, int nKb) {
+    const uint32_t x = bits[row * W + w];
+    const int valid = nKb - w * 32;
+    return valid >= 32 ? x : (x & ((1u << valid) - 1u));
+}
+
+__global__ __launch_bounds__(1024) void bitmask_count_kernel(const uint32_t* bits, int n_bh, int nQb, int nKb,
+                                                             int32_t* indptr) {
+    __shared__ int scan[1024];
+    const int W = (nKb + 31) >> 5;
+    const int64_t rows = (int64_t)n_bh * nQb;
+    int carry = 0;
+    for (int64_t g0 = 0; g0 < rows; g0 += blockDim.x) {
+        const int64_t g = g0 + threadIdx.x;
+        int cnt = 0;
+        if (g < rows)
+            for (int w = 0; w < W; ++w) cnt += __builtin_popcount(row_word(bits, g, W, w, nKb));
+        int tot;
+        const int ex = block_exclusive_sum(cnt, &tot, scan);
+        if (g < rows) {
+            const int64_t bh = g / nQb, r = g - bh * nQb;
+            indptr[bh * (nQb + 1) + r] = carry + ex;
+            if (r == nQb - 1) indptr[bh * (nQb + 1) + nQb] = carry + ex + cnt;
+        }
+        carry += tot;
+    }
+}
+
+__global__ __launch_bounds__(256) void bitmask_fill_kernel(const uint32_t* bits, int n_bh, int nQb, int nKb,
+                                                           const int32_t* indptr, int32_t* indices, int64_t cap) {
+    const int W = (nKb + 31) >> 5;
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= (int64_t)n_bh * nQb) return;
+    const int64_t bh = g / nQb, r = g - bh * nQb;
+    int64_t pos = indptr[bh * (nQb + 1) + r];
+    for (int w = 0; w < W; ++w) {
+        uint32_t x = row_word(bits, g, W, w, nKb);
+        while (x) {
+            const int c = __builtin_ctz(x);
+            x &= x - 1u;
+            if (pos < cap) indices[pos] = w * 32 + c;
+            ++pos;
+        }
     }
 }
 
@@ -564,11 +639,28 @@ hipError_t launch_predicate_tiles(const mfa_predicate& pred, int Nq, int Nk, uin
 }
 
 hipError_t launch_bsr_prepare(const int32_t* indptr, const int32_t* indices, int B, int Hkv, int nQb, int nKb,
-                              int64_t nnz, int qb, int kb, int Sq, int Skv, int causal, uint8_t* col_kind, int32_t* csc_ptr,
-                              int32_t* csc_idx, hipStream_t s) {
+                              int64_t nnz, int qb, int kb, int Sq, int Skv, int causal, const uint32_t* kv_valid,
+                              uint8_t* col_kind, int32_t* csc_ptr, int32_t* csc_idx, hipStream_t s) {
     const size_t lds = (size_t)(nKb + 256) * sizeof(int);
     hipLaunchKernelGGL(bsr_prepare_kernel, dim3(B * Hkv), dim3(256), lds, s, indptr, indices, nQb, nKb, nnz, qb, kb, Sq, Skv,
-                       causal, col_kind, csc_ptr, csc_idx);
+                       causal, kv_valid, Hkv, col_kind, csc_ptr, csc_idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_bsr_from_bitmask(const uint32_t* bits, int B, int Hkv, int nQb, int nKb, int32_t* indptr,
+                                   int32_t* indices, int64_t cap, hipStream_t s) {
+    const int n_bh = B * Hkv;
+    if (nQb == 0) return hipMemsetAsync(indptr, 0, (size_t)n_bh * sizeof(int32_t), s);
+    if (nKb == 0) {
+        hipError_t e = hipMemsetAsync(indptr, 0, (size_t)n_bh * (nQb + 1) * sizeof(int32_t), s);
+        return e;
+    }
+    hipLaunchKernelGGL(bitmask_count_kernel, dim3(1), dim3(1024), 0, s, bits, n_bh, nQb, nKb, indptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t rows = (int64_t)n_bh * nQb;
+    hipLaunchKernelGGL(bitmask_fill_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, bits, n_bh, nQb,
+                       nKb, indptr, indices, cap);
     return hipGetLastError();
 }
 

@@ -62,15 +62,16 @@ __device__ __forceinline__ TileRange make_range(const FwdDev& p, const MaskDev& 
         t.seq = s;
         const int cq0 = m.cu_q[s], cq1 = m.cu_q[s + 1];
         const int ck0 = m.cu_k[s], ck1 = m.cu_k[s + 1];
-        const int Lq = cq1 - cq0, Lk = ck1 - ck0;
+        const int Lq = cq1 - cq0, Lk_alloc = ck1 - ck0;
+        const int Lk = m.seqused_k ? min(Lk_alloc, max(m.seqused_k[s], 0)) : Lk_alloc;
         t.q_base = cq0;
-        t.k_base = ck0;
-        t.k_len = Lk;
+        t.k_base = m.block_table ? 0 : ck0;  // paged keys are addressed through the block table
+        t.k_len = m.block_table ? min(Lk, m.max_pages * m.page_size) : Lk;
         t.qt = q0 / BM;
         t.q_row0 = cq0 + q0;
         t.q_rows = min(BM, Lq - q0);
         const int i1 = q0 + t.q_rows - 1;
-        int lo = 0, hi = Lk - 1;
+        int lo = 0, hi = t.k_len - 1;
         if (m.win_left >= 0) lo = max(0, q0 - m.win_left);
         if (m.win_right >= 0) hi = min(hi, i1 + m.win_right);
         if (m.causal) hi = min(hi, i1);
@@ -80,7 +81,16 @@ __device__ __forceinline__ TileRange make_range(const FwdDev& p, const MaskDev& 
             t.begin = lo / kBN;
             t.end = hi / kBN + 1;
         }
-        if (Lq > m.max_q || Lk > m.max_k) {
+        bool bad = Lq > m.max_q || Lk_alloc > m.max_k;
+        if (m.block_table) {
+            // a sequence that needs more pages than a table row holds, or
+            // whose used pages include an id outside [0, n_pages), is an error
+            bad = bad || Lk > m.max_pages * m.page_size;
+            const int32_t* tb = m.block_table + (int64_t)s * m.max_pages;
+            const int npg = (t.k_len + m.page_size - 1) / m.page_size;
+            for (int pi = 0; pi < npg; ++pi) bad = bad || tb[pi] < 0 || tb[pi] >= m.n_pages;
+        }
+        if (bad) {
             t.len_error = true;
             if (m.err) *m.err = 1;
         }
@@ -121,6 +131,16 @@ __device__ __forceinline__ void alibi_fill(f32x16 (&s)[2], float sl, int d0, flo
     for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[h][r] = fmaf(step, (float)(h * 32 + (r >> 2) * 8 + (r & 3)), base);
+}
+
+// Paged keys (varlen with a block table): the page holding local key `key`
+// of sequence `seq` (-1 when the table's id is not a page) and the key's row
+// in it. k / v are then addressed as (page, row, head). Pages hold page_size
+// rows, a multiple of the 64-key tile, so a tile never straddles two pages.
+__device__ __forceinline__ int page_of(const MaskDev& m, int seq, int key, int& row) {
+    const int pg = m.block_table[(int64_t)seq * m.max_pages + key / m.page_size];
+    row = key % m.page_size;
+    return (pg >= 0 && pg < m.n_pages) ? pg : -1;
 }
 
 // Kind of a listed BSR block (r, c) with qb x kb blocks: token-level causal
@@ -287,6 +307,7 @@ __device__ __forceinline__ bool allowed(const FwdDev& p, const MaskDev& m, const
         const int kb = m.k_blk[(int64_t)t.b * p.Sk + key];
         return r.qvalid && ((w >> (key & 31)) & 1u) && kb <= r.qblk;
     } else if constexpr (KIND == MFA_MASK_BSR) {
+        if (m.kv_bits && !((m.kv_bits[(int64_t)t.b * m.kv_words + (key >> 5)] >> (key & 31)) & 1u)) return false;
         return !m.causal || key <= r.qi;
     } else if constexpr (KIND == MFA_MASK_VARLEN) {
         const int i = r.qi_local, j = key;
@@ -344,6 +365,11 @@ __device__ __forceinline__ void mask_scores(const FwdDev& p, const MaskDev& m, c
         if (m.causal) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) okw[kb] &= below(row - base_off - kb * 32 + 1);
+        }
+        if (m.kv_bits) {  // token validity (kv_valid_bits)
+            const uint32_t* kw = m.kv_bits + (int64_t)t.b * m.kv_words + 2 * kt;
+            okw[0] &= kw[0] >> (4 * hh);
+            okw[1] &= ((2 * kt + 1 < m.kv_words) ? kw[1] : 0u) >> (4 * hh);
         }
     } else if constexpr (KIND == MFA_MASK_VARLEN) {
         const int i = rm.qi_local;

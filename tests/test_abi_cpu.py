@@ -52,7 +52,7 @@ int main() {
   printf("mfa_attn_args %zu\nmfa_mask %zu\nmfa_attn_bwd_args %zu\n",
          sizeof(mfa_attn_args), sizeof(mfa_mask), sizeof(mfa_attn_bwd_args));
   P(mfa_attn_args, q); P(mfa_attn_args, lse); P(mfa_attn_args, o_stride); P(mfa_attn_args, alibi_slopes);
-  P(mfa_mask, tile_kind); P(mfa_mask, q_block); P(mfa_mask, cu_q); P(mfa_mask, err); P(mfa_mask, win_right); P(mfa_mask, nseq);
+  P(mfa_mask, tile_kind); P(mfa_mask, q_block); P(mfa_mask, cu_q); P(mfa_mask, err); P(mfa_mask, win_right); P(mfa_mask, nseq); P(mfa_mask, seqused_k); P(mfa_mask, n_pages);
   P(mfa_attn_bwd_args, dout); P(mfa_attn_bwd_args, dv_stride);
   return 0;
 }''')
@@ -129,10 +129,32 @@ def test_maskrep_validation(lib):
     assert _status(lib, st) == "MFA_E_ARG"
     st = lib.mfa_bsr_validate(None, None, 1, 1, 4, 4, 0, None, None)
     assert _status(lib, st) == "MFA_E_ARG"
-    st = lib.mfa_bsr_prepare(None, None, 1, 1, 3, 4, 0, 64, 64, 256, 256, 1, None, None, None, None)
+    st = lib.mfa_bsr_prepare(None, None, 1, 1, 3, 4, 0, 64, 64, 256, 256, 1, None, None, None, None, None)
     assert _status(lib, st) == "MFA_E_SHAPE"
+    st = lib.mfa_bsr_from_bitmask(None, 1, -1, 4, 4, None, None, 0, None)
+    assert _status(lib, st) == "MFA_E_SHAPE"
+    st = lib.mfa_bsr_from_bitmask(None, 1, 1, 1 << 16, 1 << 16, None, None, 0, None)
+    assert _status(lib, st) == "MFA_E_UNSUPPORTED"
     st = lib.mfa_blockid_tile_summary(None, None, None, None, 1, 8, 8, 128, 32, None, None, None, None)
     assert _status(lib, st) == "MFA_E_UNSUPPORTED"
+
+
+def test_paged_varlen_validation(lib):
+    """Page sizes that are not multiples of the 64-key tile, and paged k / v in
+    the backward, are refused before any device call."""
+    a = _args(B=1)
+    for ps, mp, npg, want in ((48, 4, 8, "MFA_E_ARG"), (0, 4, 8, "MFA_E_ARG"), (64, 0, 8, "MFA_E_ARG"),
+                              (128, 4, 0, "MFA_E_ARG")):
+        m = _ffi.Mask()
+        m.kind, m.block_table, m.page_size, m.max_pages, m.n_pages = _ffi.MASK_VARLEN, 16, ps, mp, npg
+        assert _status(lib, lib.mfa_attn_fwd(C.byref(a), C.byref(m), 0.1, None)) == want
+    m = _ffi.Mask()
+    m.kind, m.block_table, m.page_size, m.max_pages, m.n_pages = _ffi.MASK_VARLEN, 16, 64, 4, 8
+    b = _ffi.BwdArgs()
+    b.fwd = _args(B=1)
+    b.fwd.dtype = _ffi.MFA_BF16
+    st = lib.mfa_attn_bwd_dq(C.byref(b), C.byref(m), 0.1, None)
+    assert _status(lib, st) in ("MFA_E_UNSUPPORTED", "MFA_E_NO_DEVICE")
 
 
 def test_predicate_validation_and_composition(lib):
