@@ -190,9 +190,31 @@ def rows_section(dev, causal=None):
         for q0 in range(0, Ls, 128):
             q1 = min(q0 + 128, Ls) - 1
             tiles += q1 // 64 - max(0, q0 - 511) // 64 + 1
+    # the same forward with k / v in shuffled 128-row pages through a block table
+    page = 128
+    npg = [(Ls + page - 1) // page for Ls in w["lengths"].tolist()]
+    n_pages = sum(npg)
+    perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(7))
+    table = torch.full((len(npg), max(npg)), 0, dtype=torch.int32)
+    kp = torch.zeros(n_pages, page, *k.shape[1:], dtype=k.dtype, device=dev)
+    vp = torch.zeros_like(kp)
+    nxt, off = 0, 0
+    for si, Ls in enumerate(w["lengths"].tolist()):
+        for pi in range(npg[si]):
+            pg = int(perm[nxt])
+            table[si, pi] = pg
+            n = min(page, Ls - pi * page)
+            kp[pg, :n] = k[off + pi * page:off + pi * page + n]
+            vp[pg, :n] = v[off + pi * page:off + pi * page + n]
+            nxt += 1
+        off += Ls
+    prep = mfa.MaskRep.varlen(sch, Lmax, Lmax, causal=True, window=(511, 0), block_table=table.to(dev),
+                              page_size=page, n_pages=n_pages)
+    pfwd_ms = _time(lambda: mfa.attn_fwd(q, kp, vp, prep, w["scale"], "thd", out=o))
+    del kp, vp
     out["varlen_window_32seq"] = {"schedule_ms": round(sched_ms, 4), "fwd_ms": round(fwd_ms, 4),
                                   "fwd_tflops_attended_tiles": round(4.0 * 128 * 64 * 64 * tiles * 16 / fwd_ms / 1e9, 1),
-                                  "bwd_ms": round(vbwd_ms, 4)}
+                                  "bwd_ms": round(vbwd_ms, 4), "paged128_fwd_ms": round(pfwd_ms, 4)}
     # a4 + a6 + a9 on BSR
     w = W.bsr_random()
     N = 16384
@@ -207,12 +229,70 @@ def rows_section(dev, causal=None):
     bwd_ms = _time(lambda: mfa.attn_bwd(q, k, v, o, lse, do, rep, w["scale"], "bshd"), reps=5)
     tiles = int((kind != 0).sum().item())
     f = 4.0 * 64 * 64 * 128 * tiles
-    out["bsr_causal_N16384"] = {"bsr_prepare_ms": round(prep_ms, 4), "fwd_ms": round(fwd_ms, 4),
+    # the same routing given in the bitmask format, converted on the GPU
+    nKb = N // 64
+    sel = torch.zeros(2, 16, nKb, nKb, dtype=torch.bool)
+    ipc, ixc = w["indptr"], w["indices"]
+    for b_ in range(2):
+        for h_ in range(16):
+            for r_ in range(nKb):
+                sel[b_, h_, r_, torch.from_numpy(ixc[ipc[b_, h_, r_]:ipc[b_, h_, r_ + 1]]).long()] = True
+    wts = (sel.view(2, 16, nKb, nKb // 32, 32).to(torch.int64) << torch.arange(32)).sum(-1)
+    bits = wts.to(torch.int64).where(wts < 2 ** 31, wts - 2 ** 32).to(torch.int32).to(dev)
+    bm_ms = _time(lambda: mfa.bsr_from_bitmask(bits, nKb, cap=ix.numel()))
+    out["bsr_causal_N16384"] = {"bsr_prepare_ms": round(prep_ms, 4), "bitmask_to_bsr_ms": round(bm_ms, 4),
+                                "fwd_ms": round(fwd_ms, 4),
                                 "fwd_tflops_attended_tiles": round(f / fwd_ms / 1e9, 1),
                                 "bwd_ms": round(bwd_ms, 4),
                                 "bwd_tflops_algorithmic": round(2.5 * f / bwd_ms / 1e9, 1),
                                 "bwd_tflops_executed": round(3.5 * f / bwd_ms / 1e9, 1)}
+    out["tile_dispatch_N8192"] = dispatch_section(dev)
     return out
+
+
+def dispatch_section(dev):
+    """Forward time at 64- and 128-row dense-mask tiles on the causal N=8192
+    shape (B=4, H=32, D=128) for masks of different structure, with the
+    dispatcher's choice (mfa_choose_tile_m on the two maps' tile counts)."""
+    import numpy as np
+    import masked_flash_attention_amd as mfa
+    B, H, N, D = 4, 32, 8192, 128
+    g = torch.Generator().manual_seed(11)
+    q, k, v = (torch.randn(B, H, N, D, generator=g).to(torch.bfloat16).to(dev) for _ in range(3))
+    o = torch.empty_like(q)
+    i = torch.arange(N, device=dev)
+    rng = np.random.default_rng(4)
+    lens = []
+    while sum(lens) < N:
+        lens.append(int(rng.integers(32, 200)))
+    lens[-1] -= sum(lens) - N
+    doc = torch.from_numpy(np.repeat(np.arange(len(lens)), lens)).to(dev)
+    nb = N // 64
+    sel = np.random.default_rng(5).random((nb, nb)) < 0.1
+    np.fill_diagonal(sel, True)
+    masks = {
+        "causal": lambda: i[:, None] >= i[None, :],
+        "random50": lambda: torch.rand(N, N, generator=torch.Generator().manual_seed(1)).lt(0.5).to(dev),
+        "docs_causal": lambda: (doc[:, None] == doc[None, :]) & (i[:, None] >= i[None, :]),
+        "band96": lambda: ((i[:, None] - i[None, :]) >= 0) & ((i[:, None] - i[None, :]) < 96),
+        "blocks64_10pct": lambda: torch.from_numpy(np.kron(sel, np.ones((64, 64), bool))).to(dev),
+    }
+    res = {}
+    for name, mk in masks.items():
+        m = mk()
+        row = {}
+        c64 = mfa.compact_dense_mask(m, BM=64)
+        c128 = mfa.coarsen_tile_map(c64, N, N)
+        counts = {}
+        for bm, c in ((64, c64), (128, c128)):
+            counts[bm] = mfa.tile_counts(c["tile_kind"]).cpu().tolist()
+            rep = mfa.MaskRep.tiles(c)
+            row[f"fwd_ms_tile{bm}"] = round(_time(lambda: mfa.attn_fwd(q, k, v, rep, D ** -0.5, "bhsd", out=o)), 4)
+        row["choice"] = mfa.choose_tile_m(counts[64], counts[128], N)
+        row["faster"] = 64 if row["fwd_ms_tile64"] < row["fwd_ms_tile128"] else 128
+        res[name] = row
+        del m, c64, c128
+    return res
 
 
 def main():

@@ -126,7 +126,8 @@ mfa_status mfa_blockid_tile_summary(const int32_t* q_blk, const int32_t* k_blk,
  *   col_idx    (nnz) i32 non-empty key tiles, ascending within each row
  *   col_kind   (nnz) u8 kinds of those tiles (1 or 2)
  * col_idx / col_kind must hold nnz entries; nnz <= ceil(Nq/BM)*ceil(Nk/BN)
- * always suffices. BM must be 128 and BN 64 (the attention kernel's tile). */
+ * always suffices. BM is 128 or 64 and BN 64 (the attention kernels' tiles);
+ * give the attention calls the same BM as mfa_mask.tile_m. */
 mfa_status mfa_compact_dense_mask(const uint8_t* mask, int Nq, int Nk, int BM, int BN,
                                   uint8_t* tile_kind, uint32_t* fine_bits,
                                   int32_t* row_ptr, int32_t* col_idx, uint8_t* col_kind,
@@ -153,6 +154,26 @@ typedef struct mfa_predicate {
     int n_atoms[MFA_PRED_MAX_TERMS];
     mfa_pred_atom atoms[MFA_PRED_MAX_TERMS][MFA_PRED_MAX_ATOMS];
 } mfa_predicate;
+
+/* Density-aware dispatch between 128-row and 64-row dense-mask tiles
+ * (BinFlash README, "Efficiently Dispatching ...": the dispatcher picks the
+ * tiling from statistics of the coarse block mask).
+ * mfa_tile_map_coarsen: the 128-row tile map and its CSR (outputs as in
+ *   mfa_compact_dense_mask with BM = 128) from a 64-row map kind64
+ *   (ceil(Nq/64), ceil(Nk/64)) of the same mask, without reading the mask
+ *   again; the fine bits are shared. Asynchronous.
+ * mfa_tile_counts: counts[0..2] (device int64) = empty, partial and full
+ *   tiles among the n kinds of a tile map. Asynchronous.
+ * mfa_model_tile_time / mfa_choose_tile_m (host only, no device calls): the
+ *   modelled forward time of a map with those counts (setup per query tile
+ *   plus a cost per partial and per full tile, measured on MI355X), and the
+ *   tile height (64 or 128) with the smaller one. */
+mfa_status mfa_tile_map_coarsen(const uint8_t* kind64, int Nq, int Nk, uint8_t* kind128,
+                                int32_t* row_ptr, int32_t* col_idx, uint8_t* col_kind,
+                                hipStream_t stream);
+mfa_status mfa_tile_counts(const uint8_t* tile_kind, int64_t n, int64_t* counts, hipStream_t stream);
+double mfa_model_tile_time(const int64_t counts[3], int Nq, int tile_m);
+int mfa_choose_tile_m(const int64_t counts64[3], const int64_t counts128[3], int Nq);
 
 /* The tile representation of a predicate mask over an (Nq, Nk) grid: the
  * same outputs, layout and meaning as mfa_compact_dense_mask (BM = 128,
@@ -284,8 +305,7 @@ typedef struct mfa_attn_args {
 typedef struct mfa_mask {
     int kind;              /* mfa_mask_kind */
     /* BLOCKID: outputs of mfa_make_block_ids (or any ids) plus the summaries
-     * of mfa_blockid_tile_summary with BM = 128, BN = 64 (BM = 64 when the
-     * call is made with tile_m = 64). */
+     * of mfa_blockid_tile_summary with BM = 128, BN = 64. */
     const int32_t* q_blk;
     const int32_t* k_blk;
     const uint8_t* q_valid;
@@ -349,6 +369,9 @@ typedef struct mfa_mask {
     int max_pages;
     int page_size;
     int n_pages;
+    /* TILES: query rows per tile of the map (the BM it was compacted with):
+     * 128 (or 0) or 64. 64-row maps run 2-wave workgroups. */
+    int tile_m;
 } mfa_mask;
 
 /* Fused masked attention forward: out = softmax(scale q k^T + bias + mask) v

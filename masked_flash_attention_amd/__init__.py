@@ -137,6 +137,7 @@ def compact_dense_mask(mask, BM=TILE_M, BN=TILE_N):
     _ffi.check(_lib().mfa_compact_dense_mask(_p(m), Nq, Nk, BM, BN, _p(out["tile_kind"]), _p(out["fine_bits"]),
                                              _p(out["row_ptr"]), _p(out["col_idx"]), _p(out["col_kind"]),
                                              _stream()))
+    out["tile_m"] = BM
     return out
 
 
@@ -237,6 +238,55 @@ def bsr_prepare(block_indptr, block_indices, q_block, kv_block, Sq, Skv, causal,
     return col_kind[:nnz], csc_ptr, csc_idx[:nnz]
 
 
+def tile_counts(tile_kind):
+    """(empty, partial, full) tile counts of a tile map, as a device int64 tensor (mfa_tile_counts)."""
+    k = tile_kind.contiguous()
+    out = torch.empty(3, dtype=torch.int64, device=k.device)
+    _ffi.check(_lib().mfa_tile_counts(_p(k), k.numel(), _p(out), _stream()))
+    return out
+
+
+def coarsen_tile_map(compacted64, Nq, Nk):
+    """128-row tile map + CSR from a 64-row compaction (mfa_tile_map_coarsen); shares its fine bits."""
+    nQt, nKt = _cdiv(Nq, 128), _cdiv(Nk, 64)
+    dev = compacted64["tile_kind"].device
+    out = {
+        "tile_kind": torch.empty(nQt, nKt, dtype=torch.uint8, device=dev),
+        "fine_bits": compacted64["fine_bits"],
+        "row_ptr": torch.empty(nQt + 1, dtype=torch.int32, device=dev),
+        "col_idx": torch.empty(max(1, nQt * nKt), dtype=torch.int32, device=dev),
+        "col_kind": torch.empty(max(1, nQt * nKt), dtype=torch.uint8, device=dev),
+        "tile_m": 128,
+    }
+    _ffi.check(_lib().mfa_tile_map_coarsen(_p(compacted64["tile_kind"]), Nq, Nk, _p(out["tile_kind"]),
+                                           _p(out["row_ptr"]), _p(out["col_idx"]), _p(out["col_kind"]), _stream()))
+    return out
+
+
+def choose_tile_m(counts64, counts128, Nq):
+    """Tile height (64 or 128) with the smaller modelled forward time (mfa_choose_tile_m, host only)."""
+    a = (C.c_int64 * 3)(*[int(x) for x in counts64])
+    b = (C.c_int64 * 3)(*[int(x) for x in counts128])
+    return int(_lib().mfa_choose_tile_m(a, b, int(Nq)))
+
+
+def compact_dense_mask_auto(mask):
+    """Density-aware dispatch (BinFlash, "Efficiently Dispatching ..."): one
+    pass over the mask at 64-row tiles, the 128-row map derived from it, the
+    tile statistics of both read back (one sync), and the compaction whose
+    modelled forward time is smaller returned (with "tile_m" and "counts")."""
+    m = _u8(mask).contiguous()
+    Nq, Nk = m.shape
+    c64 = compact_dense_mask(m, BM=64)
+    c128 = coarsen_tile_map(c64, Nq, Nk)
+    n64 = tile_counts(c64["tile_kind"]).cpu().tolist()
+    n128 = tile_counts(c128["tile_kind"]).cpu().tolist()
+    bm = choose_tile_m(n64, n128, Nq)
+    out = c64 if bm == 64 else c128
+    out["counts"] = {64: n64, 128: n128}
+    return out
+
+
 def _kv_bits(bits, B, Skv):
     t = bits.contiguous()
     if t.dtype not in (torch.int32, torch.uint32) or tuple(t.shape) != (B, _cdiv(Skv, 32)):
@@ -303,7 +353,8 @@ class MaskRep:
     @staticmethod
     def tiles(compacted):
         return MaskRep(_ffi.MASK_TILES, {k: compacted[k] for k in
-                                         ("tile_kind", "fine_bits", "row_ptr", "col_idx", "col_kind")})
+                                         ("tile_kind", "fine_bits", "row_ptr", "col_idx", "col_kind")},
+                       {"tile_m": int(compacted.get("tile_m", TILE_M))})
 
     @staticmethod
     def blockid(q_blk, k_blk, q_valid, k_valid, summary=None):

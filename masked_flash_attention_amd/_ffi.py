@@ -36,7 +36,7 @@ class Mask(C.Structure):
                 ("max_k", C.c_int), ("err", vp),
                 ("causal", C.c_int), ("win_left", C.c_int), ("win_right", C.c_int), ("nseq", C.c_int),
                 ("seqused_k", vp), ("block_table", vp), ("max_pages", C.c_int), ("page_size", C.c_int),
-                ("n_pages", C.c_int)]
+                ("n_pages", C.c_int), ("tile_m", C.c_int)]
 
 
 class BwdArgs(C.Structure):
@@ -66,6 +66,10 @@ SIGNATURES = {
     "mfa_blockid_tile_summary": ([vp, vp, vp, vp, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, vp, vp, vp, vp],
                                  C.c_int),
     "mfa_compact_dense_mask": ([vp, C.c_int, C.c_int, C.c_int, C.c_int, vp, vp, vp, vp, vp, vp], C.c_int),
+    "mfa_tile_map_coarsen": ([vp, C.c_int, C.c_int, vp, vp, vp, vp, vp], C.c_int),
+    "mfa_tile_counts": ([vp, C.c_int64, vp, vp], C.c_int),
+    "mfa_model_tile_time": ([C.POINTER(C.c_int64), C.c_int, C.c_int], C.c_double),
+    "mfa_choose_tile_m": ([C.POINTER(C.c_int64), C.POINTER(C.c_int64), C.c_int], C.c_int),
     "mfa_predicate_tiles": ([C.POINTER(Predicate), C.c_int, C.c_int, vp, vp, vp, vp, vp, vp], C.c_int),
     "mfa_bsr_validate": ([vp, vp, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64, C.POINTER(C.c_int), vp], C.c_int),
     "mfa_bsr_prepare": ([vp, vp, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int, C.c_int, C.c_int,

@@ -19,11 +19,14 @@ hipError_t launch_block_ids(const uint8_t*, const int32_t*, int, int, int, const
                             uint8_t*, uint8_t*, hipStream_t);
 hipError_t launch_blockid_summary(const int32_t*, const int32_t*, const uint8_t*, const uint8_t*, int, int, int, int,
                                   int, int32_t*, int32_t*, uint32_t*, hipStream_t);
-hipError_t launch_compact(const uint8_t*, int, int, uint8_t*, uint32_t*, int32_t*, int32_t*, uint8_t*, hipStream_t);
-hipError_t launch_predicate_tiles(const mfa_predicate&, int, int, uint8_t*, uint32_t*, int32_t*, int32_t*, uint8_t*,
-                                  hipStream_t);
+hipError_t launch_compact(const uint8_t*, int, int, int, uint8_t*, uint32_t*, int32_t*, int32_t*, uint8_t*,
+                          hipStream_t);
+hipError_t launch_predicate_tiles(const mfa_predicate&, int, int, int, uint8_t*, uint32_t*, int32_t*, int32_t*,
+                                  uint8_t*, hipStream_t);
 hipError_t launch_bsr_prepare(const int32_t*, const int32_t*, int, int, int, int, int64_t, int, int, int, int, int,
                               const uint32_t*, uint8_t*, int32_t*, int32_t*, hipStream_t);
+hipError_t launch_coarsen_tiles(const uint8_t*, int, int, uint8_t*, int32_t*, int32_t*, uint8_t*, hipStream_t);
+hipError_t launch_tile_counts(const uint8_t*, int64_t, int64_t*, hipStream_t);
 hipError_t launch_bsr_from_bitmask(const uint32_t*, int, int, int, int, int32_t*, int32_t*, int64_t, hipStream_t);
 hipError_t launch_varlen_schedule(const int32_t*, const int32_t*, int, int, int, int, int, int, int32_t*, int32_t*,
                                   int32_t*, int32_t*, int, int32_t*, hipStream_t);
@@ -169,8 +172,8 @@ mfa_status mfa_compact_dense_mask(const uint8_t* mask, int Nq, int Nk, int BM, i
                                   uint32_t* fine_bits, int32_t* row_ptr, int32_t* col_idx, uint8_t* col_kind,
                                   hipStream_t stream) {
     if (Nq < 0 || Nk < 0) return fail(MFA_E_SHAPE, "negative size (Nq=%d, Nk=%d)", Nq, Nk);
-    if (BM != 128 || BN != 64)
-        return fail(MFA_E_UNSUPPORTED, "dense-mask tiles are built for BM=128, BN=64 (got %d, %d)", BM, BN);
+    if ((BM != 128 && BM != 64) || BN != 64)
+        return fail(MFA_E_UNSUPPORTED, "dense-mask tiles are built for BM=128 or 64, BN=64 (got %d, %d)", BM, BN);
     MFA_TRY(ensure_device());
     MFA_TRY(dev_ptr(row_ptr, "row_ptr"));
     if (Nq > 0 && Nk > 0) {
@@ -180,8 +183,57 @@ mfa_status mfa_compact_dense_mask(const uint8_t* mask, int Nq, int Nk, int BM, i
         MFA_TRY(dev_ptr(col_idx, "col_idx"));
         MFA_TRY(dev_ptr(col_kind, "col_kind"));
     }
-    return hip_ok(launch_compact(mask, Nq, Nk, tile_kind, fine_bits, row_ptr, col_idx, col_kind, stream),
+    return hip_ok(launch_compact(mask, Nq, Nk, BM, tile_kind, fine_bits, row_ptr, col_idx, col_kind, stream),
                   "compaction launch");
+}
+
+mfa_status mfa_tile_map_coarsen(const uint8_t* kind64, int Nq, int Nk, uint8_t* kind128, int32_t* row_ptr,
+                                int32_t* col_idx, uint8_t* col_kind, hipStream_t stream) {
+    if (Nq < 0 || Nk < 0) return fail(MFA_E_SHAPE, "negative size (Nq=%d, Nk=%d)", Nq, Nk);
+    MFA_TRY(ensure_device());
+    MFA_TRY(dev_ptr(row_ptr, "row_ptr"));
+    if (Nq > 0 && Nk > 0) {
+        MFA_TRY(dev_ptr(kind64, "kind64"));
+        MFA_TRY(dev_ptr(kind128, "kind128"));
+        MFA_TRY(dev_ptr(col_idx, "col_idx"));
+        MFA_TRY(dev_ptr(col_kind, "col_kind"));
+    }
+    return hip_ok(launch_coarsen_tiles(kind64, Nq, Nk, kind128, row_ptr, col_idx, col_kind, stream),
+                  "tile map coarsening launch");
+}
+
+mfa_status mfa_tile_counts(const uint8_t* tile_kind, int64_t n, int64_t* counts, hipStream_t stream) {
+    if (n < 0) return fail(MFA_E_SHAPE, "negative size");
+    MFA_TRY(ensure_device());
+    MFA_TRY(dev_ptr(counts, "counts"));
+    if (n > 0) MFA_TRY(dev_ptr(tile_kind, "tile_kind"));
+    return hip_ok(launch_tile_counts(tile_kind, n, counts, stream), "tile count launch");
+}
+
+// Modelled forward time of a tile map, in units of one full 128 x 64 tile:
+// setup per query tile plus a cost per partial and per full tile, for each
+// tile height. Least-squares fit (relative error) of MI355X forward times at
+// D = 128, B = 4, H = 32, N = 8192 over six masks (all-True, all-False, a
+// 50 %-dense random mask whose tiles are all partial, causal, causal
+// documents of 32-200 tokens, a 96-wide band); the fit is within 7 % of every
+// measured time. A 64-row tile costs 0.74 (full) to 0.83 (partial) of a
+// 128-row one, so 64-row tiles pay off only when many 128-row tiles are
+// half empty.
+static const double kTileCost[2][3] = {
+    // setup per query tile, partial tile, full tile
+    {2.31, 0.966, 0.739},  // 64-row tiles
+    {4.32, 1.164, 1.000},  // 128-row tiles
+};
+
+double mfa_model_tile_time(const int64_t counts[3], int Nq, int tile_m) {
+    const int i = tile_m == 64 ? 0 : 1;
+    const int64_t rows = tile_m == 64 ? cdiv(Nq, 64) : cdiv(Nq, 128);
+    return kTileCost[i][0] * (double)rows + kTileCost[i][1] * (double)counts[1] + kTileCost[i][2] * (double)counts[2];
+}
+
+int mfa_choose_tile_m(const int64_t counts64[3], const int64_t counts128[3], int Nq) {
+    if (!counts64 || !counts128 || Nq < 0) return 128;
+    return mfa_model_tile_time(counts64, Nq, 64) < mfa_model_tile_time(counts128, Nq, 128) ? 64 : 128;
 }
 
 mfa_status mfa_predicate_tiles(const mfa_predicate* pred, int Nq, int Nk, uint8_t* tile_kind, uint32_t* fine_bits,
@@ -203,7 +255,7 @@ mfa_status mfa_predicate_tiles(const mfa_predicate* pred, int Nq, int Nk, uint8_
     }
     mfa_predicate p = *pred;
     for (int t = p.n_terms; t < MFA_PRED_MAX_TERMS; ++t) p.n_atoms[t] = 0;
-    return hip_ok(launch_predicate_tiles(p, Nq, Nk, tile_kind, fine_bits, row_ptr, col_idx, col_kind, stream),
+    return hip_ok(launch_predicate_tiles(p, Nq, Nk, 128, tile_kind, fine_bits, row_ptr, col_idx, col_kind, stream),
                   "predicate tiles launch");
 }
 
@@ -334,6 +386,10 @@ static mfa_status fill_mask(const mfa_attn_args* a, const mfa_mask* mk, MaskDev&
             m.kv_bits = mk->kv_bits;
             break;
         case MFA_MASK_TILES:
+            if (mk->tile_m != 0 && mk->tile_m != 64 && mk->tile_m != 128)
+                return fail(MFA_E_UNSUPPORTED, "tile_m=%d: dense-mask tile maps have 128 or 64 rows", mk->tile_m);
+            BM = mk->tile_m == 64 ? 64 : 128;
+            m.tile_shift = BM == 128 ? 1 : 0;
             m.fine_bits = mk->fine_bits;
             m.row_ptr = mk->row_ptr;
             m.col_idx = mk->col_idx;

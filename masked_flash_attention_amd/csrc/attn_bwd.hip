@@ -278,7 +278,7 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
             kind = bsr_kind_of(qb, kbk, 64, 64, f.Sq, f.Sk, m.causal);
             if (kind == kTileFull && !blk_all_valid) kind = kTilePartial;
         } else if constexpr (KIND == MFA_MASK_TILES) {
-            kind = m.tile_kind[(int64_t)(qb >> 1) * f.nKt + kbk];
+            kind = m.tile_kind[(int64_t)(qb >> m.tile_shift) * f.nKt + kbk];
         } else if constexpr (KIND == MFA_MASK_BLOCKID) {
             kind = classify_blockid(m.qsum + ((int64_t)b * f.nQt + (qb >> 1)) * 4,
                                     m.ksum + ((int64_t)b * f.nKt + kbk) * 4);
@@ -633,18 +633,26 @@ static hipError_t dkdv_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) 
     return p.f.alibi ? dkdv_launch<D, KIND, true>(p, m, s) : dkdv_launch<D, KIND, false>(p, m, s);
 }
 
-template <int D, int KIND, bool BIAS>
+template <int D, int NW, int KIND, bool BIAS>
 static hipError_t dq_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) {
-    constexpr int NW = KIND == MFA_MASK_BSR ? 2 : 4;
     const size_t lds = 4 * 64 * 2 * D;
     if (p.f.total == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_dq_kernel<D, NW, KIND, BIAS>), dim3(p.f.total), dim3(NW * 64), lds, s, p, m);
     return hipGetLastError();
 }
 
+// 64-row query tiles (BSR blocks, 64-row dense-tile maps) run 2 waves, 128-row ones 4.
 template <int D, int KIND>
 static hipError_t dq_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) {
-    return p.f.alibi ? dq_launch<D, KIND, true>(p, m, s) : dq_launch<D, KIND, false>(p, m, s);
+    if constexpr (KIND == MFA_MASK_BSR) {
+        return p.f.alibi ? dq_launch<D, 2, KIND, true>(p, m, s) : dq_launch<D, 2, KIND, false>(p, m, s);
+    } else if constexpr (KIND == MFA_MASK_TILES) {
+        if (m.tile_shift == 0)
+            return p.f.alibi ? dq_launch<D, 2, KIND, true>(p, m, s) : dq_launch<D, 2, KIND, false>(p, m, s);
+        return p.f.alibi ? dq_launch<D, 4, KIND, true>(p, m, s) : dq_launch<D, 4, KIND, false>(p, m, s);
+    } else {
+        return p.f.alibi ? dq_launch<D, 4, KIND, true>(p, m, s) : dq_launch<D, 4, KIND, false>(p, m, s);
+    }
 }
 
 template <int D>

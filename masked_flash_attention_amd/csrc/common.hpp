@@ -56,6 +56,7 @@ struct MaskDev {
     const int32_t* seqused_k;    // VARLEN: keys used per sequence, or null
     const int32_t* block_table;  // VARLEN: (nseq, max_pages) pages of k / v, or null
     int max_pages, page_size, n_pages;
+    int tile_shift;   // TILES: log2(map rows per tile / 64) (1 for 128-row maps, 0 for 64)
 };
 
 // Problem description shared by the forward kernels.

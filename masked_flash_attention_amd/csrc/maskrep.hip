@@ -3,6 +3,8 @@
 // All outputs are deterministic (no order-dependent atomics): prefix counts
 // come from wave ballots (v_mbcnt) and LDS block scans.
 
+#include <algorithm>
+
 #include "sched.hpp"
 
 namespace mfa {
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(64) void blockid_summary_kernel(const int32_t* q_bl
 // Workgroup = 256 threads = 128 rows x 256 columns (4 key tiles of 64).
 // ---------------------------------------------------------------------------
 
-constexpr int kCmpRows = 128;   // BM
+constexpr int kCmpRows = 128;   // rows per workgroup strip (one 128-row tile or two 64-row ones)
 constexpr int kCmpCols = 256;   // 4 key tiles of 64 per workgroup
 constexpr int kCmpPasses = kCmpRows / 16;
 
@@ -161,11 +163,12 @@ __device__ __forceinline__ uint32_t pack4(uint32_t w) {
 // Body shared by the dense-mask and the predicate tile builders: one
 // workgroup = 128 rows x 256 columns (4 key tiles); thread t covers a 16-column
 // segment (t & 15) of row (t >> 4) + 16*pass. bits16(r, col) returns the
-// allowed bits of row r, columns [col, col + 16) (0 past Nk).
+// allowed bits of row r, columns [col, col + 16) (0 past Nk). The tile kinds
+// are written for 128-row tiles, or with bm64 for each 64-row half.
 template <class Bits16>
-__device__ __forceinline__ void tile_strip(const Bits16& bits16, int Nq, int Nk, int nKt, uint8_t* tile_kind,
-                                           uint32_t* fine_bits) {
-    __shared__ uint32_t s_any[4], s_all[4];
+__device__ __forceinline__ void tile_strip(const Bits16& bits16, int Nq, int Nk, int nKt, bool bm64,
+                                           uint8_t* tile_kind, uint32_t* fine_bits) {
+    __shared__ uint32_t s_any[8], s_all[8];  // [half][key tile]
     const int qt = blockIdx.y;
     const int col0 = blockIdx.x * kCmpCols;
     const int t = threadIdx.x, lane = t & 63;
@@ -173,7 +176,7 @@ __device__ __forceinline__ void tile_strip(const Bits16& bits16, int Nq, int Nk,
     const int rsub = t >> 4;           // row within a 16-row pass
     const int col = col0 + seg * 16;
     const int W = (Nk + 31) / 32;
-    if (t < 4) {
+    if (t < 8) {
         s_any[t] = 0;
         s_all[t] = 1;
     }
@@ -184,16 +187,17 @@ __device__ __forceinline__ void tile_strip(const Bits16& bits16, int Nq, int Nk,
         const int r = qt * kCmpRows + ps * 16 + rsub;
         words[ps] = r < Nq ? bits16(r, col) : 0u;
     }
-    bool any = false, all = true;
+    bool any[2] = {false, false}, all[2] = {true, true};  // per 64-row half
     // columns of this thread that exist
     const int ncol = max(0, min(16, Nk - col));
     const uint32_t full16 = ncol >= 16 ? 0xFFFFu : ((1u << ncol) - 1u);
 #pragma unroll
     for (int ps = 0; ps < kCmpPasses; ++ps) {
+        const int h = ps / (kCmpPasses / 2);
         const int r = qt * kCmpRows + ps * 16 + rsub;
         const uint32_t bits = words[ps];
-        any = any || bits != 0;
-        all = all && (r < Nq) && ncol == 16 && bits == full16;
+        any[h] = any[h] || bits != 0;
+        all[h] = all[h] && (r < Nq) && ncol == 16 && bits == full16;
         // pair lanes (even, odd) form one 32-bit word of the row
         const uint32_t hi = __shfl_xor(bits, 1);
         if (r < Nq && (seg & 1) == 0) {
@@ -202,26 +206,41 @@ __device__ __forceinline__ void tile_strip(const Bits16& bits16, int Nq, int Nk,
         }
     }
     // key tile of this thread: seg / 4; fold any/all over the wave, then the block
-    const uint64_t ba = __builtin_amdgcn_ballot_w64(any);
-    const uint64_t bl = __builtin_amdgcn_ballot_w64(all);
+    uint64_t ba[2], bl[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        ba[h] = __builtin_amdgcn_ballot_w64(any[h]);
+        bl[h] = __builtin_amdgcn_ballot_w64(all[h]);
+    }
     __syncthreads();
     if (lane < 4) {
         const uint64_t sel = 0x000F000F000F000Full << (4 * lane);
-        if (ba & sel) atomicOr(&s_any[lane], 1u);
-        if ((bl & sel) != sel) atomicAnd(&s_all[lane], 0u);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (ba[h] & sel) atomicOr(&s_any[h * 4 + lane], 1u);
+            if ((bl[h] & sel) != sel) atomicAnd(&s_all[h * 4 + lane], 0u);
+        }
     }
     __syncthreads();
-    if (t < 4) {
-        const int kt = col0 / 64 + t;
+    if (t < 8) {
+        const int h = t >> 2, kt = col0 / 64 + (t & 3);
         if (kt < nKt) {
-            const uint8_t k = s_all[t] ? kTileFull : (s_any[t] ? kTilePartial : kTileEmpty);
-            tile_kind[(int64_t)qt * nKt + kt] = k;
+            if (bm64) {
+                const int q64 = 2 * qt + h;
+                if (q64 * 64 < Nq) {
+                    const uint8_t k = s_all[t] ? kTileFull : (s_any[t] ? kTilePartial : kTileEmpty);
+                    tile_kind[(int64_t)q64 * nKt + kt] = k;
+                }
+            } else if (h == 0) {
+                const bool a = s_any[t] || s_any[t + 4], f = s_all[t] && s_all[t + 4];
+                tile_kind[(int64_t)qt * nKt + kt] = f ? kTileFull : (a ? kTilePartial : kTileEmpty);
+            }
         }
     }
 }
 
 template <bool VEC>
-__global__ __launch_bounds__(256) void compact_tiles_kernel(const uint8_t* mask, int Nq, int Nk, int nKt,
+__global__ __launch_bounds__(256) void compact_tiles_kernel(const uint8_t* mask, int Nq, int Nk, int nKt, bool bm64,
                                                             uint8_t* tile_kind, uint32_t* fine_bits) {
     auto bits16 = [&](int r, int col) -> uint32_t {
         const uint8_t* rp = mask + (int64_t)r * Nk;
@@ -235,7 +254,7 @@ __global__ __launch_bounds__(256) void compact_tiles_kernel(const uint8_t* mask,
         }
         return bits;
     };
-    tile_strip(bits16, Nq, Nk, nKt, tile_kind, fine_bits);
+    tile_strip(bits16, Nq, Nk, nKt, bm64, tile_kind, fine_bits);
 }
 
 // floor(n / d) and ceil(n / d) for d > 0
@@ -265,14 +284,14 @@ __device__ __forceinline__ uint32_t predicate_bits16(const mfa_predicate& P, int
     return out;
 }
 
-__global__ __launch_bounds__(256) void predicate_tiles_kernel(mfa_predicate P, int Nq, int Nk, int nKt,
+__global__ __launch_bounds__(256) void predicate_tiles_kernel(mfa_predicate P, int Nq, int Nk, int nKt, bool bm64,
                                                               uint8_t* tile_kind, uint32_t* fine_bits) {
     auto bits16 = [&](int r, int col) -> uint32_t {
         const int ncol = max(0, min(16, Nk - col));
         const uint32_t exist = ncol >= 16 ? 0xFFFFu : ((1u << ncol) - 1u);
         return predicate_bits16(P, r, col) & exist;
     };
-    tile_strip(bits16, Nq, Nk, nKt, tile_kind, fine_bits);
+    tile_strip(bits16, Nq, Nk, nKt, bm64, tile_kind, fine_bits);
 }
 
 // CSR of non-empty tiles: one workgroup per query-tile row. The row offset is
@@ -328,6 +347,49 @@ __global__ __launch_bounds__(256) void compact_csr_kernel(const uint8_t* tile_ki
         carry += n;
     }
     if (qt == nQt - 1 && threadIdx.x == 0) row_ptr[nQt] = base + carry;
+}
+
+// 128-row tile map from a 64-row one: a 128-row tile is empty iff both halves
+// are, full iff both halves exist and are full, else partial (a half past Nq
+// makes the tile ragged, so never full).
+__global__ __launch_bounds__(256) void coarsen_tiles_kernel(const uint8_t* kind64, int nQt64, int nKt, int nQt128,
+                                                            uint8_t* kind128) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)nQt128 * nKt) return;
+    const int r = (int)(i / nKt), c = (int)(i - (int64_t)r * nKt);
+    const int a = kind64[(int64_t)(2 * r) * nKt + c];
+    const int b = 2 * r + 1 < nQt64 ? kind64[(int64_t)(2 * r + 1) * nKt + c] : -1;
+    int k;
+    if (b < 0) k = a == kTileEmpty ? kTileEmpty : kTilePartial;
+    else if (a == kTileEmpty && b == kTileEmpty) k = kTileEmpty;
+    else if (a == kTileFull && b == kTileFull) k = kTileFull;
+    else k = kTilePartial;
+    kind128[i] = (uint8_t)k;
+}
+
+// Counts of empty, partial and full tiles of a tile map.
+__global__ __launch_bounds__(256) void tile_counts_kernel(const uint8_t* kind, int64_t n, int64_t* counts) {
+    __shared__ int lds[16];
+    int c1 = 0, c2 = 0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int k = kind[i];
+        c1 += k == kTilePartial;
+        c2 += k == kTileFull;
+    }
+    c1 = block_sum(c1, lds);
+    c2 = block_sum(c2, lds);
+    if (threadIdx.x == 0) {
+        atomicAdd((unsigned long long*)&counts[1], (unsigned long long)c1);
+        atomicAdd((unsigned long long*)&counts[2], (unsigned long long)c2);
+    }
+}
+
+__global__ void tile_counts_finish_kernel(int64_t n, int64_t* counts) {
+    if (threadIdx.x == 0) counts[0] = n - counts[1] - counts[2];
+}
+
+__global__ void zero_i64_kernel(int64_t* p, int n) {
+    if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -598,21 +660,23 @@ hipError_t launch_blockid_summary(const int32_t* q_blk, const int32_t* k_blk, co
     return hipGetLastError();
 }
 
-hipError_t launch_compact(const uint8_t* mask, int Nq, int Nk, uint8_t* tile_kind, uint32_t* fine_bits,
+hipError_t launch_compact(const uint8_t* mask, int Nq, int Nk, int BM, uint8_t* tile_kind, uint32_t* fine_bits,
                           int32_t* row_ptr, int32_t* col_idx, uint8_t* col_kind, hipStream_t s) {
-    const int nQt = (Nq + kCmpRows - 1) / kCmpRows, nKt = (Nk + 63) / 64;
+    const int nStrips = (Nq + kCmpRows - 1) / kCmpRows, nKt = (Nk + 63) / 64;
+    const int nQt = (Nq + BM - 1) / BM;
+    const bool bm64 = BM == 64;
     if (nQt == 0) {
         return hipMemsetAsync(row_ptr, 0, sizeof(int32_t), s);
     }
     if (nKt > 0) {
-        const dim3 grid((Nk + kCmpCols - 1) / kCmpCols, nQt);
+        const dim3 grid((Nk + kCmpCols - 1) / kCmpCols, nStrips);
         const bool vec = (Nk % 16 == 0) && (((uintptr_t)mask & 15) == 0);
         if (vec)
-            hipLaunchKernelGGL(compact_tiles_kernel<true>, grid, dim3(256), 0, s, mask, Nq, Nk, nKt, tile_kind,
+            hipLaunchKernelGGL(compact_tiles_kernel<true>, grid, dim3(256), 0, s, mask, Nq, Nk, nKt, bm64, tile_kind,
                                fine_bits);
         else
-            hipLaunchKernelGGL(compact_tiles_kernel<false>, grid, dim3(256), 0, s, mask, Nq, Nk, nKt, tile_kind,
-                               fine_bits);
+            hipLaunchKernelGGL(compact_tiles_kernel<false>, grid, dim3(256), 0, s, mask, Nq, Nk, nKt, bm64,
+                               tile_kind, fine_bits);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -620,16 +684,41 @@ hipError_t launch_compact(const uint8_t* mask, int Nq, int Nk, uint8_t* tile_kin
     return hipGetLastError();
 }
 
-hipError_t launch_predicate_tiles(const mfa_predicate& pred, int Nq, int Nk, uint8_t* tile_kind,
+hipError_t launch_coarsen_tiles(const uint8_t* kind64, int Nq, int Nk, uint8_t* kind128, int32_t* row_ptr,
+                                int32_t* col_idx, uint8_t* col_kind, hipStream_t s) {
+    const int nQt64 = (Nq + 63) / 64, nQt = (Nq + 127) / 128, nKt = (Nk + 63) / 64;
+    if (nQt == 0) return hipMemsetAsync(row_ptr, 0, sizeof(int32_t), s);
+    const int64_t n = (int64_t)nQt * nKt;
+    if (n > 0) {
+        hipLaunchKernelGGL(coarsen_tiles_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, kind64, nQt64,
+                           nKt, nQt, kind128);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(compact_csr_kernel, dim3(nQt), dim3(256), 0, s, kind128, nQt, nKt, row_ptr, col_idx, col_kind);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_counts(const uint8_t* kind, int64_t n, int64_t* counts, hipStream_t s) {
+    hipLaunchKernelGGL(zero_i64_kernel, dim3(1), dim3(64), 0, s, counts, 3);
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+    if (blocks > 0) hipLaunchKernelGGL(tile_counts_kernel, dim3((unsigned)blocks), dim3(256), 0, s, kind, n, counts);
+    hipLaunchKernelGGL(tile_counts_finish_kernel, dim3(1), dim3(64), 0, s, n, counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_predicate_tiles(const mfa_predicate& pred, int Nq, int Nk, int BM, uint8_t* tile_kind,
                                   uint32_t* fine_bits, int32_t* row_ptr, int32_t* col_idx, uint8_t* col_kind,
                                   hipStream_t s) {
-    const int nQt = (Nq + kCmpRows - 1) / kCmpRows, nKt = (Nk + 63) / 64;
+    const int nStrips = (Nq + kCmpRows - 1) / kCmpRows, nKt = (Nk + 63) / 64;
+    const int nQt = (Nq + BM - 1) / BM;
     if (nQt == 0) {
         return hipMemsetAsync(row_ptr, 0, sizeof(int32_t), s);
     }
     if (nKt > 0) {
-        const dim3 grid((Nk + kCmpCols - 1) / kCmpCols, nQt);
-        hipLaunchKernelGGL(predicate_tiles_kernel, grid, dim3(256), 0, s, pred, Nq, Nk, nKt, tile_kind, fine_bits);
+        const dim3 grid((Nk + kCmpCols - 1) / kCmpCols, nStrips);
+        hipLaunchKernelGGL(predicate_tiles_kernel, grid, dim3(256), 0, s, pred, Nq, Nk, nKt, BM == 64, tile_kind,
+                           fine_bits);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -121,8 +121,12 @@ def test_attn_fwd_null_and_mask_errors(lib):
 def test_maskrep_validation(lib):
     st = lib.mfa_make_block_ids(None, None, 1, 8, 2, None, None, None, None, None, None)
     assert _status(lib, st) == "MFA_E_ARG" and "cross_pad" in lib.mfa_last_error().decode()
-    st = lib.mfa_compact_dense_mask(None, 10, 10, 64, 64, None, None, None, None, None, None)
+    st = lib.mfa_compact_dense_mask(None, 10, 10, 32, 64, None, None, None, None, None, None)
     assert _status(lib, st) == "MFA_E_UNSUPPORTED"
+    st = lib.mfa_tile_counts(None, -1, None, None)
+    assert _status(lib, st) == "MFA_E_SHAPE"
+    st = lib.mfa_tile_map_coarsen(None, -1, 10, None, None, None, None, None)
+    assert _status(lib, st) == "MFA_E_SHAPE"
     st = lib.mfa_varlen_schedule(None, None, 2, 64, 64, 1, -1, -1, None, None, None, None, 4, None, None)
     assert _status(lib, st) == "MFA_E_UNSUPPORTED"
     st = lib.mfa_varlen_schedule(None, None, 2, 128, 64, 1, -2, -1, None, None, None, None, 4, None, None)
@@ -204,3 +208,17 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     import masked_flash_attention_amd as mfa
     assert mfa.is_available() is False
     assert "not built" in mfa.load_error()
+
+
+def test_tile_height_model_and_choice(lib):
+    """Host-only dispatch model: the causal N=8192 map keeps 128-row tiles;
+    a map whose 128-row tiles are all half empty (64 x 64 blocks) picks 64."""
+    import masked_flash_attention_amd as mfa
+    causal64, causal128 = (8128, 128, 8128), (4032, 128, 4032)
+    assert mfa.choose_tile_m(causal64, causal128, 8192) == 128
+    blocks64, blocks128 = (15384, 0, 1000), (7192, 1000, 0)
+    assert mfa.choose_tile_m(blocks64, blocks128, 8192) == 64
+    t = (C.c_int64 * 3)(0, 10, 20)
+    t2 = (C.c_int64 * 3)(0, 10, 21)
+    assert lib.mfa_model_tile_time(t2, 1000, 128) > lib.mfa_model_tile_time(t, 1000, 128) > 0
+    assert lib.mfa_choose_tile_m(None, None, 10) == 128
