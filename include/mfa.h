@@ -99,8 +99,8 @@ mfa_status mfa_make_block_ids(const uint8_t* pad, const int32_t* att, int B, int
                               uint8_t* q_valid, uint8_t* k_valid, hipStream_t stream);
 
 /* Per-tile summaries of a block-id representation, used by the attention
- * kernel to classify tiles exactly (same page, "reconstructed inside the
- * kernel"). Query tiles are BM tokens, key tiles BN tokens.
+ * kernel to classify tiles exactly (same page: the mask is rebuilt inside the
+ * kernel from the ids). Query tiles are BM tokens, key tiles BN tokens.
  *   qsum  (B, ceil(Sq/BM), 4) i32 and ksum (B, ceil(Sk/BN), 4) i32, each row
  *         {min id over valid tokens (INT32_MAX if none), max id over valid
  *         tokens (INT32_MIN if none), any valid (0/1), all BM (or BN)

@@ -5,7 +5,7 @@
 // A workgroup owns one query tile of BM rows of one (batch, query head) (or of
 // one varlen sequence). It walks only the key tiles that can hold an allowed
 // entry: the CSR list of non-empty tiles (dense-mask tiles, as in the BinFlash
-// method's "pre-sorted list of non-empty K-blocks per Q-row"), the BSR row
+// method's sorted per-query-tile list of non-empty key tiles), the BSR row
 // (flashinfer block_sparse_attention), the key-tile range of the sliding
 // window (varlen), or every key tile classified from block-id summaries
 // (opentau block ids). Full tiles skip the mask entirely; partial tiles

@@ -7,7 +7,7 @@ Every builder here is written from the plain definition on the pages, with
 NumPy loops or broadcasting; none of them reuses the GPU library's layout code.
 Conventions fixed here (readings where the pages are silent):
 
-* block ids are the inclusive prefix sum of the "opens a block" flags (int32);
+* block ids are the inclusive prefix sum of the block-opening flags (int32);
 * cross-attention key columns are prepended and carry block id -2**31;
 * a tile is "full" only if every in-range and out-of-range position of it is
   allowed; out-of-range positions count as not allowed, so a ragged edge tile is
@@ -70,8 +70,8 @@ def make_att_2d_masks(pad_masks, att_masks, cross_att_pad_masks=None):
 def make_att_block_ids(pad_masks, att_masks, n_cross_att_tokens=None, cross_att_pad_masks=None):
     """(q_blk, k_blk, q_valid, k_valid) per the opentau ``make_att_block_ids`` docs.
 
-    q_blk is the inclusive running count of block openers (int32, reading of
-    "1 opens a new attention block"); k_blk prepends ``n_cross_att_tokens``
+    q_blk is the inclusive running count of block openers (int32; a flag of
+    1 starts a new attention block); k_blk prepends ``n_cross_att_tokens``
     columns of INT32_MIN to q_blk; q_valid = pad; k_valid = [cross pad ; pad].
     ``cross_att_pad_masks`` is required iff ``n_cross_att_tokens`` is set.
     """
@@ -403,8 +403,8 @@ def cu_seqlens(lengths):
 def window_allows(i, j, causal, left, right):
     """Sliding-window predicate on sequence-local positions; -1 = unbounded side.
 
-    (-1, -1) disables the window (varlen page); "at most the previous W keys"
-    means i - j < W, i.e. left = W - 1 (omni_attention "Block masks" example).
+    (-1, -1) disables the window (varlen page); a window of the previous W
+    keys means i - j < W, i.e. left = W - 1 (omni_attention "Block masks" example).
     """
     i = np.asarray(i)
     j = np.asarray(j)

@@ -15,7 +15,7 @@ from tests.conftest import read_golden
 import workloads as W
 
 
-# --- block ids: "provably reproduces the dense mask" (opentau flash_attn_cuda) --
+# --- block ids reproduce the dense mask exactly (opentau flash_attn_cuda) -------
 
 def _all_patterns(N):
     bits = np.array(list(itertools.product([0, 1], repeat=N)), dtype=np.int32)
