@@ -406,3 +406,15 @@ def test_paged_gather_inverts_a_scatter_into_shuffled_pages():
             pages[table[s, j // page], j % page] = k[off + j]
         off += int(L)
     assert np.array_equal(M.paged_to_packed(pages, table, lengths, page), k)
+
+
+def test_splitmix64_published_vector():
+    """The input generator shared with the C client: SplitMix64 from seed
+    1234567 gives the reference implementation's first five outputs."""
+    from workloads.splitmix import splitmix64
+    z, st = splitmix64(1234567, 5)
+    assert [int(x) for x in z] == [6457827717110365317, 3203168211198807973, 9817491932198370423,
+                                   4593380528125082431, 16408922859458223821]
+    z2, _ = splitmix64(st, 1)
+    z3, _ = splitmix64(1234567, 6)
+    assert int(z2[0]) == int(z3[5])
