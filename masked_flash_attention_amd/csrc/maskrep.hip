@@ -392,6 +392,20 @@ __global__ void zero_i64_kernel(int64_t* p, int n) {
     if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
 }
 
+// Zero n int32 words with a kernel rather than hipMemsetAsync, so that the
+// call stays a kernel node when a caller captures it in a graph.
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+static hipError_t zero_i32(int32_t* p, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+    hipLaunchKernelGGL(zero_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // BSR (flashinfer block_sparse_attention): entry kinds and CSC. One workgroup
 // per (b, h); rows are visited in ascending order, the entries of one row in
@@ -666,7 +680,7 @@ hipError_t launch_compact(const uint8_t* mask, int Nq, int Nk, int BM, uint8_t* 
     const int nQt = (Nq + BM - 1) / BM;
     const bool bm64 = BM == 64;
     if (nQt == 0) {
-        return hipMemsetAsync(row_ptr, 0, sizeof(int32_t), s);
+        return zero_i32(row_ptr, 1, s);
     }
     if (nKt > 0) {
         const dim3 grid((Nk + kCmpCols - 1) / kCmpCols, nStrips);
@@ -687,7 +701,7 @@ hipError_t launch_compact(const uint8_t* mask, int Nq, int Nk, int BM, uint8_t* 
 hipError_t launch_coarsen_tiles(const uint8_t* kind64, int Nq, int Nk, uint8_t* kind128, int32_t* row_ptr,
                                 int32_t* col_idx, uint8_t* col_kind, hipStream_t s) {
     const int nQt64 = (Nq + 63) / 64, nQt = (Nq + 127) / 128, nKt = (Nk + 63) / 64;
-    if (nQt == 0) return hipMemsetAsync(row_ptr, 0, sizeof(int32_t), s);
+    if (nQt == 0) return zero_i32(row_ptr, 1, s);
     const int64_t n = (int64_t)nQt * nKt;
     if (n > 0) {
         hipLaunchKernelGGL(coarsen_tiles_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, kind64, nQt64,
@@ -713,7 +727,7 @@ hipError_t launch_predicate_tiles(const mfa_predicate& pred, int Nq, int Nk, int
     const int nStrips = (Nq + kCmpRows - 1) / kCmpRows, nKt = (Nk + 63) / 64;
     const int nQt = (Nq + BM - 1) / BM;
     if (nQt == 0) {
-        return hipMemsetAsync(row_ptr, 0, sizeof(int32_t), s);
+        return zero_i32(row_ptr, 1, s);
     }
     if (nKt > 0) {
         const dim3 grid((Nk + kCmpCols - 1) / kCmpCols, nStrips);
@@ -739,10 +753,9 @@ hipError_t launch_bsr_prepare(const int32_t* indptr, const int32_t* indices, int
 hipError_t launch_bsr_from_bitmask(const uint32_t* bits, int B, int Hkv, int nQb, int nKb, int32_t* indptr,
                                    int32_t* indices, int64_t cap, hipStream_t s) {
     const int n_bh = B * Hkv;
-    if (nQb == 0) return hipMemsetAsync(indptr, 0, (size_t)n_bh * sizeof(int32_t), s);
+    if (nQb == 0) return zero_i32(indptr, n_bh, s);
     if (nKb == 0) {
-        hipError_t e = hipMemsetAsync(indptr, 0, (size_t)n_bh * (nQb + 1) * sizeof(int32_t), s);
-        return e;
+        return zero_i32(indptr, (int64_t)n_bh * (nQb + 1), s);
     }
     hipLaunchKernelGGL(bitmask_count_kernel, dim3(1), dim3(1024), 0, s, bits, n_bh, nQb, nKb, indptr);
     hipError_t e = hipGetLastError();
