@@ -10,16 +10,18 @@ Every function states the passage of the source pages it follows. The pages are:
 * "opentau.policies.flash_attn_cuda" (API docs): block-id representation,
   ``make_att_block_ids`` and ``flash_attn_blockmask``.
 * "tensorplay.nn.attention.varlen": packed layout with cumulative lengths,
-  sliding window, GQA.
+  sliding window, GQA; intro: ``seqused_k`` and paged ``block_table``.
 * "BinFlash" (README), section "Efficiently Dispatching FlashAttention For
   Partially Filled Attention Masks": coarse block map, 32-bit packed fine mask,
   per-Q-row sorted list of non-empty K blocks, two-pass backward; section "Use":
   (N, N) bool mask, True = attend, default scale 1/sqrt(D).
 * "flashinfer.attention.prims_ts.block_sparse_attention": BSR block_indptr /
-  block_indices, canonical rows, ``mask_type='causal'`` inside blocks.
+  block_indices, canonical rows, ``mask_type='causal'`` inside blocks;
+  Parameters: ``kv_valid_bits`` and the ``exact_block_bits`` bitmask format.
 * "tensorplay.nn.attention.omni_attention", section "Block masks": mask_mod
   predicates, ``and_masks`` / ``or_masks`` / ``noop_mask`` / ``create_mask``;
-  section "Outputs": log-sum-exp output.
+  intro: ``score_mod`` (the distance-decay bias example); section "Outputs":
+  log-sum-exp output.
 
 Pins (what ties each function to something other than itself) live in
 ``tests/test_oracle_*.py``. Functions without such a pin say "parity unpinned".
