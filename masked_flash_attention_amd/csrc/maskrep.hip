@@ -275,7 +275,11 @@ __device__ __forceinline__ uint32_t predicate_bits16(const mfa_predicate& P, int
         for (int at = 0; at < P.n_atoms[tm]; ++at) {
             const mfa_pred_atom A = P.atoms[tm][at];
             const int64_t base = A.a * i + A.c;  // value at kv_idx = 0
+            // unit coefficients (causal, windows, prefixes) need no division;
+            // the coefficients are the same for every lane, so these branches are uniform
             if (A.b == 0) m &= base >= 0 ? 0xFFFFu : 0u;
+            else if (A.b == 1) m &= ge16(-base - j0);                  // j >= -base
+            else if (A.b == -1) m &= le16(base - j0);                  // j <= base
             else if (A.b > 0) m &= ge16(ceil_div(-base, A.b) - j0);   // j >= ceil(-base / b)
             else m &= le16(floor_div(base, -A.b) - j0);                // j <= floor(base / -b)
         }
