@@ -92,6 +92,8 @@ __device__ __forceinline__ void stage_vec64(const float* base, int i0, int n, fl
 #endif
 }
 
+
+
 __device__ __forceinline__ float lse_log2(float lse) {
     // exponent offset in log2 units; +inf for empty rows so that P = 0 there
     return lse == -INFINITY ? INFINITY : lse * kLog2e;
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* sQ = smem;                                   // [2][64 x D] Q
     char* sO = smem + 2 * TILEB;                       // [2][64 x D] dO
-    float* sL = (float*)(smem + 4 * TILEB);            // [2][64] LSE
+    float* sL = (float*)(smem + 4 * TILEB);            // [2][64] -LSE * log2(e)
     float* sDl = sL + 128;                             // [2][64] delta
 
     const FwdDev& f = p.f;
@@ -316,20 +318,38 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
 #pragma unroll
         for (int db = 0; db < NDB; ++db) trq[j][db] = tr_off<D>(8 * j + 4 * hh, db, lane);
 
-    auto stage = [&](int g_, uint32_t ent_, int buf) {
+    auto stage_to = [&](int g_, uint32_t ent_, char* dq_, char* do_, float* dd_) {
         const int hq = hk * f.G + g_;
         const int qb = (int)(ent_ & 0x0FFFFFFFu);
         const char* qbp = (const char*)f.q + 2 * ((int64_t)b * f.qs0 + (int64_t)hq * f.qs2);
         const char* obp = (const char*)p.dout + 2 * ((int64_t)b * p.dos0 + (int64_t)hq * p.dos2);
         const int r0 = q_base + qb * 64, rend = q_base + q_len;
-        stage_tile<D>(qbp, 2 * f.qs1, r0, rend, sQ + buf * TILEB, wave, 2, lane);
-        stage_tile<D>(obp, 2 * p.dos1, r0, rend, sO + buf * TILEB, wave, 2, lane);
+        stage_tile<D>(qbp, 2 * f.qs1, r0, rend, dq_, wave, 2, lane);
+        stage_tile<D>(obp, 2 * p.dos1, r0, rend, do_, wave, 2, lane);
         const int64_t lrow = ((int64_t)b * f.Hq + hq) * f.Sq;
-        if (wave == 0) stage_vec64(f.lse + lrow, r0, rend, sL + buf * 64, lane);
-        else stage_vec64(p.delta + lrow, r0, rend, sDl + buf * 64, lane);
+        if (wave == 1) stage_vec64(p.delta + lrow, r0, rend, dd_, lane);
+    };
+    auto stage = [&](int g_, uint32_t ent_, int buf) {
+        stage_to(g_, ent_, sQ + buf * TILEB, sO + buf * TILEB, sDl + buf * 64);
+    };
+    // Wave 0 loads the LSE of the staged rows into a register and stores it
+    // to LDS, as the exponent offset in log2 units, at the end of the step
+    // (before the barrier that publishes the buffer): the per-element
+    // conversion then costs nothing in the step that reads it.
+    auto lse_fetch = [&](int g_, uint32_t ent_) -> float {
+        const int hq = hk * f.G + g_;
+        const int r = q_base + (int)(ent_ & 0x0FFFFFFFu) * 64 + lane;
+        return r < q_base + q_len ? f.lse[((int64_t)b * f.Hq + hq) * f.Sq + r] : -INFINITY;
+    };
+    auto lse_store = [&](float lse, int buf) {
+        // -lse*log2(e); -inf for empty rows (and rows past the end) so that P = 0 there
+        sL[buf * 64 + lane] = lse == -INFINITY ? -INFINITY : -lse * kLog2e;
     };
 
-    if (have) stage(g, ent, 0);
+    if (have) {
+        stage(g, ent, 0);
+        if (wave == 0) lse_store(lse_fetch(g, ent), 0);
+    }
     vm_wait();
     __syncthreads();
     int buf = 0;
@@ -339,73 +359,106 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
         int g_n = g, pos_n = pos;
         uint32_t ent_n = 0;
         const bool have_n = next_step(g_n, pos_n, ent_n);
-        if (have_n) stage(g_n, ent_n, buf ^ 1);
-        const char* q_ = sQ + buf * TILEB;
-        const char* o_ = sO + buf * TILEB;
-        const float* l_ = sL + buf * 64;
-        const float* d_ = sDl + buf * 64;
-
-        // S = Q K^T and dP = dO V^T for the two 32-query halves
-        f32x16 s[2], dp[2];
-        if constexpr (BIAS) {
-            const float sl = f.alibi[hk * f.G + g] / f.scale;
-            alibi_fill(s, sl, key_l - qb * 64 - 4 * hh, -sl);
-        } else {
-            s[0] = f32x16{};
-            s[1] = f32x16{};
-        }
-#pragma unroll
-        for (int qh = 0; qh < 2; ++qh) {
-            dp[qh] = f32x16{};
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) {
-                const bf16x8 aq = *(const bf16x8*)(q_ + qh * 32 * ROWB + qrow_off[kc]);
-                const bf16x8 ao = *(const bf16x8*)(o_ + qh * 32 * ROWB + qrow_off[kc]);
-                s[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kc], s[qh], 0, 0, 0);
-                dp[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[kc], dp[qh], 0, 0, 0);
+        float lse_n = 0.f;
+        // The step works on restrict-qualified views of the two buffers: the
+        // reads of this step's buffer then carry alias scopes that tell the
+        // compiler they do not overlap the DMA into the other buffer, so it
+        // does not make them wait for that DMA.
+        auto body = [&](const char* __restrict__ q_, const char* __restrict__ o_, const float* __restrict__ l_,
+                        const float* __restrict__ d_, char* __restrict__ nq_, char* __restrict__ no_,
+                        float* __restrict__ nd_) {
+            if (have_n) {
+                stage_to(g_n, ent_n, nq_, no_, nd_);
+                if (wave == 0) lse_n = lse_fetch(g_n, ent_n);
             }
-        }
-        // allowed bits on partial blocks; register r of half qh is query qh*32 + (r>>2)*8 + 4*hh + (r&3)
-        uint32_t okb[2] = {0xFFFFu, 0xFFFFu};
-        if (__builtin_expect(kind == kTilePartial, 0)) {
+
+            // The two 32-query halves one after the other: S = Q K^T and
+            // dP = dO V^T (G1 operand groups), then P and dS, then
+            // dV^T += dO^T P and dK^T += Q^T dS (G2 groups). The LDS operand
+            // reads of all 2 * (G1 + G2) groups form one stream issued PF groups
+            // ahead of the MFMAs that consume them (a ring of PF + 1 slots), so
+            // that with one wave per SIMD the read latency is not exposed.
+            constexpr int G1 = NKC, G2 = 2 * NDB, GH = G1 + G2, GT = 2 * GH, PF = 3, RING = PF + 1;
+            bf16x8 ra[RING], rb[RING];
+            auto load_group = [&](int i) {
+                const int h = i / GH, j = i % GH, slot = i % RING;
+                if (j < G1) {
+                    ra[slot] = *(const bf16x8*)(q_ + h * 32 * ROWB + qrow_off[j]);
+                    rb[slot] = *(const bf16x8*)(o_ + h * 32 * ROWB + qrow_off[j]);
+                } else {
+                    const int jj = j - G1, k2 = jj / NDB, db = jj % NDB;
+                    const int o0 = (h * 2 + k2) * 16 * ROWB;
+                    const bf16x4 olo = tr_read(o_ + o0 + trq[0][db]);
+                    const bf16x4 ohi = tr_read(o_ + o0 + trq[1][db]);
+                    const bf16x4 qlo = tr_read(q_ + o0 + trq[0][db]);
+                    const bf16x4 qhi = tr_read(q_ + o0 + trq[1][db]);
+                    ra[slot] = __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    rb[slot] = __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+            };
+            f32x16 s, dp;
+            f32x4 NL[4], DL[4];
+            bf16x8 pb[2], sb[2];
 #pragma unroll
-            for (int qh = 0; qh < 2; ++qh)
-                okb[qh] = allowed_bits_T<KIND>(f, m, b, q_len, k_len, key_l, qb * 64 + qh * 32, hh, kblk, kval);
-        }
-        bf16x8 pb[4], sb[4];
+            for (int i = 0; i < PF; ++i) load_group(i);
+#pragma clang loop unroll(full)
+            for (int i = 0; i < GT; ++i) {
+                const int h = i / GH, j = i % GH, slot = i % RING;
+                if (j == 0) {
 #pragma unroll
-        for (int qh = 0; qh < 2; ++qh) {
+                    for (int gq = 0; gq < 4; ++gq) {
+                        NL[gq] = *(const f32x4*)(l_ + h * 32 + gq * 8 + 4 * hh);
+                        DL[gq] = *(const f32x4*)(d_ + h * 32 + gq * 8 + 4 * hh);
+                    }
+                    if constexpr (BIAS) {
+                        f32x16 t2[2];
+                        const float sl = f.alibi[hk * f.G + g] / f.scale;
+                        alibi_fill(t2, sl, key_l - qb * 64 - 4 * hh, -sl);
+                        s = t2[h];
+                    } else {
+                        s = f32x16{};
+                    }
+                    dp = f32x16{};
+                }
+                if (i + PF < GT) load_group(i + PF);
+                __builtin_amdgcn_sched_barrier(0);
+                if (j < G1) {
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[slot], kf[j], s, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[slot], vf[j], dp, 0, 0, 0);
+                } else {
+                    const int jj = j - G1, k2 = jj / NDB, db = jj % NDB;
+                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[slot], pb[k2], dv[db], 0, 0, 0);
+                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[slot], sb[k2], dk[db], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (j == G1 - 1) {
+                    // partial blocks: disallowed scores become -inf (P = 0 there);
+                    // register r is query h*32 + (r>>2)*8 + 4*hh + (r&3)
+                    if (__builtin_expect(kind == kTilePartial, 0)) {
+                        const uint32_t okb =
+                            allowed_bits_T<KIND>(f, m, b, q_len, k_len, key_l, qb * 64 + h * 32, hh, kblk, kval);
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const f32x4 L = *(const f32x4*)(l_ + qh * 32 + gq * 8 + 4 * hh);
-                const f32x4 Dl = *(const f32x4*)(d_ + qh * 32 + gq * 8 + 4 * hh);
+                        for (int rr = 0; rr < 16; ++rr)
+                            if (!((okb >> rr) & 1u)) s[rr] = -INFINITY;
+                    }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int rr = gq * 4 + e;
-                    float pv = fast_exp2(fmaf(s[qh][rr], c2, -lse_log2(L[e])));
-                    if (!((okb[qh] >> rr) & 1u)) pv = 0.f;
-                    const float ds = pv * (dp[qh][rr] - Dl[e]);
-                    pb[qh * 2 + (gq >> 1)][(gq & 1) * 4 + e] = (bf16)pv;
-                    sb[qh * 2 + (gq >> 1)][(gq & 1) * 4 + e] = (bf16)ds;
+                    for (int gq = 0; gq < 4; ++gq) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int rr = gq * 4 + e;
+                            const float pv = fast_exp2(fmaf(s[rr], c2, NL[gq][e]));
+                            const float ds = pv * (dp[rr] - DL[gq][e]);
+                            pb[gq >> 1][(gq & 1) * 4 + e] = (bf16)pv;
+                            sb[gq >> 1][(gq & 1) * 4 + e] = (bf16)ds;
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
-        }
-        // dV^T += dO^T P ; dK^T += Q^T dS  (k = 16-query chunks)
-#pragma unroll
-        for (int kq = 0; kq < 4; ++kq) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const int o0 = kq * 16 * ROWB;
-                const bf16x4 olo = tr_read(o_ + o0 + trq[0][db]);
-                const bf16x4 ohi = tr_read(o_ + o0 + trq[1][db]);
-                const bf16x4 qlo = tr_read(q_ + o0 + trq[0][db]);
-                const bf16x4 qhi = tr_read(q_ + o0 + trq[1][db]);
-                const bf16x8 ao = __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7);
-                const bf16x8 aq = __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7);
-                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb[kq], dv[db], 0, 0, 0);
-                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb[kq], dk[db], 0, 0, 0);
-            }
-        }
+        };
+        body(sQ + buf * TILEB, sO + buf * TILEB, sL + buf * 64, sDl + buf * 64, sQ + (buf ^ 1) * TILEB,
+             sO + (buf ^ 1) * TILEB, sDl + (buf ^ 1) * 64);
+        if (wave == 0 && have_n) lse_store(lse_n, buf ^ 1);
         vm_wait();
         __syncthreads();
         buf ^= 1;
