@@ -154,7 +154,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
             }
         }
     };
-    auto load_tile = [&](int kt, int buf, bool live) {
+    auto load_tile_to = [&](int kt, char* dk, char* dv, bool live) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer-resource builtins exist only in the device pass
         const char *kp, *vp;
         int kn, vn;
@@ -164,11 +164,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int blk = (wave * NI + i) * 1024;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sK + buf * TILEB + blk), 16, kgo[i], 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sV + buf * TILEB + blk), 16, vgo[i], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dk + blk), 16, kgo[i], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dv + blk), 16, vgo[i], 0, 0, 0);
         }
 #endif
     };
+    auto load_tile = [&](int kt, int buf, bool live) { load_tile_to(kt, sK + buf * TILEB, sV + buf * TILEB, live); };
 
     // Per-lane LDS offsets of the operand reads.
     // K operand: row kb*32 + c, logical chunk kc*2 + hh.
@@ -227,78 +228,85 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
         if (!has_next) kt_n = kt, kind_n = kTileEmpty;
         uint32_t fw_n[2];
         fine_words(kt_n, kind_n, fw_n);
-        load_tile(kt_n, buf ^ 1, has_next);  // buf^1 was released by the last barrier
+        // restrict-qualified views of the two buffers: the reads of this
+        // tile carry alias scopes that keep the compiler from making them
+        // wait for the loads into the other buffer
+        auto step = [&](const char* __restrict__ ck_, const char* __restrict__ cv_, char* __restrict__ nk_,
+                        char* __restrict__ nv_) {
+            load_tile_to(kt_n, nk_, nv_, has_next);  // buf^1 was released by the last barrier
 
-        // ---- S^T = K Q^T ----
-        f32x16 s[2];
-        if constexpr (BIAS) {
-            alibi_fill(s, sl, kt * kBN + d_row, sl);
-        } else {
-            s[0] = f32x16{};
-            s[1] = f32x16{};
-        }
-        const char* kb_ = sK + buf * TILEB;
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 a = *(const bf16x8*)(kb_ + kb * 32 * ROWB + koff[kc]);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[kb], 0, 0, 0);
+            // ---- S^T = K Q^T ----
+            f32x16 s[2];
+            if constexpr (BIAS) {
+                alibi_fill(s, sl, kt * kBN + d_row, sl);
+            } else {
+                s[0] = f32x16{};
+                s[1] = f32x16{};
             }
-        }
-
-        // ---- mask on partial or ragged tiles ----
-        if (__builtin_expect(kind == kTilePartial || (kt + 1) * kBN > t.k_len, 0))
-            mask_scores<KIND>(p, m, t, rm, row, hh, kt, fw, s);
-
-        // ---- online softmax ----
-        // Row max and row sum as 4 independent chains each (short dependency
-        // chains: a single wave issues them back to back).
-        float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            const char* kb_ = ck_;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kc = 0; kc < NKC; ++kc) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], s[kb][r]);
-        float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-        mx = max_both_halves(mx);
-        const float m_new = fmaxf(m_used, mx);
-        const bool need = (m_new - m_used) * c2 > kTau;  // false when both are -inf
-        if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
-            const float alpha = need ? fast_exp2((m_used - m_new) * c2) : 1.f;
-            m_used = need ? m_new : m_used;
-            l_part *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-        }
-        const float mb = (m_used == -INFINITY) ? 0.f : m_used * c2;
-        bf16x8 pb[4];
-        float rs4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int gp = 0; gp < 2; ++gp)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float pv = fast_exp2(fmaf(s[kb][gp * 8 + e], c2, -mb));
-                    rs4[e & 3] += pv;
-                    pb[kb * 2 + gp][e] = (bf16)pv;
+                for (int kb = 0; kb < 2; ++kb) {
+                    const bf16x8 a = *(const bf16x8*)(kb_ + kb * 32 * ROWB + koff[kc]);
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[kb], 0, 0, 0);
                 }
-        l_part += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
-
-        // ---- O^T += V^T P^T ----
-        const char* vb_ = sV + buf * TILEB;
-#pragma unroll
-        for (int kc2 = 0; kc2 < 4; ++kc2) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const bf16x4 lo = ds_read_tr(vb_ + kc2 * 16 * ROWB + voff[db]);
-                const bf16x4 hi = ds_read_tr(vb_ + (kc2 * 16 + 8) * ROWB + voff[db]);
-                const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc2], o[db], 0, 0, 0);
             }
-        }
+
+            // ---- mask on partial or ragged tiles ----
+            if (__builtin_expect(kind == kTilePartial || (kt + 1) * kBN > t.k_len, 0))
+                mask_scores<KIND>(p, m, t, rm, row, hh, kt, fw, s);
+
+            // ---- online softmax ----
+            // Row max and row sum as 4 independent chains each (short dependency
+            // chains: a single wave issues them back to back).
+            float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], s[kb][r]);
+            float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+            mx = max_both_halves(mx);
+            const float m_new = fmaxf(m_used, mx);
+            const bool need = (m_new - m_used) * c2 > kTau;  // false when both are -inf
+            if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+                const float alpha = need ? fast_exp2((m_used - m_new) * c2) : 1.f;
+                m_used = need ? m_new : m_used;
+                l_part *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            }
+            const float mb = (m_used == -INFINITY) ? 0.f : m_used * c2;
+            bf16x8 pb[4];
+            float rs4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int gp = 0; gp < 2; ++gp)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float pv = fast_exp2(fmaf(s[kb][gp * 8 + e], c2, -mb));
+                        rs4[e & 3] += pv;
+                        pb[kb * 2 + gp][e] = (bf16)pv;
+                    }
+            l_part += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
+
+            // ---- O^T += V^T P^T ----
+            const char* vb_ = cv_;
+#pragma unroll
+            for (int kc2 = 0; kc2 < 4; ++kc2) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const bf16x4 lo = ds_read_tr(vb_ + kc2 * 16 * ROWB + voff[db]);
+                    const bf16x4 hi = ds_read_tr(vb_ + (kc2 * 16 + 8) * ROWB + voff[db]);
+                    const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc2], o[db], 0, 0, 0);
+                }
+            }
+        };
+        step(sK + buf * TILEB, sV + buf * TILEB, sK + (buf ^ 1) * TILEB, sV + (buf ^ 1) * TILEB);
 
         wait_vmem();  // this wave's tile loads have landed in LDS
         __syncthreads();
