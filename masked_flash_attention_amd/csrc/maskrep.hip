@@ -257,6 +257,71 @@ __global__ __launch_bounds__(256) void compact_tiles_kernel(const uint8_t* mask,
     tile_strip(bits16, Nq, Nk, nKt, bm64, tile_kind, fine_bits);
 }
 
+// Dense masks whose row length is a multiple of 16 bytes: one workgroup of
+// 8 waves covers 128 rows x 1024 columns (16 key tiles). Wave w reads rows
+// w*16 .. w*16+15, one 1 KB row segment per instruction (lane l: columns
+// 16l .. 16l+15), so every load is a fully used 1 KB run and every row's
+// fine words leave as one 128-byte store.
+constexpr int kWideCols = 1024;
+
+__global__ __launch_bounds__(512) void compact_tiles_wide_kernel(const uint8_t* mask, int Nq, int Nk, int nKt,
+                                                                 bool bm64, uint8_t* tile_kind, uint32_t* fine_bits) {
+    __shared__ uint64_t s_any[8], s_all[8];
+    const int qt = blockIdx.y;
+    const int col0 = blockIdx.x * kWideCols;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = col0 + 16 * lane;
+    const int W = (Nk + 31) / 32;
+    const bool col_ok = col + 16 <= Nk;  // Nk is a multiple of 16 here
+    const int r0 = qt * kCmpRows + wave * 16;
+    u32x4 v[16];
+#pragma unroll
+    for (int ps = 0; ps < 16; ++ps) {
+        const int r = r0 + ps;
+        v[ps] = (r < Nq && col_ok) ? __builtin_nontemporal_load((const u32x4*)(mask + (int64_t)r * Nk + col))
+                                   : u32x4{0u, 0u, 0u, 0u};
+    }
+    uint64_t any = 0, all = ~0ull;
+#pragma unroll
+    for (int ps = 0; ps < 16; ++ps) {
+        const int r = r0 + ps;
+        const uint32_t bits = pack4(v[ps][0]) | (pack4(v[ps][1]) << 4) | (pack4(v[ps][2]) << 8) | (pack4(v[ps][3]) << 12);
+        any |= __builtin_amdgcn_ballot_w64(bits != 0u);
+        all &= __builtin_amdgcn_ballot_w64(r < Nq && col_ok && bits == 0xFFFFu);
+        // lane pairs (even, odd) form one 32-bit word of the row
+        const uint32_t hi = __shfl_xor(bits, 1);
+        const int wi = col0 / 32 + (lane >> 1);
+        if (r < Nq && (lane & 1) == 0 && wi < W) fine_bits[(int64_t)r * W + wi] = bits | (hi << 16);
+    }
+    if (lane == 0) {
+        s_any[wave] = any;
+        s_all[wave] = all;
+    }
+    __syncthreads();
+    // thread t < 32: half h = t / 16 (waves 4h .. 4h+3), key tile j = t % 16 (lanes 4j .. 4j+3)
+    const int t = threadIdx.x;
+    if (t < 32) {
+        const int h = t >> 4, j = t & 15, kt = col0 / 64 + j;
+        bool a[2] = {false, false}, f[2] = {true, true};
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                a[hh] = a[hh] || ((s_any[hh * 4 + w] >> (4 * j)) & 0xFull) != 0;
+                f[hh] = f[hh] && ((s_all[hh * 4 + w] >> (4 * j)) & 0xFull) == 0xFull;
+            }
+        if (kt < nKt) {
+            if (bm64) {
+                const int q64 = 2 * qt + h;
+                if (q64 * 64 < Nq) tile_kind[(int64_t)q64 * nKt + kt] = f[h] ? kTileFull : (a[h] ? kTilePartial : kTileEmpty);
+            } else if (h == 0) {
+                const bool aa = a[0] || a[1], ff = f[0] && f[1];
+                tile_kind[(int64_t)qt * nKt + kt] = ff ? kTileFull : (aa ? kTilePartial : kTileEmpty);
+            }
+        }
+    }
+}
+
 // floor(n / d) and ceil(n / d) for d > 0
 __device__ __forceinline__ int64_t floor_div(int64_t n, int64_t d) { return n >= 0 ? n / d : -((-n + d - 1) / d); }
 __device__ __forceinline__ int64_t ceil_div(int64_t n, int64_t d) { return -floor_div(-n, d); }
@@ -690,8 +755,8 @@ hipError_t launch_compact(const uint8_t* mask, int Nq, int Nk, int BM, uint8_t* 
         const dim3 grid((Nk + kCmpCols - 1) / kCmpCols, nStrips);
         const bool vec = (Nk % 16 == 0) && (((uintptr_t)mask & 15) == 0);
         if (vec)
-            hipLaunchKernelGGL(compact_tiles_kernel<true>, grid, dim3(256), 0, s, mask, Nq, Nk, nKt, bm64, tile_kind,
-                               fine_bits);
+            hipLaunchKernelGGL(compact_tiles_wide_kernel, dim3((Nk + kWideCols - 1) / kWideCols, nStrips), dim3(512),
+                               0, s, mask, Nq, Nk, nKt, bm64, tile_kind, fine_bits);
         else
             hipLaunchKernelGGL(compact_tiles_kernel<false>, grid, dim3(256), 0, s, mask, Nq, Nk, nKt, bm64,
                                tile_kind, fine_bits);
