@@ -83,6 +83,33 @@ __device__ __forceinline__ void stage_tile(const char* base, int64_t row_bytes, 
 #endif
 }
 
+// The same staging split into a descriptor and single instructions, so that
+// the instructions can be spread over a compute phase: each moves 1 KB
+// (RPI rows), instruction i filling LDS bytes [1024 i, 1024 i + 1024).
+template <int D>
+struct TileDma {
+    static constexpr int ROWB = 2 * D, RPI = 1024 / ROWB, CPR = D / 8, NINST = 64 / RPI;
+    __amdgpu_buffer_rsrc_t rs;
+    int64_t row_bytes;
+    __device__ __forceinline__ void init(const char* base, int64_t rb, int row0, int rows) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        row_bytes = rb;
+        const int64_t start = (int64_t)row0 * rb;
+        const int64_t total = rows > 0 ? (int64_t)(rows - 1) * rb + ROWB : 0;
+        const int nrec = (int)(total > start ? total - start : 0);
+        rs = __builtin_amdgcn_make_buffer_rsrc((void*)(base + start), 0, nrec, 0x00020000);
+#endif
+    }
+    __device__ __forceinline__ void issue(char* lds, int i, int lane) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+        const int r = i * RPI + lane / CPR;
+        const int pc = lane % CPR;
+        const int go = (int)(r * row_bytes) + ((pc ^ tswz<D>(r)) << 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + i * 1024), 16, go, 0, 0, 0);
+#endif
+    }
+};
+
 // Stage 64 consecutive fp32 values (positions [i0, i0+64) of a row of length n).
 __device__ __forceinline__ void stage_vec64(const float* base, int i0, int n, float* lds, int lane) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -191,8 +218,9 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
     bool len_error = false;
     if constexpr (KIND == MFA_MASK_VARLEN) {
         const int nKbm = (m.max_k + 63) / 64;
-        kbk = blockIdx.x % nKbm;
-        const int sh = blockIdx.x / nKbm;
+        const int wg = xcd_logical(blockIdx.x, gridDim.x, (gridDim.x & 7) == 0);
+        kbk = wg % nKbm;
+        const int sh = wg / nKbm;
         hk = sh % f.Hkv;
         const int seq = sh / f.Hkv;
         q_base = m.cu_q[seq];
@@ -207,8 +235,11 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
         }
     } else {
         const int nKb = (f.Sk + 63) / 64;
-        const int bh = blockIdx.x / nKb;
-        kbk = blockIdx.x - bh * nKb;
+        // consecutive key blocks of one (batch, head) on one XCD, so that
+        // they share that XCD's L2 copy of the head's Q and dO
+        const int wg = xcd_logical(blockIdx.x, gridDim.x, (gridDim.x & 7) == 0);
+        const int bh = wg / nKb;
+        kbk = wg - bh * nKb;
         b = bh / f.Hkv;
         hk = bh - b * f.Hkv;
     }
@@ -367,8 +398,29 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
         auto body = [&](const char* __restrict__ q_, const char* __restrict__ o_, const float* __restrict__ l_,
                         const float* __restrict__ d_, char* __restrict__ nq_, char* __restrict__ no_,
                         float* __restrict__ nd_) {
+            // The next block's Q and dO tiles. At D = 128 this wave's NPW
+            // instructions of each are issued one per operand group below,
+            // interleaved with the MFMAs, rather than all at the start of the
+            // step (a burst of them stalls the wave on the vector memory
+            // queue); at D = 64 (two waves per SIMD, no registers to spare)
+            // they are issued here.
+            constexpr bool SPREAD = D == 128;
+            constexpr int NPW = TileDma<D>::NINST / 2;
+            TileDma<D> dmq, dmo;
             if (have_n) {
-                stage_to(g_n, ent_n, nq_, no_, nd_);
+                if constexpr (SPREAD) {
+                    const int hq = hk * f.G + g_n;
+                    const int qbn = (int)(ent_n & 0x0FFFFFFFu);
+                    const char* qbp = (const char*)f.q + 2 * ((int64_t)b * f.qs0 + (int64_t)hq * f.qs2);
+                    const char* obp = (const char*)p.dout + 2 * ((int64_t)b * p.dos0 + (int64_t)hq * p.dos2);
+                    const int r0 = q_base + qbn * 64, rend = q_base + q_len;
+                    dmq.init(qbp, 2 * f.qs1, r0, rend);
+                    dmo.init(obp, 2 * p.dos1, r0, rend);
+                    const int64_t lrow = ((int64_t)b * f.Hq + hq) * f.Sq;
+                    if (wave == 1) stage_vec64(p.delta + lrow, r0, rend, nd_, lane);
+                } else {
+                    stage_to(g_n, ent_n, nq_, no_, nd_);
+                }
                 if (wave == 0) lse_n = lse_fetch(g_n, ent_n);
             }
 
@@ -421,6 +473,11 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
                     dp = f32x16{};
                 }
                 if (i + PF < GT) load_group(i + PF);
+                if (SPREAD && i < 2 * NPW && have_n) {
+                    const int ii = wave + 2 * (i >> 1);  // instruction index within the tile
+                    if (i & 1) dmo.issue(no_, ii, lane);
+                    else dmq.issue(nq_, ii, lane);
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 if (j < G1) {
                     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[slot], kf[j], s, 0, 0, 0);
