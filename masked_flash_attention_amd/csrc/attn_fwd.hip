@@ -233,7 +233,25 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
         // wait for the loads into the other buffer
         auto step = [&](const char* __restrict__ ck_, const char* __restrict__ cv_, char* __restrict__ nk_,
                         char* __restrict__ nv_) {
-            load_tile_to(kt_n, nk_, nv_, has_next);  // buf^1 was released by the last barrier
+            // The next tile's K and V loads (into buf^1, released by the last
+            // barrier) are issued a few at a time between the S MFMAs below
+            // rather than as one burst, which would stall the wave on the
+            // vector memory queue.
+            constexpr int NDMA = 2 * NI, DPK = (NDMA + NKC - 1) / NKC;  // loads per d chunk
+#if defined(__HIP_DEVICE_COMPILE__)
+            const char *kp_, *vp_;
+            int kn_, vn_;
+            tile_base(kt_n, has_next, kp_, vp_, kn_, vn_);
+            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kp_, 0, kn_, 0x00020000);
+            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vp_, 0, vn_, 0x00020000);
+#endif
+            auto dma = [&](int j) {
+#if defined(__HIP_DEVICE_COMPILE__)
+                const int i = j >> 1, blk = (wave * NI + i) * 1024;
+                if (j & 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(nv_ + blk), 16, vgo[i], 0, 0, 0);
+                else __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(nk_ + blk), 16, kgo[i], 0, 0, 0);
+#endif
+            };
 
             // ---- S^T = K Q^T ----
             f32x16 s[2];
@@ -251,6 +269,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
                     const bf16x8 a = *(const bf16x8*)(kb_ + kb * 32 * ROWB + koff[kc]);
                     s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[kb], 0, 0, 0);
                 }
+#pragma unroll
+                for (int d = 0; d < DPK; ++d)
+                    if (kc * DPK + d < NDMA) dma(kc * DPK + d);
+            }
+            // keep the loads spread: per d chunk, two operand reads, two MFMAs, DPK loads
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                if (kc * DPK < NDMA) __builtin_amdgcn_sched_group_barrier(0x020, DPK, 0);
             }
 
             // ---- mask on partial or ragged tiles ----
