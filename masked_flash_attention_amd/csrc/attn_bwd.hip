@@ -218,9 +218,10 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
     bool len_error = false;
     if constexpr (KIND == MFA_MASK_VARLEN) {
         const int nKbm = (m.max_k + 63) / 64;
-        const int wg = xcd_logical(blockIdx.x, gridDim.x, (gridDim.x & 7) == 0);
-        kbk = wg % nKbm;
-        const int sh = wg / nKbm;
+        // plain numbering: sequences differ in length, and round-robin over
+        // the XCDs keeps their work balanced
+        kbk = blockIdx.x % nKbm;
+        const int sh = blockIdx.x / nKbm;
         hk = sh % f.Hkv;
         const int seq = sh / f.Hkv;
         q_base = m.cu_q[seq];
