@@ -615,10 +615,11 @@ __global__ __launch_bounds__(NW * 64, (NW == 2 || KIND == MFA_MASK_BLOCKID) ? 1 
             }
         }
     };
-    auto stage = [&](int kt_, int buf) {
-        stage_tile<D>(kbase, 2 * f.ks1, kt_ * 64, t.k_len, sK + buf * TILEB, wave, NW, lane);
-        stage_tile<D>(vbase, 2 * f.vs1, kt_ * 64, t.k_len, sV + buf * TILEB, wave, NW, lane);
+    auto stage_to = [&](int kt_, char* dk_, char* dv_) {
+        stage_tile<D>(kbase, 2 * f.ks1, kt_ * 64, t.k_len, dk_, wave, NW, lane);
+        stage_tile<D>(vbase, 2 * f.vs1, kt_ * 64, t.k_len, dv_, wave, NW, lane);
     };
+    auto stage = [&](int kt_, int buf) { stage_to(kt_, sK + buf * TILEB, sV + buf * TILEB); };
 
     float sl = 0.f;  // bias slope in raw score units
     int d_row = 0;   // 4*hh - this lane's query position (local to the sequence)
@@ -641,52 +642,78 @@ __global__ __launch_bounds__(NW * 64, (NW == 2 || KIND == MFA_MASK_BLOCKID) ? 1 
         const bool has_next = it_n < t.end;
         uint32_t fw_n[2];
         fine_words(kt_n, has_next ? kind_n : kTileEmpty, fw_n);
-        if (has_next) stage(kt_n, buf ^ 1);
-        const char* k_ = sK + buf * TILEB;
-        const char* v_ = sV + buf * TILEB;
-
-        // S^T = K Q^T and dP^T = V dO^T (64 keys x 32 queries per wave)
-        f32x16 s[2], dp[2];
-        if constexpr (BIAS) {
-            alibi_fill(s, sl, kt * kBN + d_row, sl);
-        } else {
-            s[0] = f32x16{};
-            s[1] = f32x16{};
-        }
+        // restrict-qualified views of the two buffers: the reads of this
+        // tile carry alias scopes that keep the compiler from making them
+        // wait for the loads into the other buffer
+        auto step = [&](const char* __restrict__ k_, const char* __restrict__ v_, char* __restrict__ nk_,
+                        char* __restrict__ nv_) {
+            if (has_next) stage_to(kt_n, nk_, nv_);
+            // The two 32-key halves one after the other: S^T = K Q^T and
+            // dP^T = V dO^T (G1 operand groups, two MFMAs each), then dS,
+            // then dQ^T += K^T dS^T over the half's two 16-key chunks (G2
+            // groups). The LDS operand reads of all groups form one stream
+            // issued PF groups ahead of their MFMAs (a ring of PF + 1 slots).
+            constexpr int G1 = NKC, G2 = 2 * NDB, GH = G1 + G2, GT = 2 * GH, PF = 3, RING = PF + 1;
+            bf16x8 ra[RING], rb[RING];
+            auto load_group = [&](int i) {
+                const int h = i / GH, j = i % GH, slot = i % RING;
+                if (j < G1) {
+                    ra[slot] = *(const bf16x8*)(k_ + h * 32 * ROWB + krow_off[j]);
+                    rb[slot] = *(const bf16x8*)(v_ + h * 32 * ROWB + krow_off[j]);
+                } else {
+                    const int jj = j - G1, k2 = jj / NDB, db = jj % NDB;
+                    const int o0 = (h * 2 + k2) * 16 * ROWB;
+                    const bf16x4 lo = tr_read(k_ + o0 + trk[0][db]);
+                    const bf16x4 hi = tr_read(k_ + o0 + trk[1][db]);
+                    ra[slot] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+            };
+            f32x16 sh, dph;
+            bf16x8 sb[2];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            dp[h2] = f32x16{};
+            for (int i = 0; i < PF; ++i) load_group(i);
+#pragma clang loop unroll(full)
+            for (int i = 0; i < GT; ++i) {
+                const int h = i / GH, j = i % GH, slot = i % RING;
+                if (j == 0) {
+                    if constexpr (BIAS) {
+                        f32x16 t2[2];
+                        alibi_fill(t2, sl, kt * kBN + d_row, sl);
+                        sh = t2[h];
+                    } else {
+                        sh = f32x16{};
+                    }
+                    dph = f32x16{};
+                }
+                if (i + PF < GT) load_group(i + PF);
+                __builtin_amdgcn_sched_barrier(0);
+                if (j < G1) {
+                    sh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[slot], qf[j], sh, 0, 0, 0);
+                    dph = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[slot], of[j], dph, 0, 0, 0);
+                } else {
+                    const int jj = j - G1, k2 = jj / NDB, db = jj % NDB;
+                    dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[slot], sb[k2], dq[db], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (j == G1 - 1) {
+                    if (__builtin_expect(kind == kTilePartial || (kt + 1) * kBN > t.k_len, 0)) {
+                        f32x16 s2[2];
+                        s2[h] = sh;
+                        s2[1 - h] = f32x16{};
+                        mask_scores<KIND>(f, m, t, rm, row, hh, kt, fw, s2);
+                        sh = s2[h];
+                    }
+                    // register r is key kt*64 + h*32 + (r>>2)*8 + 4*hh + (r&3)
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) {
-                const bf16x8 ak = *(const bf16x8*)(k_ + h2 * 32 * ROWB + krow_off[kc]);
-                const bf16x8 av = *(const bf16x8*)(v_ + h2 * 32 * ROWB + krow_off[kc]);
-                s[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[kc], s[h2], 0, 0, 0);
-                dp[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[kc], dp[h2], 0, 0, 0);
+                    for (int rr = 0; rr < 16; ++rr) {
+                        const float pv = fast_exp2(fmaf(sh[rr], c2, -l2));
+                        sb[rr >> 3][rr & 7] = (bf16)(pv * (dph[rr] - dl));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
-        }
-        if (__builtin_expect(kind == kTilePartial || (kt + 1) * kBN > t.k_len, 0))
-            mask_scores<KIND>(f, m, t, rm, row, hh, kt, fw, s);
-        // register r of key half h2 is key kt*64 + h2*32 + (r>>2)*8 + 4*hh + (r&3)
-        bf16x8 sb[4];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const float pv = fast_exp2(fmaf(s[h2][rr], c2, -l2));
-                sb[h2 * 2 + (rr >> 3)][rr & 7] = (bf16)(pv * (dp[h2][rr] - dl));
-            }
-        // dQ^T += K^T dS^T
-#pragma unroll
-        for (int kc2 = 0; kc2 < 4; ++kc2) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const int o0 = kc2 * 16 * ROWB;
-                const bf16x4 lo = tr_read(k_ + o0 + trk[0][db]);
-                const bf16x4 hi = tr_read(k_ + o0 + trk[1][db]);
-                const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[kc2], dq[db], 0, 0, 0);
-            }
-        }
+        };
+        step(sK + buf * TILEB, sV + buf * TILEB, sK + (buf ^ 1) * TILEB, sV + (buf ^ 1) * TILEB);
         vm_wait();
         __syncthreads();
         buf ^= 1;
