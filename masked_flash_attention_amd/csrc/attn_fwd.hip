@@ -61,13 +61,18 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(__attribute__((address_space(3))) char*)(p));
 }
 
-template <int D, int NW, int KIND, bool BIAS>
+// BN: key-tile width, kBN or 32 (BSR rows with 64-row query blocks: a 2-wave
+// workgroup then needs 32 KB of LDS instead of 64, so four fit on a CU and
+// each SIMD runs two waves, which hide each other's wait for the next tile).
+template <int D, int NW, int KIND, bool BIAS, int BN = kBN>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, MaskDev m) {
     constexpr int BM = NW * 32;
     constexpr int NT = NW * 64;
     constexpr int ROWB = KV<D>::ROWB;
     constexpr int CPR = KV<D>::CPR;
-    constexpr int TILEB = KV<D>::TILEB;
+    constexpr int TILEB = BN * ROWB;
+    constexpr int NB = BN / 32;              // 32-key blocks of S^T per tile
+    constexpr int NK16 = BN / 16;            // 16-key chunks of the P V contraction
     constexpr int NKC = D / 16;              // 16-wide d chunks of q.k
     constexpr int NDB = D / 32;              // 32-wide d blocks of O^T
 
@@ -82,7 +87,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
     const int c = lane & 31;
 
     const int logical = xcd_logical(blockIdx.x, p.total, p.xcd_remap);
-    const TileRange t = make_range<KIND, BM>(p, m, logical);
+    const TileRange t = make_range<KIND, BM, BN>(p, m, logical);
     if (!t.active) return;
 
     const int row = t.q_row0 + wave * 32 + c;
@@ -115,8 +120,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
     // l%CPR, so it fetches the logical chunk that the swizzle puts there.
     // Rows past the key length read as zeros (buffer range check).
     constexpr int RPI = 1024 / ROWB;             // rows per wave instruction
-    constexpr int NI = kBN / RPI / NW;           // instructions per wave per tile (each of K, V)
-    static_assert(NI * RPI * NW == kBN, "tile rows must split evenly over the waves");
+    constexpr int NI = BN / RPI / NW;            // instructions per wave per tile (each of K, V)
+    static_assert(NI * RPI * NW == BN, "tile rows must split evenly over the waves");
     const char* Kbh = (const char*)K + 2 * ((int64_t)t.b * p.ks0 + (int64_t)t.hk * p.ks2 + (int64_t)t.k_base * p.ks1);
     const char* Vbh = (const char*)V + 2 * ((int64_t)t.b * p.vs0 + (int64_t)t.hk * p.vs2 + (int64_t)t.k_base * p.vs1);
     const int64_t krow = 2 * p.ks1, vrow = 2 * p.vs1;
@@ -136,7 +141,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
     // found through the table (the tile range checked every page id; a bad
     // one turned the rows into NaN, and its tiles read as zeros here).
     auto tile_base = [&](int kt, bool live, const char*& kp, const char*& vp, int& kn, int& vn) {
-        const int64_t k0 = (int64_t)kt * kBN * krow, v0 = (int64_t)kt * kBN * vrow;
+        const int64_t k0 = (int64_t)kt * BN * krow, v0 = (int64_t)kt * BN * vrow;
         kp = Kbh + k0;
         vp = Vbh + v0;
         kn = (int)(live && knrec > k0 ? knrec - k0 : 0);
@@ -187,7 +192,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
         voff[db] = vr0 * ROWB + (((col >> 3) ^ KV<D>::v_swz(vr0)) << 4) + ((col >> 2) & 1) * 8;
     }
 
-    TileCursor<KIND, BM> cursor;
+    TileCursor<KIND, BM, BN> cursor;
     cursor.init(p, m, t, lane);
     auto advance = [&](int& it, int& kt, int& kind) { cursor.seek(p, m, t, lane, it, kt, kind); };
 
@@ -197,7 +202,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
     auto fine_words = [&](int kt_, int kind_, uint32_t (&w)[2]) {
         w[0] = w[1] = 0u;
         if constexpr (KIND == MFA_MASK_TILES) {
-            if (__builtin_expect(rm.row_ok && (kind_ == kTilePartial || (kt_ + 1) * kBN > t.k_len), 0)) {
+            if (__builtin_expect(rm.row_ok && (kind_ == kTilePartial || (kt_ + 1) * BN > t.k_len), 0)) {
                 const uint32_t* fb = m.fine_bits + (int64_t)row * m.fine_words + 2 * kt_;
                 w[0] = fb[0];
                 if (2 * kt_ + 1 < m.fine_words) w[1] = fb[1];
@@ -254,18 +259,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
             };
 
             // ---- S^T = K Q^T ----
-            f32x16 s[2];
+            f32x16 s[NB];
             if constexpr (BIAS) {
-                alibi_fill(s, sl, kt * kBN + d_row, sl);
+                alibi_fill(s, sl, kt * BN + d_row, sl);
             } else {
-                s[0] = f32x16{};
-                s[1] = f32x16{};
+#pragma unroll
+                for (int kb = 0; kb < NB; ++kb) s[kb] = f32x16{};
             }
             const char* kb_ = ck_;
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
+                for (int kb = 0; kb < NB; ++kb) {
                     const bf16x8 a = *(const bf16x8*)(kb_ + kb * 32 * ROWB + koff[kc]);
                     s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[kb], 0, 0, 0);
                 }
@@ -273,24 +278,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
                 for (int d = 0; d < DPK; ++d)
                     if (kc * DPK + d < NDMA) dma(kc * DPK + d);
             }
-            // keep the loads spread: per d chunk, two operand reads, two MFMAs, DPK loads
+            // keep the loads spread: per d chunk, NB operand reads, NB MFMAs, DPK loads
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, NB, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
                 if (kc * DPK < NDMA) __builtin_amdgcn_sched_group_barrier(0x020, DPK, 0);
             }
 
             // ---- mask on partial or ragged tiles ----
-            if (__builtin_expect(kind == kTilePartial || (kt + 1) * kBN > t.k_len, 0))
-                mask_scores<KIND>(p, m, t, rm, row, hh, kt, fw, s);
+            if (__builtin_expect(kind == kTilePartial || (kt + 1) * BN > t.k_len, 0))
+                mask_scores<KIND, NB>(p, m, t, rm, row, hh, kt, fw, s);
 
             // ---- online softmax ----
             // Row max and row sum as 4 independent chains each (short dependency
             // chains: a single wave issues them back to back).
             float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], s[kb][r]);
             float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
@@ -307,10 +312,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
                     for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
             }
             const float mb = (m_used == -INFINITY) ? 0.f : m_used * c2;
-            bf16x8 pb[4];
+            bf16x8 pb[NK16];
             float rs4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
                 for (int gp = 0; gp < 2; ++gp)
 #pragma unroll
@@ -324,7 +329,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
             // ---- O^T += V^T P^T ----
             const char* vb_ = cv_;
 #pragma unroll
-            for (int kc2 = 0; kc2 < 4; ++kc2) {
+            for (int kc2 = 0; kc2 < NK16; ++kc2) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
                     const bf16x4 lo = ds_read_tr(vb_ + kc2 * 16 * ROWB + voff[db]);
@@ -436,11 +441,15 @@ __global__ __launch_bounds__(BM) void attn_fwd_f32_kernel(FwdDev p, MaskDev m) {
 
 template <int D, int NW, int KIND>
 static hipError_t launch_bf16(const FwdDev& p, const MaskDev& m, hipStream_t s) {
-    const size_t lds = 4 * KV<D>::TILEB;
+    // 64-row BSR blocks walk 32-key tiles (two waves per SIMD); everything else 64-key tiles
+    constexpr int BN = (KIND == MFA_MASK_BSR && NW == 2) ? 32 : kBN;
+    const size_t lds = 4 * (size_t)BN * KV<D>::ROWB;
     if (p.alibi)
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, KIND, true>), dim3(p.total), dim3(NW * 64), lds, s, p, m);
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, KIND, true, BN>), dim3(p.total), dim3(NW * 64), lds, s, p,
+                           m);
     else
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, KIND, false>), dim3(p.total), dim3(NW * 64), lds, s, p, m);
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, KIND, false, BN>), dim3(p.total), dim3(NW * 64), lds, s, p,
+                           m);
     return hipGetLastError();
 }
 

@@ -32,8 +32,11 @@ struct TileRange {
     bool len_error; // varlen: sequence longer than the stated max_q / max_k
 };
 
-template <int KIND, int BM>
+// BN is the key-tile width the caller walks: kBN, or 32 for BSR rows, whose
+// 64-key blocks are then visited as two 32-key tiles each.
+template <int KIND, int BM, int BN = kBN>
 __device__ __forceinline__ TileRange make_range(const FwdDev& p, const MaskDev& m, int logical) {
+    static_assert(BN == kBN || (BN == 32 && KIND == MFA_MASK_BSR), "32-key tiles are built for BSR rows only");
     TileRange t;
     t.seq = -1;
     t.active = true;
@@ -108,8 +111,8 @@ __device__ __forceinline__ TileRange make_range(const FwdDev& p, const MaskDev& 
             t.end = m.row_ptr[t.qt + 1];
         } else if constexpr (KIND == MFA_MASK_BSR) {
             const int* ip = m.indptr + ((int64_t)t.b * p.Hkv + t.hk) * (m.nQb + 1);
-            t.begin = ip[t.qt];
-            t.end = ip[t.qt + 1];
+            t.begin = ip[t.qt] * (kBN / BN);
+            t.end = ip[t.qt + 1] * (kBN / BN);
         } else {
             t.begin = 0;
             t.end = p.nKt;
@@ -125,10 +128,11 @@ __device__ __forceinline__ TileRange make_range(const FwdDev& p, const MaskDev& 
 // offset h*32 + (r>>2)*8 + (r&3) along the accumulator's row axis; d0 is
 // kv_idx - q_idx of offset 0 and `step` the bias change per unit offset (sl
 // when the row axis runs over keys, -sl when it runs over queries).
-__device__ __forceinline__ void alibi_fill(f32x16 (&s)[2], float sl, int d0, float step) {
+template <int NB>
+__device__ __forceinline__ void alibi_fill(f32x16 (&s)[NB], float sl, int d0, float step) {
     const float base = sl * (float)d0;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < NB; ++h)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[h][r] = fmaf(step, (float)(h * 32 + (r >> 2) * 8 + (r & 3)), base);
 }
@@ -168,15 +172,17 @@ __device__ __forceinline__ int classify_blockid(const int32_t* qs, const int32_t
 }
 
 // Key tile and kind of iteration `it`. Kind 0 means skip.
-template <int KIND, int BM>
+template <int KIND, int BM, int BN = kBN>
 __device__ __forceinline__ void tile_at(const FwdDev& p, const MaskDev& m, const TileRange& t, int it,
                                         int& kt, int& kind) {
     if constexpr (KIND == MFA_MASK_TILES) {
         kt = m.col_idx[it];
         kind = m.col_kind[it];
     } else if constexpr (KIND == MFA_MASK_BSR) {
-        kt = m.indices[it];
-        kind = m.bsr_kind[it];
+        constexpr int SUB = kBN / BN;  // key tiles per listed block
+        const int e = it / SUB;
+        kt = m.indices[e] * SUB + (it - e * SUB);
+        kind = m.bsr_kind[e];
     } else if constexpr (KIND == MFA_MASK_BLOCKID) {
         kt = it;
         const int nQt = p.nQt, nKt = p.nKt;
@@ -204,7 +210,7 @@ __device__ __forceinline__ void tile_at(const FwdDev& p, const MaskDev& m, const
 // window after the current one is requested when the current one is entered,
 // so its latency overlaps at least one tile of work. All members are
 // wave-uniform except the two packed entry registers.
-template <int KIND, int BM>
+template <int KIND, int BM, int BN = kBN>
 struct TileCursor {
     int base;       // list position held by lane 0 of `cur`
     uint32_t cur;   // this lane's entry of the current window
@@ -215,7 +221,7 @@ struct TileCursor {
                                                      int pos) {
         if (pos >= t.end) return 0u;
         int kt, kind;
-        tile_at<KIND, BM>(p, m, t, pos, kt, kind);
+        tile_at<KIND, BM, BN>(p, m, t, pos, kt, kind);
         return (uint32_t)kt | ((uint32_t)kind << 28);
     }
 
@@ -329,26 +335,24 @@ __device__ __forceinline__ uint32_t below(int n) {
 // s[kb] holds key kb*32 + (r>>2)*8 + 4*hh + (r&3) of the tile (query = this
 // lane's row); okw[kb] collects, at bit (r>>2)*8 + (r&3), whether that key is
 // allowed. fw: the row's two fine-bit words of the tile (dense-tile masks).
-template <int KIND>
+template <int KIND, int NB = 2>
 __device__ __forceinline__ void mask_scores(const FwdDev& p, const MaskDev& m, const TileRange& t,
                                             const RowMask<KIND>& rm, int row, int hh, int kt,
-                                            const uint32_t (&fw)[2], f32x16 (&s)[2]) {
-    uint32_t okw[2];
-    const int base_off = kt * kBN + 4 * hh;  // tile key index of bit 0 of okw[0]
+                                            const uint32_t (&fw)[2], f32x16 (&s)[NB]) {
+    uint32_t okw[NB];
+    const int base_off = kt * (NB * 32) + 4 * hh;  // tile key index of bit 0 of okw[0]
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) okw[kb] = below(t.k_len - base_off - kb * 32);
+    for (int kb = 0; kb < NB; ++kb) okw[kb] = below(t.k_len - base_off - kb * 32);
     if constexpr (KIND == MFA_MASK_TILES) {
-        okw[0] &= fw[0] >> (4 * hh);
-        okw[1] &= fw[1] >> (4 * hh);
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) okw[kb] &= fw[kb] >> (4 * hh);
     } else if constexpr (KIND == MFA_MASK_BLOCKID) {
-        const uint32_t* kw = m.kv_bits + (int64_t)t.b * m.kv_words + 2 * kt;
-        const uint32_t w0 = kw[0];
-        const uint32_t w1 = (2 * kt + 1 < m.kv_words) ? kw[1] : 0u;
-        okw[0] &= w0 >> (4 * hh);
-        okw[1] &= w1 >> (4 * hh);
+        const uint32_t* kw = m.kv_bits + (int64_t)t.b * m.kv_words + NB * kt;
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) okw[kb] &= ((NB * kt + kb < m.kv_words) ? kw[kb] : 0u) >> (4 * hh);
         const int32_t* kbp = m.k_blk + (int64_t)t.b * p.Sk;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < NB; ++kb) {
             uint32_t cmp = 0;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
@@ -364,26 +368,29 @@ __device__ __forceinline__ void mask_scores(const FwdDev& p, const MaskDev& m, c
     } else if constexpr (KIND == MFA_MASK_BSR) {
         if (m.causal) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) okw[kb] &= below(row - base_off - kb * 32 + 1);
+            for (int kb = 0; kb < NB; ++kb) okw[kb] &= below(row - base_off - kb * 32 + 1);
         }
         if (m.kv_bits) {  // token validity (kv_valid_bits)
-            const uint32_t* kw = m.kv_bits + (int64_t)t.b * m.kv_words + 2 * kt;
-            okw[0] &= kw[0] >> (4 * hh);
-            okw[1] &= ((2 * kt + 1 < m.kv_words) ? kw[1] : 0u) >> (4 * hh);
+            const uint32_t* kw = m.kv_bits + (int64_t)t.b * m.kv_words + NB * kt;
+#pragma unroll
+            for (int kb = 0; kb < NB; ++kb) okw[kb] &= ((NB * kt + kb < m.kv_words) ? kw[kb] : 0u) >> (4 * hh);
         }
     } else if constexpr (KIND == MFA_MASK_VARLEN) {
         const int i = rm.qi_local;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < NB; ++kb) {
             const int o = base_off + kb * 32;
             if (m.causal) okw[kb] &= below(i - o + 1);
             if (m.win_left >= 0) okw[kb] &= ~below(i - m.win_left - o);
             if (m.win_right >= 0) okw[kb] &= below(i + m.win_right - o + 1);
         }
     }
-    if (!rm.row_ok) okw[0] = okw[1] = 0u;
+    if (!rm.row_ok) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NB; ++kb) okw[kb] = 0u;
+    }
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = ((okw[kb] >> ((r >> 2) * 8 + (r & 3))) & 1u) ? s[kb][r] : -INFINITY;
 }
