@@ -221,8 +221,8 @@ mfa_status mfa_tile_counts(const uint8_t* tile_kind, int64_t n, int64_t* counts,
 // half empty.
 static const double kTileCost[2][3] = {
     // setup per query tile, partial tile, full tile
-    {2.31, 0.966, 0.739},  // 64-row tiles
-    {4.32, 1.164, 1.000},  // 128-row tiles
+    {2.52, 0.760, 0.623},  // 64-row tiles (32-key steps)
+    {4.37, 1.145, 1.000},  // 128-row tiles
 };
 
 double mfa_model_tile_time(const int64_t counts[3], int Nq, int tile_m) {

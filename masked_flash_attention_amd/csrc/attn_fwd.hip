@@ -203,9 +203,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
         w[0] = w[1] = 0u;
         if constexpr (KIND == MFA_MASK_TILES) {
             if (__builtin_expect(rm.row_ok && (kind_ == kTilePartial || (kt_ + 1) * BN > t.k_len), 0)) {
-                const uint32_t* fb = m.fine_bits + (int64_t)row * m.fine_words + 2 * kt_;
+                constexpr int NW32 = BN / 32;  // fine words per tile
+                const uint32_t* fb = m.fine_bits + (int64_t)row * m.fine_words + NW32 * kt_;
                 w[0] = fb[0];
-                if (2 * kt_ + 1 < m.fine_words) w[1] = fb[1];
+                if (NW32 == 2 && 2 * kt_ + 1 < m.fine_words) w[1] = fb[1];
             }
         }
     };
@@ -442,7 +443,7 @@ __global__ __launch_bounds__(BM) void attn_fwd_f32_kernel(FwdDev p, MaskDev m) {
 template <int D, int NW, int KIND>
 static hipError_t launch_bf16(const FwdDev& p, const MaskDev& m, hipStream_t s) {
     // 64-row BSR blocks walk 32-key tiles (two waves per SIMD); everything else 64-key tiles
-    constexpr int BN = (KIND == MFA_MASK_BSR && NW == 2) ? 32 : kBN;
+    constexpr int BN = ((KIND == MFA_MASK_BSR || KIND == MFA_MASK_TILES) && NW == 2) ? 32 : kBN;
     const size_t lds = 4 * (size_t)BN * KV<D>::ROWB;
     if (p.alibi)
         hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, KIND, true, BN>), dim3(p.total), dim3(NW * 64), lds, s, p,

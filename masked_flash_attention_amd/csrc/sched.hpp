@@ -36,7 +36,8 @@ struct TileRange {
 // 64-key blocks are then visited as two 32-key tiles each.
 template <int KIND, int BM, int BN = kBN>
 __device__ __forceinline__ TileRange make_range(const FwdDev& p, const MaskDev& m, int logical) {
-    static_assert(BN == kBN || (BN == 32 && KIND == MFA_MASK_BSR), "32-key tiles are built for BSR rows only");
+    static_assert(BN == kBN || (BN == 32 && (KIND == MFA_MASK_BSR || KIND == MFA_MASK_TILES)),
+                  "32-key tiles are built for BSR rows and dense-mask tile lists only");
     TileRange t;
     t.seq = -1;
     t.active = true;
@@ -107,8 +108,8 @@ __device__ __forceinline__ TileRange make_range(const FwdDev& p, const MaskDev& 
         t.q_row0 = t.qt * BM;
         t.q_rows = min(BM, p.Sq - t.q_row0);
         if constexpr (KIND == MFA_MASK_TILES) {
-            t.begin = m.row_ptr[t.qt];
-            t.end = m.row_ptr[t.qt + 1];
+            t.begin = m.row_ptr[t.qt] * (kBN / BN);
+            t.end = m.row_ptr[t.qt + 1] * (kBN / BN);
         } else if constexpr (KIND == MFA_MASK_BSR) {
             const int* ip = m.indptr + ((int64_t)t.b * p.Hkv + t.hk) * (m.nQb + 1);
             t.begin = ip[t.qt] * (kBN / BN);
@@ -176,8 +177,10 @@ template <int KIND, int BM, int BN = kBN>
 __device__ __forceinline__ void tile_at(const FwdDev& p, const MaskDev& m, const TileRange& t, int it,
                                         int& kt, int& kind) {
     if constexpr (KIND == MFA_MASK_TILES) {
-        kt = m.col_idx[it];
-        kind = m.col_kind[it];
+        constexpr int SUB = kBN / BN;  // key tiles per listed 64-key tile
+        const int e = it / SUB;
+        kt = m.col_idx[e] * SUB + (it - e * SUB);
+        kind = m.col_kind[e];
     } else if constexpr (KIND == MFA_MASK_BSR) {
         constexpr int SUB = kBN / BN;  // key tiles per listed block
         const int e = it / SUB;
