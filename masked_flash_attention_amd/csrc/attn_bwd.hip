@@ -65,11 +65,11 @@ __device__ __forceinline__ int tr_off(int r0, int db, int lane) {
 // Stage a 64-row x D bf16 tile from rows [row0, row0 + 64) of a strided
 // tensor into LDS with the tswz layout, using direct-to-LDS buffer loads
 // (rows at or past `rows` read as zeros). `nw` waves share the work.
-template <int D>
+template <int D, int NROWS = 64>
 __device__ __forceinline__ void stage_tile(const char* base, int64_t row_bytes, int row0, int rows, char* lds,
                                            int wave, int nw, int lane) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    constexpr int ROWB = 2 * D, RPI = 1024 / ROWB, CPR = D / 8, NINST = 64 / RPI;
+    constexpr int ROWB = 2 * D, RPI = 1024 / ROWB, CPR = D / 8, NINST = NROWS / RPI;
     const int64_t start = (int64_t)row0 * row_bytes;
     const int64_t total = rows > 0 ? (int64_t)(rows - 1) * row_bytes + ROWB : 0;
     const int nrec = (int)(total > start ? total - start : 0);
@@ -552,10 +552,11 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
 // cursor and the same per-element masks.
 // ---------------------------------------------------------------------------
 
-template <int D, int NW, int KIND, bool BIAS>
-__global__ __launch_bounds__(NW * 64, (NW == 2 || KIND == MFA_MASK_BLOCKID) ? 1 : 2) void bwd_dq_kernel(BwdDev p, MaskDev m) {
+template <int D, int NW, int KIND, bool BIAS, int BN = kBN>
+__global__ __launch_bounds__(NW * 64, (BN == 32 || (NW != 2 && KIND != MFA_MASK_BLOCKID)) ? 2 : 1) void bwd_dq_kernel(BwdDev p, MaskDev m) {
     constexpr int BM = NW * 32;
-    constexpr int ROWB = 2 * D, TILEB = 64 * ROWB, NKC = D / 16, NDB = D / 32;
+    constexpr int ROWB = 2 * D, TILEB = BN * ROWB, NKC = D / 16, NDB = D / 32;
+    constexpr int NH = BN / 32;  // 32-key halves per key tile
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* sK = smem;                 // [2][64 x D]
     char* sV = smem + 2 * TILEB;     // [2][64 x D]
@@ -566,7 +567,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 2 || KIND == MFA_MASK_BLOCKID) ? 1 
     const int hh = lane >> 5, c = lane & 31;
 
     const int logical = xcd_logical(blockIdx.x, f.total, f.xcd_remap);
-    const TileRange t = make_range<KIND, BM>(f, m, logical);
+    const TileRange t = make_range<KIND, BM, BN>(f, m, logical);
     if (!t.active) return;
     const int row = t.q_row0 + wave * 32 + c;
     RowMask<KIND> rm;
@@ -603,21 +604,21 @@ __global__ __launch_bounds__(NW * 64, (NW == 2 || KIND == MFA_MASK_BLOCKID) ? 1 
 #pragma unroll
         for (int db = 0; db < NDB; ++db) trk[j][db] = tr_off<D>(8 * j + 4 * hh, db, lane);
 
-    TileCursor<KIND, BM> cursor;
+    TileCursor<KIND, BM, BN> cursor;
     cursor.init(f, m, t, lane);
     auto fine_words = [&](int kt_, int kind_, uint32_t (&w)[2]) {
         w[0] = w[1] = 0u;
         if constexpr (KIND == MFA_MASK_TILES) {
-            if (rm.row_ok && (kind_ == kTilePartial || (kt_ + 1) * kBN > t.k_len)) {
-                const uint32_t* fb = m.fine_bits + (int64_t)row * m.fine_words + 2 * kt_;
+            if (rm.row_ok && (kind_ == kTilePartial || (kt_ + 1) * BN > t.k_len)) {
+                const uint32_t* fb = m.fine_bits + (int64_t)row * m.fine_words + NH * kt_;
                 w[0] = fb[0];
-                if (2 * kt_ + 1 < m.fine_words) w[1] = fb[1];
+                if (NH == 2 && 2 * kt_ + 1 < m.fine_words) w[1] = fb[1];
             }
         }
     };
     auto stage_to = [&](int kt_, char* dk_, char* dv_) {
-        stage_tile<D>(kbase, 2 * f.ks1, kt_ * 64, t.k_len, dk_, wave, NW, lane);
-        stage_tile<D>(vbase, 2 * f.vs1, kt_ * 64, t.k_len, dv_, wave, NW, lane);
+        stage_tile<D, BN>(kbase, 2 * f.ks1, kt_ * BN, t.k_len, dk_, wave, NW, lane);
+        stage_tile<D, BN>(vbase, 2 * f.vs1, kt_ * BN, t.k_len, dv_, wave, NW, lane);
     };
     auto stage = [&](int kt_, int buf) { stage_to(kt_, sK + buf * TILEB, sV + buf * TILEB); };
 
@@ -653,7 +654,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 2 || KIND == MFA_MASK_BLOCKID) ? 1 
             // then dQ^T += K^T dS^T over the half's two 16-key chunks (G2
             // groups). The LDS operand reads of all groups form one stream
             // issued PF groups ahead of their MFMAs (a ring of PF + 1 slots).
-            constexpr int G1 = NKC, G2 = 2 * NDB, GH = G1 + G2, GT = 2 * GH, PF = 3, RING = PF + 1;
+            constexpr int G1 = NKC, G2 = 2 * NDB, GH = G1 + G2, GT = NH * GH, PF = 3, RING = PF + 1;
             bf16x8 ra[RING], rb[RING];
             auto load_group = [&](int i) {
                 const int h = i / GH, j = i % GH, slot = i % RING;
@@ -677,8 +678,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 2 || KIND == MFA_MASK_BLOCKID) ? 1 
                 const int h = i / GH, j = i % GH, slot = i % RING;
                 if (j == 0) {
                     if constexpr (BIAS) {
-                        f32x16 t2[2];
-                        alibi_fill(t2, sl, kt * kBN + d_row, sl);
+                        f32x16 t2[NH];
+                        alibi_fill(t2, sl, kt * BN + d_row, sl);
                         sh = t2[h];
                     } else {
                         sh = f32x16{};
@@ -696,11 +697,11 @@ __global__ __launch_bounds__(NW * 64, (NW == 2 || KIND == MFA_MASK_BLOCKID) ? 1 
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 if (j == G1 - 1) {
-                    if (__builtin_expect(kind == kTilePartial || (kt + 1) * kBN > t.k_len, 0)) {
-                        f32x16 s2[2];
-                        s2[h] = sh;
-                        s2[1 - h] = f32x16{};
-                        mask_scores<KIND>(f, m, t, rm, row, hh, kt, fw, s2);
+                    if (__builtin_expect(kind == kTilePartial || (kt + 1) * BN > t.k_len, 0)) {
+                        f32x16 s2[NH];
+#pragma unroll
+                        for (int x = 0; x < NH; ++x) s2[x] = x == h ? sh : f32x16{};
+                        mask_scores<KIND, NH>(f, m, t, rm, row, hh, kt, fw, s2);
                         sh = s2[h];
                     }
                     // register r is key kt*64 + h*32 + (r>>2)*8 + 4*hh + (r&3)
@@ -773,9 +774,11 @@ static hipError_t dkdv_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) 
 
 template <int D, int NW, int KIND, bool BIAS>
 static hipError_t dq_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) {
-    const size_t lds = 4 * 64 * 2 * D;
+    // 64-row query tiles walk 32-key tiles, as in the forward
+    constexpr int BN = (NW == 2 && (KIND == MFA_MASK_BSR || KIND == MFA_MASK_TILES)) ? 32 : kBN;
+    const size_t lds = 4 * (size_t)BN * 2 * D;
     if (p.f.total == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, KIND, BIAS>), dim3(p.f.total), dim3(NW * 64), lds, s, p, m);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, KIND, BIAS, BN>), dim3(p.f.total), dim3(NW * 64), lds, s, p, m);
     return hipGetLastError();
 }
 
