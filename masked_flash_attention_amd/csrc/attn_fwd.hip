@@ -79,6 +79,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* sK = smem;
     char* sV = smem + 2 * TILEB;
+    // block-id masks: the k_blk values of the K/V tile, staged with it ([2][64])
+    int32_t* sKB = (int32_t*)(smem + 4 * TILEB);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -174,7 +176,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
         }
 #endif
     };
-    auto load_tile = [&](int kt, int buf, bool live) { load_tile_to(kt, sK + buf * TILEB, sV + buf * TILEB, live); };
+    // One 256-byte load (wave 0) of the tile's key block ids into LDS; keys
+    // past k_len read as 0, and the mask's range bits clear them.
+    auto load_kblk = [&](int kt, int32_t* dst, bool live) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        if constexpr (KIND == MFA_MASK_BLOCKID) {
+            if (wave == 0) {
+                const int n = live ? max(0, min(BN, t.k_len - kt * BN)) : 0;
+                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)(m.k_blk + (int64_t)t.b * p.Sk + (int64_t)kt * BN), 0, n * 4, 0x00020000);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 4, lane * 4, 0, 0, 0);
+            }
+        }
+#endif
+    };
+    auto load_tile = [&](int kt, int buf, bool live) {
+        load_tile_to(kt, sK + buf * TILEB, sV + buf * TILEB, live);
+        load_kblk(kt, sKB + buf * 64, live);
+    };
 
     // Per-lane LDS offsets of the operand reads.
     // K operand: row kb*32 + c, logical chunk kc*2 + hh.
@@ -238,7 +257,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
         // tile carry alias scopes that keep the compiler from making them
         // wait for the loads into the other buffer
         auto step = [&](const char* __restrict__ ck_, const char* __restrict__ cv_, char* __restrict__ nk_,
-                        char* __restrict__ nv_) {
+                        char* __restrict__ nv_, const int32_t* __restrict__ ckb_, int32_t* __restrict__ nkb_) {
+            load_kblk(kt_n, nkb_, has_next);
             // The next tile's K and V loads (into buf^1, released by the last
             // barrier) are issued a few at a time between the S MFMAs below
             // rather than as one burst, which would stall the wave on the
@@ -289,7 +309,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
 
             // ---- mask on partial or ragged tiles ----
             if (__builtin_expect(kind == kTilePartial || (kt + 1) * BN > t.k_len, 0))
-                mask_scores<KIND, NB>(p, m, t, rm, row, hh, kt, fw, s);
+                mask_scores<KIND, NB>(p, m, t, rm, row, hh, kt, fw, s, KIND == MFA_MASK_BLOCKID ? ckb_ : nullptr);
 
             // ---- online softmax ----
             // Row max and row sum as 4 independent chains each (short dependency
@@ -340,7 +360,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
                 }
             }
         };
-        step(sK + buf * TILEB, sV + buf * TILEB, sK + (buf ^ 1) * TILEB, sV + (buf ^ 1) * TILEB);
+        step(sK + buf * TILEB, sV + buf * TILEB, sK + (buf ^ 1) * TILEB, sV + (buf ^ 1) * TILEB, sKB + buf * 64,
+             sKB + (buf ^ 1) * 64);
 
         wait_vmem();  // this wave's tile loads have landed in LDS
         __syncthreads();
@@ -444,7 +465,7 @@ template <int D, int NW, int KIND>
 static hipError_t launch_bf16(const FwdDev& p, const MaskDev& m, hipStream_t s) {
     // 64-row BSR blocks walk 32-key tiles (two waves per SIMD); everything else 64-key tiles
     constexpr int BN = ((KIND == MFA_MASK_BSR || KIND == MFA_MASK_TILES) && NW == 2) ? 32 : kBN;
-    const size_t lds = 4 * (size_t)BN * KV<D>::ROWB;
+    const size_t lds = 4 * (size_t)BN * KV<D>::ROWB + (KIND == MFA_MASK_BLOCKID ? 2 * 64 * 4 : 0);
     if (p.alibi)
         hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, KIND, true, BN>), dim3(p.total), dim3(NW * 64), lds, s, p,
                            m);

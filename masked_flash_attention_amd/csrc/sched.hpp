@@ -338,10 +338,13 @@ __device__ __forceinline__ uint32_t below(int n) {
 // s[kb] holds key kb*32 + (r>>2)*8 + 4*hh + (r&3) of the tile (query = this
 // lane's row); okw[kb] collects, at bit (r>>2)*8 + (r&3), whether that key is
 // allowed. fw: the row's two fine-bit words of the tile (dense-tile masks).
+// kblk: block ids of the tile's keys already staged in LDS (block-id masks;
+// entry j for key kt*NB*32 + j), or null to read them from global memory.
 template <int KIND, int NB = 2>
 __device__ __forceinline__ void mask_scores(const FwdDev& p, const MaskDev& m, const TileRange& t,
                                             const RowMask<KIND>& rm, int row, int hh, int kt,
-                                            const uint32_t (&fw)[2], f32x16 (&s)[NB]) {
+                                            const uint32_t (&fw)[2], f32x16 (&s)[NB],
+                                            const int32_t* kblk = nullptr) {
     uint32_t okw[NB];
     const int base_off = kt * (NB * 32) + 4 * hh;  // tile key index of bit 0 of okw[0]
 #pragma unroll
@@ -359,10 +362,13 @@ __device__ __forceinline__ void mask_scores(const FwdDev& p, const MaskDev& m, c
             uint32_t cmp = 0;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
+                i32x4 staged = {0, 0, 0, 0};
+                if (kblk) staged = *(const i32x4*)(kblk + 4 * hh + kb * 32 + g * 8);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int key = base_off + kb * 32 + g * 8 + e;
-                    const int kbk = key < t.k_len ? kbp[key] : INT32_MAX;
+                    // keys past k_len are cleared by okw's range bits either way
+                    const int kbk = kblk ? staged[e] : (key < t.k_len ? kbp[key] : INT32_MAX);
                     cmp |= (kbk <= rm.qblk ? 1u : 0u) << (g * 8 + e);
                 }
             }
