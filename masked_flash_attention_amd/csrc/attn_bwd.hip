@@ -22,7 +22,10 @@
 // the Q / dO tiles. The dQ pass uses the forward's S^T = K Q^T layout (a lane
 // owns one query) and reads K^T transposed for dQ^T = K^T dS^T.
 // Q, dO (dK/dV pass) and K (dQ pass) tiles are read both row-wise and
-// transposed; their LDS swizzle is conflict-free for both patterns.
+// transposed; their LDS swizzle is conflict-free for both patterns. Both
+// passes run a step as 32-wide halves whose LDS operand reads are issued a
+// few MFMA groups ahead; the dK/dV grid puts a head's key blocks on one XCD,
+// and 64-row dQ tiles walk 32-key tiles (two waves per SIMD).
 
 #include "sched.hpp"
 

@@ -16,9 +16,12 @@
 //    (v_permlane32_swap) and the probabilities are already laid out as the
 //    B operand of O^T (D x 32 queries) += V^T P^T. Both contractions run over
 //    the same permutation of keys, which is free since keys are summed over.
-//  * K and V tiles (64 x D bf16) are double-buffered in LDS, XOR-swizzled so
-//    that the K operand reads (ds_read_b128) and the transposed V operand
-//    reads (ds_read_b64_tr_b16) are bank-conflict free.
+//  * K and V tiles (64 x D bf16; 32 x D for 64-row query tiles, so that two
+//    or more of their 2-wave workgroups fit on a CU) are double-buffered in
+//    LDS, XOR-swizzled so that the K operand reads (ds_read_b128) and the
+//    transposed V operand reads (ds_read_b64_tr_b16) are bank-conflict free.
+//    The next tile's loads go straight from memory to LDS, a few between the
+//    S MFMAs; block-id masks stage the tile's key block ids alongside.
 //  * Online softmax in fp32 with exp2: c = scale*log2(e) is applied to the
 //    fp32 scores after the matmul. The running max is only moved when the
 //    tile max exceeds it by more than kTau (log2 units), which bounds P by
