@@ -11,7 +11,7 @@ import masked_flash_attention_amd as mfa
 from oracle import attention as A
 from oracle import masks as M
 import workloads as W
-from tests.gpu_util import BF16_OUT_TOL, DEV, f64, note, to_dev
+from tests.gpu_util import BF16_OUT_TOL, DEV, compare_attention, f64, note, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -51,6 +51,23 @@ def test_bsr_backward_small(D, causal, gqa):
         err = float(np.abs(f64(g) - r).max())
         rel = float(np.linalg.norm(f64(g) - r) / max(np.linalg.norm(r), 1e-30))
         assert err <= BF16_OUT_TOL, f"{name} max-abs {err:.3e} (rel L2 {rel:.2e})"
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_bsr_key_tail_short_of_half_block(D, causal):
+    """N = 520 = 8*64 + 8: the last 64-key block holds 8 keys, so with 32-key
+    steps one step is partly past the end and the next wholly past it."""
+    note(f"bsr fwd+bwd N=520 D={D} causal={causal}")
+    N = 520
+    w = _small(N, 3, 3, D, seed=40 + D + causal)
+    out, lse, dq, dk, dv = _bsr_run(w, N, causal)
+    allowed = M.bsr_mask(w["indptr"], w["indices"], 64, 64, N, N, causal)
+    rdq, rdk, rdv, ro, rl, _ = A.attention_bwd(w["q"], w["k"], w["v"], w["do"], allowed, w["scale"])
+    compare_attention(f64(out), f64(lse), ro, rl, BF16_OUT_TOL)
+    for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        err = float(np.abs(f64(g) - r).max())
+        assert err <= BF16_OUT_TOL, f"{name} max-abs {err:.3e}"
 
 
 def test_bsr_backward_deterministic():
