@@ -377,7 +377,9 @@ typedef struct mfa_mask {
 /* Fused masked attention forward: out = softmax(scale q k^T + bias + mask) v
  * per (batch, head), with log-sum-exp. scale is explicit (callers usually
  * pass D^-0.5) and must be finite and positive (MFA_E_ARG otherwise). Head
- * dims 64 and 128 are built; others give MFA_E_UNSUPPORTED. */
+ * dims 64 and 128 are built; others give MFA_E_UNSUPPORTED, and so does a
+ * sequence stride of 2^23 elements or more (bf16; 2^22 for fp32) in any
+ * tensor, here and in the backward: 128 rows must span under 2 GiB. */
 mfa_status mfa_attn_fwd(const mfa_attn_args* args, const mfa_mask* mask, float scale,
                         hipStream_t stream);
 

@@ -501,6 +501,13 @@ static mfa_status check_strides(const char* name, const void* ptr, const int64_t
     }
     for (int i = 0; i < 3; ++i)
         if (st[i] < 0) return fail(MFA_E_ARG, "%s strides must be non-negative", name);
+    // Kernels address the rows of one 128-row tile with 32-bit byte offsets
+    // from the tile's first row (buffer loads); the tensor itself may be
+    // larger. Rows under 16 MiB apart keep 128 of them under 2 GiB.
+    const int64_t esize = dtype == MFA_BF16 ? 2 : 4;
+    if (st[1] >= (int64_t(1) << 24) / esize)
+        return fail(MFA_E_UNSUPPORTED, "%s sequence stride %lld elements: 128 rows must span under 2 GiB", name,
+                    (long long)st[1]);
     return ok();
 }
 

@@ -74,8 +74,10 @@ __device__ __forceinline__ void stage_tile(const char* base, int64_t row_bytes, 
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int ROWB = 2 * D, RPI = 1024 / ROWB, CPR = D / 8, NINST = NROWS / RPI;
     const int64_t start = (int64_t)row0 * row_bytes;
-    const int64_t total = rows > 0 ? (int64_t)(rows - 1) * row_bytes + ROWB : 0;
-    const int nrec = (int)(total > start ? total - start : 0);
+    // the range ends at the tile's last row or at row `rows`, whichever comes
+    // first (32 bits: the host requires 128 rows to span under 2 GiB)
+    const int rem = min(NROWS, rows - row0);
+    const int nrec = rem > 0 ? (rem - 1) * (int)row_bytes + ROWB : 0;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)(base + start), 0, nrec, 0x00020000);
     for (int i = wave; i < NINST; i += nw) {
         const int r = i * RPI + lane / CPR;
@@ -98,8 +100,8 @@ struct TileDma {
 #if defined(__HIP_DEVICE_COMPILE__)
         row_bytes = rb;
         const int64_t start = (int64_t)row0 * rb;
-        const int64_t total = rows > 0 ? (int64_t)(rows - 1) * rb + ROWB : 0;
-        const int nrec = (int)(total > start ? total - start : 0);
+        const int rem = min(64, rows - row0);  // as in stage_tile
+        const int nrec = rem > 0 ? (rem - 1) * (int)rb + ROWB : 0;
         rs = __builtin_amdgcn_make_buffer_rsrc((void*)(base + start), 0, nrec, 0x00020000);
 #endif
     }
@@ -116,7 +118,7 @@ struct TileDma {
 // Stage 64 consecutive fp32 values (positions [i0, i0+64) of a row of length n).
 __device__ __forceinline__ void stage_vec64(const float* base, int i0, int n, float* lds, int lane) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const int nrec = n > i0 ? (n - i0) * 4 : 0;
+    const int nrec = n > i0 ? min(n - i0, 64) * 4 : 0;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)(base + i0), 0, nrec, 0x00020000);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 4, lane * 4, 0, 0, 0);
 #endif

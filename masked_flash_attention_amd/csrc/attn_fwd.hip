@@ -130,8 +130,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
     const char* Kbh = (const char*)K + 2 * ((int64_t)t.b * p.ks0 + (int64_t)t.hk * p.ks2 + (int64_t)t.k_base * p.ks1);
     const char* Vbh = (const char*)V + 2 * ((int64_t)t.b * p.vs0 + (int64_t)t.hk * p.vs2 + (int64_t)t.k_base * p.vs1);
     const int64_t krow = 2 * p.ks1, vrow = 2 * p.vs1;
-    const int64_t knrec = t.k_len > 0 ? (int64_t)(t.k_len - 1) * krow + ROWB : 0;
-    const int64_t vnrec = t.k_len > 0 ? (int64_t)(t.k_len - 1) * vrow + ROWB : 0;
+    // 32-bit row strides: the host requires 128 rows to span under 2 GiB
+    const int krow32 = (int)krow, vrow32 = (int)vrow;
     int kgo[NI], vgo[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -149,8 +149,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
         const int64_t k0 = (int64_t)kt * BN * krow, v0 = (int64_t)kt * BN * vrow;
         kp = Kbh + k0;
         vp = Vbh + v0;
-        kn = (int)(live && knrec > k0 ? knrec - k0 : 0);
-        vn = (int)(live && vnrec > v0 ? vnrec - v0 : 0);
+        // the range ends at the tile's last row or at the last key, whichever
+        // comes first, so it fits 32 bits however long the sequence is
+        const int rem = live ? min(BN, t.k_len - kt * BN) : 0;
+        kn = rem > 0 ? (rem - 1) * krow32 + ROWB : 0;
+        vn = rem > 0 ? (rem - 1) * vrow32 + ROWB : 0;
         if constexpr (KIND == MFA_MASK_VARLEN) {
             if (m.block_table) {
                 int r = 0;

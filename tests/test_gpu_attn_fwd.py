@@ -289,6 +289,40 @@ def test_error_paths_on_device():
     assert e.value.status_name == "MFA_E_DTYPE"
 
 
+def test_key_span_over_4gib():
+    """K and V rows 256 KiB apart (views into larger buffers), 20037 keys: one
+    (batch, head)'s keys span 5.25 GB, past the 32-bit range of a buffer load
+    counted from the first key. Forward and backward against the oracle."""
+    Sq, Sk, D, RS = 64, 20037, 128, 1 << 17
+    note(f"key span over 4 GiB: Sk={Sk} row stride {RS} elements")
+    q, k, v, do = W.tensors(77, [(1, Sq, 1, D), (1, Sk, 1, D), (1, Sk, 1, D), (1, Sq, 1, D)])
+    views = []
+    for t in (k, v):
+        buf = torch.empty(Sk * RS, dtype=torch.bfloat16, device=DEV)
+        view = buf.as_strided((1, Sk, 1, D), (Sk * RS, RS, D, 1))
+        view.copy_(t.to(DEV))
+        views.append(view)
+    kd, vd = views
+    qd, dod = to_dev(q), to_dev(do)
+    allowed = np.ones((1, 1, Sq, Sk), bool)
+    scale = D ** -0.5
+    out, lse = mfa.attn_fwd(qd, kd, vd, mfa.MaskRep.none(), scale, "bshd")
+    dq, dk, dv = mfa.attn_bwd(qd, kd, vd, out, lse, dod, mfa.MaskRep.none(), scale, "bshd")
+    torch.cuda.synchronize()
+    kb, vb = (f64(x) for x in views)  # the bf16 values the kernels read
+    rdq, rdk, rdv, ro, rl, _ = A.attention_bwd(f64(qd), kb, vb, f64(dod), allowed, scale)
+    compare_attention(f64(out), f64(lse), ro, rl, BF16_OUT_TOL)
+    for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        err = float(np.abs(f64(g) - r).max())
+        assert err <= BF16_OUT_TOL, f"{name} max-abs {err:.3e}"
+    del views, kd, vd
+    with pytest.raises(mfa.MfaError) as e:
+        big = torch.empty((1 << 24) + 64, dtype=torch.bfloat16, device=DEV)
+        qs = big.as_strided((1, 2, 1, 64), ((1 << 24) + 64, 1 << 24, 64, 1))
+        mfa.attn_fwd(qs, qs, qs, mfa.MaskRep.none())
+    assert e.value.status_name == "MFA_E_UNSUPPORTED"
+
+
 # --- edge cases ----------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
