@@ -36,22 +36,34 @@ __device__ __forceinline__ int block_exclusive_count(bool flag, int* total, int*
     return before + in_wave;
 }
 
-// Exclusive prefix sum of small non-negative ints over the block.
-__device__ __forceinline__ int block_exclusive_sum(int v, int* total, int* lds1024) {
-    const int t = threadIdx.x, n = blockDim.x;
-    lds1024[t] = v;
-    __syncthreads();
-    // Hillis-Steele inclusive scan in LDS
-    for (int off = 1; off < n; off <<= 1) {
-        const int x = (t >= off) ? lds1024[t - off] : 0;
-        __syncthreads();
-        lds1024[t] += x;
-        __syncthreads();
+// Exclusive prefix sum of small non-negative ints over the block: a
+// shuffle scan inside each wavefront, then one over the wave totals, with
+// three barriers (the block size is a multiple of 64, at most 1024; lds
+// needs 128 ints). Every thread gets the block total.
+__device__ __forceinline__ int block_exclusive_sum(int v, int* total, int* lds) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, nw = blockDim.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
     }
-    const int incl = lds1024[t];
-    *total = lds1024[n - 1];
+    if (lane == 63) lds[w] = x;
     __syncthreads();
-    return incl - v;
+    if (w == 0) {
+        int c = lane < nw ? lds[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(c, off, 64);
+            if (lane >= off) c += y;
+        }
+        if (lane < nw) lds[64 + lane] = c;  // inclusive sums of the wave totals
+    }
+    __syncthreads();
+    const int before = w > 0 ? lds[64 + w - 1] : 0;
+    *total = lds[64 + nw - 1];
+    __syncthreads();  // lds may be reused by the next call
+    return before + x - v;
 }
 
 // ---------------------------------------------------------------------------
@@ -635,6 +647,7 @@ __global__ __launch_bounds__(1024) void varlen_schedule_kernel(const int32_t* le
     __shared__ int hist[kMaxCost + 1];
     __shared__ int s_max[2];
     __shared__ int s_cost[1024];
+    __shared__ int s_len[2][1024];  // lengths of the first 1024 sequences, for the serial passes below
     const int t = threadIdx.x, n = blockDim.x;
     for (int i = t; i <= kMaxCost; i += n) hist[i] = 0;
     if (t == 0) {
@@ -652,6 +665,10 @@ __global__ __launch_bounds__(1024) void varlen_schedule_kernel(const int32_t* le
         const int s = s0 + t;
         const int lq = s < nseq ? len_q[s] : 0;
         const int lk = s < nseq ? len_k[s] : 0;
+        if (s < 1024) {
+            s_len[0][s] = lq;
+            s_len[1][s] = lk;
+        }
         int tq, tk, tt;
         const int eq = block_exclusive_sum(lq, &tq, scan);
         const int ek = block_exclusive_sum(lk, &tk, scan);
@@ -683,24 +700,34 @@ __global__ __launch_bounds__(1024) void varlen_schedule_kernel(const int32_t* le
     // sequence are handled in chunks by the whole block.
     // Pass 1: histogram of costs.
     for (int s = 0; s < nseq; ++s) {
-        const int lq = len_q[s], lk = len_k[s];
+        const int lq = s < 1024 ? s_len[0][s] : len_q[s], lk = s < 1024 ? s_len[1][s] : len_k[s];
         const int nt = (lq + BM - 1) / BM;
         for (int i = t; i < nt; i += n) atomicAdd(&hist[varlen_cost(lq, lk, i * BM, BM, BN, causal, left, right)], 1);
     }
     __syncthreads();
-    // start[cost] = number of tiles with a larger cost (descending order)
-    if (t == 0) {
-        int acc = 0;
-        for (int c = kMaxCost; c >= 0; --c) {
-            const int h = hist[c];
-            hist[c] = acc;
-            acc += h;
+    // start[cost] = number of tiles with a larger cost (descending order): an
+    // exclusive scan of the histogram read from the top cost down, four
+    // entries per thread (the launch has exactly 1024 threads).
+    {
+        static_assert(kMaxCost + 1 == 4 * 1024, "four histogram entries per thread");
+        int h[4], sum = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h[e] = hist[kMaxCost - (4 * t + e)];
+            sum += h[e];
+        }
+        int tot;
+        int run = block_exclusive_sum(sum, &tot, scan);  // its barriers order these reads before the writes
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            hist[kMaxCost - (4 * t + e)] = run;
+            run += h[e];
         }
     }
     __syncthreads();
     // Pass 2: stable placement in (seq, q0) order, chunk by chunk.
     for (int s = 0; s < nseq; ++s) {
-        const int lq = len_q[s], lk = len_k[s];
+        const int lq = s < 1024 ? s_len[0][s] : len_q[s], lk = s < 1024 ? s_len[1][s] : len_k[s];
         const int nt = (lq + BM - 1) / BM;
         for (int i0 = 0; i0 < nt; i0 += n) {
             const int i = i0 + t;
