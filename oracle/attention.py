@@ -271,3 +271,42 @@ def attention_bwd_sampled(q, k, v, dout, allowed, scale, b, hk, rows, cols, chun
             dv += P.T @ dd[rr]
             dk += scale * (dS.T @ qq[rr])
     return dq, dk, dv
+
+
+def attention_bwd_dq_rows(q, k, v, dout, allowed, scale, rows, score_mod=None):
+    """dQ of the query rows ``rows`` for every query head, fp64.
+
+    dQ_i depends on row i alone: its scores s_i over the allowed keys, its
+    LSE_i, P_i = exp(s_i - LSE_i), O_i = P_i V, Delta_i = dO_i . O_i,
+    dP_i = dO_i V^T, dS_i = P_i (dP_i - Delta_i) and dQ_i = scale dS_i K
+    (the formulas of ``attention_bwd`` restricted to one row), so sampled rows
+    are checked without forming any other row. A row with no allowed key has
+    dQ_i = 0. ``allowed`` and ``score_mod`` as for ``attention_fwd``.
+    Returns dq (B, len(rows), Hq, D).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    Hm = _mask_heads(allowed, Hq)
+    rows = np.asarray(rows)
+    dq = np.zeros((B, rows.size, Hq, D))
+    for b in range(B):
+        for hq in range(Hq):
+            hk = hq // G
+            hm = hq * Hm // Hq
+            kk, vv = k[b, :, hk, :], v[b, :, hk, :]
+            a = _mask_rows(allowed, b, hm, rows, Sk)
+            has = a.any(axis=1)
+            s = _scores(q[b, rows, hq, :], kk, scale, score_mod, b, hq, rows)
+            sm = np.where(a, s, -np.inf)
+            m = np.where(has, sm.max(axis=1, initial=-np.inf), 0.0)
+            e = np.where(a, np.exp(sm - m[:, None]), 0.0)
+            lse = m + np.log(np.where(has, e.sum(axis=1), 1.0))
+            P = np.where(a, np.exp(sm - lse[:, None]), 0.0)
+            o = P @ vv
+            dd = do[b, rows, hq, :]
+            delta = (dd * o).sum(axis=1)
+            dP = dd @ vv.T
+            dq[b, :, hq, :] = scale * ((P * (dP - delta[:, None])) @ kk)
+    return dq

@@ -206,6 +206,28 @@ def test_sampled_backward_equals_dense_backward():
             np.testing.assert_allclose(sv, dv[b, cols, hk], rtol=1e-10, atol=1e-12)
 
 
+def test_dq_rows_equal_torch_autograd():
+    """Row-local dQ against torch autograd through float64 SDPA (a library
+    routine), with GQA, empty rows and a row subset."""
+    rng = np.random.default_rng(55)
+    B, Sq, Sk, Hq, Hkv, D = 2, 30, 26, 4, 2, 8
+    q, k, v = _rand((B, Sq, Hq, D), 56), _rand((B, Sk, Hkv, D), 57), _rand((B, Sk, Hkv, D), 58)
+    do = _rand((B, Sq, Hq, D), 59)
+    mask = rng.random((B, 1, Sq, Sk)) < 0.4
+    mask[:, :, 3] = False  # empty rows: SDPA gives NaN there, the convention gives 0
+    t = [torch.tensor(x.transpose(0, 2, 1, 3), requires_grad=True) for x in (q, k, v)]
+    o = F.scaled_dot_product_attention(*t, attn_mask=torch.from_numpy(mask), scale=0.45, enable_gqa=True)
+    g = torch.from_numpy(do.transpose(0, 2, 1, 3).copy())
+    g[:, :, 3] = 0.0
+    o = torch.where(torch.from_numpy(mask.any(-1, keepdims=True)), o, torch.zeros_like(o))
+    o.backward(g)
+    ref = t[0].grad.numpy().transpose(0, 2, 1, 3)
+    rows = np.array([0, 3, 7, 29])
+    got = A.attention_bwd_dq_rows(q, k, v, do, mask, 0.45, rows)
+    np.testing.assert_allclose(got, ref[:, rows], rtol=1e-11, atol=1e-12)
+    assert np.all(got[:, 1] == 0.0)
+
+
 # --- score_mod (tensorplay omni_attention, intro) -------------------------------------
 
 def _small_qkv(seed, B=1, S=40, H=2, D=16):
