@@ -246,7 +246,11 @@ mfa_status mfa_bsr_from_bitmask(const uint32_t* bits, int B, int Hkv, int nQb, i
  * Window (on sequence-local positions i, j): causal -> j <= i; left >= 0 ->
  * i - j <= left; right >= 0 -> j - i <= right; -1 leaves that side open.
  * work_cap must be >= sum_s ceil(len_q[s]/BM); BM = 128, BN = 64. If the
- * tiles do not fit, n_work is set to -1 and work is left unordered. */
+ * tiles do not fit, n_work is set to -1 and every work entry to (-1, -1).
+ * The order uses exact costs at every length. Tiles visiting 4096 or more
+ * key tiles (over 262,080 keys) are ranked in groups of equal cost >> 12;
+ * if one such group holds more than 16,384 tiles, n_work is set to -2 and
+ * every work entry to (-1, -1). Asynchronous. */
 mfa_status mfa_varlen_schedule(const int32_t* len_q, const int32_t* len_k, int nseq, int BM, int BN,
                                int causal, int win_left, int win_right,
                                int32_t* cu_q, int32_t* cu_k, int32_t* max_len,
@@ -390,7 +394,11 @@ mfa_status mfa_attn_fwd(const mfa_attn_args* args, const mfa_mask* mask, float s
  * required). dout/dq/dk/dv use the same stride convention as fwd. delta
  * (B, Hq, Sq) fp32 contiguous ((Hq, T) for VARLEN) is written by the
  * preprocess pass (delta_i = sum_d dout_id * out_id) and read by the others.
- * bf16, D = 128 or 64, every mask kind. Per kind the passes read:
+ * D = 128 or 64, every mask kind. dtype MFA_BF16: bf16 tensors, MFMA
+ * passes. dtype MFA_F32 (test mode): fp32 q, k, v, out, dout, dq, dk, dv,
+ * scalar fp32 passes that walk the same block lists with the same mask
+ * predicates, so the masking of both passes can be checked at 1e-4.
+ * Per kind the passes read:
  *   NONE     nothing;
  *   TILES    dQ: row_ptr, col_idx, col_kind, fine_bits; dK/dV: tile_kind,
  *            fine_bits;

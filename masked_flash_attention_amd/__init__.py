@@ -315,8 +315,11 @@ def bsr_from_bitmask(bits, n_kv_blocks, cap=None):
 def varlen_schedule(len_q, len_k=None, causal=True, window=(-1, -1), BM=TILE_M, BN=TILE_N, work_cap=None):
     """cu_seqlens, max lengths and the longest-first tile list (mfa_varlen_schedule).
 
-    ``work_cap`` defaults to an upper bound computed on the host from the
-    total length (sum ceil(L/BM) <= T/BM + nseq) so no sync is needed.
+    ``work_cap`` (required, so that no host sync is needed) bounds the tile
+    count: sum ceil(L/BM) <= total_q // BM + nseq always holds. The call is
+    asynchronous; ``n_work`` (device) reads -1 when the tiles do not fit in
+    work_cap and -2 when more than 16,384 tiles share one group of equal
+    cost >> 12 (see mfa.h), and then every work entry is -1.
     """
     lq = _i32(len_q).contiguous()
     lk = lq if len_k is None else _i32(len_k).contiguous()
@@ -532,15 +535,20 @@ def attn_bwd_dq(args, mask: MaskRep, scale):
     _ffi.check(_lib().mfa_attn_bwd_dq(C.byref(args), C.byref(m), float(scale), _stream()))
 
 
-def attn_bwd(q, k, v, out, lse, dout, mask: MaskRep, scale=None, layout="bshd", alibi_slopes=None):
+def attn_bwd(q, k, v, out, lse, dout, mask: MaskRep, scale=None, layout="bshd", alibi_slopes=None, dq=None,
+             dk=None, dv=None, delta=None):
     """Two-pass backward (any mask kind): preprocess, dK/dV over key blocks,
-    dQ over query tiles. Returns (dq, dk, dv) shaped like q, k, v. The
+    dQ over query tiles. Returns (dq, dk, dv) shaped like q, k, v (written
+    into the given tensors when passed; delta is fp32 (B, Hq, Sq)). The
     slopes must be the forward's."""
     B, Sq, Sk, Hq, Hkv, D = _dims(q, k, layout)
     if scale is None:
         scale = D ** -0.5
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    delta = torch.empty(B, Hq, Sq, dtype=torch.float32, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if delta is None:
+        delta = torch.empty(B, Hq, Sq, dtype=torch.float32, device=q.device)
     a = _bwd_args(q, k, v, out, lse, dout, dq, dk, dv, delta, layout, alibi_slopes)
     attn_bwd_preprocess(a)
     attn_bwd_dkdv(a, mask, scale)

@@ -622,21 +622,47 @@ __global__ __launch_bounds__(256) void bitmask_fill_kernel(const uint32_t* bits,
 
 // ---------------------------------------------------------------------------
 // Varlen packing and schedule ("tensorplay.nn.attention.varlen", Packed
-// layout). One workgroup of 1024 threads. Tiles are ordered by descending
-// number of visited key tiles (a counting sort over costs capped at
-// kMaxCost), ties by ascending (seq, q0).
+// layout). One workgroup of 1024 threads. The work list holds every BM-row
+// query tile (seq, q0), ordered by descending number of visited key tiles,
+// ties by ascending (seq, q0): a stable counting sort with exact costs.
+//  * Costs below kLoCost are counted per value in LDS. Longer tiles (over
+//    262,080 keys with the window open) are counted by their high digit
+//    (cost >> 12); they all precede the short ones, each high bucket is
+//    placed stably and then ranked exactly by cost inside the bucket.
+//  * Tiles are enumerated in (seq, q0) order 1024 at a time across
+//    sequence boundaries (a binary search over the tile offsets of a group
+//    of up to 1024 sequences held in LDS).
+//  * Stable placement: lanes of a wave with the same bucket are found with
+//    ballots over the bucket's bits, and the 16 waves take their positions
+//    one after the other, so equal costs keep the enumeration order.
 // ---------------------------------------------------------------------------
 
-constexpr int kMaxCost = 4095;
+constexpr int kLoCost = 4096;      // costs [0, kLoCost) counted exactly
+constexpr int kHiDigits = 8192;    // high digits 1..8192 of longer costs (a cost is at most 2^25)
+constexpr int kBucketBits = 14;    // bucket ids: cost for short tiles, kLoCost + digit - 1 for long ones
+constexpr int kMaxLongBucket = 16 * 1024;  // tiles per high digit that the exact ranking holds in registers
 
-__device__ __forceinline__ int varlen_cost(int Lq, int Lk, int q0, int BM, int BN, int causal, int left, int right) {
-    const int q1 = min(q0 + BM, Lq) - 1;
-    int lo = left >= 0 ? max(0, q0 - left) : 0;
-    int hi = Lk - 1;
+__device__ __forceinline__ int64_t varlen_cost(int64_t Lq, int64_t Lk, int64_t q0, int BM, int BN, int causal,
+                                               int left, int right) {
+    const int64_t q1 = min(q0 + BM, Lq) - 1;
+    const int64_t lo = left >= 0 ? max((int64_t)0, q0 - left) : 0;
+    int64_t hi = Lk - 1;
     if (right >= 0) hi = min(hi, q1 + right);
     if (causal) hi = min(hi, q1);
     if (hi < lo) return 0;
-    return min(hi / BN - lo / BN + 1, kMaxCost);
+    return hi / BN - lo / BN + 1;
+}
+
+// Sequence of tile `i` of a group: the last s with tp[s] <= i (tp ascending,
+// tp[0] = 0, n + 1 entries).
+__device__ __forceinline__ int tile_seq(const int* tp, int n, int i) {
+    int lo = 0, hi = n;  // tp[lo] <= i < tp[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tp[mid] <= i) lo = mid;
+        else hi = mid;
+    }
+    return lo;
 }
 
 __global__ __launch_bounds__(1024) void varlen_schedule_kernel(const int32_t* len_q, const int32_t* len_k, int nseq,
@@ -644,108 +670,200 @@ __global__ __launch_bounds__(1024) void varlen_schedule_kernel(const int32_t* le
                                                                int32_t* cu_q, int32_t* cu_k, int32_t* max_len,
                                                                int32_t* work, int work_cap, int32_t* n_work) {
     __shared__ int scan[1024];
-    __shared__ int hist[kMaxCost + 1];
+    __shared__ int hist_lo[kLoCost];     // counts, then write cursors
+    __shared__ int hist_hi[kHiDigits];   // counts, then write cursors
+    __shared__ int tp[1025];             // tile offsets of the current sequence group
     __shared__ int s_max[2];
-    __shared__ int s_cost[1024];
-    __shared__ int s_len[2][1024];  // lengths of the first 1024 sequences, for the serial passes below
+    __shared__ int s_bad;
     const int t = threadIdx.x, n = blockDim.x;
-    for (int i = t; i <= kMaxCost; i += n) hist[i] = 0;
+    const int lane = t & 63, wv = t >> 6, nwv = n >> 6;
+    for (int i = t; i < kLoCost; i += n) hist_lo[i] = 0;
+    for (int i = t; i < kHiDigits; i += n) hist_hi[i] = 0;
     if (t == 0) {
         s_max[0] = 0;
         s_max[1] = 0;
-    }
-    __syncthreads();
-    // cumulative lengths and tile counts
-    int cq = 0, ck = 0, ctile = 0;
-    if (t == 0) {
+        s_bad = 0;
         cu_q[0] = 0;
         cu_k[0] = 0;
     }
-    for (int s0 = 0; s0 < nseq; s0 += n) {
-        const int s = s0 + t;
-        const int lq = s < nseq ? len_q[s] : 0;
-        const int lk = s < nseq ? len_k[s] : 0;
-        if (s < 1024) {
-            s_len[0][s] = lq;
-            s_len[1][s] = lk;
+    __syncthreads();
+
+    // Walks the tiles of every sequence group in (seq, q0) order, 1024 per
+    // call of f(valid, seq, q0, cost); every thread calls it the same number
+    // of times (f may hold barriers). With `cum`, also writes the cumulative
+    // lengths and maxima (first walk only). Returns the tile count.
+    auto walk = [&](bool cum, auto&& f) -> int {
+        int cq = 0, ck = 0, all = 0;
+        for (int g0 = 0; g0 < nseq; g0 += n) {
+            const int s = g0 + t;
+            const int gn = min(n, nseq - g0);
+            const int lq = s < nseq ? len_q[s] : 0;
+            const int lk = s < nseq ? len_k[s] : 0;
+            int tot, tq, tk;
+            const int ex = block_exclusive_sum(s < nseq ? (lq + BM - 1) / BM : 0, &tot, scan);
+            if (cum) {
+                const int eq = block_exclusive_sum(lq, &tq, scan);
+                const int ek = block_exclusive_sum(lk, &tk, scan);
+                if (s < nseq) {
+                    cu_q[s + 1] = cq + eq + lq;
+                    cu_k[s + 1] = ck + ek + lk;
+                    atomicMax(&s_max[0], lq);
+                    atomicMax(&s_max[1], lk);
+                }
+                cq += tq;
+                ck += tk;
+            }
+            if (t < gn) tp[t] = ex;
+            if (t == 0) tp[gn] = tot;
+            __syncthreads();
+            for (int c0 = 0; c0 < tot; c0 += n) {
+                const int i = c0 + t;
+                const bool valid = i < tot;
+                int sg = 0, q0 = 0;
+                int64_t cost = -1;
+                if (valid) {
+                    const int sl = tile_seq(tp, gn, i);
+                    sg = g0 + sl;
+                    q0 = (i - tp[sl]) * BM;
+                    cost = varlen_cost(len_q[sg], len_k[sg], q0, BM, BN, causal, left, right);
+                }
+                f(valid, sg, q0, cost);
+            }
+            all += tot;
+            __syncthreads();  // tp is rewritten for the next group
         }
-        int tq, tk, tt;
-        const int eq = block_exclusive_sum(lq, &tq, scan);
-        const int ek = block_exclusive_sum(lk, &tk, scan);
-        if (s < nseq) {
-            cu_q[s + 1] = cq + eq + lq;
-            cu_k[s + 1] = ck + ek + lk;
-            atomicMax(&s_max[0], lq);
-            atomicMax(&s_max[1], lk);
-        }
-        const int nt = (lq + BM - 1) / BM;
-        block_exclusive_sum(nt, &tt, scan);
-        cq += tq;
-        ck += tk;
-        ctile += tt;
-    }
+        return all;
+    };
+
+    // Pass 1: cumulative lengths, maxima and the cost histograms.
+    const int ctile = walk(true, [&](bool valid, int, int, int64_t cost) {
+        if (!valid) return;
+        if (cost < kLoCost) atomicAdd(&hist_lo[cost], 1);
+        else atomicAdd(&hist_hi[(int)(cost >> 12) - 1], 1);
+    });
     __syncthreads();
     if (t == 0) {
         max_len[0] = s_max[0];
         max_len[1] = s_max[1];
-        n_work[0] = ctile <= work_cap ? ctile : -1;
     }
     for (int i = t; i < work_cap; i += n) {
         work[2 * i] = -1;
         work[2 * i + 1] = -1;
     }
-    if (ctile > work_cap) return;
+    for (int i = t; i < kHiDigits; i += n)
+        if (hist_hi[i] > kMaxLongBucket) s_bad = 1;
     __syncthreads();
-    // Enumerate tiles in (seq, q0) order: a thread walks sequences, tiles of a
-    // sequence are handled in chunks by the whole block.
-    // Pass 1: histogram of costs.
-    for (int s = 0; s < nseq; ++s) {
-        const int lq = s < 1024 ? s_len[0][s] : len_q[s], lk = s < 1024 ? s_len[1][s] : len_k[s];
-        const int nt = (lq + BM - 1) / BM;
-        for (int i = t; i < nt; i += n) atomicAdd(&hist[varlen_cost(lq, lk, i * BM, BM, BN, causal, left, right)], 1);
+    if (ctile > work_cap || s_bad) {
+        if (t == 0) n_work[0] = ctile > work_cap ? -1 : -2;
+        return;
     }
-    __syncthreads();
-    // start[cost] = number of tiles with a larger cost (descending order): an
-    // exclusive scan of the histogram read from the top cost down, four
-    // entries per thread (the launch has exactly 1024 threads).
+    if (t == 0) n_work[0] = ctile;
+
+    // Write cursors. Long tiles first, by descending high digit; then the
+    // short ones by descending cost.
+    int n_long;
     {
-        static_assert(kMaxCost + 1 == 4 * 1024, "four histogram entries per thread");
+        int h[8], sum = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            h[e] = hist_hi[kHiDigits - 1 - (8 * t + e)];
+            sum += h[e];
+        }
+        int run = block_exclusive_sum(sum, &n_long, scan);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            hist_hi[kHiDigits - 1 - (8 * t + e)] = run;
+            run += h[e];
+        }
+    }
+    {
         int h[4], sum = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            h[e] = hist[kMaxCost - (4 * t + e)];
+            h[e] = hist_lo[kLoCost - 1 - (4 * t + e)];
             sum += h[e];
         }
         int tot;
-        int run = block_exclusive_sum(sum, &tot, scan);  // its barriers order these reads before the writes
+        int run = n_long + block_exclusive_sum(sum, &tot, scan);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            hist[kMaxCost - (4 * t + e)] = run;
+            hist_lo[kLoCost - 1 - (4 * t + e)] = run;
             run += h[e];
         }
     }
     __syncthreads();
-    // Pass 2: stable placement in (seq, q0) order, chunk by chunk.
-    for (int s = 0; s < nseq; ++s) {
-        const int lq = s < 1024 ? s_len[0][s] : len_q[s], lk = s < 1024 ? s_len[1][s] : len_k[s];
-        const int nt = (lq + BM - 1) / BM;
-        for (int i0 = 0; i0 < nt; i0 += n) {
-            const int i = i0 + t;
-            const int cost = i < nt ? varlen_cost(lq, lk, i * BM, BM, BN, causal, left, right) : -1;
-            s_cost[t] = cost;
-            __syncthreads();
-            int rank = 0;
-            if (cost >= 0)
-                for (int u = 0; u < t; ++u) rank += (s_cost[u] == cost);
-            const int pos = cost >= 0 ? hist[cost] + rank : 0;
-            __syncthreads();
-            if (cost >= 0) {
-                work[2 * pos] = s;
-                work[2 * pos + 1] = i * BM;
-                atomicAdd(&hist[cost], 1);
+
+    // Pass 2: stable placement. Lanes of one wave with the same bucket are
+    // found with ballots over the bucket id's bits; waves then take their
+    // positions in order.
+    walk(false, [&](bool valid, int sg, int q0, int64_t cost) {
+        const int bucket = !valid ? -1 : (cost < kLoCost ? (int)cost : kLoCost + (int)(cost >> 12) - 1);
+        uint64_t same = __builtin_amdgcn_ballot_w64(valid);
+        if (!valid) same = 0;
+#pragma unroll
+        for (int bit = 0; bit < kBucketBits; ++bit) {
+            const bool on = valid && ((bucket >> bit) & 1);
+            const uint64_t bo = __builtin_amdgcn_ballot_w64(on);
+            same &= on ? bo : ~bo;
+        }
+        const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+        const int rank = __builtin_popcountll(same & below);
+        const bool leader = valid && rank == 0;
+        int* cursor = !valid ? nullptr : (bucket < kLoCost ? &hist_lo[bucket] : &hist_hi[bucket - kLoCost]);
+        for (int w = 0; w < nwv; ++w) {
+            if (wv == w && valid) {
+                const int pos = *cursor + rank;
+                work[2 * pos] = sg;
+                work[2 * pos + 1] = q0;
+                __builtin_amdgcn_wave_barrier();
+                if (leader) *cursor = pos + __builtin_popcountll(same);
             }
             __syncthreads();
         }
+    });
+
+    // Pass 3: inside each high-digit bucket (placed in (seq, q0) order), rank
+    // every tile by (cost descending, position ascending) and move it there.
+    if (n_long == 0) return;
+    __syncthreads();
+    for (int dg = kHiDigits - 1; dg >= 0; --dg) {
+        // cursor after pass 2 = bucket end; the next higher digit's end is its start
+        const int end = hist_hi[dg];
+        const int start = dg + 1 < kHiDigits ? hist_hi[dg + 1] : 0;
+        const int k = end - start;
+        if (k < 2) continue;  // uniform: LDS values read by every thread
+        constexpr int J = kMaxLongBucket / 1024;
+        int it_s[J], it_q[J], it_r[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int u = t + j * n;
+            it_r[j] = -1;
+            if (u < k) {
+                it_s[j] = work[2 * (start + u)];
+                it_q[j] = work[2 * (start + u) + 1];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int u = t + j * n;
+            if (u >= k) continue;
+            const int64_t cu = varlen_cost(len_q[it_s[j]], len_k[it_s[j]], it_q[j], BM, BN, causal, left, right);
+            int r = 0;
+            for (int x = 0; x < k; ++x) {
+                const int sx = work[2 * (start + x)], qx = work[2 * (start + x) + 1];
+                const int64_t cx = varlen_cost(len_q[sx], len_k[sx], qx, BM, BN, causal, left, right);
+                r += (cx > cu || (cx == cu && x < u)) ? 1 : 0;
+            }
+            it_r[j] = r;
+        }
+        __syncthreads();  // every read of the bucket precedes the moves
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            if (it_r[j] < 0) continue;
+            work[2 * (start + it_r[j])] = it_s[j];
+            work[2 * (start + it_r[j]) + 1] = it_q[j];
+        }
+        __syncthreads();
     }
 }
 

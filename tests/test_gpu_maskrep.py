@@ -145,25 +145,56 @@ def test_bsr_validate_rejects_noncanonical():
     assert e.value.status_name == "MFA_E_NONCANONICAL"
 
 
-@pytest.mark.parametrize("case", ["cfg3", "mixed", "tiny"])
-def test_varlen_schedule_bit_exact(case):
-    note(f"varlen schedule {case}")
+def _varlen_case(case):
+    """(len_q, causal, window) of a schedule-only case (no q/k/v needed)."""
+    rng = np.random.default_rng(7)
     if case == "cfg3":
-        L = W.varlen_window(H=1, D=8)["lengths"]
-        win = (511, 0)
-    elif case == "mixed":
-        L = np.array([1, 128, 129, 0, 4000, 300, 7], np.int32)
-        win = (200, 0)
-    else:
-        L = np.array([5, 11], np.int32)
-        win = (-1, -1)
+        return W.varlen_window(H=1, D=8)["lengths"], True, (511, 0)
+    if case == "mixed":
+        return np.array([1, 128, 129, 0, 4000, 300, 7], np.int32), True, (200, 0)
+    if case == "tiny":
+        return np.array([5, 11], np.int32), True, (-1, -1)
+    if case == "long_causal_open":
+        # tiles past 262,080 keys visit 4096+ key tiles (two high digits)
+        return np.array([600_000, 3000, 128, 270_000], np.int32), True, (-1, -1)
+    if case == "long_noncausal_ties":
+        # every tile of a sequence has the same cost: ties ordered by (seq, q0)
+        return np.array([300_000, 5, 300_000, 262_145], np.int32), False, (-1, -1)
+    if case == "two_sided_window":
+        return rng.integers(0, 5000, 40).astype(np.int32), False, (700, 300)
+    if case == "many_sequences":
+        # more sequences than one 1024-thread group
+        return rng.integers(0, 400, 2500).astype(np.int32), True, (255, 0)
+    raise ValueError(case)
+
+
+@pytest.mark.parametrize("case", ["cfg3", "mixed", "tiny", "long_causal_open", "long_noncausal_ties",
+                                  "two_sided_window", "many_sequences"])
+def test_varlen_schedule_bit_exact(case):
+    L, causal, win = _varlen_case(case)
+    note(f"varlen schedule {case}: nseq={L.size} max_len={int(L.max())} causal={causal} window={win}")
     cap = int(L.sum()) // 128 + L.size
-    s = mfa.varlen_schedule(to_dev(L), causal=True, window=win, work_cap=cap)
+    s = mfa.varlen_schedule(to_dev(L), causal=causal, window=win, work_cap=cap)
     torch.cuda.synchronize()
-    cu_q, cu_k, mq, mk, work = M.varlen_schedule(L, L, 128, 64, True, win[0], win[1])
+    cu_q, cu_k, mq, mk, work = M.varlen_schedule(L, L, 128, 64, causal, win[0], win[1])
     assert np.array_equal(_np(s["cu_q"]), cu_q) and np.array_equal(_np(s["cu_k"]), cu_k)
     assert _np(s["max_len"]).tolist() == [mq, mk]
     n = int(_np(s["n_work"])[0])
     assert n == len(work)
     assert np.array_equal(_np(s["work"])[:n], work)
     assert np.all(_np(s["work"])[n:] == -1)
+
+
+def test_varlen_schedule_limits():
+    """Too small a work_cap gives n_work = -1; more than 16,384 tiles in one
+    group of equal cost >> 12 gives n_work = -2; both leave every entry -1."""
+    L = np.array([1000, 1000], np.int32)
+    note("varlen schedule: work_cap too small")
+    s = mfa.varlen_schedule(to_dev(L), causal=True, work_cap=10)
+    torch.cuda.synchronize()
+    assert int(_np(s["n_work"])[0]) == -1 and np.all(_np(s["work"]) == -1)
+    L = np.array([16_385 * 128], np.int32)  # non-causal: every tile visits 32,770 key tiles
+    note("varlen schedule: over-full long-cost group")
+    s = mfa.varlen_schedule(to_dev(L), causal=False, work_cap=16_385)
+    torch.cuda.synchronize()
+    assert int(_np(s["n_work"])[0]) == -2 and np.all(_np(s["work"]) == -1)
