@@ -230,7 +230,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
             if (__builtin_expect(rm.row_ok && (kind_ == kTilePartial || (kt_ + 1) * BN > t.k_len), 0)) {
                 constexpr int NW32 = BN / 32;  // fine words per tile
                 const uint32_t* fb = m.fine_bits + (int64_t)row * m.fine_words + NW32 * kt_;
-                w[0] = fb[0];
+                // the row holds fine_words words; a tile's words past them are 0
+                if (NW32 * kt_ < m.fine_words) w[0] = fb[0];
                 if (NW32 == 2 && 2 * kt_ + 1 < m.fine_words) w[1] = fb[1];
             }
         }

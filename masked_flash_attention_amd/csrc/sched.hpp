@@ -181,11 +181,14 @@ __device__ __forceinline__ void tile_at(const FwdDev& p, const MaskDev& m, const
         const int e = it / SUB;
         kt = m.col_idx[e] * SUB + (it - e * SUB);
         kind = m.col_kind[e];
+        // a 32-key half that starts at or past the last key holds no key
+        if (SUB > 1 && kt * BN >= t.k_len) kind = kTileEmpty;
     } else if constexpr (KIND == MFA_MASK_BSR) {
         constexpr int SUB = kBN / BN;  // key tiles per listed block
         const int e = it / SUB;
         kt = m.indices[e] * SUB + (it - e * SUB);
         kind = m.bsr_kind[e];
+        if (SUB > 1 && kt * BN >= t.k_len) kind = kTileEmpty;
     } else if constexpr (KIND == MFA_MASK_BLOCKID) {
         kt = it;
         const int nQt = p.nQt, nKt = p.nKt;
