@@ -30,9 +30,9 @@ hipError_t launch_tile_counts(const uint8_t*, int64_t, int64_t*, hipStream_t);
 hipError_t launch_bsr_from_bitmask(const uint32_t*, int, int, int, int, int32_t*, int32_t*, int64_t, hipStream_t);
 hipError_t launch_varlen_schedule(const int32_t*, const int32_t*, int, int, int, int, int, int, int32_t*, int32_t*,
                                   int32_t*, int32_t*, int, int32_t*, hipStream_t);
-hipError_t launch_bwd_preprocess(const BwdDev& p, int D, hipStream_t s);
-hipError_t launch_bwd_dkdv(const BwdDev& p, const MaskDev& m, int D, hipStream_t s);
-hipError_t launch_bwd_dq(const BwdDev& p, const MaskDev& m, int D, hipStream_t s);
+hipError_t launch_bwd_preprocess(const BwdDev& p, int D, int dtype, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdDev& p, const MaskDev& m, int D, int dtype, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdDev& p, const MaskDev& m, int D, int dtype, int BM, hipStream_t s);
 }  // namespace mfa
 
 using namespace mfa;
@@ -553,14 +553,13 @@ mfa_status mfa_attn_fwd(const mfa_attn_args* a, const mfa_mask* mk, float scale,
 static mfa_status check_bwd(const mfa_attn_bwd_args* a, bool need_tensors) {
     if (!a) return fail(MFA_E_ARG, "args is NULL");
     MFA_TRY(check_attn_shapes(&a->fwd));
-    if (a->fwd.dtype != MFA_BF16) return fail(MFA_E_UNSUPPORTED, "the backward is built for bf16 only");
     if (a->fwd.B == 0 || a->fwd.Sq == 0 || !need_tensors) return ok();
     MFA_TRY(ensure_device());
     MFA_TRY(dev_ptr(a->fwd.out, "out"));
     MFA_TRY(dev_ptr(a->dout, "dout"));
     MFA_TRY(dev_ptr(a->delta, "delta"));
-    MFA_TRY(check_strides("out", a->fwd.out, a->fwd.o_stride, MFA_BF16));
-    MFA_TRY(check_strides("dout", a->dout, a->do_stride, MFA_BF16));
+    MFA_TRY(check_strides("out", a->fwd.out, a->fwd.o_stride, a->fwd.dtype));
+    MFA_TRY(check_strides("dout", a->dout, a->do_stride, a->fwd.dtype));
     return ok();
 }
 
@@ -639,11 +638,11 @@ mfa_status mfa_attn_bwd_preprocess(const mfa_attn_bwd_args* a, hipStream_t strea
     if (a->fwd.B == 0 || a->fwd.Sq == 0) return ok();
     BwdDev p;
     fill_bwd(a, 1.f, p);
-    return hip_ok(launch_bwd_preprocess(p, a->fwd.D, stream), "backward preprocess launch");
+    return hip_ok(launch_bwd_preprocess(p, a->fwd.D, a->fwd.dtype, stream), "backward preprocess launch");
 }
 
 static mfa_status bwd_common(const mfa_attn_bwd_args* a, const mfa_mask* mk, float scale, bool dkdv, BwdDev& p,
-                             MaskDev& m) {
+                             MaskDev& m, int& BM) {
     MFA_TRY(check_bwd(a, true));
     if (!(scale > 0.f && scale <= FLT_MAX)) return fail(MFA_E_ARG, "scale must be finite and positive");
     if (a->fwd.B == 0 || a->fwd.Sq == 0) return ok();
@@ -654,10 +653,10 @@ static mfa_status bwd_common(const mfa_attn_bwd_args* a, const mfa_mask* mk, flo
         MFA_TRY(dev_ptr(a->fwd.k, "k"));
         MFA_TRY(dev_ptr(a->fwd.v, "v"));
     }
-    MFA_TRY(check_strides("q", a->fwd.q, a->fwd.q_stride, MFA_BF16));
-    MFA_TRY(check_strides("k", a->fwd.k, a->fwd.k_stride, MFA_BF16));
-    MFA_TRY(check_strides("v", a->fwd.v, a->fwd.v_stride, MFA_BF16));
-    int BM = 128;
+    MFA_TRY(check_strides("q", a->fwd.q, a->fwd.q_stride, a->fwd.dtype));
+    MFA_TRY(check_strides("k", a->fwd.k, a->fwd.k_stride, a->fwd.dtype));
+    MFA_TRY(check_strides("v", a->fwd.v, a->fwd.v_stride, a->fwd.dtype));
+    BM = 128;
     MFA_TRY(check_bwd_mask(a, mk, dkdv, m, BM));
     fill_bwd(a, scale, p);
     // the dQ pass runs the forward's grid; the dK/dV pass reads nQt / nKt of
@@ -677,23 +676,25 @@ static mfa_status bwd_common(const mfa_attn_bwd_args* a, const mfa_mask* mk, flo
 mfa_status mfa_attn_bwd_dkdv(const mfa_attn_bwd_args* a, const mfa_mask* mk, float scale, hipStream_t stream) {
     BwdDev p;
     MaskDev m;
-    MFA_TRY(bwd_common(a, mk, scale, true, p, m));
+    int BM = 128;
+    MFA_TRY(bwd_common(a, mk, scale, true, p, m, BM));
     if (a->fwd.B == 0 || a->fwd.Sq == 0 || a->fwd.Sk == 0) return ok();
     MFA_TRY(dev_ptr(a->dk, "dk"));
     MFA_TRY(dev_ptr(a->dv, "dv"));
-    MFA_TRY(check_strides("dk", a->dk, a->dk_stride, MFA_BF16));
-    MFA_TRY(check_strides("dv", a->dv, a->dv_stride, MFA_BF16));
-    return hip_ok(launch_bwd_dkdv(p, m, a->fwd.D, stream), "backward dK/dV launch");
+    MFA_TRY(check_strides("dk", a->dk, a->dk_stride, a->fwd.dtype));
+    MFA_TRY(check_strides("dv", a->dv, a->dv_stride, a->fwd.dtype));
+    return hip_ok(launch_bwd_dkdv(p, m, a->fwd.D, a->fwd.dtype, stream), "backward dK/dV launch");
 }
 
 mfa_status mfa_attn_bwd_dq(const mfa_attn_bwd_args* a, const mfa_mask* mk, float scale, hipStream_t stream) {
     BwdDev p;
     MaskDev m;
-    MFA_TRY(bwd_common(a, mk, scale, false, p, m));
+    int BM = 128;
+    MFA_TRY(bwd_common(a, mk, scale, false, p, m, BM));
     if (a->fwd.B == 0 || a->fwd.Sq == 0) return ok();
     MFA_TRY(dev_ptr(a->dq, "dq"));
-    MFA_TRY(check_strides("dq", a->dq, a->dq_stride, MFA_BF16));
-    return hip_ok(launch_bwd_dq(p, m, a->fwd.D, stream), "backward dQ launch");
+    MFA_TRY(check_strides("dq", a->dq, a->dq_stride, a->fwd.dtype));
+    return hip_ok(launch_bwd_dq(p, m, a->fwd.D, a->fwd.dtype, BM, stream), "backward dQ launch");
 }
 
 }  // extern "C"

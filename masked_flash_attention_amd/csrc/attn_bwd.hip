@@ -167,10 +167,32 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdDev p) {
 // dK / dV pass
 // ---------------------------------------------------------------------------
 
+// Whether query i (index within the batch entry or the varlen sequence) may
+// attend to key key_l, from the key side: kblk / kval are the key's block id
+// and validity (BLOCKID), kval its kv_valid_bits bit (BSR). Evaluated only on
+// partial blocks; full blocks need no test, empty blocks are never visited.
+template <int KIND>
+__device__ __forceinline__ bool allowed_qk(const FwdDev& f, const MaskDev& m, int b, int q_len, int k_len, int key_l,
+                                           int i, int kblk, bool kval) {
+    bool ok = i < q_len && key_l < k_len;
+    if constexpr (KIND == MFA_MASK_BSR) {
+        ok = ok && kval && (!m.causal || key_l <= i);
+    } else if constexpr (KIND == MFA_MASK_TILES) {
+        if (ok) ok = (m.fine_bits[(int64_t)i * m.fine_words + (key_l >> 5)] >> (key_l & 31)) & 1u;
+    } else if constexpr (KIND == MFA_MASK_BLOCKID) {
+        if (ok) {
+            const int64_t qi = (int64_t)b * f.Sq + i;
+            ok = kval && m.q_valid[qi] && kblk <= m.q_blk[qi];
+        }
+    } else if constexpr (KIND == MFA_MASK_VARLEN) {
+        ok = ok && (!m.causal || key_l <= i) && (m.win_left < 0 || i - key_l <= m.win_left) &&
+             (m.win_right < 0 || key_l - i <= m.win_right);
+    }
+    return ok;
+}
+
 // Allowed bits of one 32-query half in the dK/dV layout: bit rr says whether
-// query qi0 + (rr>>2)*8 + 4*hh + (rr&3) (index within the batch entry or the
-// varlen sequence) may attend to this lane's key key_l. Used on partial
-// blocks only; full blocks need none, empty blocks are never visited.
+// query qi0 + (rr>>2)*8 + 4*hh + (rr&3) may attend to this lane's key key_l.
 template <int KIND>
 __device__ __forceinline__ uint32_t allowed_bits_T(const FwdDev& f, const MaskDev& m, int b, int q_len, int k_len,
                                                    int key_l, int qi0, int hh, int kblk, bool kval) {
@@ -178,23 +200,141 @@ __device__ __forceinline__ uint32_t allowed_bits_T(const FwdDev& f, const MaskDe
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
         const int i = qi0 + (rr >> 2) * 8 + 4 * hh + (rr & 3);
-        bool ok = i < q_len && key_l < k_len;
-        if constexpr (KIND == MFA_MASK_BSR) {
-            ok = ok && kval && (!m.causal || key_l <= i);
-        } else if constexpr (KIND == MFA_MASK_TILES) {
-            if (ok) ok = (m.fine_bits[(int64_t)i * m.fine_words + (key_l >> 5)] >> (key_l & 31)) & 1u;
-        } else if constexpr (KIND == MFA_MASK_BLOCKID) {
-            if (ok) {
-                const int64_t qi = (int64_t)b * f.Sq + i;
-                ok = kval && m.q_valid[qi] && kblk <= m.q_blk[qi];
-            }
-        } else if constexpr (KIND == MFA_MASK_VARLEN) {
-            ok = ok && (!m.causal || key_l <= i) && (m.win_left < 0 || i - key_l <= m.win_left) &&
-                 (m.win_right < 0 || key_l - i <= m.win_right);
-        }
-        bits |= (ok ? 1u : 0u) << rr;
+        bits |= (allowed_qk<KIND>(f, m, b, q_len, k_len, key_l, i, kblk, kval) ? 1u : 0u) << rr;
     }
     return bits;
+}
+
+// The 64-key block of one dK/dV workgroup: (batch or varlen sequence, kv
+// head, key block) and the query / key extents it works in.
+struct KeyBlock {
+    int b, hk, kbk;
+    int q_base, q_len;  // query rows [q_base, q_base + q_len) (varlen: the sequence)
+    int k_base, k_len;  // key rows k_base + [0, k_len) are attended
+    int k_alloc;        // keys whose gradient rows are written (k_len of them attended)
+    bool len_error;     // varlen: sequence longer than the stated max_q / max_k
+    bool active;        // false: the block lies past its sequence's keys
+};
+
+template <int KIND>
+__device__ __forceinline__ KeyBlock key_block(const BwdDev& p, const MaskDev& m, int wg_id, int n_wg, bool remap) {
+    const FwdDev& f = p.f;
+    KeyBlock kb;
+    kb.b = 0;
+    kb.hk = 0;
+    kb.kbk = 0;
+    kb.q_base = 0;
+    kb.q_len = f.Sq;
+    kb.k_base = 0;
+    kb.k_len = f.Sk;
+    kb.k_alloc = f.Sk;
+    kb.len_error = false;
+    kb.active = true;
+    if constexpr (KIND == MFA_MASK_VARLEN) {
+        const int nKbm = (m.max_k + 63) / 64;
+        // plain numbering: sequences differ in length, and round-robin over
+        // the XCDs keeps their work balanced
+        kb.kbk = wg_id % nKbm;
+        const int sh = wg_id / nKbm;
+        kb.hk = sh % f.Hkv;
+        const int seq = sh / f.Hkv;
+        kb.q_base = m.cu_q[seq];
+        kb.q_len = m.cu_q[seq + 1] - kb.q_base;
+        kb.k_base = m.cu_k[seq];
+        kb.k_alloc = m.cu_k[seq + 1] - kb.k_base;
+        kb.k_len = m.seqused_k ? min(kb.k_alloc, max(m.seqused_k[seq], 0)) : kb.k_alloc;
+        if (kb.kbk * 64 >= kb.k_alloc) kb.active = false;
+        kb.len_error = kb.q_len > m.max_q || kb.k_alloc > m.max_k;
+    } else {
+        const int nKb = (f.Sk + 63) / 64;
+        // consecutive key blocks of one (batch, head) on one XCD, so that
+        // they share that XCD's L2 copy of the head's Q and dO
+        const int wg = xcd_logical(wg_id, n_wg, remap && (n_wg & 7) == 0);
+        const int bh = wg / nKb;
+        kb.kbk = wg - bh * nKb;
+        kb.b = bh / f.Hkv;
+        kb.hk = bh - kb.b * f.Hkv;
+    }
+    return kb;
+}
+
+// The query blocks (64 rows) that can attend to a key block, as entries
+// qb | kind << 28 (kind 0: skip) at list positions [pbeg, pend): the CSC list
+// (BSR), the dense tile map or the block-id summaries (both at 128-row
+// granularity: a 64-row block takes its tile's kind), the window arithmetic
+// (varlen) or every block (no mask).
+template <int KIND>
+struct QueryBlocks {
+    int pbeg, pend, e0;
+    bool blk_all_valid;  // BSR with kv_valid_bits: every key of the block valid
+    __device__ __forceinline__ void init(const FwdDev& f, const MaskDev& m, const KeyBlock& kb) {
+        pbeg = 0;
+        pend = (kb.q_len + 63) / 64;
+        e0 = 0;
+        blk_all_valid = true;
+        if constexpr (KIND == MFA_MASK_BSR) {
+            bool any_valid = true;
+            if (m.kv_bits) {
+                const uint32_t* kw = m.kv_bits + (int64_t)kb.b * m.kv_words + 2 * kb.kbk;
+                const uint32_t w0 = kw[0], w1 = (2 * kb.kbk + 1 < m.kv_words) ? kw[1] : 0u;
+                blk_all_valid = w0 == 0xFFFFFFFFu && w1 == 0xFFFFFFFFu;
+                any_valid = (w0 | w1) != 0u;
+            }
+            const int nKb = (f.Sk + 63) / 64;
+            const int* cp = m.csc_ptr + ((int64_t)kb.b * f.Hkv + kb.hk) * (nKb + 1);
+            e0 = cp[kb.kbk];
+            pend = any_valid ? cp[kb.kbk + 1] - e0 : 0;
+        } else if constexpr (KIND == MFA_MASK_VARLEN) {
+            const int j0 = kb.kbk * 64, j1 = min(j0 + 63, kb.k_len - 1);
+            int lo = 0, hi = j1 >= j0 ? kb.q_len - 1 : -1;  // no used key in the block: no query block
+            if (m.causal) lo = max(lo, j0);
+            if (m.win_right >= 0) lo = max(lo, j0 - m.win_right);
+            if (m.win_left >= 0) hi = min(hi, j1 + m.win_left);
+            pbeg = lo / 64;
+            pend = hi >= lo ? hi / 64 + 1 : pbeg;
+        }
+    }
+    __device__ __forceinline__ uint32_t fetch(const FwdDev& f, const MaskDev& m, const KeyBlock& kb, int pos) const {
+        if (pos >= pend) return 0u;
+        int qb = pos, kind = kTileFull;
+        if constexpr (KIND == MFA_MASK_BSR) {
+            qb = m.csc_idx[e0 + pos];
+            kind = bsr_kind_of(qb, kb.kbk, 64, 64, f.Sq, f.Sk, m.causal);
+            if (kind == kTileFull && !blk_all_valid) kind = kTilePartial;
+        } else if constexpr (KIND == MFA_MASK_TILES) {
+            kind = m.tile_kind[(int64_t)(qb >> m.tile_shift) * f.nKt + kb.kbk];
+        } else if constexpr (KIND == MFA_MASK_BLOCKID) {
+            kind = classify_blockid(m.qsum + ((int64_t)kb.b * f.nQt + (qb >> 1)) * 4,
+                                    m.ksum + ((int64_t)kb.b * f.nKt + kb.kbk) * 4);
+        } else if constexpr (KIND == MFA_MASK_VARLEN) {
+            const int i0 = qb * 64, i1 = min(i0 + 63, kb.q_len - 1);
+            const int j0 = kb.kbk * 64, j1 = min(j0 + 63, kb.k_len - 1);
+            bool full = (i1 - i0 == 63) && (j1 - j0 == 63);
+            if (m.causal) full = full && j1 <= i0;
+            if (m.win_left >= 0) full = full && i1 - j0 <= m.win_left;
+            if (m.win_right >= 0) full = full && j1 - i0 <= m.win_right;
+            kind = full ? kTileFull : kTilePartial;
+        }
+        return (uint32_t)qb | ((uint32_t)kind << 28);
+    }
+};
+
+// Key-side mask values of key key_l: block id and validity (BLOCKID), the
+// kv_valid_bits bit (BSR; true without the bitmap).
+template <int KIND>
+__device__ __forceinline__ void key_side(const FwdDev& f, const MaskDev& m, const KeyBlock& kb, int key_l, bool key_ok,
+                                         int& kblk, bool& kval) {
+    kblk = INT32_MAX;
+    kval = false;
+    if constexpr (KIND == MFA_MASK_BLOCKID) {
+        if (key_ok) {
+            kblk = m.k_blk[(int64_t)kb.b * f.Sk + key_l];
+            kval = (m.kv_bits[(int64_t)kb.b * m.kv_words + (key_l >> 5)] >> (key_l & 31)) & 1u;
+        }
+    } else if constexpr (KIND == MFA_MASK_BSR) {
+        kval = true;
+        if (m.kv_bits) kval = key_ok && ((m.kv_bits[(int64_t)kb.b * m.kv_words + (key_l >> 5)] >> (key_l & 31)) & 1u);
+    }
 }
 
 // One workgroup (2 waves, 64 keys) per (batch or varlen sequence, kv head,
@@ -217,41 +357,15 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hh = lane >> 5, c = lane & 31;
 
-    int b = 0, hk = 0, kbk = 0;
-    int q_base = 0, q_len = f.Sq, k_base = 0, k_len = f.Sk;
-    int k_alloc = f.Sk;  // keys whose gradient rows are written (k_len of them are attended)
-    bool len_error = false;
-    if constexpr (KIND == MFA_MASK_VARLEN) {
-        const int nKbm = (m.max_k + 63) / 64;
-        // plain numbering: sequences differ in length, and round-robin over
-        // the XCDs keeps their work balanced
-        kbk = blockIdx.x % nKbm;
-        const int sh = blockIdx.x / nKbm;
-        hk = sh % f.Hkv;
-        const int seq = sh / f.Hkv;
-        q_base = m.cu_q[seq];
-        q_len = m.cu_q[seq + 1] - q_base;
-        k_base = m.cu_k[seq];
-        k_alloc = m.cu_k[seq + 1] - k_base;
-        k_len = m.seqused_k ? min(k_alloc, max(m.seqused_k[seq], 0)) : k_alloc;
-        if (kbk * 64 >= k_alloc) return;
-        if (q_len > m.max_q || k_alloc > m.max_k) {
-            len_error = true;
-            if (m.err && threadIdx.x == 0) *m.err = 1;
-        }
-    } else {
-        const int nKb = (f.Sk + 63) / 64;
-        // consecutive key blocks of one (batch, head) on one XCD, so that
-        // they share that XCD's L2 copy of the head's Q and dO
-        const int wg = xcd_logical(blockIdx.x, gridDim.x, (gridDim.x & 7) == 0);
-        const int bh = wg / nKb;
-        kbk = wg - bh * nKb;
-        b = bh / f.Hkv;
-        hk = bh - b * f.Hkv;
-    }
+    const KeyBlock kblock = key_block<KIND>(p, m, blockIdx.x, gridDim.x, true);
+    if (!kblock.active) return;
+    if (KIND == MFA_MASK_VARLEN && kblock.len_error && m.err && threadIdx.x == 0) *m.err = 1;
+    const int b = kblock.b, hk = kblock.hk, kbk = kblock.kbk;
+    const int q_base = kblock.q_base, q_len = kblock.q_len, k_len = kblock.k_len, k_alloc = kblock.k_alloc;
+    const bool len_error = kblock.len_error;
     const int key_l = kbk * 64 + wave * 32 + c;  // key within the batch entry / sequence
     const bool key_ok = key_l < k_len;
-    const int key = k_base + key_l;              // row of k, v, dk, dv
+    const int key = kblock.k_base + key_l;       // row of k, v, dk, dv
 
     // stationary K and V fragments (B operands: K^T, V^T with lane = key)
     bf16x8 kf[NKC], vf[NKC];
@@ -270,68 +384,15 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
         dk[db] = f32x16{};
         dv[db] = f32x16{};
     }
-    // key-side mask values
-    int kblk = INT32_MAX;
-    bool kval = false;
-    if constexpr (KIND == MFA_MASK_BLOCKID) {
-        if (key_ok) {
-            kblk = m.k_blk[(int64_t)b * f.Sk + key_l];
-            kval = (m.kv_bits[(int64_t)b * m.kv_words + (key_l >> 5)] >> (key_l & 31)) & 1u;
-        }
-    }
-    // BSR token validity: whole-block state from the block's two words
-    bool blk_all_valid = true, blk_any_valid = true;
-    if constexpr (KIND == MFA_MASK_BSR) {
-        kval = true;
-        if (m.kv_bits) {
-            const uint32_t* kw = m.kv_bits + (int64_t)b * m.kv_words + 2 * kbk;
-            const uint32_t w0 = kw[0], w1 = (2 * kbk + 1 < m.kv_words) ? kw[1] : 0u;
-            blk_all_valid = w0 == 0xFFFFFFFFu && w1 == 0xFFFFFFFFu;
-            blk_any_valid = (w0 | w1) != 0u;
-            kval = key_ok && (((key_l < 32 + kbk * 64 ? w0 : w1) >> (key_l & 31)) & 1u);
-        }
-    }
+    int kblk;
+    bool kval;
+    key_side<KIND>(f, m, kblock, key_l, key_ok, kblk, kval);
 
     // ---- the query blocks of this key block ----
-    const int nQb = (q_len + 63) / 64;
-    int pbeg = 0, pend = nQb, e0 = 0;
-    if constexpr (KIND == MFA_MASK_BSR) {
-        const int nKb = (f.Sk + 63) / 64;
-        const int* cp = m.csc_ptr + ((int64_t)b * f.Hkv + hk) * (nKb + 1);
-        e0 = cp[kbk];
-        pend = blk_any_valid ? cp[kbk + 1] - e0 : 0;
-    } else if constexpr (KIND == MFA_MASK_VARLEN) {
-        const int j0 = kbk * 64, j1 = min(j0 + 63, k_len - 1);
-        int lo = 0, hi = j1 >= j0 ? q_len - 1 : -1;  // no used key in the block: no query block
-        if (m.causal) lo = max(lo, j0);
-        if (m.win_right >= 0) lo = max(lo, j0 - m.win_right);
-        if (m.win_left >= 0) hi = min(hi, j1 + m.win_left);
-        pbeg = lo / 64;
-        pend = hi >= lo ? hi / 64 + 1 : pbeg;
-    }
-    auto fetch = [&](int pos) -> uint32_t {
-        if (pos >= pend) return 0u;
-        int qb = pos, kind = kTileFull;
-        if constexpr (KIND == MFA_MASK_BSR) {
-            qb = m.csc_idx[e0 + pos];
-            kind = bsr_kind_of(qb, kbk, 64, 64, f.Sq, f.Sk, m.causal);
-            if (kind == kTileFull && !blk_all_valid) kind = kTilePartial;
-        } else if constexpr (KIND == MFA_MASK_TILES) {
-            kind = m.tile_kind[(int64_t)(qb >> m.tile_shift) * f.nKt + kbk];
-        } else if constexpr (KIND == MFA_MASK_BLOCKID) {
-            kind = classify_blockid(m.qsum + ((int64_t)b * f.nQt + (qb >> 1)) * 4,
-                                    m.ksum + ((int64_t)b * f.nKt + kbk) * 4);
-        } else if constexpr (KIND == MFA_MASK_VARLEN) {
-            const int i0 = qb * 64, i1 = min(i0 + 63, q_len - 1);
-            const int j0 = kbk * 64, j1 = min(j0 + 63, k_len - 1);
-            bool full = (i1 - i0 == 63) && (j1 - j0 == 63);
-            if (m.causal) full = full && j1 <= i0;
-            if (m.win_left >= 0) full = full && i1 - j0 <= m.win_left;
-            if (m.win_right >= 0) full = full && j1 - i0 <= m.win_right;
-            kind = full ? kTileFull : kTilePartial;
-        }
-        return (uint32_t)qb | ((uint32_t)kind << 28);
-    };
+    QueryBlocks<KIND> qbl;
+    qbl.init(f, m, kblock);
+    const int pbeg = qbl.pbeg, pend = qbl.pend;
+    auto fetch = [&](int pos) -> uint32_t { return qbl.fetch(f, m, kblock, pos); };
     ScanWindow win;
     win.init(fetch, pbeg, lane);
     int g = 0, pos = pbeg;
@@ -616,7 +677,8 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || (NW != 2 && KIND != MFA_MASK_
         if constexpr (KIND == MFA_MASK_TILES) {
             if (rm.row_ok && (kind_ == kTilePartial || (kt_ + 1) * BN > t.k_len)) {
                 const uint32_t* fb = m.fine_bits + (int64_t)row * m.fine_words + NH * kt_;
-                w[0] = fb[0];
+                // the row holds fine_words words; a tile's words past them are 0
+                if (NH * kt_ < m.fine_words) w[0] = fb[0];
                 if (NH == 2 && 2 * kt_ + 1 < m.fine_words) w[1] = fb[1];
             }
         }
@@ -745,10 +807,160 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || (NW != 2 && KIND != MFA_MASK_
 }
 
 // ---------------------------------------------------------------------------
+// fp32 test mode: scalar kernels that walk the same lists with the same
+// predicates as the bf16 passes (the dK/dV pass the key block's query-block
+// list and allowed_qk, the dQ pass the forward's tile schedule and the
+// per-element predicate of sched.hpp), in fp32 arithmetic with libm exp, so
+// that the mask logic of both passes is checked at tight tolerance.
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_preprocess_f32_kernel(BwdDev p) {
+    const int64_t rows = (int64_t)p.f.B * p.f.Sq * p.f.Hq;
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= rows) return;
+    const int h = (int)(r % p.f.Hq);
+    const int64_t bi = r / p.f.Hq;
+    const int i = (int)(bi % p.f.Sq);
+    const int b = (int)(bi / p.f.Sq);
+    const float* o = (const float*)p.f.o + (int64_t)b * p.f.os0 + (int64_t)i * p.f.os1 + (int64_t)h * p.f.os2;
+    const float* d = (const float*)p.dout + (int64_t)b * p.dos0 + (int64_t)i * p.dos1 + (int64_t)h * p.dos2;
+    float acc = 0.f;
+    for (int e = 0; e < D; ++e) acc = fmaf(o[e], d[e], acc);
+    p.delta[((int64_t)b * p.f.Hq + h) * p.f.Sq + i] = acc;
+}
+
+// One thread per key: 64-key blocks as in the bf16 pass (one 64-thread
+// workgroup each), summing over the query rows of the listed query blocks
+// of every query head of the group.
+template <int D, int KIND>
+__global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(BwdDev p, MaskDev m) {
+    const FwdDev& f = p.f;
+    const KeyBlock kb = key_block<KIND>(p, m, blockIdx.x, gridDim.x, false);
+    if (!kb.active) return;
+    if (KIND == MFA_MASK_VARLEN && kb.len_error && m.err && threadIdx.x == 0) *m.err = 1;
+    const int key_l = kb.kbk * 64 + threadIdx.x;
+    const bool key_ok = key_l < kb.k_len;
+    const int key = kb.k_base + key_l;
+    int kblk;
+    bool kval;
+    key_side<KIND>(f, m, kb, key_l, key_ok, kblk, kval);
+    QueryBlocks<KIND> qbl;
+    qbl.init(f, m, kb);
+    const float* kp = (const float*)f.k + (int64_t)kb.b * f.ks0 + (int64_t)key * f.ks1 + (int64_t)kb.hk * f.ks2;
+    const float* vp = (const float*)f.v + (int64_t)kb.b * f.vs0 + (int64_t)key * f.vs1 + (int64_t)kb.hk * f.vs2;
+    float dk[D], dv[D];
+    for (int e = 0; e < D; ++e) dk[e] = dv[e] = 0.f;
+    if (key_ok) {
+        for (int g = 0; g < f.G; ++g) {
+            const int hq = kb.hk * f.G + g;
+            const float slope = f.alibi ? f.alibi[hq] : 0.f;
+            for (int pos = qbl.pbeg; pos < qbl.pend; ++pos) {
+                const uint32_t ent = qbl.fetch(f, m, kb, pos);
+                const int kind = (int)(ent >> 28);
+                if (kind == kTileEmpty) continue;
+                const int qb = (int)(ent & 0x0FFFFFFFu);
+                for (int r = 0; r < 64; ++r) {
+                    const int i = qb * 64 + r;
+                    if (i >= kb.q_len) break;
+                    if (kind == kTilePartial && !allowed_qk<KIND>(f, m, kb.b, kb.q_len, kb.k_len, key_l, i, kblk, kval))
+                        continue;
+                    const int qrow = kb.q_base + i;
+                    const float lse = f.lse[((int64_t)kb.b * f.Hq + hq) * f.Sq + qrow];
+                    if (lse == -INFINITY) continue;  // a row with no allowed key
+                    const float* qp = (const float*)f.q + (int64_t)kb.b * f.qs0 + (int64_t)qrow * f.qs1 + (int64_t)hq * f.qs2;
+                    const float* dp = (const float*)p.dout + (int64_t)kb.b * p.dos0 + (int64_t)qrow * p.dos1 +
+                                      (int64_t)hq * p.dos2;
+                    float sc = 0.f, dpv = 0.f;
+                    for (int e = 0; e < D; ++e) {
+                        sc = fmaf(qp[e], kp[e], sc);
+                        dpv = fmaf(dp[e], vp[e], dpv);
+                    }
+                    sc = sc * f.scale + slope * (float)(key_l - i);
+                    const float pr = expf(sc - lse);
+                    const float ds = pr * (dpv - p.delta[((int64_t)kb.b * f.Hq + hq) * f.Sq + qrow]);
+                    for (int e = 0; e < D; ++e) {
+                        dv[e] = fmaf(pr, dp[e], dv[e]);
+                        dk[e] = fmaf(ds, qp[e], dk[e]);
+                    }
+                }
+            }
+        }
+    }
+    if (key_l >= kb.k_alloc) return;  // keys past the used length get zero gradients
+    float* dkp = (float*)p.dk + (int64_t)kb.b * p.dks0 + (int64_t)key * p.dks1 + (int64_t)kb.hk * p.dks2;
+    float* dvp = (float*)p.dv + (int64_t)kb.b * p.dvs0 + (int64_t)key * p.dvs1 + (int64_t)kb.hk * p.dvs2;
+    const float nanv = __builtin_nanf("");
+    for (int e = 0; e < D; ++e) {
+        dkp[e] = kb.len_error ? nanv : dk[e] * f.scale;
+        dvp[e] = kb.len_error ? nanv : dv[e];
+    }
+}
+
+// One thread per query row of the forward's query tile, walking the
+// forward's key tiles (tile_at) with the per-element predicate.
+template <int D, int BM, int KIND>
+__global__ __launch_bounds__(BM) void bwd_dq_f32_kernel(BwdDev p, MaskDev m) {
+    const FwdDev& f = p.f;
+    const TileRange t = make_range<KIND, BM>(f, m, blockIdx.x);
+    if (!t.active) return;
+    const int row = t.q_row0 + threadIdx.x;
+    RowMask<KIND> rm;
+    rm.init(f, m, t, row);
+    if (!rm.row_ok) return;
+    const float* qp = (const float*)f.q + (int64_t)t.b * f.qs0 + (int64_t)row * f.qs1 + (int64_t)t.hq * f.qs2;
+    const float* dp = (const float*)p.dout + (int64_t)t.b * p.dos0 + (int64_t)row * p.dos1 + (int64_t)t.hq * p.dos2;
+    const float* K = (const float*)f.k + (int64_t)t.b * f.ks0 + (int64_t)t.hk * f.ks2 + (int64_t)t.k_base * f.ks1;
+    const float* V = (const float*)f.v + (int64_t)t.b * f.vs0 + (int64_t)t.hk * f.vs2 + (int64_t)t.k_base * f.vs1;
+    const int64_t lrow = ((int64_t)t.b * f.Hq + t.hq) * f.Sq + row;
+    const float lse = f.lse[lrow], dl = p.delta[lrow];
+    const float slope = f.alibi ? f.alibi[t.hq] : 0.f;
+    float q[D], dq[D];
+    for (int e = 0; e < D; ++e) {
+        q[e] = qp[e];
+        dq[e] = 0.f;
+    }
+    if (lse != -INFINITY) {
+        for (int it = t.begin; it < t.end; ++it) {
+            int kt, kind;
+            tile_at<KIND, BM>(f, m, t, it, kt, kind);
+            if (kind == kTileEmpty) continue;
+            for (int j = 0; j < kBN; ++j) {
+                const int key = kt * kBN + j;
+                if (key >= t.k_len) break;
+                if (kind == kTilePartial && !allowed<KIND>(f, m, t, rm, key)) continue;
+                const float* kr = K + (int64_t)key * f.ks1;
+                const float* vr = V + (int64_t)key * f.vs1;
+                float sc = 0.f, dpv = 0.f;
+                for (int e = 0; e < D; ++e) {
+                    sc = fmaf(q[e], kr[e], sc);
+                    dpv = fmaf(dp[e], vr[e], dpv);
+                }
+                sc = sc * f.scale + slope * (float)(key - (row - t.q_base));
+                const float ds = expf(sc - lse) * (dpv - dl);
+                for (int e = 0; e < D; ++e) dq[e] = fmaf(ds, kr[e], dq[e]);
+            }
+        }
+    }
+    float* dqp = (float*)p.dq + (int64_t)t.b * p.dqs0 + (int64_t)row * p.dqs1 + (int64_t)t.hq * p.dqs2;
+    for (int e = 0; e < D; ++e) dqp[e] = t.len_error ? __builtin_nanf("") : dq[e] * f.scale;
+}
+
+// ---------------------------------------------------------------------------
 // Host launch
 // ---------------------------------------------------------------------------
 
-hipError_t launch_bwd_preprocess(const BwdDev& p, int D, hipStream_t s) {
+static hipError_t launch_bwd_preprocess_f32(const BwdDev& p, int D, hipStream_t s) {
+    const int64_t rows = (int64_t)p.f.B * p.f.Sq * p.f.Hq;
+    const int grid = (int)((rows + 255) / 256);
+    if (grid == 0) return hipSuccess;
+    if (D == 128) hipLaunchKernelGGL(bwd_preprocess_f32_kernel<128>, dim3(grid), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(bwd_preprocess_f32_kernel<64>, dim3(grid), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_preprocess(const BwdDev& p, int D, int dtype, hipStream_t s) {
+    if (dtype == MFA_F32) return launch_bwd_preprocess_f32(p, D, s);
     const int64_t rows = (int64_t)p.f.B * p.f.Sq * p.f.Hq;
     const int per_wg = 4 * (64 / (D / 8));
     const int grid = (int)((rows + per_wg - 1) / per_wg);
@@ -801,6 +1013,48 @@ static hipError_t dq_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) {
     }
 }
 
+template <int D, int KIND>
+static hipError_t dkdv_f32_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) {
+    const int64_t grid = KIND == MFA_MASK_VARLEN
+                             ? (int64_t)m.nseq * p.f.Hkv * ((m.max_k + 63) / 64)
+                             : (int64_t)p.f.B * p.f.Hkv * ((p.f.Sk + 63) / 64);
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, KIND>), dim3((unsigned)grid), dim3(64), 0, s, p, m);
+    return hipGetLastError();
+}
+
+template <int D, int KIND>
+static hipError_t dq_f32_launch(const BwdDev& p, const MaskDev& m, int BM, hipStream_t s) {
+    if (p.f.total == 0) return hipSuccess;
+    if (BM == 64) hipLaunchKernelGGL((bwd_dq_f32_kernel<D, 64, KIND>), dim3(p.f.total), dim3(64), 0, s, p, m);
+    else hipLaunchKernelGGL((bwd_dq_f32_kernel<D, 128, KIND>), dim3(p.f.total), dim3(128), 0, s, p, m);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t dkdv_f32_kind(const BwdDev& p, const MaskDev& m, hipStream_t s) {
+    switch (m.kind) {
+        case MFA_MASK_NONE: return dkdv_f32_launch<D, MFA_MASK_NONE>(p, m, s);
+        case MFA_MASK_BLOCKID: return dkdv_f32_launch<D, MFA_MASK_BLOCKID>(p, m, s);
+        case MFA_MASK_TILES: return dkdv_f32_launch<D, MFA_MASK_TILES>(p, m, s);
+        case MFA_MASK_BSR: return dkdv_f32_launch<D, MFA_MASK_BSR>(p, m, s);
+        case MFA_MASK_VARLEN: return dkdv_f32_launch<D, MFA_MASK_VARLEN>(p, m, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int D>
+static hipError_t dq_f32_kind(const BwdDev& p, const MaskDev& m, int BM, hipStream_t s) {
+    switch (m.kind) {
+        case MFA_MASK_NONE: return dq_f32_launch<D, MFA_MASK_NONE>(p, m, BM, s);
+        case MFA_MASK_BLOCKID: return dq_f32_launch<D, MFA_MASK_BLOCKID>(p, m, BM, s);
+        case MFA_MASK_TILES: return dq_f32_launch<D, MFA_MASK_TILES>(p, m, BM, s);
+        case MFA_MASK_BSR: return dq_f32_launch<D, MFA_MASK_BSR>(p, m, BM, s);
+        case MFA_MASK_VARLEN: return dq_f32_launch<D, MFA_MASK_VARLEN>(p, m, BM, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int D>
 static hipError_t dkdv_kind(const BwdDev& p, const MaskDev& m, hipStream_t s) {
     switch (m.kind) {
@@ -825,11 +1079,13 @@ static hipError_t dq_kind(const BwdDev& p, const MaskDev& m, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_dkdv(const BwdDev& p, const MaskDev& m, int D, hipStream_t s) {
+hipError_t launch_bwd_dkdv(const BwdDev& p, const MaskDev& m, int D, int dtype, hipStream_t s) {
+    if (dtype == MFA_F32) return D == 128 ? dkdv_f32_kind<128>(p, m, s) : dkdv_f32_kind<64>(p, m, s);
     return D == 128 ? dkdv_kind<128>(p, m, s) : dkdv_kind<64>(p, m, s);
 }
 
-hipError_t launch_bwd_dq(const BwdDev& p, const MaskDev& m, int D, hipStream_t s) {
+hipError_t launch_bwd_dq(const BwdDev& p, const MaskDev& m, int D, int dtype, int BM, hipStream_t s) {
+    if (dtype == MFA_F32) return D == 128 ? dq_f32_kind<128>(p, m, BM, s) : dq_f32_kind<64>(p, m, BM, s);
     return D == 128 ? dq_kind<128>(p, m, s) : dq_kind<64>(p, m, s);
 }
 

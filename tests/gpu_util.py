@@ -63,3 +63,31 @@ def compare_attention(out, lse, ref_out, ref_lse, out_tol, lse_tol=LSE_TOL, rows
     assert err_o <= out_tol, f"out max-abs error {err_o:.3e} > {out_tol}"
     assert err_l <= lse_tol, f"lse max-abs error {err_l:.3e} > {lse_tol}"
     return err_o, err_l
+
+
+def tile_rows(n, tile, salt):
+    """One index in every `tile`-sized block of [0, n): block t contributes
+    t*tile + (37 t + salt) mod len(block), so different blocks (and different
+    salts, e.g. per (batch, head)) land on different lanes and waves."""
+    starts = np.arange(0, n, tile)
+    lens = np.minimum(tile, n - starts)
+    return starts + (37 * np.arange(starts.size) + salt) % lens
+
+
+def nan_like(t):
+    """A NaN-filled tensor like t: outputs the kernel leaves unwritten stay NaN."""
+    return torch.full_like(t, float("nan"))
+
+
+def bsr_row_mask(ip_bh, ix, blk, N, rows, causal=True):
+    """Allowed keys (len(rows), N) of query rows under one (batch, head)'s BSR
+    rows ip_bh (its nQb + 1 offsets into ix), causal inside blocks."""
+    rows = np.asarray(rows)
+    nKb = -(-N // blk)
+    blocks = np.zeros((rows.size, nKb), bool)
+    for n, r in enumerate(rows // blk):
+        blocks[n, ix[ip_bh[r]:ip_bh[r + 1]]] = True
+    a = np.repeat(blocks, blk, axis=1)[:, :N]
+    if causal:
+        a &= np.arange(N)[None, :] <= rows[:, None]
+    return a

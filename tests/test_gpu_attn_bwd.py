@@ -11,7 +11,7 @@ import masked_flash_attention_amd as mfa
 from oracle import attention as A
 from oracle import masks as M
 import workloads as W
-from tests.gpu_util import BF16_OUT_TOL, DEV, compare_attention, f64, note, to_dev
+from tests.gpu_util import BF16_OUT_TOL, DEV, bsr_row_mask, compare_attention, f64, nan_like, note, tile_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -102,34 +102,44 @@ def test_bsr_delta_matches_oracle():
     assert float(np.abs(f64(delta) - rdelta).max()) <= 5e-2
 
 
-def test_cfg5_backward_sampled():
+def test_cfg5_backward_every_block():
     """B=2, N=16384, H=16, D=128, 64x64 BSR blocks, causal inside blocks:
-    forward + two-pass backward at full size; dQ rows and dK/dV columns of two
-    (batch, head) slices checked against the oracle."""
-    note("cfg5 bwd full size")
+    forward + two-pass backward at full size into NaN-filled dq / dk / dv.
+    One dQ row of every 64-row query block of every (b, h) against the
+    oracle's row-local gradient; one dK/dV column of every 64-key block of
+    three (b, h) slices; every gradient must be finite."""
+    note("cfg5 bwd full size, every block")
     w = W.bsr_random()
-    N, blk = 16384, 64
-    out, lse, dq, dk, dv = _bsr_run(w, N, True)
+    B, N, H, D = w["q"].shape
+    blk = 64
     ip, ix = w["indptr"], w["indices"]
-    rows = np.array([0, 63, 64, 5000, 16383])
-    cols = np.array([0, 1, 64, 9000, 16383])
-    for b, h in [(0, 3), (1, 15)]:
-        seg = ip[b, h]
-        listed = [set(ix[seg[r]:seg[r + 1]].tolist()) for r in range(N // blk)]
-
-        def allowed(bb, hm, rr, listed=listed):
-            rr = np.asarray(rr)
-            blocks = np.zeros((len(rr), N // blk), bool)
-            for n, i in enumerate(rr):
-                blocks[n, list(listed[i // blk])] = True
-            a = np.repeat(blocks, blk, axis=1)
-            return a & (np.arange(N)[None, :] <= rr[:, None])
-        allowed.heads = 16
-        rq, rk, rv = A.attention_bwd_sampled(w["q"], w["k"], w["v"], w["do"], allowed, w["scale"], b, h, rows,
-                                             cols, chunk=2048)
-        for name, g, r in (("dq", f64(dq[b, rows, h]), rq[0]), ("dk", f64(dk[b, cols, h]), rk),
+    ipd, ixd = to_dev(ip), to_dev(ix)
+    kind, cp, ci = mfa.bsr_prepare(ipd, ixd, blk, blk, N, N, True)
+    rep = mfa.MaskRep.bsr(ipd, ixd, kind, causal=True, csc_ptr=cp, csc_idx=ci)
+    q, k, v, do = (to_dev(w[x]) for x in ("q", "k", "v", "do"))
+    out, lse = mfa.attn_fwd(q, k, v, rep, w["scale"], "bshd")
+    dq, dk, dv = nan_like(q), nan_like(k), nan_like(v)
+    mfa.attn_bwd(q, k, v, out, lse, do, rep, w["scale"], "bshd", dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    for b in range(B):
+        for h in range(H):
+            rows = tile_rows(N, blk, 3 * b + 17 * h)
+            allowed = lambda bb, hm, rr, b=b, h=h: bsr_row_mask(ip[b, h], ix, blk, N, rr)  # noqa: E731
+            allowed.heads = 1
+            sl = [w[x][b, :, h].double().numpy()[None, :, None, :] for x in ("q", "k", "v", "do")]
+            rq = A.attention_bwd_dq_rows(*sl, allowed, w["scale"], rows)
+            err = float(np.abs(f64(dq[b, rows, h]) - rq[0, :, 0]).max())
+            assert err <= BF16_OUT_TOL, f"dq (b={b}, h={h}) max-abs {err:.3e}"
+    cols_fixed = np.array([0, 1, 64, 9000, 16383])
+    for b, h in [(0, 3), (1, 15), (1, 0)]:
+        cols = np.unique(np.concatenate([tile_rows(N, blk, 29 * b + h), cols_fixed]))
+        allowed = lambda bb, hm, rr, b=b, h=h: bsr_row_mask(ip[b, h], ix, blk, N, rr)  # noqa: E731
+        allowed.heads = 1
+        sl = [w[x][b, :, h].double().numpy()[None, :, None, :] for x in ("q", "k", "v", "do")]
+        rq, rk, rv = A.attention_bwd_sampled(*sl, allowed, w["scale"], 0, 0, cols_fixed, cols, chunk=2048)
+        for name, g, r in (("dq", f64(dq[b, cols_fixed, h]), rq[0]), ("dk", f64(dk[b, cols, h]), rk),
                            ("dv", f64(dv[b, cols, h]), rv)):
             err = float(np.abs(g - r).max())
             assert err <= BF16_OUT_TOL, f"{name} (b={b}, h={h}) max-abs {err:.3e}"
-    for t in (dq, dk, dv):
-        assert torch.isfinite(t.float()).all()

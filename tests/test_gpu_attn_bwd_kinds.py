@@ -12,7 +12,7 @@ import masked_flash_attention_amd as mfa
 from oracle import attention as A
 from oracle import masks as M
 import workloads as W
-from tests.gpu_util import BF16_OUT_TOL, DEV, f64, grad_tolerance, note, to_dev
+from tests.gpu_util import BF16_OUT_TOL, DEV, f64, grad_tolerance, nan_like, note, tile_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -170,11 +170,13 @@ def test_autograd_wrapper_matches_oracle():
 
 # --- full size: causal dense mask, B=4, H=32, N=8192, D=128 -------------------------------
 
-def test_cfg2_causal_backward_sampled():
-    """The benchmark's causal workload through the dense-tile backward at full
-    size; dQ rows and dK/dV columns of two (batch, head) slices against the
-    oracle's sampled gradients."""
-    note("cfg2 causal bwd full size")
+def test_cfg2_causal_backward_every_tile():
+    """The benchmark's causal workload through the dense-tile backward at
+    full size into NaN-filled dq / dk / dv: one dQ row of every 128-row query
+    tile of every (b, h) against the oracle's row-local gradient, one dK/dV
+    column of every 64-key block of two (b, h) slices; every gradient must
+    be finite."""
+    note("cfg2 causal bwd full size, every tile")
     w = W.causal_dense()
     B, H, N, D = w["q"].shape
     do = W.tensors(2002, [(B, H, N, D)])[0]
@@ -182,18 +184,25 @@ def test_cfg2_causal_backward_sampled():
     rep = mfa.MaskRep.tiles(mfa.compact_dense_mask(to_dev(mask)))
     qd, kd, vd, dod = (to_dev(t) for t in (w["q"], w["k"], w["v"], do))
     out, lse = mfa.attn_fwd(qd, kd, vd, rep, w["scale"], "bhsd")
-    dq, dk, dv = mfa.attn_bwd(qd, kd, vd, out, lse, dod, rep, w["scale"], "bhsd")
+    dq, dk, dv = nan_like(qd), nan_like(kd), nan_like(vd)
+    mfa.attn_bwd(qd, kd, vd, out, lse, dod, rep, w["scale"], "bhsd", dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
-    rows = np.array([0, 1, 127, 128, 4095, 8191])
-    cols = np.array([0, 63, 64, 4095, 8190, 8191])
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
 
     def allowed(bb, hm, rr):
         return mask[np.asarray(rr)]
     allowed.heads = 1
-    sl = lambda t, b, h: t[b:b + 1, h:h + 1].transpose(1, 2)  # noqa: E731  -> (1, N, 1, D)
+    sl = lambda t, b, h: t[b, h].double().numpy()[None, :, None, :]  # noqa: E731  -> (1, N, 1, D)
+    for b in range(B):
+        for h in range(H):
+            rows = tile_rows(N, 128, 5 * b + 7 * h)
+            rq = A.attention_bwd_dq_rows(sl(w["q"], b, h), sl(w["k"], b, h), sl(w["v"], b, h), sl(do, b, h),
+                                         allowed, w["scale"], rows)
+            _check_grads([dq[b, h, rows]], [rq[0, :, 0]], tag=f"cfg2 dq b={b} h={h}")
+    rows = np.array([0, 1, 127, 128, 4095, 8191])
     for b, h in ((0, 0), (3, 31)):
+        cols = np.unique(np.concatenate([tile_rows(N, 64, 3 * b + h), [0, 63, 64, 4095, 8190, 8191]]))
         rq, rk, rv = A.attention_bwd_sampled(sl(w["q"], b, h), sl(w["k"], b, h), sl(w["v"], b, h), sl(do, b, h),
                                              allowed, w["scale"], 0, 0, rows, cols, chunk=2048)
         _check_grads([dq[b, h, rows], dk[b, h, cols], dv[b, h, cols]], [rq[0], rk, rv], tag=f"cfg2 b={b} h={h}")
-    for t in (dq, dk, dv):
-        assert torch.isfinite(t.float()).all()
