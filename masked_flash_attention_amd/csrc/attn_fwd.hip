@@ -37,6 +37,8 @@
 // row, fp32 arithmetic with libm exp/log, used to check the tiling and masking
 // logic at tight tolerance.
 
+#include <type_traits>
+
 #include "sched.hpp"
 
 namespace mfa {
@@ -116,7 +118,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
     f32x16 o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-    float m_used = -INFINITY;
+    float M = 0.f;       // scaled running max (log2 units); 0 until m_set
+    bool m_set = false;  // the row has seen an allowed key
     float l_part = 0.f;
 
     // ---- staging of K/V tiles: direct global->LDS buffer loads ----
@@ -252,8 +255,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
         sl = p.alibi[t.hq] / p.scale;
         d_row = 4 * hh - (row - t.q_base);
     }
-    int buf = 0;
-    if (it < t.end) do {
+    // One tile with the buffer parity BUF known at compile time, so that
+    // every LDS operand read and DMA target is a per-lane base plus an
+    // immediate offset; the loop below runs it for buffers 0 and 1 in turn.
+    auto iter = [&](auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
         int it_n = it + 1, kt_n = kt, kind_n = kTileEmpty;
         advance(it_n, kt_n, kind_n);
         const bool has_next = it_n < t.end;
@@ -319,37 +325,52 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
                 mask_scores<KIND, NB>(p, m, t, rm, row, hh, kt, fw, s, KIND == MFA_MASK_BLOCKID ? ckb_ : nullptr);
 
             // ---- online softmax ----
-            // Row max and row sum as 4 independent chains each (short dependency
-            // chains: a single wave issues them back to back).
-            float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            // Scores are scaled and shifted first, t = s*c - M (M: the scaled
+            // running max, 0 until the row has seen a key), and the tile max
+            // is taken over t: t comes out of an FMA, so the max needs no
+            // NaN canonicalisation, and the exponent argument is ready. M is
+            // only moved when the tile max exceeds it by more than kTau.
+            // Row max and row sum as 4 independent chains each (short
+            // dependency chains: a single wave issues them back to back).
 #pragma unroll
             for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], s[kb][r]);
-            float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-            mx = max_both_halves(mx);
-            const float m_new = fmaxf(m_used, mx);
-            const bool need = (m_new - m_used) * c2 > kTau;  // false when both are -inf
+                for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], c2, -M);
+            float mx4[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
+#pragma unroll
+            for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+                for (int r = (kb == 0 ? 4 : 0); r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], s[kb][r]);
+            float T = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+            T = max_both_halves(T);
+            // T = -inf: no allowed key of this row in the tile, M stays
+            const bool need = T > kTau || (!m_set && T > -INFINITY);
             if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
-                const float alpha = need ? fast_exp2((m_used - m_new) * c2) : 1.f;
-                m_used = need ? m_new : m_used;
+                const float sh = need ? T : 0.f;
+                const float alpha = (need && m_set) ? fast_exp2(-T) : 1.f;
+                M += sh;
+                m_set = m_set || need;
                 l_part *= alpha;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+#pragma unroll
+                for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[kb][r] -= sh;
             }
-            const float mb = (m_used == -INFINITY) ? 0.f : m_used * c2;
             bf16x8 pb[NK16];
-            float rs4[4] = {0.f, 0.f, 0.f, 0.f};
+            float rs4[4];
 #pragma unroll
             for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
                 for (int gp = 0; gp < 2; ++gp)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float pv = fast_exp2(fmaf(s[kb][gp * 8 + e], c2, -mb));
-                        rs4[e & 3] += pv;
+                        const float pv = fast_exp2(s[kb][gp * 8 + e]);
+                        if (kb == 0 && gp == 0 && e < 4) rs4[e] = pv;
+                        else rs4[e & 3] += pv;
                         pb[kb * 2 + gp][e] = (bf16)pv;
                     }
             l_part += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
@@ -372,13 +393,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
 
         wait_vmem();  // this wave's tile loads have landed in LDS
         __syncthreads();
-        buf ^= 1;
         it = it_n;
         kt = kt_n;
         kind = kind_n;
         fw[0] = fw_n[0];
         fw[1] = fw_n[1];
-    } while (it < t.end);
+    };
+    while (it < t.end) {
+        iter(std::integral_constant<int, 0>{});
+        if (it >= t.end) break;
+        iter(std::integral_constant<int, 1>{});
+    }
 
     // ---- epilogue ----
     const float l_tot = sum_both_halves(l_part);
@@ -398,7 +423,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
         }
     }
     if (p.lse && hh == 0) {
-        float L = empty ? -INFINITY : (m_used * c2 + fast_log2(l_tot)) * kLn2;
+        float L = empty ? -INFINITY : (M + fast_log2(l_tot)) * kLn2;
         if (t.len_error) L = __builtin_nanf("");
         p.lse[((int64_t)t.b * p.Hq + t.hq) * p.Sq + row] = L;
     }
