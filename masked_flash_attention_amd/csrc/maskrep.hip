@@ -430,6 +430,71 @@ __global__ __launch_bounds__(256) void compact_csr_kernel(const uint8_t* tile_ki
     if (qt == nQt - 1 && threadIdx.x == 0) row_ptr[nQt] = base + carry;
 }
 
+// The same CSR in linear work for large maps: each tile row's count of
+// non-empty tiles goes to row_ptr[qt + 1], one workgroup scans row_ptr in
+// place, then each row writes its entries at row_ptr[qt]. (The single kernel
+// above recounts every earlier row: quadratic in the number of tile rows.)
+__global__ __launch_bounds__(256) void csr_count_kernel(const uint8_t* tile_kind, int nKt, int32_t* row_ptr) {
+    __shared__ int lds[16];
+    const int qt = blockIdx.x;
+    const uint8_t* rowk = tile_kind + (int64_t)qt * nKt;
+    int cnt = 0;
+    for (int kt = threadIdx.x; kt < nKt; kt += blockDim.x) cnt += rowk[kt] != 0;
+    const int tot = block_sum(cnt, lds);
+    if (threadIdx.x == 0) {
+        row_ptr[qt + 1] = tot;
+        if (qt == 0) row_ptr[0] = 0;
+    }
+}
+
+__global__ __launch_bounds__(1024) void csr_scan_kernel(int nQt, int32_t* row_ptr) {
+    __shared__ int scan[128];
+    int carry = 0;
+    for (int i0 = 1; i0 <= nQt; i0 += blockDim.x) {
+        const int i = i0 + threadIdx.x;
+        const int v = i <= nQt ? row_ptr[i] : 0;
+        int tot;
+        const int ex = block_exclusive_sum(v, &tot, scan);
+        if (i <= nQt) row_ptr[i] = carry + ex + v;
+        carry += tot;
+    }
+}
+
+__global__ __launch_bounds__(256) void csr_fill_kernel(const uint8_t* tile_kind, int nKt, const int32_t* row_ptr,
+                                                       int32_t* col_idx, uint8_t* col_kind) {
+    __shared__ int lds[16];
+    const int qt = blockIdx.x;
+    const int base = row_ptr[qt];
+    const uint8_t* rowk = tile_kind + (int64_t)qt * nKt;
+    int carry = 0;
+    for (int k0 = 0; k0 < nKt; k0 += blockDim.x) {
+        const int kt = k0 + threadIdx.x;
+        const uint8_t k = kt < nKt ? rowk[kt] : 0;
+        int n;
+        const int pos = block_exclusive_count(k != 0, &n, lds);
+        if (k != 0) {
+            col_idx[base + carry + pos] = kt;
+            col_kind[base + carry + pos] = k;
+        }
+        carry += n;
+    }
+}
+
+// CSR of a tile map: the single quadratic-recount kernel for small maps
+// (one launch), the linear three-kernel form for large ones.
+static hipError_t launch_csr(const uint8_t* tile_kind, int nQt, int nKt, int32_t* row_ptr, int32_t* col_idx,
+                             uint8_t* col_kind, hipStream_t s) {
+    if ((int64_t)nQt * nQt * nKt <= (int64_t)(1 << 22)) {
+        hipLaunchKernelGGL(compact_csr_kernel, dim3(nQt), dim3(256), 0, s, tile_kind, nQt, nKt, row_ptr, col_idx,
+                           col_kind);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(csr_count_kernel, dim3(nQt), dim3(256), 0, s, tile_kind, nKt, row_ptr);
+    hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, s, nQt, row_ptr);
+    hipLaunchKernelGGL(csr_fill_kernel, dim3(nQt), dim3(256), 0, s, tile_kind, nKt, row_ptr, col_idx, col_kind);
+    return hipGetLastError();
+}
+
 // 128-row tile map from a 64-row one: a 128-row tile is empty iff both halves
 // are, full iff both halves exist and are full, else partial (a half past Nq
 // makes the tile ragged, so never full).
@@ -508,41 +573,64 @@ __device__ __forceinline__ int key_range_validity(const uint32_t* words, int j0,
     return (any ? 1 : 0) | (all ? 2 : 0);
 }
 
-__global__ __launch_bounds__(256) void bsr_prepare_kernel(const int32_t* indptr, const int32_t* indices, int nQb,
-                                                          int nKb, int64_t nnz, int qb, int kb, int Sq, int Skv, int causal,
-                                                          const uint32_t* kv_valid, int Hkv, uint8_t* col_kind,
-                                                          int32_t* csc_ptr, int32_t* csc_idx) {
+// Row of flat entry e: the last r with ip[r] <= e (ip non-decreasing,
+// ip[0] <= e < ip[nQb]).
+__device__ __forceinline__ int bsr_row_of(const int* ip, int nQb, int e) {
+    int lo = 0, hi = nQb;  // ip[lo] <= e < ip[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (ip[mid] <= e) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+constexpr int kBsrColBits = 14;  // column ids below 16384 (the host enforces nKb <= 16384)
+
+// One 1024-thread workgroup per (batch, kv head). Entries are processed in
+// row-major chunks of 1024: first every entry's kind and its column's count
+// (LDS atomics, order-free), then a scan of the counts into csc_ptr, then a
+// stable scatter: lanes of a wave with the same column are matched with
+// ballots over the column's bits and the 16 waves take their positions one
+// after the other, so each column lists its rows in ascending order.
+__global__ __launch_bounds__(1024) void bsr_prepare_kernel(const int32_t* indptr, const int32_t* indices, int nQb,
+                                                           int nKb, int64_t nnz, int qb, int kb, int Sq, int Skv,
+                                                           int causal, const uint32_t* kv_valid, int Hkv,
+                                                           uint8_t* col_kind, int32_t* csc_ptr, int32_t* csc_idx) {
     extern __shared__ int cnt[];  // nKb ints, then 1024 scan scratch
     int* scan = cnt + nKb;
     const int bh = blockIdx.x;
+    const int t = threadIdx.x, n = blockDim.x, lane = t & 63, wv = t >> 6, nwv = n >> 6;
     const int* ip = indptr + (int64_t)bh * (nQb + 1);
     int32_t* cp = csc_ptr + (int64_t)bh * (nKb + 1);
-    for (int c = threadIdx.x; c < nKb; c += blockDim.x) cnt[c] = 0;
+    for (int c = t; c < nKb; c += n) cnt[c] = 0;
     __syncthreads();
-    // Rows are expected canonical (mfa_bsr_validate); out-of-range offsets or
-    // ids are skipped here so that malformed input cannot write out of bounds.
-    for (int r = 0; r < nQb; ++r) {
-        const int e0 = max(ip[r], 0), e1 = (int)min((int64_t)ip[r + 1], nnz);
-        for (int e = e0 + threadIdx.x; e < e1; e += blockDim.x) {
-            const int c = indices[e];
-            if (c < 0 || c >= nKb) continue;
-            int kind = bsr_kind_of(r, c, qb, kb, Sq, Skv, causal);
-            if (kv_valid && kind != kTileEmpty) {
-                // token validity (kv_valid_bits): no valid key -> empty, an invalid key -> not full
-                const int v = key_range_validity(kv_valid + (int64_t)(bh / Hkv) * ((Skv + 31) >> 5), c * kb,
-                                                 min((c + 1) * kb, Skv) - 1);
-                if (!(v & 1)) kind = kTileEmpty;
-                else if (kind == kTileFull && !(v & 2)) kind = kTilePartial;
-            }
-            col_kind[e] = (uint8_t)kind;
-            cnt[c] += 1;  // distinct columns within one row
+    // Rows are expected canonical (mfa_bsr_validate); ids out of range are
+    // skipped and every write is bounded, so malformed input cannot write
+    // out of bounds.
+    const int e_begin = max(ip[0], 0), e_end = (int)min((int64_t)ip[nQb], nnz);
+    const uint32_t* kvw = kv_valid ? kv_valid + (int64_t)(bh / Hkv) * ((Skv + 31) >> 5) : nullptr;
+    for (int e0 = e_begin; e0 < e_end; e0 += n) {
+        const int e = e0 + t;
+        if (e >= e_end) continue;
+        const int c = indices[e];
+        if (c < 0 || c >= nKb) continue;
+        const int r = bsr_row_of(ip, nQb, e);
+        int kind = bsr_kind_of(r, c, qb, kb, Sq, Skv, causal);
+        if (kvw && kind != kTileEmpty) {
+            // token validity (kv_valid_bits): no valid key -> empty, an invalid key -> not full
+            const int v = key_range_validity(kvw, c * kb, min((c + 1) * kb, Skv) - 1);
+            if (!(v & 1)) kind = kTileEmpty;
+            else if (kind == kTileFull && !(v & 2)) kind = kTilePartial;
         }
-        __syncthreads();
+        col_kind[e] = (uint8_t)kind;
+        atomicAdd(&cnt[c], 1);
     }
+    __syncthreads();
     // exclusive scan of column counts, in chunks of blockDim
     int carry = ip[0];
-    for (int c0 = 0; c0 < nKb; c0 += blockDim.x) {
-        const int c = c0 + threadIdx.x;
+    for (int c0 = 0; c0 < nKb; c0 += n) {
+        const int c = c0 + t;
         const int v = c < nKb ? cnt[c] : 0;
         int tot;
         const int ex = block_exclusive_sum(v, &tot, scan);
@@ -553,18 +641,36 @@ __global__ __launch_bounds__(256) void bsr_prepare_kernel(const int32_t* indptr,
         carry += tot;
         __syncthreads();
     }
-    if (threadIdx.x == 0) cp[nKb] = carry;
+    if (t == 0) cp[nKb] = carry;
     __syncthreads();
-    for (int r = 0; r < nQb; ++r) {
-        const int e0 = max(ip[r], 0), e1 = (int)min((int64_t)ip[r + 1], nnz);
-        for (int e = e0 + threadIdx.x; e < e1; e += blockDim.x) {
-            const int c = indices[e];
-            if (c < 0 || c >= nKb) continue;
-            const int dst = cnt[c];
-            if (dst >= 0 && dst < nnz) csc_idx[dst] = r;
-            cnt[c] = dst + 1;
+    for (int e0 = e_begin; e0 < e_end; e0 += n) {
+        const int e = e0 + t;
+        int c = -1, r = 0;
+        if (e < e_end) {
+            c = indices[e];
+            if (c < 0 || c >= nKb) c = -1;
+            else r = bsr_row_of(ip, nQb, e);
         }
-        __syncthreads();
+        const bool valid = c >= 0;
+        uint64_t same = __builtin_amdgcn_ballot_w64(valid);
+        if (!valid) same = 0;
+#pragma unroll
+        for (int bit = 0; bit < kBsrColBits; ++bit) {
+            const bool on = valid && ((c >> bit) & 1);
+            const uint64_t bo = __builtin_amdgcn_ballot_w64(on);
+            same &= on ? bo : ~bo;
+        }
+        const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+        const int rank = __builtin_popcountll(same & below);
+        for (int w = 0; w < nwv; ++w) {
+            if (wv == w && valid) {
+                const int pos = cnt[c] + rank;
+                if (pos >= 0 && pos < nnz) csc_idx[pos] = r;
+                __builtin_amdgcn_wave_barrier();
+                if (rank == 0) cnt[c] += __builtin_popcountll(same);
+            }
+            __syncthreads();
+        }
     }
 }
 
@@ -908,8 +1014,7 @@ hipError_t launch_compact(const uint8_t* mask, int Nq, int Nk, int BM, uint8_t* 
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(compact_csr_kernel, dim3(nQt), dim3(256), 0, s, tile_kind, nQt, nKt, row_ptr, col_idx, col_kind);
-    return hipGetLastError();
+    return launch_csr(tile_kind, nQt, nKt, row_ptr, col_idx, col_kind, s);
 }
 
 hipError_t launch_coarsen_tiles(const uint8_t* kind64, int Nq, int Nk, uint8_t* kind128, int32_t* row_ptr,
@@ -923,8 +1028,7 @@ hipError_t launch_coarsen_tiles(const uint8_t* kind64, int Nq, int Nk, uint8_t* 
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(compact_csr_kernel, dim3(nQt), dim3(256), 0, s, kind128, nQt, nKt, row_ptr, col_idx, col_kind);
-    return hipGetLastError();
+    return launch_csr(kind128, nQt, nKt, row_ptr, col_idx, col_kind, s);
 }
 
 hipError_t launch_tile_counts(const uint8_t* kind, int64_t n, int64_t* counts, hipStream_t s) {
@@ -950,17 +1054,18 @@ hipError_t launch_predicate_tiles(const mfa_predicate& pred, int Nq, int Nk, int
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(compact_csr_kernel, dim3(nQt), dim3(256), 0, s, tile_kind, nQt, nKt, row_ptr, col_idx,
-                       col_kind);
-    return hipGetLastError();
+    return launch_csr(tile_kind, nQt, nKt, row_ptr, col_idx, col_kind, s);
 }
 
 hipError_t launch_bsr_prepare(const int32_t* indptr, const int32_t* indices, int B, int Hkv, int nQb, int nKb,
                               int64_t nnz, int qb, int kb, int Sq, int Skv, int causal, const uint32_t* kv_valid,
                               uint8_t* col_kind, int32_t* csc_ptr, int32_t* csc_idx, hipStream_t s) {
-    const size_t lds = (size_t)(nKb + 256) * sizeof(int);
-    hipLaunchKernelGGL(bsr_prepare_kernel, dim3(B * Hkv), dim3(256), lds, s, indptr, indices, nQb, nKb, nnz, qb, kb, Sq, Skv,
-                       causal, kv_valid, Hkv, col_kind, csc_ptr, csc_idx);
+    const size_t lds = (size_t)(nKb + 1024) * sizeof(int);  // at most 68 KB (nKb <= 16384)
+    hipError_t e = hipFuncSetAttribute((const void*)&bsr_prepare_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bsr_prepare_kernel, dim3(B * Hkv), dim3(1024), lds, s, indptr, indices, nQb, nKb, nnz, qb, kb, Sq,
+                       Skv, causal, kv_valid, Hkv, col_kind, csc_ptr, csc_idx);
     return hipGetLastError();
 }
 

@@ -67,9 +67,9 @@ def test_blockid_tile_summary_bit_exact(case):
         assert np.array_equal(_np(got[2]).view(np.uint32), ref[2])
 
 
-def _check_compaction(m):
-    ref = M.compact_dense_mask(m, 128, 64)
-    got = mfa.compact_dense_mask(to_dev(m))
+def _check_compaction(m, BM=128):
+    ref = M.compact_dense_mask(m, BM, 64)
+    got = mfa.compact_dense_mask(to_dev(m), BM=BM)
     torch.cuda.synchronize()
     nnz = int(ref["row_ptr"][-1])
     assert np.array_equal(_np(got["tile_kind"]), ref["tile_kind"])
@@ -80,7 +80,7 @@ def _check_compaction(m):
 
 
 @pytest.mark.parametrize("case", ["causal8192", "random_vec", "random_ragged", "all_true", "all_false",
-                                  "one_col", "one_row", "tall"])
+                                  "one_col", "one_row", "tall", "rows65536"])
 def test_compact_dense_mask_bit_exact(case):
     note(f"compaction {case}")
     rng = np.random.default_rng(11)
@@ -98,8 +98,13 @@ def test_compact_dense_mask_bit_exact(case):
         m = rng.random((200, 1)) < 0.5
     elif case == "one_row":
         m = rng.random((1, 4096)) < 0.5
-    else:
+    elif case == "tall":
         m = rng.random((2000, 48)) < 0.9
+    else:
+        # 65,536 query rows (512 tile rows x 16 key tiles): the CSR takes the
+        # linear count / scan / fill path
+        m = W.random_dense_mask(65536, 1024, 0.02, seed=3)
+        _check_compaction(m, BM=64)
     _check_compaction(m)
 
 
@@ -114,21 +119,37 @@ def test_compact_nonbool_bytes_count_as_true():
     assert np.array_equal(_np(got["tile_kind"]), ref["tile_kind"])
 
 
-@pytest.mark.parametrize("case", ["cfg5", "small_ragged"])
+@pytest.mark.parametrize("case", ["cfg5", "small_ragged", "wide_rows", "many_kv_blocks"])
 def test_bsr_prepare_bit_exact(case):
     note(f"bsr prepare {case}")
+    causal = True
     if case == "cfg5":
         w = W.bsr_random(D=8)
-        N, blk = 16384, 64
-    else:
+        Sq = Skv = 16384
+    elif case == "small_ragged":
         w = W.bsr_random(B=2, N=1000, H=3, D=8, block=64, frac_den=3, seed=9)
-        N, blk = 1000, 64
+        Sq = Skv = 1000
+    elif case == "wide_rows":
+        # every earlier block listed: up to 64 entries per row, columns shared by many rows
+        w = W.bsr_random(B=1, N=4096, H=2, D=8, block=64, frac_den=1, seed=10)
+        Sq = Skv = 4096
+    else:
+        # 8 query-block rows over 16,384 key blocks (the most the column pass holds), non-causal
+        rng = np.random.default_rng(11)
+        B, H, nq, nk = 1, 2, 8, 16384
+        rows = [np.sort(rng.choice(nk, int(rng.integers(0, 400)), replace=False)) for _ in range(B * H * nq)]
+        counts = np.array([len(r) for r in rows])
+        indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        w = {"indptr": np.stack([indptr[i * nq:(i + 1) * nq + 1] for i in range(B * H)]).reshape(B, H, nq + 1),
+             "indices": np.concatenate(rows).astype(np.int32)}
+        Sq, Skv, causal = nq * 64, nk * 64, False
+    blk = 64
     ip, ix = w["indptr"], w["indices"]
-    nb = -(-N // blk)
+    nb = -(-Skv // blk)
     assert mfa.bsr_validate(to_dev(ip), to_dev(ix), nb) == M.bsr_validate(ip, ix, nb)
-    kind, cp, ci = mfa.bsr_prepare(to_dev(ip), to_dev(ix), blk, blk, N, N, True)
+    kind, cp, ci = mfa.bsr_prepare(to_dev(ip), to_dev(ix), blk, blk, Sq, Skv, causal)
     torch.cuda.synchronize()
-    assert np.array_equal(_np(kind), M.bsr_col_kind(ip, ix, blk, blk, N, N, True))
+    assert np.array_equal(_np(kind), M.bsr_col_kind(ip, ix, blk, blk, Sq, Skv, causal))
     rp, ri = M.bsr_to_csc(ip, ix, nb)
     assert np.array_equal(_np(cp), rp)
     assert np.array_equal(_np(ci), ri)
