@@ -63,8 +63,9 @@ def _mask_heads(allowed, Hq):
 
 
 def alibi(slopes):
-    """score_mod adding slope[h] * (kv_idx - q_idx); slopes of 1 give the
-    omni_attention intro's example, score - (q_idx - kv_idx)."""
+    """score_mod adding slope[h] * (kv_idx - q_idx): a linear penalty on the
+    distance of earlier keys; a slope of 1 on every head is the
+    distance-decay example of the omni_attention intro."""
     sl = np.asarray(slopes, dtype=np.float64)
 
     def mod(score, b, h, q_idx, kv_idx):

@@ -489,13 +489,18 @@ def varlen_schedule(lengths_q, lengths_k, BM, BN, causal, left, right):
 # ---------------------------------------------------------------------------
 
 def causal(b, h, q_idx, kv_idx):
-    return q_idx >= kv_idx
+    """Key at or before the query: the causal window with both sides open."""
+    return window_allows(q_idx, kv_idx, True, -1, -1)
 
 
 def past_window(w):
-    """Predicate 'q_idx - kv_idx < w' (each query sees at most w past keys)."""
+    """Keys less than w positions back from the query (w of them including
+    the query's own position); keys after the query are not restricted here,
+    so it is combined with ``causal`` for a causal sliding window."""
     def pred(b, h, q_idx, kv_idx):
-        return q_idx - kv_idx < w
+        if w <= 0:  # the key must then lie at least 1 - w positions after the query
+            return np.asarray(kv_idx) - np.asarray(q_idx) >= 1 - w
+        return window_allows(q_idx, kv_idx, False, w - 1, -1)
     return pred
 
 
