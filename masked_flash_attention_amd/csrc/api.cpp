@@ -4,9 +4,11 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cfloat>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -53,24 +55,70 @@ mfa_status fail(mfa_status s, const char* fmt, ...) {
 
 mfa_status ok() { return MFA_OK; }
 
+// Launch log: with MFA_LOG set (and not "0") in the environment, every
+// launching call prints its kernel variant and grid to stderr.
+bool log_enabled() {
+    static const bool on = [] {
+        const char* v = std::getenv("MFA_LOG");
+        return v && *v && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+void log_launch(const char* fmt, ...) {
+    if (!log_enabled()) return;
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    std::fprintf(stderr, "[mfa] %s\n", buf);
+}
+
+const char* kind_name(int k) {
+    switch (k) {
+        case MFA_MASK_NONE: return "none";
+        case MFA_MASK_BLOCKID: return "blockid";
+        case MFA_MASK_TILES: return "tiles";
+        case MFA_MASK_BSR: return "bsr";
+        case MFA_MASK_VARLEN: return "varlen";
+    }
+    return "?";
+}
+
 #define MFA_TRY(expr)                      \
     do {                                   \
         mfa_status _s = (expr);            \
         if (_s != MFA_OK) return _s;       \
     } while (0)
 
+// Per-device result of the architecture check (0 unknown, 1 gfx950, 2 other),
+// so that each call costs one hipGetDevice after the first.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
 mfa_status ensure_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        int n = 0;
+        hipError_t e = hipGetDeviceCount(&n);
+        (void)hipGetLastError();
+        return fail(MFA_E_NO_DEVICE, "no HIP device available (%s)", hipGetErrorString(e));
+    }
+    const int cached = dev < kMaxDevices ? g_arch_ok[dev].load(std::memory_order_relaxed) : 0;
+    if (cached == 1) return ok();
     int n = 0;
     hipError_t e = hipGetDeviceCount(&n);
     if (e != hipSuccess || n == 0) {
         (void)hipGetLastError();
         return fail(MFA_E_NO_DEVICE, "no HIP device available (%s)", hipGetErrorString(e));
     }
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return fail(MFA_E_NO_DEVICE, "hipGetDevice failed");
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(MFA_E_NO_DEVICE, "hipGetDeviceProperties failed");
-    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    const bool good = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices) g_arch_ok[dev].store(good ? 1 : 2, std::memory_order_relaxed);
+    if (!good)
         return fail(MFA_E_NO_DEVICE, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
     return ok();
 }
@@ -183,6 +231,7 @@ mfa_status mfa_compact_dense_mask(const uint8_t* mask, int Nq, int Nk, int BM, i
         MFA_TRY(dev_ptr(col_idx, "col_idx"));
         MFA_TRY(dev_ptr(col_kind, "col_kind"));
     }
+    log_launch("compact_dense_mask Nq=%d Nk=%d BM=%d BN=%d", Nq, Nk, BM, BN);
     return hip_ok(launch_compact(mask, Nq, Nk, BM, tile_kind, fine_bits, row_ptr, col_idx, col_kind, stream),
                   "compaction launch");
 }
@@ -320,6 +369,8 @@ mfa_status mfa_bsr_prepare(const int32_t* indptr, const int32_t* indices, int B,
         MFA_TRY(dev_ptr(col_kind, "col_kind"));
         MFA_TRY(dev_ptr(csc_idx, "csc_idx"));
     }
+    log_launch("bsr_prepare B=%d Hkv=%d nQb=%d nKb=%d nnz=%lld causal=%d kv_valid=%d", B, Hkv, nQb, nKb,
+               (long long)nnz, causal ? 1 : 0, kv_valid_bits != nullptr);
     return hip_ok(launch_bsr_prepare(indptr, indices, B, Hkv, nQb, nKb, nnz, q_block, kv_block, Sq, Skv, causal ? 1 : 0,
                                      kv_valid_bits, col_kind, csc_ptr, csc_idx, stream),
                   "bsr prepare launch");
@@ -355,6 +406,8 @@ mfa_status mfa_varlen_schedule(const int32_t* len_q, const int32_t* len_k, int n
         MFA_TRY(dev_ptr(len_k, "len_k"));
     }
     if (work_cap > 0) MFA_TRY(dev_ptr(work, "work"));
+    log_launch("varlen_schedule nseq=%d work_cap=%d causal=%d window=(%d, %d)", nseq, work_cap, causal ? 1 : 0,
+               win_left, win_right);
     return hip_ok(launch_varlen_schedule(len_q, len_k, nseq, BM, BN, causal ? 1 : 0, win_left, win_right, cu_q, cu_k,
                                          max_len, work, work_cap, n_work, stream),
                   "varlen schedule launch");
@@ -545,6 +598,9 @@ mfa_status mfa_attn_fwd(const mfa_attn_args* a, const mfa_mask* mk, float scale,
     }
     if (p.total == 0) return ok();
     p.xcd_remap = (a->dtype == MFA_BF16) && (p.total % 8 == 0) ? 1 : 0;
+    log_launch("attn_fwd %s D=%d mask=%s BM=%d grid=%d x %d threads xcd_remap=%d bias=%d", a->dtype == MFA_BF16 ? "bf16"
+               : "f32", a->D, kind_name(mk->kind), BM, p.total, a->dtype == MFA_BF16 ? BM / 32 * 64 : BM, p.xcd_remap,
+               a->alibi_slopes != nullptr);
     return hip_ok(launch_attn_fwd(a->dtype, a->D, BM, p, m, stream), "attention forward launch");
 }
 
@@ -683,6 +739,9 @@ mfa_status mfa_attn_bwd_dkdv(const mfa_attn_bwd_args* a, const mfa_mask* mk, flo
     MFA_TRY(dev_ptr(a->dv, "dv"));
     MFA_TRY(check_strides("dk", a->dk, a->dk_stride, a->fwd.dtype));
     MFA_TRY(check_strides("dv", a->dv, a->dv_stride, a->fwd.dtype));
+    log_launch("attn_bwd_dkdv %s D=%d mask=%s B=%d Hkv=%d Sk=%d (64-key blocks) bias=%d",
+               a->fwd.dtype == MFA_BF16 ? "bf16" : "f32", a->fwd.D, kind_name(mk->kind), a->fwd.B, a->fwd.Hkv,
+               a->fwd.Sk, a->fwd.alibi_slopes != nullptr);
     return hip_ok(launch_bwd_dkdv(p, m, a->fwd.D, a->fwd.dtype, stream), "backward dK/dV launch");
 }
 
@@ -694,6 +753,8 @@ mfa_status mfa_attn_bwd_dq(const mfa_attn_bwd_args* a, const mfa_mask* mk, float
     if (a->fwd.B == 0 || a->fwd.Sq == 0) return ok();
     MFA_TRY(dev_ptr(a->dq, "dq"));
     MFA_TRY(check_strides("dq", a->dq, a->dq_stride, a->fwd.dtype));
+    log_launch("attn_bwd_dq %s D=%d mask=%s BM=%d grid=%d bias=%d", a->fwd.dtype == MFA_BF16 ? "bf16" : "f32",
+               a->fwd.D, kind_name(mk->kind), BM, p.f.total, a->fwd.alibi_slopes != nullptr);
     return hip_ok(launch_bwd_dq(p, m, a->fwd.D, a->fwd.dtype, BM, stream), "backward dQ launch");
 }
 

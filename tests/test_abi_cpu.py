@@ -222,3 +222,41 @@ def test_tile_height_model_and_choice(lib):
     t2 = (C.c_int64 * 3)(0, 10, 21)
     assert lib.mfa_model_tile_time(t2, 1000, 128) > lib.mfa_model_tile_time(t, 1000, 128) > 0
     assert lib.mfa_choose_tile_m(None, None, 10) == 128
+
+
+def test_host_code_under_sanitizers(tmp_path):
+    """The C ABI's host code (api.cpp) built with AddressSanitizer and
+    UndefinedBehaviorSanitizer on its host side only, linked with the
+    kernels' objects and driven by tests/c_abi/mfa_host_checks.cpp (every
+    entry point with NULL pointers, bad shapes and enums, non-finite scales;
+    the dispatch model; per-thread error messages). Any sanitizer report or
+    failed check makes the driver exit non-zero."""
+    from masked_flash_attention_amd import build as B
+    objs = [os.path.join(B.BUILD, f) for f in ("maskrep.o", "attn_fwd.o", "attn_bwd.o")]
+    if not all(os.path.exists(o) for o in objs):
+        B.build(verbose=False)
+    hipcc = B.hipcc()
+    clangxx = os.path.join(os.path.dirname(os.path.realpath(hipcc)), "..", "lib", "llvm", "bin", "clang++")
+    if not os.path.exists(clangxx):
+        clangxx = "/opt/rocm/llvm/bin/clang++"
+    api_o, drv_o, exe = tmp_path / "api_san.o", tmp_path / "driver.o", tmp_path / "host_checks"
+    san_host = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                "-Xarch_host", "-fno-sanitize-recover=undefined"]
+    steps = [
+        [hipcc] + B.COMMON + ["-g", "-O1"] + san_host +
+        ["-x", "hip", "-c", os.path.join(B.CSRC, "api.cpp"), "-o", str(api_o)],
+        [clangxx, "-std=c++17", "-g", "-O1", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+         "-I", "/opt/rocm/include", "-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=undefined",
+         "-c", os.path.join(ROOT, "tests", "c_abi", "mfa_host_checks.cpp"), "-o", str(drv_o)],
+        [hipcc, "--offload-arch=gfx950", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+         str(drv_o), str(api_o)] + objs + ["-o", str(exe)],
+    ]
+    for cmd in steps:
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, f"{' '.join(cmd)}\n{r.stderr[-2000:]}"
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:verify_asan_link_order=0:abort_on_error=0",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1", HIP_VISIBLE_DEVICES="")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "host checks passed" in r.stdout
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr

@@ -23,8 +23,12 @@ def test_c_only_client_matches_oracle(tmp_path):
     note("C ABI client")
     assert os.path.exists(DEMO), "tests/c_abi/mfa_c_demo is not built (run __graft_entry__.build())"
     out_file = tmp_path / "out.bin"
-    r = subprocess.run([DEMO, str(out_file)], capture_output=True, text=True, timeout=120)
+    env = dict(os.environ, MFA_LOG="1")
+    r = subprocess.run([DEMO, str(out_file)], capture_output=True, text=True, timeout=120, env=env)
     assert r.returncode == 0, f"C client failed ({r.returncode}): {r.stdout} {r.stderr}"
+    # MFA_LOG: each launching call names its kernel variant and grid
+    assert "[mfa] compact_dense_mask Nq=300 Nk=300 BM=128 BN=64" in r.stderr, r.stderr
+    assert "[mfa] attn_fwd bf16 D=128 mask=tiles BM=128 grid=6 x 256 threads" in r.stderr, r.stderr
     N, H, D = 300, 2, 128
     n = N * H * D
     raw = np.fromfile(out_file, dtype=np.uint8)
