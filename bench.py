@@ -288,7 +288,7 @@ def dispatch_section(dev):
             counts[bm] = mfa.tile_counts(c["tile_kind"]).cpu().tolist()
             rep = mfa.MaskRep.tiles(c)
             row[f"fwd_ms_tile{bm}"] = round(_time(lambda: mfa.attn_fwd(q, k, v, rep, D ** -0.5, "bhsd", out=o)), 4)
-        row["choice"] = mfa.choose_tile_m(counts[64], counts[128], N)
+        row["choice"] = mfa.choose_tile_m(counts[64], counts[128], N, D)
         row["faster"] = 64 if row["fwd_ms_tile64"] < row["fwd_ms_tile128"] else 128
         res[name] = row
         del m, c64, c128

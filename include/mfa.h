@@ -165,15 +165,16 @@ typedef struct mfa_predicate {
  * mfa_tile_counts: counts[0..2] (device int64) = empty, partial and full
  *   tiles among the n kinds of a tile map. Asynchronous.
  * mfa_model_tile_time / mfa_choose_tile_m (host only, no device calls): the
- *   modelled forward time of a map with those counts (setup per query tile
- *   plus a cost per partial and per full tile, measured on MI355X), and the
- *   tile height (64 or 128) with the smaller one. */
+ *   modelled forward time of a map with those counts at head dim D (64 or
+ *   128; setup per query tile plus a cost per partial and per full tile,
+ *   fitted to MI355X forward times), and the tile height to use: 64 only
+ *   when its modelled time is at least 5% below the 128-row one. */
 mfa_status mfa_tile_map_coarsen(const uint8_t* kind64, int Nq, int Nk, uint8_t* kind128,
                                 int32_t* row_ptr, int32_t* col_idx, uint8_t* col_kind,
                                 hipStream_t stream);
 mfa_status mfa_tile_counts(const uint8_t* tile_kind, int64_t n, int64_t* counts, hipStream_t stream);
-double mfa_model_tile_time(const int64_t counts[3], int Nq, int tile_m);
-int mfa_choose_tile_m(const int64_t counts64[3], const int64_t counts128[3], int Nq);
+double mfa_model_tile_time(const int64_t counts[3], int Nq, int tile_m, int D);
+int mfa_choose_tile_m(const int64_t counts64[3], const int64_t counts128[3], int Nq, int D);
 
 /* The tile representation of a predicate mask over an (Nq, Nk) grid: the
  * same outputs, layout and meaning as mfa_compact_dense_mask (BM = 128,

@@ -263,25 +263,27 @@ def coarsen_tile_map(compacted64, Nq, Nk):
     return out
 
 
-def choose_tile_m(counts64, counts128, Nq):
-    """Tile height (64 or 128) with the smaller modelled forward time (mfa_choose_tile_m, host only)."""
+def choose_tile_m(counts64, counts128, Nq, head_dim=128):
+    """Tile height (64 or 128) for a mask with these tile counts at this head
+    dim (mfa_choose_tile_m, host only)."""
     a = (C.c_int64 * 3)(*[int(x) for x in counts64])
     b = (C.c_int64 * 3)(*[int(x) for x in counts128])
-    return int(_lib().mfa_choose_tile_m(a, b, int(Nq)))
+    return int(_lib().mfa_choose_tile_m(a, b, int(Nq), int(head_dim)))
 
 
-def compact_dense_mask_auto(mask):
+def compact_dense_mask_auto(mask, head_dim=128):
     """Density-aware dispatch (BinFlash, "Efficiently Dispatching ..."): one
     pass over the mask at 64-row tiles, the 128-row map derived from it, the
     tile statistics of both read back (one sync), and the compaction whose
-    modelled forward time is smaller returned (with "tile_m" and "counts")."""
+    modelled forward time at this head dim is smaller returned (with
+    "tile_m" and "counts")."""
     m = _u8(mask).contiguous()
     Nq, Nk = m.shape
     c64 = compact_dense_mask(m, BM=64)
     c128 = coarsen_tile_map(c64, Nq, Nk)
     n64 = tile_counts(c64["tile_kind"]).cpu().tolist()
     n128 = tile_counts(c128["tile_kind"]).cpu().tolist()
-    bm = choose_tile_m(n64, n128, Nq)
+    bm = choose_tile_m(n64, n128, Nq, head_dim)
     out = c64 if bm == 64 else c128
     out["counts"] = {64: n64, 128: n128}
     return out

@@ -68,8 +68,8 @@ SIGNATURES = {
     "mfa_compact_dense_mask": ([vp, C.c_int, C.c_int, C.c_int, C.c_int, vp, vp, vp, vp, vp, vp], C.c_int),
     "mfa_tile_map_coarsen": ([vp, C.c_int, C.c_int, vp, vp, vp, vp, vp], C.c_int),
     "mfa_tile_counts": ([vp, C.c_int64, vp, vp], C.c_int),
-    "mfa_model_tile_time": ([C.POINTER(C.c_int64), C.c_int, C.c_int], C.c_double),
-    "mfa_choose_tile_m": ([C.POINTER(C.c_int64), C.POINTER(C.c_int64), C.c_int], C.c_int),
+    "mfa_model_tile_time": ([C.POINTER(C.c_int64), C.c_int, C.c_int, C.c_int], C.c_double),
+    "mfa_choose_tile_m": ([C.POINTER(C.c_int64), C.POINTER(C.c_int64), C.c_int, C.c_int], C.c_int),
     "mfa_predicate_tiles": ([C.POINTER(Predicate), C.c_int, C.c_int, vp, vp, vp, vp, vp, vp], C.c_int),
     "mfa_bsr_validate": ([vp, vp, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64, C.POINTER(C.c_int), vp], C.c_int),
     "mfa_bsr_prepare": ([vp, vp, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int, C.c_int, C.c_int,

@@ -261,28 +261,33 @@ mfa_status mfa_tile_counts(const uint8_t* tile_kind, int64_t n, int64_t* counts,
 
 // Modelled forward time of a tile map, in units of one full 128 x 64 tile:
 // setup per query tile plus a cost per partial and per full tile, for each
-// tile height. Least-squares fit (relative error) of MI355X forward times at
-// D = 128, B = 4, H = 32, N = 8192 over six masks (all-True, all-False, a
-// 50 %-dense random mask whose tiles are all partial, causal, causal
-// documents of 32-200 tokens, a 96-wide band); the fit is within 7 % of every
-// measured time. A 64-row tile costs 0.74 (full) to 0.83 (partial) of a
-// 128-row one, so 64-row tiles pay off only when many 128-row tiles are
-// half empty.
-static const double kTileCost[2][3] = {
+// head dim and tile height. Least-squares fit (relative error) of MI355X
+// forward times at B = 4, H = 32, N = 4096 and 8192, per head dim, over
+// eight masks (all-True, all-False, a 50 %-dense random mask whose tiles are
+// all partial, causal, causal documents of 32-200 tokens, a 96-wide band,
+// 10 % of 64 x 64 blocks, 30 % of 128 x 128 blocks); the fit is within 18 %
+// of every measured time. A 64-row tile costs 0.63-0.66 (full) to
+// 0.84 (partial) of a full 128-row one, so 64-row tiles pay off only when
+// many 128-row tiles are half empty; near ties keep 128 rows, and on those
+// sixteen cases per head dim the choice is never more than 6 % slower than
+// the faster height.
+static const double kTileCost[2][2][3] = {
     // setup per query tile, partial tile, full tile
-    {2.52, 0.760, 0.623},  // 64-row tiles (32-key steps)
-    {4.37, 1.145, 1.000},  // 128-row tiles
+    {{1.807, 0.844, 0.633}, {3.475, 1.320, 1.000}},  // D = 64: 64-row, 128-row tiles
+    {{2.196, 0.835, 0.663}, {4.287, 1.236, 1.000}},  // D = 128
 };
 
-double mfa_model_tile_time(const int64_t counts[3], int Nq, int tile_m) {
-    const int i = tile_m == 64 ? 0 : 1;
+double mfa_model_tile_time(const int64_t counts[3], int Nq, int tile_m, int D) {
+    if (!counts || Nq < 0) return 0.0;
+    const int d = D == 64 ? 0 : 1, h = tile_m == 64 ? 0 : 1;
     const int64_t rows = tile_m == 64 ? cdiv(Nq, 64) : cdiv(Nq, 128);
-    return kTileCost[i][0] * (double)rows + kTileCost[i][1] * (double)counts[1] + kTileCost[i][2] * (double)counts[2];
+    return kTileCost[d][h][0] * (double)rows + kTileCost[d][h][1] * (double)counts[1] +
+           kTileCost[d][h][2] * (double)counts[2];
 }
 
-int mfa_choose_tile_m(const int64_t counts64[3], const int64_t counts128[3], int Nq) {
+int mfa_choose_tile_m(const int64_t counts64[3], const int64_t counts128[3], int Nq, int D) {
     if (!counts64 || !counts128 || Nq < 0) return 128;
-    return mfa_model_tile_time(counts64, Nq, 64) < mfa_model_tile_time(counts128, Nq, 128) ? 64 : 128;
+    return mfa_model_tile_time(counts64, Nq, 64, D) < 0.95 * mfa_model_tile_time(counts128, Nq, 128, D) ? 64 : 128;
 }
 
 mfa_status mfa_predicate_tiles(const mfa_predicate* pred, int Nq, int Nk, uint8_t* tile_kind, uint32_t* fine_bits,

@@ -151,13 +151,16 @@ static void mask_representation_validation() {
 
 static void dispatch_model() {
     const int64_t causal64[3] = {8128, 128, 8128}, causal128[3] = {4032, 128, 4032};
-    EXPECT(mfa_choose_tile_m(causal64, causal128, 8192) == 128);
     const int64_t blk64[3] = {15384, 0, 1000}, blk128[3] = {7192, 1000, 0};
-    EXPECT(mfa_choose_tile_m(blk64, blk128, 8192) == 64);
-    EXPECT(mfa_choose_tile_m(nullptr, causal128, 8192) == 128);
+    for (int D : {64, 128}) {
+        EXPECT(mfa_choose_tile_m(causal64, causal128, 8192, D) == 128);
+        EXPECT(mfa_choose_tile_m(blk64, blk128, 8192, D) == 64);
+        EXPECT(mfa_choose_tile_m(nullptr, causal128, 8192, D) == 128);
+    }
     const int64_t zero[3] = {0, 0, 0};
-    EXPECT(mfa_model_tile_time(zero, 0, 128) == 0.0);
-    EXPECT(mfa_model_tile_time(causal128, 8192, 128) > mfa_model_tile_time(zero, 8192, 128));
+    EXPECT(mfa_model_tile_time(zero, 0, 128, 128) == 0.0);
+    EXPECT(mfa_model_tile_time(nullptr, 10, 128, 128) == 0.0);
+    EXPECT(mfa_model_tile_time(causal128, 8192, 128, 64) > mfa_model_tile_time(zero, 8192, 128, 64));
 }
 
 static void names_and_thread_local_errors() {

@@ -215,13 +215,19 @@ def test_tile_height_model_and_choice(lib):
     a map whose 128-row tiles are all half empty (64 x 64 blocks) picks 64."""
     import masked_flash_attention_amd as mfa
     causal64, causal128 = (8128, 128, 8128), (4032, 128, 4032)
-    assert mfa.choose_tile_m(causal64, causal128, 8192) == 128
     blocks64, blocks128 = (15384, 0, 1000), (7192, 1000, 0)
-    assert mfa.choose_tile_m(blocks64, blocks128, 8192) == 64
+    for D in (64, 128):
+        assert mfa.choose_tile_m(causal64, causal128, 8192, D) == 128
+        assert mfa.choose_tile_m(blocks64, blocks128, 8192, D) == 64
     t = (C.c_int64 * 3)(0, 10, 20)
     t2 = (C.c_int64 * 3)(0, 10, 21)
-    assert lib.mfa_model_tile_time(t2, 1000, 128) > lib.mfa_model_tile_time(t, 1000, 128) > 0
-    assert lib.mfa_choose_tile_m(None, None, 10) == 128
+    assert lib.mfa_model_tile_time(t2, 1000, 128, 128) > lib.mfa_model_tile_time(t, 1000, 128, 128) > 0
+    assert lib.mfa_choose_tile_m(None, None, 10, 128) == 128
+    # near ties keep 128-row tiles: 64 only with a modelled gain of 5 % or more
+    # (at D = 128 a full 64-row tile models as 0.663 of a full 128-row one)
+    c128 = (0, 0, 100)
+    assert mfa.choose_tile_m((0, 0, 148), c128, 0, 128) == 128   # 2 % below
+    assert mfa.choose_tile_m((0, 0, 140), c128, 0, 128) == 64    # 7 % below
 
 
 def test_host_code_under_sanitizers(tmp_path):
