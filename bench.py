@@ -66,30 +66,48 @@ def read_traffic(bytes_algo_per_launch):
 
 
 def cpu_baseline(w, tile_flops_per_bh, seconds):
-    """Time the fp64 oracle on whole (batch, head) slices until `seconds` pass."""
+    """Time the fp64 oracle on whole (batch, head) slices until `seconds` pass:
+    a thread pool over the slices, one worker per host CPU (at most 16), each
+    slice's NumPy/BLAS work on one thread, so `cores` is the threads used."""
+    import concurrent.futures as cf
     from oracle import attention as A
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+        from threadpoolctl import threadpool_limits
     except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+        threadpool_limits = None
+    host_cpus = os.cpu_count() or 1
+    workers = max(1, min(16, host_cpus))
     mask = w["mask"][None, None]
-    done = 0
-    t0 = time.perf_counter()
     pairs = [(b, h) for b in range(w["q"].shape[0]) for h in range(w["q"].shape[1])]
-    for b, h in pairs:
+
+    def one(bh):
+        b, h = bh
         q = w["q"][b:b + 1, h:h + 1].double().numpy().transpose(0, 2, 1, 3)
         k = w["k"][b:b + 1, h:h + 1].double().numpy().transpose(0, 2, 1, 3)
         v = w["v"][b:b + 1, h:h + 1].double().numpy().transpose(0, 2, 1, 3)
-        A.attention_fwd(q, k, v, mask, w["scale"], chunk=2048)
-        done += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(tile_flops_per_bh * done / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{done} of {len(pairs)} (batch, head) slices, all 8192 query rows each, fp64 NumPy "
-                      f"dense masked softmax ({dt:.1f} s); attended-tile FLOPs of the sample over that time"}
+        A.attention_fwd(q, k, v, mask, w["scale"], chunk=1024)
+
+    import contextlib
+    limit = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+    done = 0
+    with limit, cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        t0 = time.perf_counter()
+        it = iter(pairs)
+        running = {ex.submit(one, p) for p in [next(it) for _ in range(min(workers, len(pairs)))]}
+        while running:
+            fin, running = cf.wait(running, return_when=cf.FIRST_COMPLETED)
+            done += len(fin)
+            if time.perf_counter() - t0 < seconds:
+                for _ in fin:
+                    nxt = next(it, None)
+                    if nxt is not None:
+                        running.add(ex.submit(one, nxt))
+        dt = time.perf_counter() - t0
+    return {"value": round(tile_flops_per_bh * done / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(workers),
+            "kind": "oracle", "host_cpus": int(host_cpus), "threads": int(workers), "blas_threads_per_worker": 1,
+            "sample": f"{done} of {len(pairs)} (batch, head) slices, all 8192 query rows each, fp64 NumPy dense "
+                      f"masked softmax on a pool of {workers} threads (host reports {host_cpus} CPUs), "
+                      f"{dt:.1f} s; attended-tile FLOPs of the sample over that time"}
 
 
 def _time(fn, reps=10, warm=2):
