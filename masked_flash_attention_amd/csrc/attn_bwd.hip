@@ -351,6 +351,10 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
     char* sO = smem + 2 * TILEB;                       // [2][64 x D] dO
     float* sL = (float*)(smem + 4 * TILEB);            // [2][64] -LSE * log2(e)
     float* sDl = sL + 128;                             // [2][64] delta
+    // query-side mask data of a partial block, staged with its Q / dO:
+    int32_t* sQb = (int32_t*)(sDl + 128);              // [2][64] query block ids (block-id masks)
+    uint32_t* sQv = (uint32_t*)(sQb + 128);            // [2][2] query validity bits (block-id masks)
+    uint32_t* sFb = sQv + 4;                           // [2][2][64] fine-mask words per 32-key half (dense tiles)
 
     const FwdDev& f = p.f;
     const int lane = threadIdx.x & 63;
@@ -427,8 +431,19 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
         const int64_t lrow = ((int64_t)b * f.Hq + hq) * f.Sq;
         if (wave == 1) stage_vec64(p.delta + lrow, r0, rend, dd_, lane);
     };
+    // Block-id masks: the 64 query block ids of a partial block, by wave 1
+    // into LDS with the block's Q / dO (rows past the end read as 0; their
+    // validity bit is 0).
+    auto stage_qblk = [&](uint32_t ent_, int32_t* dst) {
+        if constexpr (KIND == MFA_MASK_BLOCKID) {
+            if (wave == 1 && (int)(ent_ >> 28) == kTilePartial)
+                stage_vec64((const float*)(m.q_blk + (int64_t)b * f.Sq), (int)(ent_ & 0x0FFFFFFFu) * 64, q_len,
+                            (float*)dst, lane);
+        }
+    };
     auto stage = [&](int g_, uint32_t ent_, int buf) {
         stage_to(g_, ent_, sQ + buf * TILEB, sO + buf * TILEB, sDl + buf * 64);
+        stage_qblk(ent_, sQb + buf * 64);
     };
     // Wave 0 loads the LSE of the staged rows into a register and stores it
     // to LDS, as the exponent offset in log2 units, at the end of the step
@@ -443,10 +458,37 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
         // -lse*log2(e); -inf for empty rows (and rows past the end) so that P = 0 there
         sL[buf * 64 + lane] = lse == -INFINITY ? -INFINITY : -lse * kLog2e;
     };
+    // Row-side mask values of a partial block, row = this lane, loaded into
+    // registers with the block's staging and stored to LDS at the end of the
+    // step: the validity of the row (block ids, wave 0) and this wave's fine
+    // word of the row (dense tiles: wave w's keys are word 2*kbk + w).
+    auto side_fetch = [&](uint32_t ent_) -> uint32_t {
+        uint32_t v = 0u;
+        if ((int)(ent_ >> 28) != kTilePartial) return v;
+        const int i = (int)(ent_ & 0x0FFFFFFFu) * 64 + lane;  // query index within the batch entry
+        if constexpr (KIND == MFA_MASK_BLOCKID) {
+            if (wave == 0 && i < q_len) v = m.q_valid[(int64_t)b * f.Sq + i] != 0;
+        } else if constexpr (KIND == MFA_MASK_TILES) {
+            const int wd = 2 * kbk + wave;
+            if (i < q_len && wd < m.fine_words) v = m.fine_bits[(int64_t)i * m.fine_words + wd];
+        }
+        return v;
+    };
+    auto side_store = [&](uint32_t v, int buf) {
+        if constexpr (KIND == MFA_MASK_BLOCKID) {
+            if (wave == 0) {
+                const uint64_t vm = __builtin_amdgcn_ballot_w64(v != 0u);
+                if (lane < 2) sQv[buf * 2 + lane] = (uint32_t)(lane ? vm >> 32 : vm);
+            }
+        } else if constexpr (KIND == MFA_MASK_TILES) {
+            sFb[buf * 128 + wave * 64 + lane] = v;
+        }
+    };
 
     if (have) {
         stage(g, ent, 0);
         if (wave == 0) lse_store(lse_fetch(g, ent), 0);
+        side_store(side_fetch(ent), 0);
     }
     vm_wait();
     __syncthreads();
@@ -458,6 +500,12 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
         uint32_t ent_n = 0;
         const bool have_n = next_step(g_n, pos_n, ent_n);
         float lse_n = 0.f;
+        uint32_t side_n = 0u;
+        const int32_t* qbs = sQb + buf * 64;    // this block's staged query-side mask data
+        const uint32_t* fbs = sFb + buf * 128 + wave * 64;
+        const uint64_t qvm = KIND == MFA_MASK_BLOCKID
+                                 ? ((uint64_t)sQv[buf * 2 + 1] << 32) | sQv[buf * 2]
+                                 : 0ull;
         // The step works on restrict-qualified views of the two buffers: the
         // reads of this step's buffer then carry alias scopes that tell the
         // compiler they do not overlap the DMA into the other buffer, so it
@@ -488,7 +536,9 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
                 } else {
                     stage_to(g_n, ent_n, nq_, no_, nd_);
                 }
+                stage_qblk(ent_n, sQb + (buf ^ 1) * 64);
                 if (wave == 0) lse_n = lse_fetch(g_n, ent_n);
+                side_n = side_fetch(ent_n);
             }
 
             // The two 32-query halves one after the other: S = Q K^T and
@@ -559,8 +609,32 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
                     // partial blocks: disallowed scores become -inf (P = 0 there);
                     // register r is query h*32 + (r>>2)*8 + 4*hh + (r&3)
                     if (__builtin_expect(kind == kTilePartial, 0)) {
-                        const uint32_t okb =
-                            allowed_bits_T<KIND>(f, m, b, q_len, k_len, key_l, qb * 64 + h * 32, hh, kblk, kval);
+                        uint32_t okb = 0u;
+                        if constexpr (KIND == MFA_MASK_BLOCKID) {
+                            // staged block ids and validity of the half's rows
+                            const uint32_t vw = (uint32_t)(qvm >> (h * 32));
+                            uint32_t cmp = 0u, vb = 0u;
+#pragma unroll
+                            for (int gq = 0; gq < 4; ++gq) {
+                                const i32x4 q4 = *(const i32x4*)(qbs + h * 32 + gq * 8 + 4 * hh);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) cmp |= (kblk <= q4[e] ? 1u : 0u) << (gq * 4 + e);
+                                vb |= ((vw >> (gq * 8 + 4 * hh)) & 0xFu) << (gq * 4);
+                            }
+                            okb = kval ? (cmp & vb) : 0u;
+                        } else if constexpr (KIND == MFA_MASK_TILES) {
+                            // staged fine words of the half's rows, bit c = this lane's key
+                            uint32_t bits = 0u;
+#pragma unroll
+                            for (int gq = 0; gq < 4; ++gq) {
+                                const u32x4 w4 = *(const u32x4*)(fbs + h * 32 + gq * 8 + 4 * hh);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) bits |= ((w4[e] >> c) & 1u) << (gq * 4 + e);
+                            }
+                            okb = key_ok ? bits : 0u;
+                        } else {
+                            okb = allowed_bits_T<KIND>(f, m, b, q_len, k_len, key_l, qb * 64 + h * 32, hh, kblk, kval);
+                        }
 #pragma unroll
                         for (int rr = 0; rr < 16; ++rr)
                             if (!((okb >> rr) & 1u)) s[rr] = -INFINITY;
@@ -583,6 +657,7 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
         body(sQ + buf * TILEB, sO + buf * TILEB, sL + buf * 64, sDl + buf * 64, sQ + (buf ^ 1) * TILEB,
              sO + (buf ^ 1) * TILEB, sDl + (buf ^ 1) * 64);
         if (wave == 0 && have_n) lse_store(lse_n, buf ^ 1);
+        if (have_n) side_store(side_n, buf ^ 1);
         vm_wait();
         __syncthreads();
         buf ^= 1;
@@ -626,6 +701,7 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || (NW != 2 && KIND != MFA_MASK_
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* sK = smem;                 // [2][64 x D]
     char* sV = smem + 2 * TILEB;     // [2][64 x D]
+    int32_t* sKB = (int32_t*)(smem + 4 * TILEB);  // [2][BN] key block ids (block-id masks)
 
     const FwdDev& f = p.f;
     const int lane = threadIdx.x & 63;
@@ -673,21 +749,19 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || (NW != 2 && KIND != MFA_MASK_
     TileCursor<KIND, BM, BN> cursor;
     cursor.init(f, m, t, lane);
     auto fine_words = [&](int kt_, int kind_, uint32_t (&w)[2]) {
-        w[0] = w[1] = 0u;
-        if constexpr (KIND == MFA_MASK_TILES) {
-            if (rm.row_ok && (kind_ == kTilePartial || (kt_ + 1) * BN > t.k_len)) {
-                const uint32_t* fb = m.fine_bits + (int64_t)row * m.fine_words + NH * kt_;
-                // the row holds fine_words words; a tile's words past them are 0
-                if (NH * kt_ < m.fine_words) w[0] = fb[0];
-                if (NH == 2 && 2 * kt_ + 1 < m.fine_words) w[1] = fb[1];
-            }
-        }
+        tile_mask_words<KIND, NH>(m, t, rm, row, kt_, kind_, w);
     };
-    auto stage_to = [&](int kt_, char* dk_, char* dv_) {
+    auto stage_to = [&](int kt_, char* dk_, char* dv_, int32_t* dkb_) {
         stage_tile<D, BN>(kbase, 2 * f.ks1, kt_ * BN, t.k_len, dk_, wave, NW, lane);
         stage_tile<D, BN>(vbase, 2 * f.vs1, kt_ * BN, t.k_len, dv_, wave, NW, lane);
+        // block-id masks: the tile's key block ids (keys past k_len read as
+        // 0; the mask's range bits clear them)
+        if constexpr (KIND == MFA_MASK_BLOCKID) {
+            static_assert(BN == 64, "block-id masks walk 64-key tiles");
+            if (wave == 0) stage_vec64((const float*)(m.k_blk + (int64_t)t.b * f.Sk), kt_ * BN, t.k_len, (float*)dkb_, lane);
+        }
     };
-    auto stage = [&](int kt_, int buf) { stage_to(kt_, sK + buf * TILEB, sV + buf * TILEB); };
+    auto stage = [&](int kt_, int buf) { stage_to(kt_, sK + buf * TILEB, sV + buf * TILEB, sKB + buf * BN); };
 
     float sl = 0.f;  // bias slope in raw score units
     int d_row = 0;   // 4*hh - this lane's query position (local to the sequence)
@@ -714,8 +788,8 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || (NW != 2 && KIND != MFA_MASK_
         // tile carry alias scopes that keep the compiler from making them
         // wait for the loads into the other buffer
         auto step = [&](const char* __restrict__ k_, const char* __restrict__ v_, char* __restrict__ nk_,
-                        char* __restrict__ nv_) {
-            if (has_next) stage_to(kt_n, nk_, nv_);
+                        char* __restrict__ nv_, const int32_t* __restrict__ kb_, int32_t* __restrict__ nkb_) {
+            if (has_next) stage_to(kt_n, nk_, nv_, nkb_);
             // The two 32-key halves one after the other: S^T = K Q^T and
             // dP^T = V dO^T (G1 operand groups, two MFMAs each), then dS,
             // then dQ^T += K^T dS^T over the half's two 16-key chunks (G2
@@ -768,7 +842,8 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || (NW != 2 && KIND != MFA_MASK_
                         f32x16 s2[NH];
 #pragma unroll
                         for (int x = 0; x < NH; ++x) s2[x] = x == h ? sh : f32x16{};
-                        mask_scores<KIND, NH>(f, m, t, rm, row, hh, kt, fw, s2);
+                        mask_scores<KIND, NH>(f, m, t, rm, row, hh, kt, fw, s2,
+                                              KIND == MFA_MASK_BLOCKID ? kb_ : nullptr);
                         sh = s2[h];
                     }
                     // register r is key kt*64 + h*32 + (r>>2)*8 + 4*hh + (r&3)
@@ -781,7 +856,8 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || (NW != 2 && KIND != MFA_MASK_
                 }
             }
         };
-        step(sK + buf * TILEB, sV + buf * TILEB, sK + (buf ^ 1) * TILEB, sV + (buf ^ 1) * TILEB);
+        step(sK + buf * TILEB, sV + buf * TILEB, sK + (buf ^ 1) * TILEB, sV + (buf ^ 1) * TILEB, sKB + buf * BN,
+             sKB + (buf ^ 1) * BN);
         vm_wait();
         __syncthreads();
         buf ^= 1;
@@ -972,7 +1048,8 @@ hipError_t launch_bwd_preprocess(const BwdDev& p, int D, int dtype, hipStream_t 
 
 template <int D, int KIND, bool BIAS>
 static hipError_t dkdv_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) {
-    const size_t lds = 4 * 64 * 2 * D + 4 * 64 * sizeof(float);
+    // Q / dO double buffers, LSE and delta, query block ids, validity bits, fine words
+    const size_t lds = 4 * 64 * 2 * D + 4 * 64 * sizeof(float) + 2 * 64 * 4 + 16 + 2 * 2 * 64 * 4;
     hipError_t e = hipFuncSetAttribute((const void*)&bwd_dkdv_kernel<D, KIND, BIAS>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -993,8 +1070,12 @@ template <int D, int NW, int KIND, bool BIAS>
 static hipError_t dq_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) {
     // 64-row query tiles walk 32-key tiles, as in the forward
     constexpr int BN = (NW == 2 && (KIND == MFA_MASK_BSR || KIND == MFA_MASK_TILES)) ? 32 : kBN;
-    const size_t lds = 4 * (size_t)BN * 2 * D;
+    // K / V double buffers, and the key block ids of block-id masks
+    const size_t lds = 4 * (size_t)BN * 2 * D + (KIND == MFA_MASK_BLOCKID ? 2 * BN * sizeof(int32_t) : 0);
     if (p.f.total == 0) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute((const void*)&bwd_dq_kernel<D, NW, KIND, BIAS, BN>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_kernel<D, NW, KIND, BIAS, BN>), dim3(p.f.total), dim3(NW * 64), lds, s, p, m);
     return hipGetLastError();
 }

@@ -224,20 +224,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
     cursor.init(p, m, t, lane);
     auto advance = [&](int& it, int& kt, int& kind) { cursor.seek(p, m, t, lane, it, kt, kind); };
 
-    // Dense-tile masks: the two fine-bit words of this lane's row for a
-    // partial (or ragged) tile, loaded one tile ahead together with that
-    // tile's K/V, so that the mask never waits on a load of its own.
+    // The mask words of a partial (or ragged) tile, loaded one tile ahead
+    // together with that tile's K/V.
     auto fine_words = [&](int kt_, int kind_, uint32_t (&w)[2]) {
-        w[0] = w[1] = 0u;
-        if constexpr (KIND == MFA_MASK_TILES) {
-            if (__builtin_expect(rm.row_ok && (kind_ == kTilePartial || (kt_ + 1) * BN > t.k_len), 0)) {
-                constexpr int NW32 = BN / 32;  // fine words per tile
-                const uint32_t* fb = m.fine_bits + (int64_t)row * m.fine_words + NW32 * kt_;
-                // the row holds fine_words words; a tile's words past them are 0
-                if (NW32 * kt_ < m.fine_words) w[0] = fb[0];
-                if (NW32 == 2 && 2 * kt_ + 1 < m.fine_words) w[1] = fb[1];
-            }
-        }
+        tile_mask_words<KIND, NB>(m, t, rm, row, kt_, kind_, w);
     };
 
     int it = t.begin, kt = 0, kind = 0;

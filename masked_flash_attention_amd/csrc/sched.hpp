@@ -337,10 +337,38 @@ __device__ __forceinline__ uint32_t below(int n) {
     return n <= 0 ? 0u : (n >= 32 ? 0xFFFFFFFFu : ((1u << n) - 1u));
 }
 
+// The 32-bit mask words a partial (or ragged) key tile kt of NB 32-key
+// blocks needs, loaded one tile ahead with the tile's K/V so that the mask
+// never waits on a load of its own: the row's fine bits (dense-mask tiles),
+// or the tile's key validity bits (block ids; BSR with kv_valid_bits, all
+// ones without). Words past the row's end read as 0.
+template <int KIND, int NB>
+__device__ __forceinline__ void tile_mask_words(const MaskDev& m, const TileRange& t, const RowMask<KIND>& rm,
+                                                int row, int kt, int kind, uint32_t (&w)[2]) {
+    w[0] = w[1] = 0u;
+    if (!(kind == kTilePartial || (kt + 1) * (NB * 32) > t.k_len)) return;
+    if constexpr (KIND == MFA_MASK_TILES) {
+        if (rm.row_ok) {
+            const uint32_t* fb = m.fine_bits + (int64_t)row * m.fine_words + NB * kt;
+            if (NB * kt < m.fine_words) w[0] = fb[0];
+            if (NB == 2 && NB * kt + 1 < m.fine_words) w[1] = fb[1];
+        }
+    } else if constexpr (KIND == MFA_MASK_BLOCKID || KIND == MFA_MASK_BSR) {
+        if (KIND == MFA_MASK_BSR && !m.kv_bits) {
+            w[0] = w[1] = 0xFFFFFFFFu;
+        } else {
+            const uint32_t* kw = m.kv_bits + (int64_t)t.b * m.kv_words + NB * kt;
+            if (NB * kt < m.kv_words) w[0] = kw[0];
+            if (NB == 2 && NB * kt + 1 < m.kv_words) w[1] = kw[1];
+        }
+    }
+}
+
 // Sets the scores of disallowed keys of key tile kt to -inf. Register r of
 // s[kb] holds key kb*32 + (r>>2)*8 + 4*hh + (r&3) of the tile (query = this
 // lane's row); okw[kb] collects, at bit (r>>2)*8 + (r&3), whether that key is
-// allowed. fw: the row's two fine-bit words of the tile (dense-tile masks).
+// allowed. fw: the tile's mask words from tile_mask_words (the row's fine
+// bits for dense-tile masks, the key validity bits for block ids and BSR).
 // kblk: block ids of the tile's keys already staged in LDS (block-id masks;
 // entry j for key kt*NB*32 + j), or null to read them from global memory.
 template <int KIND, int NB = 2>
@@ -356,9 +384,8 @@ __device__ __forceinline__ void mask_scores(const FwdDev& p, const MaskDev& m, c
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb) okw[kb] &= fw[kb] >> (4 * hh);
     } else if constexpr (KIND == MFA_MASK_BLOCKID) {
-        const uint32_t* kw = m.kv_bits + (int64_t)t.b * m.kv_words + NB * kt;
 #pragma unroll
-        for (int kb = 0; kb < NB; ++kb) okw[kb] &= ((NB * kt + kb < m.kv_words) ? kw[kb] : 0u) >> (4 * hh);
+        for (int kb = 0; kb < NB; ++kb) okw[kb] &= fw[kb] >> (4 * hh);
         const int32_t* kbp = m.k_blk + (int64_t)t.b * p.Sk;
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb) {
@@ -382,11 +409,9 @@ __device__ __forceinline__ void mask_scores(const FwdDev& p, const MaskDev& m, c
 #pragma unroll
             for (int kb = 0; kb < NB; ++kb) okw[kb] &= below(row - base_off - kb * 32 + 1);
         }
-        if (m.kv_bits) {  // token validity (kv_valid_bits)
-            const uint32_t* kw = m.kv_bits + (int64_t)t.b * m.kv_words + NB * kt;
+        // token validity (kv_valid_bits; all ones without)
 #pragma unroll
-            for (int kb = 0; kb < NB; ++kb) okw[kb] &= ((NB * kt + kb < m.kv_words) ? kw[kb] : 0u) >> (4 * hh);
-        }
+        for (int kb = 0; kb < NB; ++kb) okw[kb] &= fw[kb] >> (4 * hh);
     } else if constexpr (KIND == MFA_MASK_VARLEN) {
         const int i = rm.qi_local;
 #pragma unroll
