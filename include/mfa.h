@@ -421,6 +421,8 @@ typedef struct mfa_attn_bwd_args {
     int64_t dq_stride[3];
     int64_t dk_stride[3];
     int64_t dv_stride[3];
+    void* workspace;         /* optional device scratch of the dK/dV pass (below); may be NULL */
+    int64_t workspace_bytes; /* its size in bytes */
 } mfa_attn_bwd_args;
 
 mfa_status mfa_attn_bwd_preprocess(const mfa_attn_bwd_args* args, hipStream_t stream);
@@ -428,6 +430,33 @@ mfa_status mfa_attn_bwd_dkdv(const mfa_attn_bwd_args* args, const mfa_mask* mask
                              hipStream_t stream);
 mfa_status mfa_attn_bwd_dq(const mfa_attn_bwd_args* args, const mfa_mask* mask, float scale,
                            hipStream_t stream);
+
+/* Query-head split of the dK/dV pass. dK and dV of a key block sum over the
+ * query rows of every query head of its GQA group (Hq / Hkv heads). When the
+ * key blocks alone (B * Hkv * ceil(Sk / 64)) give the device too few
+ * workgroups, the pass splits the group's heads over S workgroups per key
+ * block; they write fp32 partial sums, and a reduce pass adds the S sums in
+ * order (so the result does not depend on scheduling) and writes dk / dv.
+ * The sums take S * 2 * B * Sk * Hkv * D * 4 bytes of device memory, which
+ * the caller passes as args->workspace / workspace_bytes (16-byte aligned,
+ * device memory on the current device, owned by the caller, not to be used
+ * by anything else until the pass has run on the stream). With less
+ * workspace (or NULL) the pass takes the largest split that fits, down to
+ * S = 1, which needs none. bf16 only: the fp32 test mode and VARLEN masks
+ * never split.
+ * mfa_attn_bwd_dkdv_workspace: *bytes = the workspace of the preferred
+ * split on the current device, *splits = that split (1: none; bytes 0).
+ * Validation errors as for mfa_attn_bwd_dkdv; MFA_E_NO_DEVICE without a
+ * gfx950 device. */
+mfa_status mfa_attn_bwd_dkdv_workspace(const mfa_attn_bwd_args* args, const mfa_mask* mask, int64_t* bytes,
+                                       int* splits);
+
+/* The split model (host only, no device needed): the smallest divisor S > 1
+ * of group with key_blocks * S >= 2 * n_cu * W, where W = 2 workgroups per
+ * CU at head_dim 128 and 4 at 64 (the dK/dV workgroups a CU holds at once),
+ * or group when none reaches it; 1 when group <= 1, key_blocks <= 0, or
+ * key_blocks alone reaches it. */
+int mfa_choose_dkdv_split(int64_t key_blocks, int group, int head_dim, int n_cu);
 
 #ifdef __cplusplus
 }

@@ -527,7 +527,27 @@ def attn_bwd_preprocess(args):
     _ffi.check(_lib().mfa_attn_bwd_preprocess(C.byref(args), _stream()))
 
 
-def attn_bwd_dkdv(args, mask: MaskRep, scale):
+def attn_bwd_dkdv_workspace(args, mask: MaskRep):
+    """(bytes, splits): workspace of the dK/dV pass's preferred query-head
+    split on the current device (mfa_attn_bwd_dkdv_workspace)."""
+    m = mask.to_c()
+    nb, ns = C.c_int64(0), C.c_int(0)
+    _ffi.check(_lib().mfa_attn_bwd_dkdv_workspace(C.byref(args), C.byref(m), C.byref(nb), C.byref(ns)))
+    return int(nb.value), int(ns.value)
+
+
+def choose_dkdv_split(key_blocks, group, head_dim, n_cu):
+    """Query-head split of the dK/dV pass (mfa_choose_dkdv_split, host only)."""
+    return int(_lib().mfa_choose_dkdv_split(int(key_blocks), int(group), int(head_dim), int(n_cu)))
+
+
+def attn_bwd_dkdv(args, mask: MaskRep, scale, workspace=None):
+    """dK/dV pass. workspace: a device uint8 tensor for the query-head split
+    (attn_bwd_dkdv_workspace gives its size), or None for no split."""
+    if workspace is not None:
+        args.workspace, args.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    else:
+        args.workspace, args.workspace_bytes = None, 0
     m = mask.to_c()
     _ffi.check(_lib().mfa_attn_bwd_dkdv(C.byref(args), C.byref(m), float(scale), _stream()))
 
@@ -553,7 +573,9 @@ def attn_bwd(q, k, v, out, lse, dout, mask: MaskRep, scale=None, layout="bshd", 
         delta = torch.empty(B, Hq, Sq, dtype=torch.float32, device=q.device)
     a = _bwd_args(q, k, v, out, lse, dout, dq, dk, dv, delta, layout, alibi_slopes)
     attn_bwd_preprocess(a)
-    attn_bwd_dkdv(a, mask, scale)
+    nbytes, _ = attn_bwd_dkdv_workspace(a, mask)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+    attn_bwd_dkdv(a, mask, scale, workspace=ws)
     attn_bwd_dq(a, mask, scale)
     return dq, dk, dv
 

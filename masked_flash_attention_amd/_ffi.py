@@ -41,7 +41,8 @@ class Mask(C.Structure):
 
 class BwdArgs(C.Structure):
     _fields_ = [("fwd", AttnArgs), ("dout", vp), ("dq", vp), ("dk", vp), ("dv", vp), ("delta", vp),
-                ("do_stride", i64x3), ("dq_stride", i64x3), ("dk_stride", i64x3), ("dv_stride", i64x3)]
+                ("do_stride", i64x3), ("dq_stride", i64x3), ("dk_stride", i64x3), ("dv_stride", i64x3),
+                ("workspace", vp), ("workspace_bytes", C.c_int64)]
 
 
 PRED_MAX_TERMS = 4
@@ -81,6 +82,9 @@ SIGNATURES = {
     "mfa_attn_bwd_preprocess": ([C.POINTER(BwdArgs), vp], C.c_int),
     "mfa_attn_bwd_dkdv": ([C.POINTER(BwdArgs), C.POINTER(Mask), C.c_float, vp], C.c_int),
     "mfa_attn_bwd_dq": ([C.POINTER(BwdArgs), C.POINTER(Mask), C.c_float, vp], C.c_int),
+    "mfa_attn_bwd_dkdv_workspace": ([C.POINTER(BwdArgs), C.POINTER(Mask), C.POINTER(C.c_int64),
+                                     C.POINTER(C.c_int)], C.c_int),
+    "mfa_choose_dkdv_split": ([C.c_int64, C.c_int, C.c_int, C.c_int], C.c_int),
 }
 
 _lib = None

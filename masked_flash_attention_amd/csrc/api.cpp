@@ -147,6 +147,42 @@ mfa_status hip_ok(hipError_t e, const char* what) {
 
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+int device_cus();
+
+// Heaviest-first order over a run of (batch, head) pairs (FwdDev::lpt_group)
+// when the grid is at most four workgroups per slot of the device (slots:
+// two resident 128-row workgroups per CU, four 64-row ones): with so few
+// rounds, a heavy tile that starts last sets the end of the launch. Each
+// XCD's share of the logical ids (total / 8 with the XCD remap) is one run,
+// so every XCD gets the same mix of levels and its heads stay in its L2.
+// Larger grids keep the (batch, head)-major order, whose working set per XCD
+// is one or two heads.
+int lpt_group_for(const FwdDev& p, int BM) {
+    if (p.nQt <= 1 || p.total <= 0) return 0;
+    const int slots = device_cus() * (BM >= 128 ? 2 : 4);
+    if (slots <= 0 || p.total > 4 * slots) return 0;
+    const int chunk = p.xcd_remap ? p.total / 8 : p.total;
+    if (chunk % p.nQt != 0) return 0;
+    return chunk / p.nQt;
+}
+
+// Compute units of the current device (cached per device).
+std::atomic<int> g_n_cu[kMaxDevices];
+
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    const int cached = dev < kMaxDevices ? g_n_cu[dev].load(std::memory_order_relaxed) : 0;
+    if (cached > 0) return cached;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    if (dev < kMaxDevices) g_n_cu[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
@@ -603,9 +639,10 @@ mfa_status mfa_attn_fwd(const mfa_attn_args* a, const mfa_mask* mk, float scale,
     }
     if (p.total == 0) return ok();
     p.xcd_remap = (a->dtype == MFA_BF16) && (p.total % 8 == 0) ? 1 : 0;
-    log_launch("attn_fwd %s D=%d mask=%s BM=%d grid=%d x %d threads xcd_remap=%d bias=%d", a->dtype == MFA_BF16 ? "bf16"
-               : "f32", a->D, kind_name(mk->kind), BM, p.total, a->dtype == MFA_BF16 ? BM / 32 * 64 : BM, p.xcd_remap,
-               a->alibi_slopes != nullptr);
+    if (mk->kind != MFA_MASK_VARLEN) p.lpt_group = lpt_group_for(p, BM);
+    log_launch("attn_fwd %s D=%d mask=%s BM=%d grid=%d x %d threads xcd_remap=%d lpt_group=%d bias=%d",
+               a->dtype == MFA_BF16 ? "bf16" : "f32", a->D, kind_name(mk->kind), BM, p.total,
+               a->dtype == MFA_BF16 ? BM / 32 * 64 : BM, p.xcd_remap, p.lpt_group, a->alibi_slopes != nullptr);
     return hip_ok(launch_attn_fwd(a->dtype, a->D, BM, p, m, stream), "attention forward launch");
 }
 
@@ -731,6 +768,41 @@ static mfa_status bwd_common(const mfa_attn_bwd_args* a, const mfa_mask* mk, flo
         p.f.total = a->fwd.B * a->fwd.Hq * p.f.nQt;
     }
     p.f.xcd_remap = (p.f.total % 8 == 0) ? 1 : 0;
+    if (mk->kind != MFA_MASK_VARLEN && !dkdv) p.f.lpt_group = lpt_group_for(p.f, BM);
+    return ok();
+}
+
+int mfa_choose_dkdv_split(int64_t key_blocks, int group, int head_dim, int n_cu) {
+    if (group <= 1 || key_blocks <= 0 || n_cu <= 0) return 1;
+    const int64_t target = 2 * (int64_t)n_cu * (head_dim == 128 ? 2 : 4);
+    if (key_blocks >= target) return 1;
+    for (int s = 2; s < group; ++s)
+        if (group % s == 0 && key_blocks * s >= target) return s;
+    return group;
+}
+
+// Preferred head split of the dK/dV pass and the workspace bytes per split.
+static void dkdv_split(const mfa_attn_bwd_args* a, const mfa_mask* mk, int& splits, int64_t& per_split) {
+    splits = 1;
+    per_split = 2 * (int64_t)a->fwd.B * a->fwd.Sk * a->fwd.Hkv * a->fwd.D * (int64_t)sizeof(float);
+    if (a->fwd.dtype != MFA_BF16 || mk->kind == MFA_MASK_VARLEN || a->fwd.B == 0 || a->fwd.Sq == 0 ||
+        a->fwd.Sk == 0)
+        return;
+    const int64_t key_blocks = (int64_t)a->fwd.B * a->fwd.Hkv * cdiv(a->fwd.Sk, 64);
+    splits = mfa_choose_dkdv_split(key_blocks, a->fwd.Hq / a->fwd.Hkv, a->fwd.D, device_cus());
+}
+
+mfa_status mfa_attn_bwd_dkdv_workspace(const mfa_attn_bwd_args* a, const mfa_mask* mk, int64_t* bytes,
+                                       int* splits) {
+    if (!bytes || !splits) return fail(MFA_E_ARG, "bytes / splits is NULL");
+    MFA_TRY(check_bwd(a, false));
+    if (!mk) return fail(MFA_E_ARG, "mask is NULL");
+    MFA_TRY(ensure_device());
+    int S = 1;
+    int64_t per = 0;
+    dkdv_split(a, mk, S, per);
+    *splits = S;
+    *bytes = S > 1 ? S * per : 0;
     return ok();
 }
 
@@ -744,9 +816,24 @@ mfa_status mfa_attn_bwd_dkdv(const mfa_attn_bwd_args* a, const mfa_mask* mk, flo
     MFA_TRY(dev_ptr(a->dv, "dv"));
     MFA_TRY(check_strides("dk", a->dk, a->dk_stride, a->fwd.dtype));
     MFA_TRY(check_strides("dv", a->dv, a->dv_stride, a->fwd.dtype));
-    log_launch("attn_bwd_dkdv %s D=%d mask=%s B=%d Hkv=%d Sk=%d (64-key blocks) bias=%d",
+    // the largest split up to the preferred one whose sums fit the workspace
+    int pref = 1, S = 1;
+    int64_t per = 0;
+    dkdv_split(a, mk, pref, per);
+    const int G = a->fwd.Hq / a->fwd.Hkv;
+    if (pref > 1 && a->workspace) {
+        for (int s = pref; s > 1 && S == 1; --s)
+            if (G % s == 0 && s * per <= a->workspace_bytes) S = s;
+        if (S > 1) {
+            MFA_TRY(dev_ptr(a->workspace, "workspace"));
+            if (!aligned16(a->workspace)) return fail(MFA_E_ARG, "workspace must be 16-byte aligned");
+        }
+    }
+    p.gsplit = S;
+    p.ws = S > 1 ? (float*)a->workspace : nullptr;
+    log_launch("attn_bwd_dkdv %s D=%d mask=%s B=%d Hkv=%d Sk=%d (64-key blocks) head_split=%d bias=%d",
                a->fwd.dtype == MFA_BF16 ? "bf16" : "f32", a->fwd.D, kind_name(mk->kind), a->fwd.B, a->fwd.Hkv,
-               a->fwd.Sk, a->fwd.alibi_slopes != nullptr);
+               a->fwd.Sk, S, a->fwd.alibi_slopes != nullptr);
     return hip_ok(launch_bwd_dkdv(p, m, a->fwd.D, a->fwd.dtype, stream), "backward dK/dV launch");
 }
 
@@ -758,8 +845,9 @@ mfa_status mfa_attn_bwd_dq(const mfa_attn_bwd_args* a, const mfa_mask* mk, float
     if (a->fwd.B == 0 || a->fwd.Sq == 0) return ok();
     MFA_TRY(dev_ptr(a->dq, "dq"));
     MFA_TRY(check_strides("dq", a->dq, a->dq_stride, a->fwd.dtype));
-    log_launch("attn_bwd_dq %s D=%d mask=%s BM=%d grid=%d bias=%d", a->fwd.dtype == MFA_BF16 ? "bf16" : "f32",
-               a->fwd.D, kind_name(mk->kind), BM, p.f.total, a->fwd.alibi_slopes != nullptr);
+    log_launch("attn_bwd_dq %s D=%d mask=%s BM=%d grid=%d lpt_group=%d bias=%d",
+               a->fwd.dtype == MFA_BF16 ? "bf16" : "f32", a->fwd.D, kind_name(mk->kind), BM, p.f.total,
+               p.f.lpt_group, a->fwd.alibi_slopes != nullptr);
     return hip_ok(launch_bwd_dq(p, m, a->fwd.D, a->fwd.dtype, BM, stream), "backward dQ launch");
 }
 

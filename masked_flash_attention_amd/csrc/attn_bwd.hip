@@ -214,6 +214,8 @@ struct KeyBlock {
     int k_alloc;        // keys whose gradient rows are written (k_len of them attended)
     bool len_error;     // varlen: sequence longer than the stated max_q / max_k
     bool active;        // false: the block lies past its sequence's keys
+    int split;          // query-head split of the block (0 without one)
+    int g0, g1;         // the split's query heads within the GQA group: [g0, g1)
 };
 
 template <int KIND>
@@ -230,6 +232,9 @@ __device__ __forceinline__ KeyBlock key_block(const BwdDev& p, const MaskDev& m,
     kb.k_alloc = f.Sk;
     kb.len_error = false;
     kb.active = true;
+    kb.split = 0;
+    kb.g0 = 0;
+    kb.g1 = f.G;
     if constexpr (KIND == MFA_MASK_VARLEN) {
         const int nKbm = (m.max_k + 63) / 64;
         // plain numbering: sequences differ in length, and round-robin over
@@ -247,11 +252,16 @@ __device__ __forceinline__ KeyBlock key_block(const BwdDev& p, const MaskDev& m,
         kb.len_error = kb.q_len > m.max_q || kb.k_alloc > m.max_k;
     } else {
         const int nKb = (f.Sk + 63) / 64;
-        // consecutive key blocks of one (batch, head) on one XCD, so that
-        // they share that XCD's L2 copy of the head's Q and dO
+        // consecutive key blocks of one (batch, kv head, head split) on one
+        // XCD, so that they share that XCD's L2 copy of the heads' Q and dO
         const int wg = xcd_logical(wg_id, n_wg, remap && (n_wg & 7) == 0);
-        const int bh = wg / nKb;
-        kb.kbk = wg - bh * nKb;
+        const int bhs = wg / nKb;
+        kb.kbk = wg - bhs * nKb;
+        const int S = p.gsplit > 1 ? p.gsplit : 1;
+        const int bh = bhs / S;
+        kb.split = bhs - bh * S;
+        kb.g0 = kb.split * (f.G / S);
+        kb.g1 = kb.g0 + f.G / S;
         kb.b = bh / f.Hkv;
         kb.hk = bh - kb.b * f.Hkv;
     }
@@ -399,13 +409,14 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
     auto fetch = [&](int pos) -> uint32_t { return qbl.fetch(f, m, kblock, pos); };
     ScanWindow win;
     win.init(fetch, pbeg, lane);
-    int g = 0, pos = pbeg;
+    const int g_end = kblock.g1;
+    int g = kblock.g0, pos = pbeg;
     uint32_t ent = 0;
     bool have = win.seek(fetch, pos, pend, lane, ent);
     auto next_step = [&](int& g_, int& pos_, uint32_t& ent_) -> bool {
         ++pos_;
         if (win.seek(fetch, pos_, pend, lane, ent_)) return true;
-        if (++g_ >= f.G) return false;
+        if (++g_ >= g_end) return false;
         pos_ = pbeg;
         return win.seek(fetch, pos_, pend, lane, ent_);
     };
@@ -668,6 +679,22 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
     }
 
     if (key_l >= k_alloc) return;  // keys past the used length get zero gradients
+    if (p.gsplit > 1) {
+        // this split's sums over its query heads, fp32 and unscaled; the
+        // reduce pass adds the splits in order and writes dk / dv
+        const int64_t ri = (((int64_t)kblock.split * f.B + b) * f.Sk + key) * f.Hkv + hk;
+        float* wk = p.ws + ri * D;
+        float* wv = p.ws + ((int64_t)p.gsplit * f.B * f.Sk * f.Hkv + ri) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int o = db * 32 + gq * 8 + 4 * hh;
+                *(f32x4*)(wk + o) = f32x4{dk[db][gq * 4], dk[db][gq * 4 + 1], dk[db][gq * 4 + 2], dk[db][gq * 4 + 3]};
+                *(f32x4*)(wv + o) = f32x4{dv[db][gq * 4], dv[db][gq * 4 + 1], dv[db][gq * 4 + 2], dv[db][gq * 4 + 3]};
+            }
+        return;
+    }
     const float nanv = __builtin_nanf("");
     bf16* dkp = (bf16*)p.dk + (int64_t)b * p.dks0 + (int64_t)key * p.dks1 + (int64_t)hk * p.dks2;
     bf16* dvp = (bf16*)p.dv + (int64_t)b * p.dvs0 + (int64_t)key * p.dvs1 + (int64_t)hk * p.dvs2;
@@ -685,6 +712,53 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
             *(bf16x4*)(dvp + db * 32 + gq * 8 + 4 * hh) = wv;
         }
     }
+}
+
+// Sum of the query-head splits of the dK/dV pass: for every (batch, key,
+// kv head) row, dk = scale * sum_s wk[s] and dv = sum_s wv[s], the splits
+// added in order (the result does not depend on which split ran first).
+// Eight values of a row per thread.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdDev p) {
+    constexpr int TPR = D / 8;
+    const FwdDev& f = p.f;
+    const int64_t rows = (int64_t)f.B * f.Sk * f.Hkv;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t r = t / TPR;
+    if (r >= rows) return;
+    const int d = (int)(t - r * TPR) * 8;
+    const int hk = (int)(r % f.Hkv);
+    const int64_t bk = r / f.Hkv;
+    const int key = (int)(bk % f.Sk);
+    const int b = (int)(bk / f.Sk);
+    const int64_t sstride = rows * D;  // floats per split of one tensor
+    const float* wk = p.ws + r * D + d;
+    const float* wv = wk + (int64_t)p.gsplit * sstride;
+    f32x4 k0 = *(const f32x4*)wk, k1 = *(const f32x4*)(wk + 4);
+    f32x4 v0 = *(const f32x4*)wv, v1 = *(const f32x4*)(wv + 4);
+    for (int s = 1; s < p.gsplit; ++s) {
+        k0 += *(const f32x4*)(wk + s * sstride);
+        k1 += *(const f32x4*)(wk + s * sstride + 4);
+        v0 += *(const f32x4*)(wv + s * sstride);
+        v1 += *(const f32x4*)(wv + s * sstride + 4);
+    }
+    bf16* dkp = (bf16*)p.dk + (int64_t)b * p.dks0 + (int64_t)key * p.dks1 + (int64_t)hk * p.dks2 + d;
+    bf16* dvp = (bf16*)p.dv + (int64_t)b * p.dvs0 + (int64_t)key * p.dvs1 + (int64_t)hk * p.dvs2 + d;
+    bf16x4 a, c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        a[e] = (bf16)(k0[e] * f.scale);
+        c[e] = (bf16)v0[e];
+    }
+    *(bf16x4*)dkp = a;
+    *(bf16x4*)dvp = c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        a[e] = (bf16)(k1[e] * f.scale);
+        c[e] = (bf16)v1[e];
+    }
+    *(bf16x4*)(dkp + 4) = a;
+    *(bf16x4*)(dvp + 4) = c;
 }
 
 // ---------------------------------------------------------------------------
@@ -751,17 +825,28 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || (NW != 2 && KIND != MFA_MASK_
     auto fine_words = [&](int kt_, int kind_, uint32_t (&w)[2]) {
         tile_mask_words<KIND, NH>(m, t, rm, row, kt_, kind_, w);
     };
-    auto stage_to = [&](int kt_, char* dk_, char* dv_, int32_t* dkb_) {
+    auto stage_to = [&](int kt_, char* dk_, char* dv_) {
         stage_tile<D, BN>(kbase, 2 * f.ks1, kt_ * BN, t.k_len, dk_, wave, NW, lane);
         stage_tile<D, BN>(vbase, 2 * f.vs1, kt_ * BN, t.k_len, dv_, wave, NW, lane);
-        // block-id masks: the tile's key block ids (keys past k_len read as
-        // 0; the mask's range bits clear them)
+    };
+    auto stage = [&](int kt_, int buf) { stage_to(kt_, sK + buf * TILEB, sV + buf * TILEB); };
+    // Block-id masks: wave 0 loads the raw key block ids of a partial (or
+    // ragged) tile into a register (lane = key) with the tile's K/V, and at
+    // the end of the step stores them, folded with the key validity bits,
+    // into the tile's LDS slot.
+    auto kblk_raw = [&](int kt_, int kind_) -> int {
         if constexpr (KIND == MFA_MASK_BLOCKID) {
             static_assert(BN == 64, "block-id masks walk 64-key tiles");
-            if (wave == 0) stage_vec64((const float*)(m.k_blk + (int64_t)t.b * f.Sk), kt_ * BN, t.k_len, (float*)dkb_, lane);
+            if (wave == 0 && (kind_ == kTilePartial || (kt_ + 1) * BN > t.k_len))
+                return blockid_key_raw<BN>(f, m, t, kt_, lane);
+        }
+        return INT32_MAX;
+    };
+    auto kblk_store = [&](int kt_, int raw, const uint32_t (&w)[2], int32_t* dst) {
+        if constexpr (KIND == MFA_MASK_BLOCKID) {
+            if (wave == 0) dst[lane] = blockid_key_fold<BN>(t, kt_, raw, w, lane);
         }
     };
-    auto stage = [&](int kt_, int buf) { stage_to(kt_, sK + buf * TILEB, sV + buf * TILEB, sKB + buf * BN); };
 
     float sl = 0.f;  // bias slope in raw score units
     int d_row = 0;   // 4*hh - this lane's query position (local to the sequence)
@@ -774,7 +859,10 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || (NW != 2 && KIND != MFA_MASK_
     cursor.seek(f, m, t, lane, it, kt, kind);
     uint32_t fw[2];
     fine_words(kt, kind, fw);
-    if (it < t.end) stage(kt, 0);
+    if (it < t.end) {
+        stage(kt, 0);
+        kblk_store(kt, kblk_raw(kt, kind), fw, sKB);
+    }
     vm_wait();
     __syncthreads();
     int buf = 0;
@@ -789,7 +877,8 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || (NW != 2 && KIND != MFA_MASK_
         // wait for the loads into the other buffer
         auto step = [&](const char* __restrict__ k_, const char* __restrict__ v_, char* __restrict__ nk_,
                         char* __restrict__ nv_, const int32_t* __restrict__ kb_, int32_t* __restrict__ nkb_) {
-            if (has_next) stage_to(kt_n, nk_, nv_, nkb_);
+            if (has_next) stage_to(kt_n, nk_, nv_);
+            const int kraw_n = kblk_raw(kt_n, has_next ? kind_n : kTileEmpty);
             // The two 32-key halves one after the other: S^T = K Q^T and
             // dP^T = V dO^T (G1 operand groups, two MFMAs each), then dS,
             // then dQ^T += K^T dS^T over the half's two 16-key chunks (G2
@@ -855,6 +944,7 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || (NW != 2 && KIND != MFA_MASK_
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
+            kblk_store(kt_n, kraw_n, fw_n, nkb_);
         };
         step(sK + buf * TILEB, sV + buf * TILEB, sK + (buf ^ 1) * TILEB, sV + (buf ^ 1) * TILEB, sKB + buf * BN,
              sKB + (buf ^ 1) * BN);
@@ -1053,11 +1143,18 @@ static hipError_t dkdv_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) 
     hipError_t e = hipFuncSetAttribute((const void*)&bwd_dkdv_kernel<D, KIND, BIAS>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
+    const int S = p.gsplit > 1 ? p.gsplit : 1;
     const int64_t grid = KIND == MFA_MASK_VARLEN
                              ? (int64_t)m.nseq * p.f.Hkv * ((m.max_k + 63) / 64)
-                             : (int64_t)p.f.B * p.f.Hkv * ((p.f.Sk + 63) / 64);
+                             : (int64_t)p.f.B * p.f.Hkv * S * ((p.f.Sk + 63) / 64);
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, KIND, BIAS>), dim3((unsigned)grid), dim3(128), lds, s, p, m);
+    if (S > 1) {
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t threads = (int64_t)p.f.B * p.f.Sk * p.f.Hkv * (D / 8);
+        hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p);
+    }
     return hipGetLastError();
 }
 

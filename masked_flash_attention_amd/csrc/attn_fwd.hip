@@ -185,23 +185,23 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
         }
 #endif
     };
-    // One 256-byte load (wave 0) of the tile's key block ids into LDS; keys
-    // past k_len read as 0, and the mask's range bits clear them.
-    auto load_kblk = [&](int kt, int32_t* dst, bool live) {
-#if defined(__HIP_DEVICE_COMPILE__)
+    auto load_tile = [&](int kt, int buf, bool live) { load_tile_to(kt, sK + buf * TILEB, sV + buf * TILEB, live); };
+    // Block-id masks: wave 0 loads the raw key block ids of a partial (or
+    // ragged) tile into a register (lane = key) with the tile's K/V, and at
+    // the end of the step stores them, folded with the key validity bits,
+    // into the tile's LDS slot.
+    auto kblk_raw = [&](int kt_, int kind_) -> int {
         if constexpr (KIND == MFA_MASK_BLOCKID) {
-            if (wave == 0) {
-                const int n = live ? max(0, min(BN, t.k_len - kt * BN)) : 0;
-                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                    (void*)(m.k_blk + (int64_t)t.b * p.Sk + (int64_t)kt * BN), 0, n * 4, 0x00020000);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 4, lane * 4, 0, 0, 0);
-            }
+            static_assert(BN == 64, "block-id masks walk 64-key tiles");
+            if (wave == 0 && (kind_ == kTilePartial || (kt_ + 1) * BN > t.k_len))
+                return blockid_key_raw<BN>(p, m, t, kt_, lane);
         }
-#endif
+        return INT32_MAX;
     };
-    auto load_tile = [&](int kt, int buf, bool live) {
-        load_tile_to(kt, sK + buf * TILEB, sV + buf * TILEB, live);
-        load_kblk(kt, sKB + buf * 64, live);
+    auto kblk_store = [&](int kt_, int raw, const uint32_t (&w)[2], int32_t* dst) {
+        if constexpr (KIND == MFA_MASK_BLOCKID) {
+            if (wave == 0) dst[lane] = blockid_key_fold<BN>(t, kt_, raw, w, lane);
+        }
     };
 
     // Per-lane LDS offsets of the operand reads.
@@ -234,7 +234,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
     advance(it, kt, kind);
     uint32_t fw[2];
     fine_words(kt, kind, fw);
-    if (it < t.end) load_tile(kt, 0, true);
+    if (it < t.end) {
+        load_tile(kt, 0, true);
+        kblk_store(kt, kblk_raw(kt, kind), fw, sKB);
+    }
     wait_vmem();
     __syncthreads();
 
@@ -261,7 +264,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
         // wait for the loads into the other buffer
         auto step = [&](const char* __restrict__ ck_, const char* __restrict__ cv_, char* __restrict__ nk_,
                         char* __restrict__ nv_, const int32_t* __restrict__ ckb_, int32_t* __restrict__ nkb_) {
-            load_kblk(kt_n, nkb_, has_next);
+            const int kraw_n = kblk_raw(kt_n, kind_n);
             // The next tile's K and V loads (into buf^1, released by the last
             // barrier) are issued a few at a time between the S MFMAs below
             // rather than as one burst, which would stall the wave on the
@@ -377,6 +380,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
                     o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc2], o[db], 0, 0, 0);
                 }
             }
+            kblk_store(kt_n, kraw_n, fw_n, nkb_);
         };
         step(sK + buf * TILEB, sV + buf * TILEB, sK + (buf ^ 1) * TILEB, sV + (buf ^ 1) * TILEB, sKB + buf * 64,
              sKB + (buf ^ 1) * 64);

@@ -76,6 +76,13 @@ struct FwdDev {
     const float* alibi;  // per query head slopes of the bias slope * (kv - q), or null
     int total;        // workgroups launched
     int xcd_remap;    // 1: logical id = (w % 8) * (total / 8) + w / 8
+    // Order of the query tiles over the logical ids (dense-tile, block-id,
+    // BSR and unmasked layouts). 0: (batch, head) major, each head's tiles
+    // heaviest (last) first. lpt_group > 0: runs of lpt_group * nQt ids cover
+    // lpt_group consecutive (batch, head) pairs, level by level from the last
+    // query tile to the first, so that the heaviest tiles of the run start
+    // before any lighter one (for grids of a few workgroups per slot).
+    int lpt_group;
 };
 
 // Backward problem: the forward's tensors plus dO, dQ, dK, dV and delta.
@@ -90,6 +97,11 @@ struct BwdDev {
     int64_t dqs0, dqs1, dqs2;
     int64_t dks0, dks1, dks2;
     int64_t dvs0, dvs1, dvs2;
+    // dK/dV query-head split (GQA): gsplit workgroups per key block, each
+    // over G / gsplit query heads, writing fp32 partial sums to ws
+    // ([2][gsplit][B][Sk][Hkv][D]: dK, then dV) for the reduce pass; 1: no split
+    float* ws;
+    int gsplit;
 };
 
 __device__ __forceinline__ int xcd_logical(int w, int total, int remap) {

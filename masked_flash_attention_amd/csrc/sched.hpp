@@ -100,8 +100,17 @@ __device__ __forceinline__ TileRange make_range(const FwdDev& p, const MaskDev& 
         }
         return t;
     } else {
-        const int bh = logical / p.nQt;
-        t.qt = p.nQt - 1 - (logical - bh * p.nQt);  // heaviest (last) query tiles first
+        int bh, lvl;  // lvl: query tiles from the last one, heaviest first
+        if (p.lpt_group > 0) {
+            const int run = p.lpt_group * p.nQt;
+            const int c = logical / run, i = logical - c * run;
+            lvl = i / p.lpt_group;
+            bh = c * p.lpt_group + (i - lvl * p.lpt_group);
+        } else {
+            bh = logical / p.nQt;
+            lvl = logical - bh * p.nQt;
+        }
+        t.qt = p.nQt - 1 - lvl;
         t.b = bh / p.Hq;
         t.hq = bh - t.b * p.Hq;
         t.hk = t.hq / p.G;
@@ -364,18 +373,63 @@ __device__ __forceinline__ void tile_mask_words(const MaskDev& m, const TileRang
     }
 }
 
+// Block-id masks: the key block id that the mask of a partial (or ragged)
+// key tile compares against, for key kt*BN + lane of the tile. raw is the
+// key's k_blk entry (loaded with blockid_key_raw), w the tile's key validity
+// words (tile_mask_words): keys that are invalid or past k_len fold to
+// INT32_MAX, which no row block id below INT32_MAX reaches.
+template <int BN>
+__device__ __forceinline__ int blockid_key_raw(const FwdDev& p, const MaskDev& m, const TileRange& t, int kt,
+                                               int lane) {
+    const int j = kt * BN + lane;
+    return (lane < BN && j < t.k_len) ? m.k_blk[(int64_t)t.b * p.Sk + j] : INT32_MAX;
+}
+template <int BN>
+__device__ __forceinline__ int blockid_key_fold(const TileRange& t, int kt, int raw, const uint32_t (&w)[2],
+                                                int lane) {
+    const int j = kt * BN + lane;
+    const bool ok = lane < BN && j < t.k_len && ((w[(lane >> 5) & 1] >> (lane & 31)) & 1u);
+    return ok ? raw : INT32_MAX;
+}
+
 // Sets the scores of disallowed keys of key tile kt to -inf. Register r of
 // s[kb] holds key kb*32 + (r>>2)*8 + 4*hh + (r&3) of the tile (query = this
 // lane's row); okw[kb] collects, at bit (r>>2)*8 + (r&3), whether that key is
 // allowed. fw: the tile's mask words from tile_mask_words (the row's fine
 // bits for dense-tile masks, the key validity bits for block ids and BSR).
-// kblk: block ids of the tile's keys already staged in LDS (block-id masks;
-// entry j for key kt*NB*32 + j), or null to read them from global memory.
+// kblk: the tile's folded key block ids staged in LDS (block-id masks,
+// blockid_key_fold; entry j for key kt*NB*32 + j), or null to read the raw
+// ids and validity bits from global memory.
 template <int KIND, int NB = 2>
 __device__ __forceinline__ void mask_scores(const FwdDev& p, const MaskDev& m, const TileRange& t,
                                             const RowMask<KIND>& rm, int row, int hh, int kt,
                                             const uint32_t (&fw)[2], f32x16 (&s)[NB],
                                             const int32_t* kblk = nullptr) {
+    if constexpr (KIND == MFA_MASK_BLOCKID) {
+        // Folded ids: one compare per score (a key is allowed iff its folded id
+        // is at most the row's block id), exact unless a valid row's block id
+        // is INT32_MAX, which takes the general path below. Rows that are
+        // invalid or past the end are cleared afterwards.
+        const bool row_bad = !rm.qvalid || !rm.row_ok;
+        if (kblk && __builtin_amdgcn_ballot_w64(!row_bad && rm.qblk == INT32_MAX) == 0ull) {
+#pragma unroll
+            for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const i32x4 k4 = *(const i32x4*)(kblk + 4 * hh + kb * 32 + g * 8);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        s[kb][g * 4 + e] = k4[e] <= rm.qblk ? s[kb][g * 4 + e] : -INFINITY;
+                }
+            if (__builtin_amdgcn_ballot_w64(row_bad) != 0ull) {
+#pragma unroll
+                for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[kb][r] = row_bad ? -INFINITY : s[kb][r];
+            }
+            return;
+        }
+    }
     uint32_t okw[NB];
     const int base_off = kt * (NB * 32) + 4 * hh;  // tile key index of bit 0 of okw[0]
 #pragma unroll
@@ -392,13 +446,11 @@ __device__ __forceinline__ void mask_scores(const FwdDev& p, const MaskDev& m, c
             uint32_t cmp = 0;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                i32x4 staged = {0, 0, 0, 0};
-                if (kblk) staged = *(const i32x4*)(kblk + 4 * hh + kb * 32 + g * 8);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int key = base_off + kb * 32 + g * 8 + e;
                     // keys past k_len are cleared by okw's range bits either way
-                    const int kbk = kblk ? staged[e] : (key < t.k_len ? kbp[key] : INT32_MAX);
+                    const int kbk = key < t.k_len ? kbp[key] : INT32_MAX;
                     cmp |= (kbk <= rm.qblk ? 1u : 0u) << (g * 8 + e);
                 }
             }

@@ -106,6 +106,18 @@ static void attention_validation() {
     EXPECT(is_or_nodev(mfa_attn_bwd_dkdv(&b, &none, 0.1f, nullptr), MFA_E_ARG));
     EXPECT(is(mfa_attn_bwd_dq(&b, nullptr, 0.1f, nullptr), MFA_E_NO_DEVICE) ||
            is(mfa_attn_bwd_dq(&b, nullptr, 0.1f, nullptr), MFA_E_ARG));
+    // workspace query of the dK/dV head split
+    int64_t bytes = -1;
+    int splits = -1;
+    b.fwd = args();
+    EXPECT(is(mfa_attn_bwd_dkdv_workspace(&b, &none, nullptr, &splits), MFA_E_ARG));
+    EXPECT(is(mfa_attn_bwd_dkdv_workspace(&b, nullptr, &bytes, &splits), MFA_E_ARG));
+    EXPECT(is(mfa_attn_bwd_dkdv_workspace(nullptr, &none, &bytes, &splits), MFA_E_ARG));
+    b.fwd.Hq = 3;
+    EXPECT(is(mfa_attn_bwd_dkdv_workspace(&b, &none, &bytes, &splits), MFA_E_SHAPE));
+    b.fwd = args();
+    mfa_status st = mfa_attn_bwd_dkdv_workspace(&b, &none, &bytes, &splits);
+    EXPECT(is(st, MFA_E_NO_DEVICE) || (is(st, MFA_OK) && splits >= 1 && bytes >= 0));
 }
 
 static void mask_representation_validation() {
@@ -161,6 +173,10 @@ static void dispatch_model() {
     EXPECT(mfa_model_tile_time(zero, 0, 128, 128) == 0.0);
     EXPECT(mfa_model_tile_time(nullptr, 10, 128, 128) == 0.0);
     EXPECT(mfa_model_tile_time(causal128, 8192, 128, 64) > mfa_model_tile_time(zero, 8192, 128, 64));
+    EXPECT(mfa_choose_dkdv_split(320, 8, 128, 256) == 4);
+    EXPECT(mfa_choose_dkdv_split(320, 8, 64, 256) == 8);
+    EXPECT(mfa_choose_dkdv_split(1 << 20, 8, 128, 256) == 1);
+    EXPECT(mfa_choose_dkdv_split(-5, 8, 128, 256) == 1);
 }
 
 static void names_and_thread_local_errors() {

@@ -53,7 +53,8 @@ int main() {
          sizeof(mfa_attn_args), sizeof(mfa_mask), sizeof(mfa_attn_bwd_args));
   P(mfa_attn_args, q); P(mfa_attn_args, lse); P(mfa_attn_args, o_stride); P(mfa_attn_args, alibi_slopes);
   P(mfa_mask, tile_kind); P(mfa_mask, q_block); P(mfa_mask, cu_q); P(mfa_mask, err); P(mfa_mask, win_right); P(mfa_mask, nseq); P(mfa_mask, seqused_k); P(mfa_mask, n_pages);
-  P(mfa_attn_bwd_args, dout); P(mfa_attn_bwd_args, dv_stride);
+  P(mfa_attn_bwd_args, dout); P(mfa_attn_bwd_args, dv_stride); P(mfa_attn_bwd_args, workspace);
+  P(mfa_attn_bwd_args, workspace_bytes);
   return 0;
 }''')
     exe = tmp_path / "layout"
@@ -228,6 +229,25 @@ def test_tile_height_model_and_choice(lib):
     c128 = (0, 0, 100)
     assert mfa.choose_tile_m((0, 0, 148), c128, 0, 128) == 128   # 2 % below
     assert mfa.choose_tile_m((0, 0, 140), c128, 0, 128) == 64    # 7 % below
+
+
+def test_dkdv_head_split_model(lib):
+    """Host-only split model of the dK/dV pass: the smallest divisor S of the
+    GQA group with key_blocks * S >= 2 * CUs * (2 at D=128, 4 at D=64)."""
+    import masked_flash_attention_amd as mfa
+    cs = mfa.choose_dkdv_split
+    # block-id GQA with cross columns: 8 * 2 * 20 = 320 key blocks, G = 8, 256 CUs
+    assert cs(320, 8, 128, 256) == 4      # 1280 >= 1024; 2 would give 640
+    assert cs(320, 8, 64, 256) == 8       # target 2048: no divisor below 8 reaches it
+    assert cs(100, 6, 128, 256) == 6      # 2 and 3 fall short: the whole group
+    assert cs(1024, 8, 128, 256) == 1     # enough key blocks already
+    assert cs(1023, 3, 128, 256) == 3
+    assert cs(600, 4, 128, 256) == 2
+    assert cs(320, 1, 128, 256) == 1      # no GQA
+    assert cs(0, 8, 128, 256) == 1
+    assert cs(320, 8, 128, 0) == 1        # no device information
+    assert cs(10, 8, 128, 1) == 1         # 10 >= 4
+    assert cs(3, 8, 128, 1) == 2          # 6 >= 4
 
 
 def test_host_code_under_sanitizers(tmp_path):
