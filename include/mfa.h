@@ -451,6 +451,23 @@ mfa_status mfa_attn_bwd_dq(const mfa_attn_bwd_args* args, const mfa_mask* mask, 
 mfa_status mfa_attn_bwd_dkdv_workspace(const mfa_attn_bwd_args* args, const mfa_mask* mask, int64_t* bytes,
                                        int* splits);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the dK/dV
+ * pass of mfa_attn_bwd_dkdv with the head split's partial sums in a static
+ * device scratch array of the library (mfa_bwd_scratch_bytes(), 96 MiB, held
+ * by each device the library runs on until the process ends) instead of a
+ * workspace; args->workspace is ignored. It takes the preferred split
+ * (mfa_attn_bwd_dkdv_workspace) and fails with MFA_E_UNSUPPORTED, before
+ * any launch, when that split's sums need more than the scratch holds. It
+ * calls no allocator (the scratch's device address is looked up once per
+ * device, on the first call there). All calls on one device share the
+ * scratch: calls that overlap on one device (on different streams, or from
+ * several threads without ordering) race and give wrong gradients. The
+ * results equal mfa_attn_bwd_dkdv's with a workspace of the preferred size. */
+mfa_status mfa_attn_bwd_dkdv_noalloc(const mfa_attn_bwd_args* args, const mfa_mask* mask, float scale,
+                                     hipStream_t stream);
+int64_t mfa_bwd_scratch_bytes(void);
+
 /* The split model (host only, no device needed): the smallest divisor S > 1
  * of group with key_blocks * S >= 2 * n_cu * W, where W = 2 workgroups per
  * CU at head_dim 128 and 4 at 64 (the dK/dV workgroups a CU holds at once),

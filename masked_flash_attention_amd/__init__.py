@@ -552,6 +552,19 @@ def attn_bwd_dkdv(args, mask: MaskRep, scale, workspace=None):
     _ffi.check(_lib().mfa_attn_bwd_dkdv(C.byref(args), C.byref(m), float(scale), _stream()))
 
 
+def attn_bwd_dkdv_noalloc(args, mask: MaskRep, scale):
+    """dK/dV pass that allocates nothing (mfa_attn_bwd_dkdv_noalloc): the head
+    split's partial sums go to the library's static device scratch
+    (bwd_scratch_bytes()); calls that overlap on one device race."""
+    m = mask.to_c()
+    _ffi.check(_lib().mfa_attn_bwd_dkdv_noalloc(C.byref(args), C.byref(m), float(scale), _stream()))
+
+
+def bwd_scratch_bytes():
+    """Size of the static scratch of attn_bwd_dkdv_noalloc."""
+    return int(_lib().mfa_bwd_scratch_bytes())
+
+
 def attn_bwd_dq(args, mask: MaskRep, scale):
     m = mask.to_c()
     _ffi.check(_lib().mfa_attn_bwd_dq(C.byref(args), C.byref(m), float(scale), _stream()))

@@ -85,6 +85,8 @@ SIGNATURES = {
     "mfa_attn_bwd_dkdv_workspace": ([C.POINTER(BwdArgs), C.POINTER(Mask), C.POINTER(C.c_int64),
                                      C.POINTER(C.c_int)], C.c_int),
     "mfa_choose_dkdv_split": ([C.c_int64, C.c_int, C.c_int, C.c_int], C.c_int),
+    "mfa_attn_bwd_dkdv_noalloc": ([C.POINTER(BwdArgs), C.POINTER(Mask), C.c_float, vp], C.c_int),
+    "mfa_bwd_scratch_bytes": ([], C.c_int64),
 }
 
 _lib = None

@@ -35,6 +35,7 @@ hipError_t launch_varlen_schedule(const int32_t*, const int32_t*, int, int, int,
 hipError_t launch_bwd_preprocess(const BwdDev& p, int D, int dtype, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdDev& p, const MaskDev& m, int D, int dtype, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdDev& p, const MaskDev& m, int D, int dtype, int BM, hipStream_t s);
+hipError_t bwd_scratch(void** ptr);
 }  // namespace mfa
 
 using namespace mfa;
@@ -806,7 +807,12 @@ mfa_status mfa_attn_bwd_dkdv_workspace(const mfa_attn_bwd_args* a, const mfa_mas
     return ok();
 }
 
-mfa_status mfa_attn_bwd_dkdv(const mfa_attn_bwd_args* a, const mfa_mask* mk, float scale, hipStream_t stream) {
+// The dK/dV pass with its head-split buffer from the caller's workspace
+// (use_scratch false: the largest split up to the preferred one whose sums
+// fit) or from the library's static scratch (use_scratch true: the preferred
+// split, an error if its sums do not fit).
+static mfa_status bwd_dkdv_run(const mfa_attn_bwd_args* a, const mfa_mask* mk, float scale, hipStream_t stream,
+                               bool use_scratch) {
     BwdDev p;
     MaskDev m;
     int BM = 128;
@@ -816,26 +822,48 @@ mfa_status mfa_attn_bwd_dkdv(const mfa_attn_bwd_args* a, const mfa_mask* mk, flo
     MFA_TRY(dev_ptr(a->dv, "dv"));
     MFA_TRY(check_strides("dk", a->dk, a->dk_stride, a->fwd.dtype));
     MFA_TRY(check_strides("dv", a->dv, a->dv_stride, a->fwd.dtype));
-    // the largest split up to the preferred one whose sums fit the workspace
     int pref = 1, S = 1;
     int64_t per = 0;
     dkdv_split(a, mk, pref, per);
     const int G = a->fwd.Hq / a->fwd.Hkv;
-    if (pref > 1 && a->workspace) {
+    void* ws = nullptr;
+    if (use_scratch) {
+        if (pref > 1) {
+            if (pref * per > kBwdScratchBytes)
+                return fail(MFA_E_UNSUPPORTED,
+                            "the dK/dV head split (%d ways) needs %lld bytes of scratch; the static scratch holds "
+                            "%lld; call mfa_attn_bwd_dkdv with a workspace instead",
+                            pref, (long long)(pref * per), (long long)kBwdScratchBytes);
+            MFA_TRY(hip_ok(bwd_scratch(&ws), "static scratch lookup"));
+            S = pref;
+        }
+    } else if (pref > 1 && a->workspace) {
         for (int s = pref; s > 1 && S == 1; --s)
             if (G % s == 0 && s * per <= a->workspace_bytes) S = s;
         if (S > 1) {
             MFA_TRY(dev_ptr(a->workspace, "workspace"));
             if (!aligned16(a->workspace)) return fail(MFA_E_ARG, "workspace must be 16-byte aligned");
+            ws = a->workspace;
         }
     }
     p.gsplit = S;
-    p.ws = S > 1 ? (float*)a->workspace : nullptr;
-    log_launch("attn_bwd_dkdv %s D=%d mask=%s B=%d Hkv=%d Sk=%d (64-key blocks) head_split=%d bias=%d",
-               a->fwd.dtype == MFA_BF16 ? "bf16" : "f32", a->fwd.D, kind_name(mk->kind), a->fwd.B, a->fwd.Hkv,
-               a->fwd.Sk, S, a->fwd.alibi_slopes != nullptr);
+    p.ws = (float*)ws;
+    log_launch("attn_bwd_dkdv%s %s D=%d mask=%s B=%d Hkv=%d Sk=%d (64-key blocks) head_split=%d bias=%d",
+               use_scratch ? "_noalloc" : "", a->fwd.dtype == MFA_BF16 ? "bf16" : "f32", a->fwd.D,
+               kind_name(mk->kind), a->fwd.B, a->fwd.Hkv, a->fwd.Sk, S, a->fwd.alibi_slopes != nullptr);
     return hip_ok(launch_bwd_dkdv(p, m, a->fwd.D, a->fwd.dtype, stream), "backward dK/dV launch");
 }
+
+mfa_status mfa_attn_bwd_dkdv(const mfa_attn_bwd_args* a, const mfa_mask* mk, float scale, hipStream_t stream) {
+    return bwd_dkdv_run(a, mk, scale, stream, false);
+}
+
+mfa_status mfa_attn_bwd_dkdv_noalloc(const mfa_attn_bwd_args* a, const mfa_mask* mk, float scale,
+                                     hipStream_t stream) {
+    return bwd_dkdv_run(a, mk, scale, stream, true);
+}
+
+int64_t mfa_bwd_scratch_bytes(void) { return kBwdScratchBytes; }
 
 mfa_status mfa_attn_bwd_dq(const mfa_attn_bwd_args* a, const mfa_mask* mk, float scale, hipStream_t stream) {
     BwdDev p;

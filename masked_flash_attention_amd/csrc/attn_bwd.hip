@@ -27,6 +27,7 @@
 // few MFMA groups ahead; the dK/dV grid puts a head's key blocks on one XCD,
 // and 64-row dQ tiles walk 32-key tiles (two waves per SIMD).
 
+#include <mutex>
 #include "sched.hpp"
 
 namespace mfa {
@@ -1255,6 +1256,39 @@ static hipError_t dq_kind(const BwdDev& p, const MaskDev& m, hipStream_t s) {
         case MFA_MASK_VARLEN: return dq_launch<D, MFA_MASK_VARLEN>(p, m, s);
     }
     return hipErrorInvalidValue;
+}
+
+// Static device scratch of the no-allocation dK/dV entry point: the fp32
+// partial sums of the query-head split live here instead of in a caller
+// workspace. Each device holds its own copy from module load to process
+// exit; calls on one device share it (overlapping calls race). Every byte a
+// split reads is written by the same call's dK/dV kernel first, so nothing
+// is cleared between calls.
+static __device__ __align__(256) char scratch[kBwdScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // device address of `scratch` per device, once known
+}  // namespace
+
+// The device address of this device's scratch array (host code must pass
+// this, never the array's name, to kernels). Looked up once per device, with
+// that device current.
+hipError_t bwd_scratch(void** ptr) {
+    *ptr = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* q = nullptr;
+        e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = q;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_bwd_dkdv(const BwdDev& p, const MaskDev& m, int D, int dtype, hipStream_t s) {

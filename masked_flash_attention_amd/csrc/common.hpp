@@ -86,6 +86,12 @@ struct FwdDev {
 };
 
 // Backward problem: the forward's tensors plus dO, dQ, dK, dV and delta.
+// Size of the static device scratch of mfa_attn_bwd_dkdv_noalloc (96 MiB):
+// the dK/dV query-head split's partial sums of a GQA problem with up to
+// 12 Mi (batch, key, kv head, d) elements, e.g. B=8, Sk=1280, Hkv=2, D=128
+// split four ways (80 MiB).
+constexpr int64_t kBwdScratchBytes = int64_t(96) << 20;
+
 struct BwdDev {
     FwdDev f;
     const void* dout;
