@@ -367,8 +367,13 @@ typedef struct mfa_mask {
      *              positive multiple of 64. cu_k still gives the key lengths.
      *              A sequence needing more than max_pages pages, or whose
      *              pages include an id outside [0, n_pages), gets NaN rows
-     *              and sets *err. Forward only (the backward passes return
-     *              MFA_E_UNSUPPORTED). */
+     *              and sets *err. In the backward, dk / dv are page pools
+     *              like k / v (their strides likewise (page, row, head)):
+     *              key j's gradient rows go to the same (page, row) as its
+     *              k / v rows. Keys whose page lies past the table row or
+     *              outside the pool are not written, nor are pages no key
+     *              maps to; pages must not hold keys of two sequences
+     *              (their rows would be written twice, in no fixed order). */
     const int32_t* seqused_k;
     const int32_t* block_table;
     int max_pages;

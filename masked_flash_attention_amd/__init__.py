@@ -387,8 +387,8 @@ class MaskRep:
                page_size=None, n_pages=None):
         """Packed variable-length mask. seqused_k: optional (nseq,) int32 keys
         used per sequence. block_table (nseq, max_pages) int32 with page_size
-        and n_pages: k / v are page pools (n_pages, page_size, Hkv, D)
-        (forward only)."""
+        and n_pages: k / v are page pools (n_pages, page_size, Hkv, D), and
+        so are dk / dv in the backward."""
         t = {"cu_q": sched["cu_q"], "cu_k": sched["cu_k"], "work": sched["work"]}
         ints = {"work_cap": sched["work_cap"], "max_q": int(max_q), "max_k": int(max_k),
                 "causal": int(bool(causal)), "win_left": int(window[0]), "win_right": int(window[1]),

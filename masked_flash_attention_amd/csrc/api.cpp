@@ -715,8 +715,6 @@ static mfa_status check_bwd_mask(const mfa_attn_bwd_args* a, const mfa_mask* mk,
             }
             break;
         case MFA_MASK_VARLEN:
-            if (mk->block_table)
-                return fail(MFA_E_UNSUPPORTED, "paged k / v (block_table) is supported by the forward only");
             MFA_TRY(dev_ptr(mk->cu_q, "cu_q"));
             MFA_TRY(dev_ptr(mk->cu_k, "cu_k"));
             MFA_TRY(dev_ptr(mk->err, "err", true));

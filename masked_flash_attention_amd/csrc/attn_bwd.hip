@@ -217,7 +217,27 @@ struct KeyBlock {
     bool active;        // false: the block lies past its sequence's keys
     int split;          // query-head split of the block (0 without one)
     int g0, g1;         // the split's query heads within the GQA group: [g0, g1)
+    int seq;            // varlen sequence (-1 otherwise)
 };
+
+// Where key key_l's rows of k, v, dk, dv sit: (outer, row) indices for the
+// (stride 0, stride 1) pair of those tensors: (batch, k_base + key_l), or,
+// with a block table, (page, row in page). false: a paged key whose page is
+// past the table row or outside the pool (nothing is read or written).
+__device__ __forceinline__ bool key_rows(const MaskDev& m, const KeyBlock& kb, int key_l, int64_t& outer,
+                                         int64_t& row) {
+    if (m.block_table && kb.seq >= 0) {
+        int r = 0;
+        if (key_l / m.page_size >= m.max_pages) return false;
+        const int pg = page_of(m, kb.seq, key_l, r);
+        outer = pg;
+        row = r;
+        return pg >= 0;
+    }
+    outer = kb.b;
+    row = kb.k_base + key_l;
+    return true;
+}
 
 template <int KIND>
 __device__ __forceinline__ KeyBlock key_block(const BwdDev& p, const MaskDev& m, int wg_id, int n_wg, bool remap) {
@@ -236,6 +256,7 @@ __device__ __forceinline__ KeyBlock key_block(const BwdDev& p, const MaskDev& m,
     kb.split = 0;
     kb.g0 = 0;
     kb.g1 = f.G;
+    kb.seq = -1;
     if constexpr (KIND == MFA_MASK_VARLEN) {
         const int nKbm = (m.max_k + 63) / 64;
         // plain numbering: sequences differ in length, and round-robin over
@@ -246,11 +267,25 @@ __device__ __forceinline__ KeyBlock key_block(const BwdDev& p, const MaskDev& m,
         const int seq = sh / f.Hkv;
         kb.q_base = m.cu_q[seq];
         kb.q_len = m.cu_q[seq + 1] - kb.q_base;
+        kb.seq = seq;
         kb.k_base = m.cu_k[seq];
         kb.k_alloc = m.cu_k[seq + 1] - kb.k_base;
         kb.k_len = m.seqused_k ? min(kb.k_alloc, max(m.seqused_k[seq], 0)) : kb.k_alloc;
         if (kb.kbk * 64 >= kb.k_alloc) kb.active = false;
         kb.len_error = kb.q_len > m.max_q || kb.k_alloc > m.max_k;
+        if (m.block_table) {
+            // paged keys (as in the forward): the used keys must fit the
+            // table row, and their pages must lie in the pool
+            kb.k_base = 0;
+            const int cap = m.max_pages * m.page_size;
+            bool bad = kb.k_len > cap;
+            const int used = min(kb.k_len, cap);
+            const int32_t* tb = m.block_table + (int64_t)seq * m.max_pages;
+            for (int pi = 0; pi < (used + m.page_size - 1) / m.page_size; ++pi)
+                bad = bad || tb[pi] < 0 || tb[pi] >= m.n_pages;
+            kb.k_len = used;
+            kb.len_error = kb.len_error || bad;
+        }
     } else {
         const int nKb = (f.Sk + 63) / 64;
         // consecutive key blocks of one (batch, kv head, head split) on one
@@ -379,14 +414,15 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
     const int q_base = kblock.q_base, q_len = kblock.q_len, k_len = kblock.k_len, k_alloc = kblock.k_alloc;
     const bool len_error = kblock.len_error;
     const int key_l = kbk * 64 + wave * 32 + c;  // key within the batch entry / sequence
-    const bool key_ok = key_l < k_len;
-    const int key = kblock.k_base + key_l;       // row of k, v, dk, dv
+    int64_t ko = 0, kr = 0;                      // (batch or page, row) of k, v, dk, dv
+    const bool key_addr = key_rows(m, kblock, key_l, ko, kr);
+    const bool key_ok = key_l < k_len && key_addr;
 
     // stationary K and V fragments (B operands: K^T, V^T with lane = key)
     bf16x8 kf[NKC], vf[NKC];
     {
-        const bf16* kp = (const bf16*)f.k + (int64_t)b * f.ks0 + (int64_t)key * f.ks1 + (int64_t)hk * f.ks2 + hh * 8;
-        const bf16* vp = (const bf16*)f.v + (int64_t)b * f.vs0 + (int64_t)key * f.vs1 + (int64_t)hk * f.vs2 + hh * 8;
+        const bf16* kp = (const bf16*)f.k + ko * f.ks0 + kr * f.ks1 + (int64_t)hk * f.ks2 + hh * 8;
+        const bf16* vp = (const bf16*)f.v + ko * f.vs0 + kr * f.vs1 + (int64_t)hk * f.vs2 + hh * 8;
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
             kf[kc] = key_ok ? *(const bf16x8*)(kp + kc * 16) : bf16x8{};
@@ -679,11 +715,13 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
         ent = ent_n;
     }
 
-    if (key_l >= k_alloc) return;  // keys past the used length get zero gradients
+    // keys past the used length get zero gradients; paged keys outside the
+    // table or the pool are not written
+    if (key_l >= k_alloc || !key_addr) return;
     if (p.gsplit > 1) {
         // this split's sums over its query heads, fp32 and unscaled; the
         // reduce pass adds the splits in order and writes dk / dv
-        const int64_t ri = (((int64_t)kblock.split * f.B + b) * f.Sk + key) * f.Hkv + hk;
+        const int64_t ri = (((int64_t)kblock.split * f.B + b) * f.Sk + kr) * f.Hkv + hk;
         float* wk = p.ws + ri * D;
         float* wv = p.ws + ((int64_t)p.gsplit * f.B * f.Sk * f.Hkv + ri) * D;
 #pragma unroll
@@ -697,8 +735,8 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
         return;
     }
     const float nanv = __builtin_nanf("");
-    bf16* dkp = (bf16*)p.dk + (int64_t)b * p.dks0 + (int64_t)key * p.dks1 + (int64_t)hk * p.dks2;
-    bf16* dvp = (bf16*)p.dv + (int64_t)b * p.dvs0 + (int64_t)key * p.dvs1 + (int64_t)hk * p.dvs2;
+    bf16* dkp = (bf16*)p.dk + ko * p.dks0 + kr * p.dks1 + (int64_t)hk * p.dks2;
+    bf16* dvp = (bf16*)p.dv + ko * p.dvs0 + kr * p.dvs1 + (int64_t)hk * p.dvs2;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -827,8 +865,25 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || (NW != 2 && KIND != MFA_MASK_
         tile_mask_words<KIND, NH>(m, t, rm, row, kt_, kind_, w);
     };
     auto stage_to = [&](int kt_, char* dk_, char* dv_) {
-        stage_tile<D, BN>(kbase, 2 * f.ks1, kt_ * BN, t.k_len, dk_, wave, NW, lane);
-        stage_tile<D, BN>(vbase, 2 * f.vs1, kt_ * BN, t.k_len, dv_, wave, NW, lane);
+        const char* kb_ = kbase;
+        const char* vb_ = vbase;
+        int r0 = kt_ * BN, rend = t.k_len;
+        if constexpr (KIND == MFA_MASK_VARLEN) {
+            if (m.block_table) {
+                // paged keys: the tile lies inside one page (page_size is a
+                // multiple of 64); a bad page id reads as zeros (the
+                // sequence's rows are NaN)
+                int r = 0;
+                const int pg = page_of(m, t.seq, kt_ * BN, r);
+                const int n = pg >= 0 ? min(BN, t.k_len - kt_ * BN) : 0;
+                kb_ = (const char*)f.k + 2 * ((int64_t)max(pg, 0) * f.ks0 + (int64_t)t.hk * f.ks2);
+                vb_ = (const char*)f.v + 2 * ((int64_t)max(pg, 0) * f.vs0 + (int64_t)t.hk * f.vs2);
+                r0 = r;
+                rend = r + n;
+            }
+        }
+        stage_tile<D, BN>(kb_, 2 * f.ks1, r0, rend, dk_, wave, NW, lane);
+        stage_tile<D, BN>(vb_, 2 * f.vs1, r0, rend, dv_, wave, NW, lane);
     };
     auto stage = [&](int kt_, int buf) { stage_to(kt_, sK + buf * TILEB, sV + buf * TILEB); };
     // Block-id masks: wave 0 loads the raw key block ids of a partial (or
@@ -1007,15 +1062,16 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(BwdDev p, MaskDev m) {
     if (!kb.active) return;
     if (KIND == MFA_MASK_VARLEN && kb.len_error && m.err && threadIdx.x == 0) *m.err = 1;
     const int key_l = kb.kbk * 64 + threadIdx.x;
-    const bool key_ok = key_l < kb.k_len;
-    const int key = kb.k_base + key_l;
+    int64_t ko = 0, kr = 0;  // (batch or page, row) of k, v, dk, dv
+    const bool key_addr = key_rows(m, kb, key_l, ko, kr);
+    const bool key_ok = key_l < kb.k_len && key_addr;
     int kblk;
     bool kval;
     key_side<KIND>(f, m, kb, key_l, key_ok, kblk, kval);
     QueryBlocks<KIND> qbl;
     qbl.init(f, m, kb);
-    const float* kp = (const float*)f.k + (int64_t)kb.b * f.ks0 + (int64_t)key * f.ks1 + (int64_t)kb.hk * f.ks2;
-    const float* vp = (const float*)f.v + (int64_t)kb.b * f.vs0 + (int64_t)key * f.vs1 + (int64_t)kb.hk * f.vs2;
+    const float* kp = (const float*)f.k + ko * f.ks0 + kr * f.ks1 + (int64_t)kb.hk * f.ks2;
+    const float* vp = (const float*)f.v + ko * f.vs0 + kr * f.vs1 + (int64_t)kb.hk * f.vs2;
     float dk[D], dv[D];
     for (int e = 0; e < D; ++e) dk[e] = dv[e] = 0.f;
     if (key_ok) {
@@ -1054,9 +1110,11 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(BwdDev p, MaskDev m) {
             }
         }
     }
-    if (key_l >= kb.k_alloc) return;  // keys past the used length get zero gradients
-    float* dkp = (float*)p.dk + (int64_t)kb.b * p.dks0 + (int64_t)key * p.dks1 + (int64_t)kb.hk * p.dks2;
-    float* dvp = (float*)p.dv + (int64_t)kb.b * p.dvs0 + (int64_t)key * p.dvs1 + (int64_t)kb.hk * p.dvs2;
+    // keys past the used length get zero gradients; paged keys outside the
+    // table or the pool are not written
+    if (key_l >= kb.k_alloc || !key_addr) return;
+    float* dkp = (float*)p.dk + ko * p.dks0 + kr * p.dks1 + (int64_t)kb.hk * p.dks2;
+    float* dvp = (float*)p.dv + ko * p.dvs0 + kr * p.dvs1 + (int64_t)kb.hk * p.dvs2;
     const float nanv = __builtin_nanf("");
     for (int e = 0; e < D; ++e) {
         dkp[e] = kb.len_error ? nanv : dk[e] * f.scale;
@@ -1098,6 +1156,15 @@ __global__ __launch_bounds__(BM) void bwd_dq_f32_kernel(BwdDev p, MaskDev m) {
                 if (kind == kTilePartial && !allowed<KIND>(f, m, t, rm, key)) continue;
                 const float* kr = K + (int64_t)key * f.ks1;
                 const float* vr = V + (int64_t)key * f.vs1;
+                if constexpr (KIND == MFA_MASK_VARLEN) {
+                    if (m.block_table) {  // paged keys: (page, row in page)
+                        int r = 0;
+                        const int pg = page_of(m, t.seq, key, r);
+                        if (pg < 0) continue;  // the sequence's rows are NaN (len_error)
+                        kr = (const float*)f.k + (int64_t)pg * f.ks0 + (int64_t)r * f.ks1 + (int64_t)t.hk * f.ks2;
+                        vr = (const float*)f.v + (int64_t)pg * f.vs0 + (int64_t)r * f.vs1 + (int64_t)t.hk * f.vs2;
+                    }
+                }
                 float sc = 0.f, dpv = 0.f;
                 for (int e = 0; e < D; ++e) {
                     sc = fmaf(q[e], kr[e], sc);

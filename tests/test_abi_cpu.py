@@ -158,8 +158,9 @@ def test_paged_varlen_validation(lib):
     b = _ffi.BwdArgs()
     b.fwd = _args(B=1)
     b.fwd.dtype = _ffi.MFA_BF16
+    # the backward accepts paged k / v too (here it stops at the device check)
     st = lib.mfa_attn_bwd_dq(C.byref(b), C.byref(m), 0.1, None)
-    assert _status(lib, st) in ("MFA_E_UNSUPPORTED", "MFA_E_NO_DEVICE")
+    assert _status(lib, st) == "MFA_E_NO_DEVICE"
 
 
 def test_predicate_validation_and_composition(lib):
