@@ -26,9 +26,11 @@ Conventions (readings where the pages are silent):
   sizes where the dense mask does not fit in memory;
 * ``score_mod(score, b, h, q_idx, kv_idx)`` (tensorplay omni_attention,
   intro: it receives the current score and its coordinates and returns the
-  modified score) is applied to the scaled scores before masking; the
-  backward takes it to be additive (a term that does not depend on the
-  score, as positional biases are), so dS is unchanged by it.
+  modified score) is applied to the scaled scores before masking. In the
+  backward, dS is multiplied by the mod's derivative with respect to the
+  incoming score, ``score_mod.grad(score, b, h, q_idx, kv_idx)``, when the
+  mod carries one (the soft cap does); a mod without it is additive (a term
+  that does not depend on the score, as positional biases are): derivative 1.
 """
 
 from __future__ import annotations
@@ -73,11 +75,43 @@ def alibi(slopes):
     return mod
 
 
+def softcap(cap, inner=None):
+    """score_mod cap * tanh(x / cap), x the incoming score after the optional
+    ``inner`` mod (e.g. ``alibi(slopes)``): a soft cap on the scores, one of
+    the one-line score_mods the omni_attention intro lists. Carries
+    ``.grad`` = d mod / d score = (1 - tanh(x / cap)^2) * d inner / d score."""
+    cap = float(cap)
+
+    def pre(score, b, h, q_idx, kv_idx):
+        return score if inner is None else inner(score, b, h, q_idx, kv_idx)
+
+    def mod(score, b, h, q_idx, kv_idx):
+        return cap * np.tanh(pre(score, b, h, q_idx, kv_idx) / cap)
+
+    def grad(score, b, h, q_idx, kv_idx):
+        t = np.tanh(pre(score, b, h, q_idx, kv_idx) / cap)
+        g = 1.0 - t * t
+        if inner is not None and hasattr(inner, "grad"):
+            g = g * inner.grad(score, b, h, q_idx, kv_idx)
+        return g
+
+    mod.grad = grad
+    return mod
+
+
 def _scores(q_rows, k_all, scale, score_mod, b, hq, rr):
     s = scale * (q_rows @ k_all.T)
     if score_mod is not None:
         s = score_mod(s, b, hq, np.asarray(rr)[:, None], np.arange(k_all.shape[0])[None, :])
     return s
+
+
+def _mod_grad(q_rows, k_cols, scale, score_mod, b, hq, rr, cols=None):
+    """Derivative of the score_mod at the scaled scores (1 for additive mods)."""
+    if score_mod is None or not hasattr(score_mod, "grad"):
+        return 1.0
+    kj = np.arange(k_cols.shape[0]) if cols is None else np.asarray(cols)
+    return score_mod.grad(scale * (q_rows @ k_cols.T), b, hq, np.asarray(rr)[:, None], kj[None, :])
 
 
 def attention_fwd(q, k, v, allowed, scale, rows=None, chunk=1024, score_mod=None):
@@ -163,12 +197,13 @@ def attention_bwd(q, k, v, dout, allowed, scale, score_mod=None, term_sums=False
             dP = do[b, :, hq, :] @ v[b, :, hk, :].T
             dl = (P * dP).sum(axis=1)
             delta[b, hq] = dl
-            dS = P * (dP - dl[:, None])
+            gm = _mod_grad(q[b, :, hq, :], k[b, :, hk, :], scale, score_mod, b, hq, rows)
+            dS = P * (dP - dl[:, None]) * gm
             dq[b, :, hq, :] = scale * (dS @ k[b, :, hk, :])
             dk[b, :, hk, :] += scale * (dS.T @ q[b, :, hq, :])
             if term_sums:
                 Bi = (np.abs(do[b, :, hq, :]) * np.abs(out[b, :, hq, :])).sum(axis=1) + (P * np.abs(dP)).sum(axis=1)
-                E = P * (np.abs(dP) + np.abs(dl)[:, None] + Bi[:, None])
+                E = P * np.abs(gm) * (np.abs(dP) + np.abs(dl)[:, None] + Bi[:, None])
                 tq[b, :, hq, :] = scale * (E @ np.abs(k[b, :, hk, :]))
                 tk[b, :, hk, :] += scale * (E.T @ np.abs(q[b, :, hq, :]))
                 tv[b, :, hk, :] += P.T @ np.abs(do[b, :, hq, :])
@@ -227,7 +262,7 @@ def attention_bwd_sampled(q, k, v, dout, allowed, scale, b, hk, rows, cols, chun
     P, dP and Delta, and dK_j / dV_j (for j in ``cols``) sum column j over all
     query rows and all query heads of the group. ``allowed`` is a callable
     ``allowed(b, hm, rows) -> (len(rows), Sk)`` (as for ``attention_fwd``);
-    ``score_mod`` as there (additive). Returns dq (G, len(rows), D) for the group's heads, dk (len(cols), D),
+    ``score_mod`` as there. Returns dq (G, len(rows), D) for the group's heads, dk (len(cols), D),
     dv (len(cols), D).
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
@@ -257,7 +292,8 @@ def attention_bwd_sampled(q, k, v, dout, allowed, scale, b, hk, rows, cols, chun
         fin = np.isfinite(L[rows])
         P = np.where(a & fin[:, None], np.exp(s - np.where(fin, L[rows], 0.0)[:, None]), 0.0)
         dP = dd[rows] @ vv.T
-        dq[g] = scale * ((P * (dP - delta[rows][:, None])) @ kk)
+        gm = _mod_grad(qq[rows], kk, scale, score_mod, b, hq, rows)
+        dq[g] = scale * ((P * (dP - delta[rows][:, None]) * gm) @ kk)
         # dK / dV columns, all query rows in chunks
         for c0 in range(0, Sq, chunk):
             rr = np.arange(c0, min(c0 + chunk, Sq))
@@ -268,7 +304,7 @@ def attention_bwd_sampled(q, k, v, dout, allowed, scale, b, hk, rows, cols, chun
             fin = np.isfinite(L[rr])
             P = np.where(a & fin[:, None], np.exp(s - np.where(fin, L[rr], 0.0)[:, None]), 0.0)
             dP = dd[rr] @ vv[cols].T
-            dS = P * (dP - delta[rr][:, None])
+            dS = P * (dP - delta[rr][:, None]) * _mod_grad(qq[rr], kk[cols], scale, score_mod, b, hq, rr, cols)
             dv += P.T @ dd[rr]
             dk += scale * (dS.T @ qq[rr])
     return dq, dk, dv
@@ -309,5 +345,6 @@ def attention_bwd_dq_rows(q, k, v, dout, allowed, scale, rows, score_mod=None):
             dd = do[b, rows, hq, :]
             delta = (dd * o).sum(axis=1)
             dP = dd @ vv.T
-            dq[b, :, hq, :] = scale * ((P * (dP - delta[:, None])) @ kk)
+            gm = _mod_grad(q[b, rows, hq, :], kk, scale, score_mod, b, hq, rows)
+            dq[b, :, hq, :] = scale * ((P * (dP - delta[:, None]) * gm) @ kk)
     return dq

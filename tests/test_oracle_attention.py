@@ -363,3 +363,101 @@ def test_term_sums_bound_the_gradients():
     B_ = np.einsum("bshd,bshd->bsh", pos, np.abs(v)) + np.abs(dP)
     E = 2 * np.abs(dP) + B_
     np.testing.assert_allclose(tq, 0.5 * E[..., None] * np.abs(k), rtol=1e-12)
+
+
+# --- soft cap score_mod -----------------------------------------------------------------------
+
+def _torch_softcap_attention(q, k, v, mask, scale, cap, slopes=None):
+    """Independent torch float64 reference: scores scale q.k (+ slope (j - i)),
+    then cap * tanh(. / cap), then the mask, softmax and the value sum; GQA
+    by repeating k / v heads. Inputs numpy (B, S, H, D); returns tensors with
+    requires_grad for q, k, v and the output (B, H, Sq, D)."""
+    G = q.shape[2] // k.shape[2]
+    t = [torch.tensor(x.transpose(0, 2, 1, 3), requires_grad=True) for x in (q, k, v)]
+    kk = t[1].repeat_interleave(G, dim=1)
+    vv = t[2].repeat_interleave(G, dim=1)
+    s = scale * (t[0] @ kk.transpose(-1, -2))
+    if slopes is not None:
+        Sq, Sk = q.shape[1], k.shape[1]
+        pos = torch.arange(Sk, dtype=torch.float64)[None, :] - torch.arange(Sq, dtype=torch.float64)[:, None]
+        s = s + torch.tensor(slopes)[None, :, None, None] * pos
+    s = cap * torch.tanh(s / cap)
+    s = s.masked_fill(~torch.from_numpy(mask), float("-inf"))
+    o = torch.softmax(s, dim=-1) @ vv
+    return t, o
+
+
+@pytest.mark.parametrize("with_alibi", [False, True])
+def test_softcap_equals_torch_autograd(with_alibi):
+    rng = np.random.default_rng(80)
+    B, Sq, Sk, Hq, Hkv, D = 2, 19, 27, 4, 2, 8
+    q, k, v = _rand((B, Sq, Hq, D), 81) * 2.0, _rand((B, Sk, Hkv, D), 82) * 2.0, _rand((B, Sk, Hkv, D), 83)
+    do = _rand((B, Sq, Hq, D), 84)
+    mask = rng.random((B, 1, Sq, Sk)) < 0.6
+    mask[..., 2] = True
+    slopes = np.array([0.25, -0.5, 1.0, 0.0625]) if with_alibi else None
+    mod = A.softcap(1.5, A.alibi(slopes) if with_alibi else None)
+    out, lse = A.attention_fwd(q, k, v, mask, 0.7, score_mod=mod)
+    dq, dk, dv, *_ = A.attention_bwd(q, k, v, do, mask, 0.7, score_mod=mod)
+    t, o = _torch_softcap_attention(q, k, v, np.broadcast_to(mask, (B, Hq, Sq, Sk)), 0.7, 1.5, slopes)
+    np.testing.assert_allclose(out, o.detach().numpy().transpose(0, 2, 1, 3), rtol=1e-11, atol=1e-12)
+    o.backward(torch.from_numpy(do.transpose(0, 2, 1, 3).copy()))
+    for g, tt in zip((dq, dk, dv), t):
+        np.testing.assert_allclose(g, tt.grad.numpy().transpose(0, 2, 1, 3), rtol=1e-10, atol=1e-12)
+
+
+def test_softcap_finite_differences_and_limits():
+    q, k, v = _rand((1, 4, 2, 3), 85) * 3.0, _rand((1, 5, 1, 3), 86) * 3.0, _rand((1, 5, 1, 3), 87)
+    do = _rand((1, 4, 2, 3), 88)
+    mask = np.random.default_rng(89).random((1, 1, 4, 5)) < 0.7
+    mask[..., 0] = True
+    mod = A.softcap(0.8)
+    dq, dk, dv, *_ = A.attention_bwd(q, k, v, do, mask, 0.5, score_mod=mod)
+
+    def loss(qq, kk, vv):
+        o, _ = A.attention_fwd(qq, kk, vv, mask, 0.5, score_mod=mod)
+        return float((o * do).sum())
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            num[idx] = (loss(*[xp if y is x else y for y in (q, k, v)]) -
+                        loss(*[xm if y is x else y for y in (q, k, v)])) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+    # a cap far above every score changes nothing; a tiny cap flattens the
+    # weights to the plain mean of the allowed values
+    o_big, l_big = A.attention_fwd(q, k, v, mask, 0.5, score_mod=A.softcap(1e9))
+    o_ref, l_ref = A.attention_fwd(q, k, v, mask, 0.5)
+    np.testing.assert_allclose(o_big, o_ref, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(l_big, l_ref, rtol=1e-9, atol=1e-12)
+    o_small, _ = A.attention_fwd(q, k, v, mask, 0.5, score_mod=A.softcap(1e-9))
+    for hq in range(2):
+        for i in range(4):
+            m = mask[0, 0, i]
+            np.testing.assert_allclose(o_small[0, i, hq], v[0, m, 0].mean(axis=0), rtol=1e-7, atol=1e-8)
+
+
+def test_softcap_sampled_and_row_backward_agree_with_dense():
+    rng = np.random.default_rng(90)
+    B, S, Hq, Hkv, D = 1, 33, 4, 2, 8
+    q, k, v = _rand((B, S, Hq, D), 91) * 2.0, _rand((B, S, Hkv, D), 92) * 2.0, _rand((B, S, Hkv, D), 93)
+    do = _rand((B, S, Hq, D), 94)
+    mask = np.tril(np.ones((S, S), bool))[None, None] & (rng.random((1, 1, S, S)) < 0.8)
+    mask[..., 0] = True
+    mod = A.softcap(2.0, A.alibi([0.5, 1.0, 0.25, 0.125]))
+    dq, dk, dv, *_ = A.attention_bwd(q, k, v, do, mask, 0.3, score_mod=mod)
+
+    def allowed(b, hm, rr):
+        return mask[0, 0][rr]
+    allowed.heads = 1
+    rows, cols = np.array([0, 7, 32]), np.array([0, 16, 32])
+    for hk in range(Hkv):
+        sq, sk, sv = A.attention_bwd_sampled(q, k, v, do, allowed, 0.3, 0, hk, rows, cols, chunk=8, score_mod=mod)
+        np.testing.assert_allclose(sq, dq[0][rows][:, hk * 2:hk * 2 + 2].transpose(1, 0, 2), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(sk, dk[0, cols, hk], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(sv, dv[0, cols, hk], rtol=1e-10, atol=1e-12)
+    rq = A.attention_bwd_dq_rows(q, k, v, do, allowed, 0.3, rows, score_mod=mod)
+    np.testing.assert_allclose(rq[0], dq[0][rows], rtol=1e-10, atol=1e-12)
