@@ -303,6 +303,13 @@ typedef struct mfa_attn_args {
      * both backward passes, which must get the forward's slopes. Slopes must
      * be finite. */
     const float* alibi_slopes;
+    /* Soft cap, or 0 for none: every score x (the scaled score plus the bias
+     * above, if any) becomes softcap * tanh(x / softcap) before the mask and
+     * the softmax, the soft-cap score_mod of tensorplay omni_attention
+     * (intro). The log-sum-exp is of the capped scores, and the backward
+     * passes (which must get the forward's value) take its derivative
+     * 1 - tanh^2(x / softcap) into dS. Must be finite and >= 0. */
+    float softcap;
 } mfa_attn_args;
 
 /* Mask representation for one attention call. Only the fields of `kind` are

@@ -472,13 +472,14 @@ def _slopes_ptr(alibi_slopes, Hq, device):
 
 
 def attn_fwd(q, k, v, mask: MaskRep, scale=None, layout="bshd", out=None, return_lse=True, lse=None,
-             alibi_slopes=None):
+             alibi_slopes=None, softcap=None):
     """Masked attention forward (mfa_attn_fwd). Returns (out, lse or None).
 
     layout: "bshd" (B, S, H, D), "bhsd" (B, H, S, D) or "thd" (packed varlen).
     lse is fp32 (B, Hq, Sq) ((Hq, T) for "thd"). alibi_slopes: optional
     (Hq,) fp32 tensor; adds slope[h] * (kv_idx - q_idx) to the scaled scores
-    (positions local to the sequence for "thd").
+    (positions local to the sequence for "thd"). softcap: optional positive
+    float; each score x (after the bias) becomes softcap * tanh(x / softcap).
     """
     B, Sq, Sk, Hq, Hkv, D = _dims(q, k, layout)
     if scale is None:
@@ -497,12 +498,13 @@ def attn_fwd(q, k, v, mask: MaskRep, scale=None, layout="bshd", out=None, return
     a.v_stride = _ffi.i64x3(*_bsh_strides(v, layout))
     a.o_stride = _ffi.i64x3(*_bsh_strides(out, layout))
     a.alibi_slopes = _slopes_ptr(alibi_slopes, Hq, q.device)
+    a.softcap = float(softcap or 0.0)
     m = mask.to_c()
     _ffi.check(_lib().mfa_attn_fwd(C.byref(a), C.byref(m), float(scale), _stream()))
     return out, (lse if return_lse else None)
 
 
-def _bwd_args(q, k, v, out, lse, dout, dq, dk, dv, delta, layout, alibi_slopes=None):
+def _bwd_args(q, k, v, out, lse, dout, dq, dk, dv, delta, layout, alibi_slopes=None, softcap=None):
     B, Sq, Sk, Hq, Hkv, D = _dims(q, k, layout)
     a = _ffi.BwdArgs()
     f = a.fwd
@@ -514,6 +516,7 @@ def _bwd_args(q, k, v, out, lse, dout, dq, dk, dv, delta, layout, alibi_slopes=N
     f.v_stride = _ffi.i64x3(*_bsh_strides(v, layout))
     f.o_stride = _ffi.i64x3(*_bsh_strides(out, layout))
     f.alibi_slopes = _slopes_ptr(alibi_slopes, Hq, q.device)
+    f.softcap = float(softcap or 0.0)
     a.dout, a.dq, a.dk, a.dv, a.delta = dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), \
         delta.data_ptr()
     a.do_stride = _ffi.i64x3(*_bsh_strides(dout, layout))
@@ -571,11 +574,11 @@ def attn_bwd_dq(args, mask: MaskRep, scale):
 
 
 def attn_bwd(q, k, v, out, lse, dout, mask: MaskRep, scale=None, layout="bshd", alibi_slopes=None, dq=None,
-             dk=None, dv=None, delta=None):
+             dk=None, dv=None, delta=None, softcap=None):
     """Two-pass backward (any mask kind): preprocess, dK/dV over key blocks,
     dQ over query tiles. Returns (dq, dk, dv) shaped like q, k, v (written
     into the given tensors when passed; delta is fp32 (B, Hq, Sq)). The
-    slopes must be the forward's."""
+    slopes and the soft cap must be the forward's."""
     B, Sq, Sk, Hq, Hkv, D = _dims(q, k, layout)
     if scale is None:
         scale = D ** -0.5
@@ -584,7 +587,7 @@ def attn_bwd(q, k, v, out, lse, dout, mask: MaskRep, scale=None, layout="bshd", 
     dv = torch.empty_like(v) if dv is None else dv
     if delta is None:
         delta = torch.empty(B, Hq, Sq, dtype=torch.float32, device=q.device)
-    a = _bwd_args(q, k, v, out, lse, dout, dq, dk, dv, delta, layout, alibi_slopes)
+    a = _bwd_args(q, k, v, out, lse, dout, dq, dk, dv, delta, layout, alibi_slopes, softcap)
     attn_bwd_preprocess(a)
     nbytes, _ = attn_bwd_dkdv_workspace(a, mask)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
@@ -595,13 +598,13 @@ def attn_bwd(q, k, v, out, lse, dout, mask: MaskRep, scale=None, layout="bshd", 
 
 class _MaskedAttention(torch.autograd.Function):
     """Forward and backward both run the library's kernels; the mask
-    representation, scale and bias slopes are constants of the graph."""
+    representation, scale, bias slopes and soft cap are constants of the graph."""
 
     @staticmethod
-    def forward(ctx, q, k, v, mask, scale, layout, alibi_slopes):
-        out, lse = attn_fwd(q, k, v, mask, scale, layout, alibi_slopes=alibi_slopes)
+    def forward(ctx, q, k, v, mask, scale, layout, alibi_slopes, softcap):
+        out, lse = attn_fwd(q, k, v, mask, scale, layout, alibi_slopes=alibi_slopes, softcap=softcap)
         ctx.save_for_backward(q, k, v, out, lse)
-        ctx.mask, ctx.scale, ctx.layout, ctx.slopes = mask, scale, layout, alibi_slopes
+        ctx.mask, ctx.scale, ctx.layout, ctx.slopes, ctx.softcap = mask, scale, layout, alibi_slopes, softcap
         return out
 
     @staticmethod
@@ -609,16 +612,18 @@ class _MaskedAttention(torch.autograd.Function):
         q, k, v, out, lse = ctx.saved_tensors
         if dout.stride(-1) != 1 or dout.data_ptr() % 16:
             dout = dout.contiguous()
-        dq, dk, dv = attn_bwd(q, k, v, out, lse, dout, ctx.mask, ctx.scale, ctx.layout, ctx.slopes)
-        return dq, dk, dv, None, None, None, None
+        dq, dk, dv = attn_bwd(q, k, v, out, lse, dout, ctx.mask, ctx.scale, ctx.layout, ctx.slopes,
+                              softcap=ctx.softcap)
+        return dq, dk, dv, None, None, None, None, None
 
 
-def masked_attention(q, k, v, mask: MaskRep, scale=None, layout="bshd", alibi_slopes=None):
-    """Differentiable masked attention: out = softmax(scale q k^T + bias + mask) v.
+def masked_attention(q, k, v, mask: MaskRep, scale=None, layout="bshd", alibi_slopes=None, softcap=None):
+    """Differentiable masked attention: out = softmax(cap(scale q k^T + bias) + mask) v,
+    cap(x) = softcap * tanh(x / softcap) when softcap is given, else x.
 
     bf16 q, k, v with requires_grad as needed; gradients come from the
-    two-pass backward (mfa_attn_bwd_*). layout and alibi_slopes as for
-    attn_fwd (the slopes get no gradient)."""
+    two-pass backward (mfa_attn_bwd_*). layout, alibi_slopes and softcap as
+    for attn_fwd (the slopes get no gradient)."""
     if scale is None:
         scale = q.shape[-1] ** -0.5
-    return _MaskedAttention.apply(q, k, v, mask, float(scale), layout, alibi_slopes)
+    return _MaskedAttention.apply(q, k, v, mask, float(scale), layout, alibi_slopes, softcap)

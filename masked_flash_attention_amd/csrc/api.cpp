@@ -461,6 +461,8 @@ static mfa_status check_attn_shapes(const mfa_attn_args* a) {
         return fail(MFA_E_SHAPE, "bad sizes B=%d Sq=%d Sk=%d Hq=%d Hkv=%d", a->B, a->Sq, a->Sk, a->Hq, a->Hkv);
     if (a->Hq % a->Hkv != 0) return fail(MFA_E_SHAPE, "Hq=%d is not a multiple of Hkv=%d", a->Hq, a->Hkv);
     if (a->D != 64 && a->D != 128) return fail(MFA_E_UNSUPPORTED, "head dim %d not built (64, 128 are)", a->D);
+    if (!(a->softcap >= 0.f && a->softcap <= FLT_MAX))
+        return fail(MFA_E_ARG, "softcap must be finite and >= 0 (0: none)");
     return ok();
 }
 
@@ -586,6 +588,12 @@ static void fill_fwd(const mfa_attn_args* a, float scale, FwdDev& p) {
     p.scale = scale;
     p.c2 = scale * kLog2e;
     p.alibi = a->alibi_slopes;
+    p.cap = a->softcap;
+    if (a->softcap > 0.f) {
+        p.cap_raw = a->softcap / scale;
+        p.cap_k2 = 2.f * scale * kLog2e / a->softcap;
+        p.cap_tinv = scale / a->softcap;
+    }
 }
 
 static mfa_status check_strides(const char* name, const void* ptr, const int64_t* st, int dtype) {
@@ -641,9 +649,10 @@ mfa_status mfa_attn_fwd(const mfa_attn_args* a, const mfa_mask* mk, float scale,
     if (p.total == 0) return ok();
     p.xcd_remap = (a->dtype == MFA_BF16) && (p.total % 8 == 0) ? 1 : 0;
     if (mk->kind != MFA_MASK_VARLEN) p.lpt_group = lpt_group_for(p, BM);
-    log_launch("attn_fwd %s D=%d mask=%s BM=%d grid=%d x %d threads xcd_remap=%d lpt_group=%d bias=%d",
+    log_launch("attn_fwd %s D=%d mask=%s BM=%d grid=%d x %d threads xcd_remap=%d lpt_group=%d bias=%d softcap=%g",
                a->dtype == MFA_BF16 ? "bf16" : "f32", a->D, kind_name(mk->kind), BM, p.total,
-               a->dtype == MFA_BF16 ? BM / 32 * 64 : BM, p.xcd_remap, p.lpt_group, a->alibi_slopes != nullptr);
+               a->dtype == MFA_BF16 ? BM / 32 * 64 : BM, p.xcd_remap, p.lpt_group, a->alibi_slopes != nullptr,
+               (double)a->softcap);
     return hip_ok(launch_attn_fwd(a->dtype, a->D, BM, p, m, stream), "attention forward launch");
 }
 

@@ -389,8 +389,9 @@ __device__ __forceinline__ void key_side(const FwdDev& f, const MaskDev& m, cons
 // 128-row granularity: a 64-row block takes its tile's kind), the window
 // arithmetic (varlen) or all blocks (no mask); they are walked through a
 // ScanWindow, once per query head of the GQA group.
-template <int D, int KIND, bool BIAS>
+template <int D, int KIND, int MOD>
 __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p, MaskDev m) {
+    constexpr bool BIAS = (MOD & kModBias) != 0, CAP = (MOD & kModCap) != 0;
     constexpr int ROWB = 2 * D, TILEB = 64 * ROWB, NKC = D / 16, NDB = D / 32;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* sQ = smem;                                   // [2][64 x D] Q
@@ -654,6 +655,11 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 if (j == G1 - 1) {
+                    // soft cap before the mask (masked scores stay -inf)
+                    if constexpr (CAP) {
+#pragma unroll
+                        for (int rr = 0; rr < 16; ++rr) s[rr] = softcap_raw(s[rr], f);
+                    }
                     // partial blocks: disallowed scores become -inf (P = 0 there);
                     // register r is query h*32 + (r>>2)*8 + 4*hh + (r&3)
                     if (__builtin_expect(kind == kTilePartial, 0)) {
@@ -693,7 +699,8 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
                         for (int e = 0; e < 4; ++e) {
                             const int rr = gq * 4 + e;
                             const float pv = fast_exp2(fmaf(s[rr], c2, NL[gq][e]));
-                            const float ds = pv * (dp[rr] - DL[gq][e]);
+                            float ds = pv * (dp[rr] - DL[gq][e]);
+                            if constexpr (CAP) ds *= softcap_grad(s[rr], f);
                             pb[gq >> 1][(gq & 1) * 4 + e] = (bf16)pv;
                             sb[gq >> 1][(gq & 1) * 4 + e] = (bf16)ds;
                         }
@@ -806,8 +813,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdDev p) {
 // cursor and the same per-element masks.
 // ---------------------------------------------------------------------------
 
-template <int D, int NW, int KIND, bool BIAS, int BN = kBN>
+template <int D, int NW, int KIND, int MOD, int BN = kBN>
 __global__ __launch_bounds__(NW * 64, (BN == 32 || (NW != 2 && KIND != MFA_MASK_BLOCKID)) ? 2 : 1) void bwd_dq_kernel(BwdDev p, MaskDev m) {
+    constexpr bool BIAS = (MOD & kModBias) != 0, CAP = (MOD & kModCap) != 0;
     constexpr int BM = NW * 32;
     constexpr int ROWB = 2 * D, TILEB = BN * ROWB, NKC = D / 16, NDB = D / 32;
     constexpr int NH = BN / 32;  // 32-key halves per key tile
@@ -983,6 +991,10 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || (NW != 2 && KIND != MFA_MASK_
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 if (j == G1 - 1) {
+                    if constexpr (CAP) {  // soft cap before the mask
+#pragma unroll
+                        for (int rr = 0; rr < 16; ++rr) sh[rr] = softcap_raw(sh[rr], f);
+                    }
                     if (__builtin_expect(kind == kTilePartial || (kt + 1) * BN > t.k_len, 0)) {
                         f32x16 s2[NH];
 #pragma unroll
@@ -995,7 +1007,9 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || (NW != 2 && KIND != MFA_MASK_
 #pragma unroll
                     for (int rr = 0; rr < 16; ++rr) {
                         const float pv = fast_exp2(fmaf(sh[rr], c2, -l2));
-                        sb[rr >> 3][rr & 7] = (bf16)(pv * (dph[rr] - dl));
+                        float ds = pv * (dph[rr] - dl);
+                        if constexpr (CAP) ds *= softcap_grad(sh[rr], f);
+                        sb[rr >> 3][rr & 7] = (bf16)ds;
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -1100,8 +1114,14 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(BwdDev p, MaskDev m) {
                         dpv = fmaf(dp[e], vp[e], dpv);
                     }
                     sc = sc * f.scale + slope * (float)(key_l - i);
+                    float gcap = 1.f;  // derivative of the soft cap
+                    if (f.cap > 0.f) {
+                        const float th = tanhf(sc / f.cap);
+                        sc = f.cap * th;
+                        gcap = 1.f - th * th;
+                    }
                     const float pr = expf(sc - lse);
-                    const float ds = pr * (dpv - p.delta[((int64_t)kb.b * f.Hq + hq) * f.Sq + qrow]);
+                    const float ds = pr * (dpv - p.delta[((int64_t)kb.b * f.Hq + hq) * f.Sq + qrow]) * gcap;
                     for (int e = 0; e < D; ++e) {
                         dv[e] = fmaf(pr, dp[e], dv[e]);
                         dk[e] = fmaf(ds, qp[e], dk[e]);
@@ -1171,7 +1191,13 @@ __global__ __launch_bounds__(BM) void bwd_dq_f32_kernel(BwdDev p, MaskDev m) {
                     dpv = fmaf(dp[e], vr[e], dpv);
                 }
                 sc = sc * f.scale + slope * (float)(key - (row - t.q_base));
-                const float ds = expf(sc - lse) * (dpv - dl);
+                float gcap = 1.f;  // derivative of the soft cap
+                if (f.cap > 0.f) {
+                    const float th = tanhf(sc / f.cap);
+                    sc = f.cap * th;
+                    gcap = 1.f - th * th;
+                }
+                const float ds = expf(sc - lse) * (dpv - dl) * gcap;
                 for (int e = 0; e < D; ++e) dq[e] = fmaf(ds, kr[e], dq[e]);
             }
         }
@@ -1204,11 +1230,14 @@ hipError_t launch_bwd_preprocess(const BwdDev& p, int D, int dtype, hipStream_t 
     return hipGetLastError();
 }
 
-template <int D, int KIND, bool BIAS>
+// The score modifications of the call as the kernels' template bits.
+static int mod_bits(const FwdDev& f) { return (f.alibi ? kModBias : 0) | (f.cap > 0.f ? kModCap : 0); }
+
+template <int D, int KIND, int MOD>
 static hipError_t dkdv_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) {
     // Q / dO double buffers, LSE and delta, query block ids, validity bits, fine words
     const size_t lds = 4 * 64 * 2 * D + 4 * 64 * sizeof(float) + 2 * 64 * 4 + 16 + 2 * 2 * 64 * 4;
-    hipError_t e = hipFuncSetAttribute((const void*)&bwd_dkdv_kernel<D, KIND, BIAS>,
+    hipError_t e = hipFuncSetAttribute((const void*)&bwd_dkdv_kernel<D, KIND, MOD>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int S = p.gsplit > 1 ? p.gsplit : 1;
@@ -1216,7 +1245,7 @@ static hipError_t dkdv_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) 
                              ? (int64_t)m.nseq * p.f.Hkv * ((m.max_k + 63) / 64)
                              : (int64_t)p.f.B * p.f.Hkv * S * ((p.f.Sk + 63) / 64);
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, KIND, BIAS>), dim3((unsigned)grid), dim3(128), lds, s, p, m);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, KIND, MOD>), dim3((unsigned)grid), dim3(128), lds, s, p, m);
     if (S > 1) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1228,34 +1257,48 @@ static hipError_t dkdv_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) 
 
 template <int D, int KIND>
 static hipError_t dkdv_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) {
-    return p.f.alibi ? dkdv_launch<D, KIND, true>(p, m, s) : dkdv_launch<D, KIND, false>(p, m, s);
+    switch (mod_bits(p.f)) {
+        case 0: return dkdv_launch<D, KIND, 0>(p, m, s);
+        case kModBias: return dkdv_launch<D, KIND, kModBias>(p, m, s);
+        case kModCap: return dkdv_launch<D, KIND, kModCap>(p, m, s);
+        default: return dkdv_launch<D, KIND, kModBias | kModCap>(p, m, s);
+    }
 }
 
-template <int D, int NW, int KIND, bool BIAS>
+template <int D, int NW, int KIND, int MOD>
 static hipError_t dq_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) {
     // 64-row query tiles walk 32-key tiles, as in the forward
     constexpr int BN = (NW == 2 && (KIND == MFA_MASK_BSR || KIND == MFA_MASK_TILES)) ? 32 : kBN;
     // K / V double buffers, and the key block ids of block-id masks
     const size_t lds = 4 * (size_t)BN * 2 * D + (KIND == MFA_MASK_BLOCKID ? 2 * BN * sizeof(int32_t) : 0);
     if (p.f.total == 0) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute((const void*)&bwd_dq_kernel<D, NW, KIND, BIAS, BN>,
+    hipError_t e = hipFuncSetAttribute((const void*)&bwd_dq_kernel<D, NW, KIND, MOD, BN>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, KIND, BIAS, BN>), dim3(p.f.total), dim3(NW * 64), lds, s, p, m);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, KIND, MOD, BN>), dim3(p.f.total), dim3(NW * 64), lds, s, p, m);
     return hipGetLastError();
 }
 
 // 64-row query tiles (BSR blocks, 64-row dense-tile maps) run 2 waves, 128-row ones 4.
+template <int D, int NW, int KIND>
+static hipError_t dq_launch_mod(const BwdDev& p, const MaskDev& m, hipStream_t s) {
+    switch (mod_bits(p.f)) {
+        case 0: return dq_launch<D, NW, KIND, 0>(p, m, s);
+        case kModBias: return dq_launch<D, NW, KIND, kModBias>(p, m, s);
+        case kModCap: return dq_launch<D, NW, KIND, kModCap>(p, m, s);
+        default: return dq_launch<D, NW, KIND, kModBias | kModCap>(p, m, s);
+    }
+}
+
 template <int D, int KIND>
 static hipError_t dq_launch(const BwdDev& p, const MaskDev& m, hipStream_t s) {
     if constexpr (KIND == MFA_MASK_BSR) {
-        return p.f.alibi ? dq_launch<D, 2, KIND, true>(p, m, s) : dq_launch<D, 2, KIND, false>(p, m, s);
+        return dq_launch_mod<D, 2, KIND>(p, m, s);
     } else if constexpr (KIND == MFA_MASK_TILES) {
-        if (m.tile_shift == 0)
-            return p.f.alibi ? dq_launch<D, 2, KIND, true>(p, m, s) : dq_launch<D, 2, KIND, false>(p, m, s);
-        return p.f.alibi ? dq_launch<D, 4, KIND, true>(p, m, s) : dq_launch<D, 4, KIND, false>(p, m, s);
+        if (m.tile_shift == 0) return dq_launch_mod<D, 2, KIND>(p, m, s);
+        return dq_launch_mod<D, 4, KIND>(p, m, s);
     } else {
-        return p.f.alibi ? dq_launch<D, 4, KIND, true>(p, m, s) : dq_launch<D, 4, KIND, false>(p, m, s);
+        return dq_launch_mod<D, 4, KIND>(p, m, s);
     }
 }
 

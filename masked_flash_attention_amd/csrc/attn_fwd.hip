@@ -69,8 +69,9 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const char* p) {
 // BN: key-tile width, kBN or 32 (BSR rows with 64-row query blocks: a 2-wave
 // workgroup then needs 32 KB of LDS instead of 64, so four fit on a CU and
 // each SIMD runs two waves, which hide each other's wait for the next tile).
-template <int D, int NW, int KIND, bool BIAS, int BN = kBN>
+template <int D, int NW, int KIND, int MOD, int BN = kBN>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, MaskDev m) {
+    constexpr bool BIAS = (MOD & kModBias) != 0, CAP = (MOD & kModCap) != 0;
     constexpr int BM = NW * 32;
     constexpr int NT = NW * 64;
     constexpr int ROWB = KV<D>::ROWB;
@@ -312,6 +313,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
                 __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
                 if (kc * DPK < NDMA) __builtin_amdgcn_sched_group_barrier(0x020, DPK, 0);
             }
+            // ---- soft cap (before the mask: masked scores stay -inf) ----
+            if constexpr (CAP) {
+#pragma unroll
+                for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[kb][r] = softcap_raw(s[kb][r], p);
+            }
 
             // ---- mask on partial or ragged tiles ----
             if (__builtin_expect(kind == kTilePartial || (kt + 1) * BN > t.k_len, 0))
@@ -465,6 +473,7 @@ __global__ __launch_bounds__(BM) void attn_fwd_f32_kernel(FwdDev p, MaskDev m) {
             for (int d = 0; d < D; ++d) s = fmaf(q[d], kp[d], s);
             s *= p.scale;
             if (p.alibi) s += p.alibi[t.hq] * (float)(key - (row - t.q_base));
+            if (p.cap > 0.f) s = p.cap * tanhf(s / p.cap);
             const float mn = fmaxf(mrun, s);
             const float corr = expf(mrun - mn);
             const float pe = expf(s - mn);
@@ -492,12 +501,19 @@ static hipError_t launch_bf16(const FwdDev& p, const MaskDev& m, hipStream_t s) 
     // 64-row BSR blocks walk 32-key tiles (two waves per SIMD); everything else 64-key tiles
     constexpr int BN = ((KIND == MFA_MASK_BSR || KIND == MFA_MASK_TILES) && NW == 2) ? 32 : kBN;
     const size_t lds = 4 * (size_t)BN * KV<D>::ROWB + (KIND == MFA_MASK_BLOCKID ? 2 * 64 * 4 : 0);
-    if (p.alibi)
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, KIND, true, BN>), dim3(p.total), dim3(NW * 64), lds, s, p,
-                           m);
-    else
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, KIND, false, BN>), dim3(p.total), dim3(NW * 64), lds, s, p,
-                           m);
+    const dim3 grid(p.total), block(NW * 64);
+    switch ((p.alibi ? kModBias : 0) | (p.cap > 0.f ? kModCap : 0)) {
+        case 0: hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, KIND, 0, BN>), grid, block, lds, s, p, m); break;
+        case kModBias:
+            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, KIND, kModBias, BN>), grid, block, lds, s, p, m);
+            break;
+        case kModCap:
+            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, KIND, kModCap, BN>), grid, block, lds, s, p, m);
+            break;
+        default:
+            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, KIND, kModBias | kModCap, BN>), grid, block, lds, s, p,
+                               m);
+    }
     return hipGetLastError();
 }
 

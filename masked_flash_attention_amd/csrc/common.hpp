@@ -74,6 +74,10 @@ struct FwdDev {
     int nQt, nKt;
     float scale, c2;  // c2 = scale * log2(e)
     const float* alibi;  // per query head slopes of the bias slope * (kv - q), or null
+    // soft cap cap * tanh(x / cap) of the scaled scores x (0: none), with
+    // cap_raw = cap / scale, cap_k2 = 2 * scale * log2(e) / cap and
+    // cap_tinv = scale / cap for the raw-score form used by the MFMA kernels
+    float cap, cap_raw, cap_k2, cap_tinv;
     int total;        // workgroups launched
     int xcd_remap;    // 1: logical id = (w % 8) * (total / 8) + w / 8
     // Order of the query tiles over the logical ids (dense-tile, block-id,
@@ -190,6 +194,26 @@ struct ScanWindow {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Score modifications compiled into a kernel variant (template bit set).
+constexpr int kModBias = 1;  // per-head slope * (kv - q)
+constexpr int kModCap = 2;   // soft cap
+
+// Soft cap of a raw score s (q.k plus any bias, in units of 1 / scale):
+// cap * tanh(scale * s / cap), returned in the same raw units. Uses
+// tanh(y) = 1 - 2 / (exp(2y) + 1): one exp2 and one reciprocal, and it
+// saturates to -+cap_raw where exp2 underflows or overflows.
+__device__ __forceinline__ float softcap_raw(float s, const FwdDev& p) {
+    const float e = fast_exp2(s * p.cap_k2);
+    return fmaf(__builtin_amdgcn_rcpf(e + 1.f), -2.f * p.cap_raw, p.cap_raw);
+}
+
+// Derivative 1 - tanh^2 of the soft cap at a capped raw score sc; 0 for a
+// masked score (-inf), so that a zero probability times it stays 0.
+__device__ __forceinline__ float softcap_grad(float sc, const FwdDev& p) {
+    const float t = sc * p.cap_tinv;
+    return fmaxf(fmaf(-t, t, 1.f), 0.f);
+}
 
 // Value of `x` held by lane (lane ^ 32), via the gfx950 cross-half swap.
 __device__ __forceinline__ float other_half(float x) {

@@ -52,6 +52,7 @@ int main() {
   printf("mfa_attn_args %zu\nmfa_mask %zu\nmfa_attn_bwd_args %zu\n",
          sizeof(mfa_attn_args), sizeof(mfa_mask), sizeof(mfa_attn_bwd_args));
   P(mfa_attn_args, q); P(mfa_attn_args, lse); P(mfa_attn_args, o_stride); P(mfa_attn_args, alibi_slopes);
+  P(mfa_attn_args, softcap);
   P(mfa_mask, tile_kind); P(mfa_mask, q_block); P(mfa_mask, cu_q); P(mfa_mask, err); P(mfa_mask, win_right); P(mfa_mask, nseq); P(mfa_mask, seqused_k); P(mfa_mask, n_pages);
   P(mfa_attn_bwd_args, dout); P(mfa_attn_bwd_args, dv_stride); P(mfa_attn_bwd_args, workspace);
   P(mfa_attn_bwd_args, workspace_bytes);
@@ -89,6 +90,9 @@ def _status(lib, code):
     (dict(Hkv=0), "MFA_E_SHAPE"),
     (dict(Sq=-1), "MFA_E_SHAPE"),
     (dict(D=96), "MFA_E_UNSUPPORTED"),
+    (dict(softcap=-1.0), "MFA_E_ARG"),
+    (dict(softcap=float("nan")), "MFA_E_ARG"),
+    (dict(softcap=float("inf")), "MFA_E_ARG"),
     (dict(dtype=7), "MFA_E_DTYPE"),
 ])
 def test_attn_fwd_rejects_before_any_device_call(lib, kw, want):

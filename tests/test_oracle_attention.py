@@ -399,7 +399,8 @@ def test_softcap_equals_torch_autograd(with_alibi):
     mod = A.softcap(1.5, A.alibi(slopes) if with_alibi else None)
     out, lse = A.attention_fwd(q, k, v, mask, 0.7, score_mod=mod)
     dq, dk, dv, *_ = A.attention_bwd(q, k, v, do, mask, 0.7, score_mod=mod)
-    t, o = _torch_softcap_attention(q, k, v, np.broadcast_to(mask, (B, Hq, Sq, Sk)), 0.7, 1.5, slopes)
+    t, o = _torch_softcap_attention(q, k, v, np.ascontiguousarray(np.broadcast_to(mask, (B, Hq, Sq, Sk))), 0.7, 1.5,
+                                    slopes)
     np.testing.assert_allclose(out, o.detach().numpy().transpose(0, 2, 1, 3), rtol=1e-11, atol=1e-12)
     o.backward(torch.from_numpy(do.transpose(0, 2, 1, 3).copy()))
     for g, tt in zip((dq, dk, dv), t):
