@@ -64,6 +64,12 @@ static void attention_validation() {
     a = args();
     a.D = 96;
     EXPECT(is(mfa_attn_fwd(&a, &none, 0.1f, nullptr), MFA_E_UNSUPPORTED));
+    const float bad_caps[] = {-1.f, NAN, INFINITY};
+    for (float cap : bad_caps) {
+        a = args();
+        a.softcap = cap;
+        EXPECT(is(mfa_attn_fwd(&a, &none, 0.1f, nullptr), MFA_E_ARG));
+    }
     a = args(7);
     EXPECT(is(mfa_attn_fwd(&a, &none, 0.1f, nullptr), MFA_E_DTYPE));
     a = args();
@@ -118,6 +124,11 @@ static void attention_validation() {
     b.fwd = args();
     mfa_status st = mfa_attn_bwd_dkdv_workspace(&b, &none, &bytes, &splits);
     EXPECT(is(st, MFA_E_NO_DEVICE) || (is(st, MFA_OK) && splits >= 1 && bytes >= 0));
+    // the allocation-free dK/dV entry point validates like the workspace one
+    EXPECT(is(mfa_attn_bwd_dkdv_noalloc(nullptr, &none, 0.1f, nullptr), MFA_E_ARG));
+    EXPECT(is(mfa_attn_bwd_dkdv_noalloc(&b, nullptr, 0.1f, nullptr), MFA_E_ARG) ||
+           is(mfa_attn_bwd_dkdv_noalloc(&b, nullptr, 0.1f, nullptr), MFA_E_NO_DEVICE));
+    EXPECT(mfa_bwd_scratch_bytes() == (int64_t(96) << 20));
 }
 
 static void mask_representation_validation() {
