@@ -111,15 +111,20 @@ def cpu_baseline(w, tile_flops_per_bh, seconds):
 
 
 def _time(fn, reps=10, warm=2):
+    """Mean ms per call of `reps` back-to-back calls between one pair of
+    events: the host enqueues faster than these kernels run, so the figure
+    is GPU time, without the per-call host preparation that a pair of events
+    around each call would include for sub-millisecond kernels."""
     for _ in range(warm):
         fn()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for e0, e1 in ev:
-        e0.record()
-        fn()
-        e1.record()
     torch.cuda.synchronize()
-    return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return float(e0.elapsed_time(e1)) / reps
 
 
 def _tiles_blockid(qsum, ksum):
@@ -165,6 +170,16 @@ def rows_section(dev, causal=None):
         out["causal_dense_N8192_alibi"] = {"fwd_ms": round(afwd_ms, 4),
                                            "fwd_tflops_attended_tiles": round(f / afwd_ms / 1e9, 1),
                                            "bwd_ms": round(abwd_ms, 4)}
+        # the same step with the soft cap 30 * tanh(x / 30) on the scores
+        oc = torch.empty_like(q)
+        cfwd_ms = _time(lambda: mfa.attn_fwd(q, k, v, rep, scale, "bhsd", out=oc, softcap=30.0))
+        do = torch.randn_like(q)
+        oc, lse = mfa.attn_fwd(q, k, v, rep, scale, "bhsd", softcap=30.0)
+        cbwd_ms = _time(lambda: mfa.attn_bwd(q, k, v, oc, lse, do, rep, scale, "bhsd", softcap=30.0), reps=5)
+        del do, oc, lse
+        out["causal_dense_N8192_softcap30"] = {"fwd_ms": round(cfwd_ms, 4),
+                                               "fwd_tflops_attended_tiles": round(f / cfwd_ms / 1e9, 1),
+                                               "bwd_ms": round(cbwd_ms, 4)}
     # a1/a2 + a6 on the block-causal tiny and the GQA + cross workloads
     for name, w, nc in (("blockcausal_tiny_N256", W.blockcausal_tiny(), None),
                         ("blockcausal_gqa_cross_N1024", W.blockcausal_gqa_cross(), 256)):
@@ -229,10 +244,14 @@ def rows_section(dev, causal=None):
     prep = mfa.MaskRep.varlen(sch, Lmax, Lmax, causal=True, window=(511, 0), block_table=table.to(dev),
                               page_size=page, n_pages=n_pages)
     pfwd_ms = _time(lambda: mfa.attn_fwd(q, kp, vp, prep, w["scale"], "thd", out=o))
-    del kp, vp
+    po, plse = mfa.attn_fwd(q, kp, vp, prep, w["scale"], "thd")
+    dkp, dvp = torch.empty_like(kp), torch.empty_like(vp)
+    pbwd_ms = _time(lambda: mfa.attn_bwd(q, kp, vp, po, plse, do, prep, w["scale"], "thd", dk=dkp, dv=dvp), reps=5)
+    del kp, vp, dkp, dvp, po, plse
     out["varlen_window_32seq"] = {"schedule_ms": round(sched_ms, 4), "fwd_ms": round(fwd_ms, 4),
                                   "fwd_tflops_attended_tiles": round(4.0 * 128 * 64 * 64 * tiles * 16 / fwd_ms / 1e9, 1),
-                                  "bwd_ms": round(vbwd_ms, 4), "paged128_fwd_ms": round(pfwd_ms, 4)}
+                                  "bwd_ms": round(vbwd_ms, 4), "paged128_fwd_ms": round(pfwd_ms, 4),
+                                  "paged128_bwd_ms": round(pbwd_ms, 4)}
     # a4 + a6 + a9 on BSR
     w = W.bsr_random()
     N = 16384
