@@ -647,7 +647,12 @@ mfa_status mfa_attn_fwd(const mfa_attn_args* a, const mfa_mask* mk, float scale,
         p.total = a->B * a->Hq * p.nQt;
     }
     if (p.total == 0) return ok();
-    p.xcd_remap = (a->dtype == MFA_BF16) && (p.total % 8 == 0) ? 1 : 0;
+    // XCD-aware numbering groups consecutive logical tiles on one XCD. The
+    // varlen work list is sorted heaviest first, so that grouping would give
+    // the first XCD all the heaviest tiles: varlen keeps the hardware's
+    // round-robin, which spreads the list over the XCDs in order (and puts
+    // each query head on the same XCD when Hq is a multiple of 8).
+    p.xcd_remap = (a->dtype == MFA_BF16) && (p.total % 8 == 0) && mk->kind != MFA_MASK_VARLEN ? 1 : 0;
     if (mk->kind != MFA_MASK_VARLEN) p.lpt_group = lpt_group_for(p, BM);
     log_launch("attn_fwd %s D=%d mask=%s BM=%d grid=%d x %d threads xcd_remap=%d lpt_group=%d bias=%d softcap=%g",
                a->dtype == MFA_BF16 ? "bf16" : "f32", a->D, kind_name(mk->kind), BM, p.total,
@@ -775,7 +780,7 @@ static mfa_status bwd_common(const mfa_attn_bwd_args* a, const mfa_mask* mk, flo
     } else {
         p.f.total = a->fwd.B * a->fwd.Hq * p.f.nQt;
     }
-    p.f.xcd_remap = (p.f.total % 8 == 0) ? 1 : 0;
+    p.f.xcd_remap = (p.f.total % 8 == 0) && mk->kind != MFA_MASK_VARLEN ? 1 : 0;  // as in the forward
     if (mk->kind != MFA_MASK_VARLEN && !dkdv) p.f.lpt_group = lpt_group_for(p.f, BM);
     return ok();
 }
