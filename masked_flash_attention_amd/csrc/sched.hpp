@@ -483,14 +483,15 @@ __device__ __forceinline__ void mask_scores(const FwdDev& p, const MaskDev& m, c
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int bit = (r >> 2) * 8 + (r & 3);
-            if constexpr (KIND == MFA_MASK_BSR) {
+            if constexpr (KIND == MFA_MASK_BSR || KIND == MFA_MASK_VARLEN) {
                 // the bit as an all-ones / all-zeros mask (a sign-extending
                 // bit-field extract), then a bit-field select of the score or
                 // -inf: two VALU instructions per score instead of a test, a
                 // compare and a select. Faster in the 2-wave BSR kernels
-                // (3-4 %); in the 4-wave kernels the compiler then allocates
-                // the main loop differently and the causal forward was 4 %
-                // slower, so they keep the compare and select.
+                // (3-4 %) and the varlen ones (3 %, many partial tiles); in
+                // the dense-tile kernels the compiler then allocates the main
+                // loop differently and the causal forward was 4 % slower, so
+                // they keep the compare and select.
                 const int keep = __builtin_amdgcn_sbfe((int)okw[kb], bit, 1);
                 s[kb][r] = __int_as_float((__float_as_int(s[kb][r]) & keep) | (int)(0xFF800000u & ~(uint32_t)keep));
             } else {
