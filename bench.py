@@ -18,6 +18,7 @@ Prints ONE JSON line. --gpus N > 1 is not supported (single-GPU path).
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -38,11 +39,20 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+def _code_only(text):
+    """Source text without comments and blank lines: what the compiler sees,
+    so that editing a comment does not orphan the recorded counters."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
+def kernel_source_hash(files=("attn_fwd.hip", "sched.hpp", "common.hpp")):
+    """Hash of the code (comments ignored) of the sources the forward kernel is built from."""
     h = hashlib.sha256()
-    for f in ("attn_fwd.hip", "sched.hpp", "common.hpp"):
-        with open(os.path.join(ROOT, "masked_flash_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in files:
+        with open(os.path.join(ROOT, "masked_flash_attention_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -388,7 +388,10 @@ __device__ __forceinline__ void key_side(const FwdDev& f, const MaskDev& m, cons
 // the CSC list (BSR), the dense tile map or the block-id summaries (both at
 // 128-row granularity: a 64-row block takes its tile's kind), the window
 // arithmetic (varlen) or all blocks (no mask); they are walked through a
-// ScanWindow, once per query head of the GQA group.
+// ScanWindow, once per query head of the GQA group. With a head split
+// (p.gsplit > 1) there are gsplit workgroups per key block, each over its
+// share of the group's heads, writing fp32 partial sums for the reduce pass.
+// MOD: score modifications compiled in (kModBias, kModCap).
 template <int D, int KIND, int MOD>
 __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p, MaskDev m) {
     constexpr bool BIAS = (MOD & kModBias) != 0, CAP = (MOD & kModCap) != 0;

@@ -69,6 +69,8 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const char* p) {
 // BN: key-tile width, kBN or 32 (BSR rows with 64-row query blocks: a 2-wave
 // workgroup then needs 32 KB of LDS instead of 64, so four fit on a CU and
 // each SIMD runs two waves, which hide each other's wait for the next tile).
+// MOD: score modifications compiled in (kModBias: per-head slope bias,
+// kModCap: soft cap); the unmodified variant pays for neither.
 template <int D, int NW, int KIND, int MOD, int BN = kBN>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, MaskDev m) {
     constexpr bool BIAS = (MOD & kModBias) != 0, CAP = (MOD & kModCap) != 0;
