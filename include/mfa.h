@@ -407,6 +407,8 @@ mfa_status mfa_attn_fwd(const mfa_attn_args* args, const mfa_mask* mask, float s
  * required). dout/dq/dk/dv use the same stride convention as fwd. delta
  * (B, Hq, Sq) fp32 contiguous ((Hq, T) for VARLEN) is written by the
  * preprocess pass (delta_i = sum_d dout_id * out_id) and read by the others.
+ * With no query rows (Sq = 0) and keys present, the dK/dV pass writes
+ * dk = dv = 0 (q, lse, out and dout are then not read).
  * D = 128 or 64, every mask kind. dtype MFA_BF16: bf16 tensors, MFMA
  * passes. dtype MFA_F32 (test mode): fp32 q, k, v, out, dout, dq, dk, dv,
  * scalar fp32 passes that walk the same block lists with the same mask

@@ -756,9 +756,14 @@ static mfa_status bwd_common(const mfa_attn_bwd_args* a, const mfa_mask* mk, flo
                              MaskDev& m, int& BM) {
     MFA_TRY(check_bwd(a, true));
     if (!(scale > 0.f && scale <= FLT_MAX)) return fail(MFA_E_ARG, "scale must be finite and positive");
-    if (a->fwd.B == 0 || a->fwd.Sq == 0) return ok();
-    MFA_TRY(dev_ptr(a->fwd.q, "q"));
-    MFA_TRY(dev_ptr(a->fwd.lse, "lse"));
+    // No query rows: the dQ pass has nothing to do, while the dK/dV pass
+    // still runs, to write dK = dV = 0 (its key blocks list no query block).
+    if (a->fwd.B == 0 || (a->fwd.Sq == 0 && (!dkdv || a->fwd.Sk == 0))) return ok();
+    MFA_TRY(ensure_device());
+    if (a->fwd.Sq > 0) {
+        MFA_TRY(dev_ptr(a->fwd.q, "q"));
+        MFA_TRY(dev_ptr(a->fwd.lse, "lse"));
+    }
     MFA_TRY(dev_ptr(a->fwd.alibi_slopes, "alibi_slopes", true));
     if (a->fwd.Sk > 0) {
         MFA_TRY(dev_ptr(a->fwd.k, "k"));
@@ -829,7 +834,7 @@ static mfa_status bwd_dkdv_run(const mfa_attn_bwd_args* a, const mfa_mask* mk, f
     MaskDev m;
     int BM = 128;
     MFA_TRY(bwd_common(a, mk, scale, true, p, m, BM));
-    if (a->fwd.B == 0 || a->fwd.Sq == 0 || a->fwd.Sk == 0) return ok();
+    if (a->fwd.B == 0 || a->fwd.Sk == 0) return ok();
     MFA_TRY(dev_ptr(a->dk, "dk"));
     MFA_TRY(dev_ptr(a->dv, "dv"));
     MFA_TRY(check_strides("dk", a->dk, a->dk_stride, a->fwd.dtype));

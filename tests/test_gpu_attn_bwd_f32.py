@@ -179,3 +179,35 @@ def test_f32_zero_keys_and_rows_past_end():
     out, lse, got = _run(q1, k1, v1, d1, mfa.MaskRep.none(), 0.09, "bshd")
     ref = A.attention_bwd(q1, k1, v1, d1, np.ones((1, 1, 1, 70), bool), 0.09)[:3]
     _check(got, ref, "Sq=1")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, F32])
+def test_no_query_rows_give_zero_dk_dv(dtype):
+    """Sq = 0 with keys present: dK = dV = 0 for every key (written, not left
+    as they were), for plain attention and for varlen sequences with no
+    query tokens; dq is empty."""
+    note(f"bwd with no query rows {dtype}")
+    k, v = W.tensors(770, [(2, 70, 2, 64), (2, 70, 2, 64)])
+    kd, vd = to_dev(k, dtype), to_dev(v, dtype)
+    q = torch.zeros(2, 0, 4, 64, dtype=dtype, device=DEV)
+    out = torch.zeros_like(q)
+    lse = torch.zeros(2, 4, 0, device=DEV)
+    dk, dv = nan_like(kd), nan_like(vd)
+    mfa.attn_bwd(q, kd, vd, out, lse, out, mfa.MaskRep.none(), 0.125, "bshd", dq=torch.empty_like(q), dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+    # varlen: three sequences with keys and no query tokens
+    Lq = np.array([0, 0, 0], np.int32)
+    Lk = np.array([5, 64, 31], np.int32)
+    kv = W.tensors(771, [(100, 2, 64), (100, 2, 64)])
+    kd, vd = to_dev(kv[0], dtype), to_dev(kv[1], dtype)
+    s = mfa.varlen_schedule(to_dev(Lq), to_dev(Lk), causal=False, window=(-1, -1), work_cap=4)
+    rep = mfa.MaskRep.varlen(s, 0, int(Lk.max()), causal=False)
+    q = torch.zeros(0, 4, 64, dtype=dtype, device=DEV)
+    out = torch.zeros_like(q)
+    lse = torch.zeros(4, 0, device=DEV)
+    dk, dv = nan_like(kd), nan_like(vd)
+    mfa.attn_bwd(q, kd, vd, out, lse, out, rep, 0.125, "thd", dq=torch.empty_like(q), dk=dk, dv=dv,
+                 delta=torch.empty(4, 0, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
