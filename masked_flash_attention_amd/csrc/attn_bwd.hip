@@ -817,7 +817,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdDev p) {
 // ---------------------------------------------------------------------------
 
 template <int D, int NW, int KIND, int MOD, int BN = kBN>
-__global__ __launch_bounds__(NW * 64, (BN == 32 || (NW != 2 && KIND != MFA_MASK_BLOCKID)) ? 2 : 1) void bwd_dq_kernel(BwdDev p, MaskDev m) {
+// Two waves per SIMD except for 2-wave workgroups over 64-key tiles. (The
+// block-id variant once ran one wave per SIMD to avoid spills; with its key
+// block ids staged in LDS it spills at most 4 VGPRs at two waves, and the
+// block-id GQA dQ pass runs 0.164 -> 0.115 ms.)
+__global__ __launch_bounds__(NW * 64, (BN == 32 || NW != 2) ? 2 : 1) void bwd_dq_kernel(BwdDev p, MaskDev m) {
     constexpr bool BIAS = (MOD & kModBias) != 0, CAP = (MOD & kModCap) != 0;
     constexpr int BM = NW * 32;
     constexpr int ROWB = 2 * D, TILEB = BN * ROWB, NKC = D / 16, NDB = D / 32;
