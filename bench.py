@@ -48,11 +48,15 @@ def _code_only(text):
 
 
 def kernel_source_hash(files=("attn_fwd.hip", "sched.hpp", "common.hpp")):
-    """Hash of the code (comments ignored) of the sources the forward kernel is built from."""
+    """Hash of the code (comments ignored) of the sources the forward kernel is
+    built from, and of the compiler flags of the compiled ones among them."""
+    from masked_flash_attention_amd.build import SOURCES, flag_signature
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, "masked_flash_attention_amd", "csrc", f), encoding="utf-8") as fh:
             h.update(_code_only(fh.read()).encode())
+        if f in SOURCES:
+            h.update(flag_signature(f).encode())
     return h.hexdigest()[:16]
 
 

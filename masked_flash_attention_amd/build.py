@@ -29,6 +29,34 @@ COMMON = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wno-unused-command-line-argument",
 ]
+# Extra flags per source. attn_bwd.hip: the dK/dV pass at D = 128 holds its
+# dK and dV accumulators (128 registers) beside about 250 other live values,
+# one wave per SIMD. With the backend's default AGPR form for every MFMA, the
+# S and dP results also landed in AGPRs and were copied to VGPRs for the
+# softmax, with dK/dV blocks shuttled back and forth: about 450 accumulator
+# moves per 64-query step. The VGPR form leaves the choice to the register
+# allocator, which keeps S and dP in VGPRs (about 100 moves left; dK/dV pass
+# 5.72 -> 5.41 ms on causal N=8192, identical code otherwise).
+EXTRA = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
+def flags_for(src):
+    """hipcc flags of one source (gfx950, no packed fp32, plus its extras)."""
+    return COMMON + EXTRA.get(src, [])
+
+
+def flag_signature(src):
+    """The flags of one source without the include paths (which depend on
+    where the tree lies): what code generation depends on."""
+    out, skip = [], False
+    for f in flags_for(src):
+        if skip:
+            skip = False
+        elif f == "-I":
+            skip = True
+        else:
+            out.append(f)
+    return " ".join(out)
 
 
 def hipcc():
@@ -40,7 +68,7 @@ def hipcc():
 
 def _compile(src, debug):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + COMMON + (["-g"] if debug else []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + flags_for(src) + (["-g"] if debug else []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
