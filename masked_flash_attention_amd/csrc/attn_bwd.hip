@@ -92,25 +92,35 @@ __device__ __forceinline__ void stage_tile(const char* base, int64_t row_bytes, 
 // The same staging split into a descriptor and single instructions, so that
 // the instructions can be spread over a compute phase: each moves 1 KB
 // (RPI rows), instruction i filling LDS bytes [1024 i, 1024 i + 1024).
+// Instruction i reads row i*RPI + lane/CPR, chunk lane%CPR swizzled by the
+// row. At D = 128 (RPI = 4) the swizzle depends on i only through i mod 4,
+// so a lane's offset is lane_off(i mod 4) plus the wave-uniform i*RPI rows:
+// one add per instruction instead of a 64-bit multiply-add.
 template <int D>
 struct TileDma {
+    static_assert(D == 128, "the lane offsets below assume 4 rows per instruction");
     static constexpr int ROWB = 2 * D, RPI = 1024 / ROWB, CPR = D / 8, NINST = 64 / RPI;
     __amdgpu_buffer_rsrc_t rs;
-    int64_t row_bytes;
+    int row_bytes;  // 32 bits: the host requires 128 rows to span under 2 GiB
     __device__ __forceinline__ void init(const char* base, int64_t rb, int row0, int rows) {
 #if defined(__HIP_DEVICE_COMPILE__)
-        row_bytes = rb;
+        row_bytes = (int)rb;
         const int64_t start = (int64_t)row0 * rb;
         const int rem = min(64, rows - row0);  // as in stage_tile
         const int nrec = rem > 0 ? (rem - 1) * (int)rb + ROWB : 0;
         rs = __builtin_amdgcn_make_buffer_rsrc((void*)(base + start), 0, nrec, 0x00020000);
 #endif
     }
-    __device__ __forceinline__ void issue(char* lds, int i, int lane) const {
-#if defined(__HIP_DEVICE_COMPILE__)
+    // The lane's part of instruction i's byte offset (its row within the
+    // instruction's RPI rows, and its swizzled chunk); depends on i mod 4.
+    static __device__ __forceinline__ int lane_off(int i, int lane, int64_t rb) {
         const int r = i * RPI + lane / CPR;
-        const int pc = lane % CPR;
-        const int go = (int)(r * row_bytes) + ((pc ^ tswz<D>(r)) << 4);
+        return (lane / CPR) * (int)rb + (((lane % CPR) ^ tswz<D>(r)) << 4);
+    }
+    // Instruction i, with loff = lane_off(i', lane, row bytes) for some i' = i mod 4.
+    __device__ __forceinline__ void issue(char* lds, int i, int loff) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+        const int go = loff + i * RPI * row_bytes;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + i * 1024), 16, go, 0, 0, 0);
 #endif
     }
@@ -472,6 +482,17 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
 #pragma unroll
         for (int db = 0; db < NDB; ++db) trq[j][db] = tr_off<D>(8 * j + 4 * hh, db, lane);
 
+    // Lane offsets of this wave's spread Q / dO staging instructions
+    // (D = 128): the wave issues instructions wave + 2k, whose residue mod 4
+    // is wave + 2 (k & 1).
+    int q_loff[2] = {0, 0}, o_loff[2] = {0, 0};
+    if constexpr (D == 128) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            q_loff[j] = TileDma<128>::lane_off(wave + 2 * j, lane, 2 * f.qs1);
+            o_loff[j] = TileDma<128>::lane_off(wave + 2 * j, lane, 2 * p.dos1);
+        }
+    }
     auto stage_to = [&](int g_, uint32_t ent_, char* dq_, char* do_, float* dd_) {
         const int hq = hk * f.G + g_;
         const int qb = (int)(ent_ & 0x0FFFFFFFu);
@@ -572,8 +593,8 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
             // queue); at D = 64 (two waves per SIMD, no registers to spare)
             // they are issued here.
             constexpr bool SPREAD = D == 128;
-            constexpr int NPW = TileDma<D>::NINST / 2;
-            TileDma<D> dmq, dmo;
+            constexpr int NPW = SPREAD ? TileDma<128>::NINST / 2 : 0;
+            TileDma<128> dmq, dmo;  // used at D = 128 only
             if (have_n) {
                 if constexpr (SPREAD) {
                     const int hq = hk * f.G + g_n;
@@ -644,8 +665,8 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
                 if (i + PF < GT) load_group(i + PF);
                 if (SPREAD && i < 2 * NPW && have_n) {
                     const int ii = wave + 2 * (i >> 1);  // instruction index within the tile
-                    if (i & 1) dmo.issue(no_, ii, lane);
-                    else dmq.issue(nq_, ii, lane);
+                    if (i & 1) dmo.issue(no_, ii, o_loff[(i >> 1) & 1]);
+                    else dmq.issue(nq_, ii, q_loff[(i >> 1) & 1]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 if (j < G1) {
