@@ -594,16 +594,23 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
             // they are issued here.
             constexpr bool SPREAD = D == 128;
             constexpr int NPW = SPREAD ? TileDma<128>::NINST / 2 : 0;
+            // Without a next block the spread instructions are still issued,
+            // with an empty range (they write zeros into the free buffer), so
+            // that the MFMA phase below carries no branch per instruction.
             TileDma<128> dmq, dmo;  // used at D = 128 only
+            if constexpr (SPREAD) {
+                const int hq = hk * f.G + (have_n ? g_n : g);
+                const int qbn = have_n ? (int)(ent_n & 0x0FFFFFFFu) : 0;
+                const char* qbp = (const char*)f.q + 2 * ((int64_t)b * f.qs0 + (int64_t)hq * f.qs2);
+                const char* obp = (const char*)p.dout + 2 * ((int64_t)b * p.dos0 + (int64_t)hq * p.dos2);
+                const int r0 = q_base + qbn * 64, rend = have_n ? q_base + q_len : r0;
+                dmq.init(qbp, 2 * f.qs1, r0, rend);
+                dmo.init(obp, 2 * p.dos1, r0, rend);
+            }
             if (have_n) {
                 if constexpr (SPREAD) {
                     const int hq = hk * f.G + g_n;
-                    const int qbn = (int)(ent_n & 0x0FFFFFFFu);
-                    const char* qbp = (const char*)f.q + 2 * ((int64_t)b * f.qs0 + (int64_t)hq * f.qs2);
-                    const char* obp = (const char*)p.dout + 2 * ((int64_t)b * p.dos0 + (int64_t)hq * p.dos2);
-                    const int r0 = q_base + qbn * 64, rend = q_base + q_len;
-                    dmq.init(qbp, 2 * f.qs1, r0, rend);
-                    dmo.init(obp, 2 * p.dos1, r0, rend);
+                    const int r0 = q_base + (int)(ent_n & 0x0FFFFFFFu) * 64, rend = q_base + q_len;
                     const int64_t lrow = ((int64_t)b * f.Hq + hq) * f.Sq;
                     if (wave == 1) stage_vec64(p.delta + lrow, r0, rend, nd_, lane);
                 } else {
@@ -663,7 +670,7 @@ __global__ __launch_bounds__(128, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdDev p
                     dp = f32x16{};
                 }
                 if (i + PF < GT) load_group(i + PF);
-                if (SPREAD && i < 2 * NPW && have_n) {
+                if (SPREAD && i < 2 * NPW) {
                     const int ii = wave + 2 * (i >> 1);  // instruction index within the tile
                     if (i & 1) dmo.issue(no_, ii, o_loff[(i >> 1) & 1]);
                     else dmq.issue(nq_, ii, q_loff[(i >> 1) & 1]);
