@@ -91,33 +91,35 @@ __device__ __forceinline__ void stage_tile(const char* base, int64_t row_bytes, 
 
 // The same staging split into a descriptor and single instructions, so that
 // the instructions can be spread over a compute phase: each moves 1 KB
-// (RPI rows), instruction i filling LDS bytes [1024 i, 1024 i + 1024).
-// Instruction i reads row i*RPI + lane/CPR, chunk lane%CPR swizzled by the
-// row. At D = 128 (RPI = 4) the swizzle depends on i only through i mod 4,
-// so a lane's offset is lane_off(i mod 4) plus the wave-uniform i*RPI rows:
-// one add per instruction instead of a 64-bit multiply-add.
-template <int D>
+// (RPI rows), instruction i filling LDS bytes [1024 i, 1024 i + 1024) of an
+// NROWS-row tile. Instruction i reads row i*RPI + lane/CPR, chunk lane%CPR
+// swizzled by the row; the swizzle depends on i only through i mod 4
+// (D = 128) or i mod 2 (D = 64). A wave of NW >= 2 issues instructions
+// wave + NW*k, so two lane offsets (k even, k odd) plus the wave-uniform
+// i*RPI rows give every offset: one add per instruction instead of a
+// 64-bit multiply-add.
+template <int D, int NROWS = 64>
 struct TileDma {
-    static_assert(D == 128, "the lane offsets below assume 4 rows per instruction");
-    static constexpr int ROWB = 2 * D, RPI = 1024 / ROWB, CPR = D / 8, NINST = 64 / RPI;
+    static constexpr int ROWB = 2 * D, RPI = 1024 / ROWB, CPR = D / 8, NINST = NROWS / RPI;
     __amdgpu_buffer_rsrc_t rs;
     int row_bytes;  // 32 bits: the host requires 128 rows to span under 2 GiB
     __device__ __forceinline__ void init(const char* base, int64_t rb, int row0, int rows) {
 #if defined(__HIP_DEVICE_COMPILE__)
         row_bytes = (int)rb;
         const int64_t start = (int64_t)row0 * rb;
-        const int rem = min(64, rows - row0);  // as in stage_tile
+        const int rem = min(NROWS, rows - row0);  // as in stage_tile
         const int nrec = rem > 0 ? (rem - 1) * (int)rb + ROWB : 0;
         rs = __builtin_amdgcn_make_buffer_rsrc((void*)(base + start), 0, nrec, 0x00020000);
 #endif
     }
-    // The lane's part of instruction i's byte offset (its row within the
-    // instruction's RPI rows, and its swizzled chunk); depends on i mod 4.
+    // The lane's part of instruction i's byte offset: its row within the
+    // instruction's RPI rows, and its swizzled chunk.
     static __device__ __forceinline__ int lane_off(int i, int lane, int64_t rb) {
         const int r = i * RPI + lane / CPR;
         return (lane / CPR) * (int)rb + (((lane % CPR) ^ tswz<D>(r)) << 4);
     }
-    // Instruction i, with loff = lane_off(i', lane, row bytes) for some i' = i mod 4.
+    // Instruction i, with loff = lane_off(i', lane, row bytes) for an i' that
+    // has the same swizzle (i' = i mod 4).
     __device__ __forceinline__ void issue(char* lds, int i, int loff) const {
 #if defined(__HIP_DEVICE_COMPILE__)
         const int go = loff + i * RPI * row_bytes;
@@ -907,10 +909,12 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || NW != 2) ? 2 : 1) void bwd_dq
     auto fine_words = [&](int kt_, int kind_, uint32_t (&w)[2]) {
         tile_mask_words<KIND, NH>(m, t, rm, row, kt_, kind_, w);
     };
-    auto stage_to = [&](int kt_, char* dk_, char* dv_) {
-        const char* kb_ = kbase;
-        const char* vb_ = vbase;
-        int r0 = kt_ * BN, rend = t.k_len;
+    // Where key tile kt_ lies: K and V bases and the row range [r0, rend).
+    auto tile_src = [&](int kt_, const char*& kb_, const char*& vb_, int& r0, int& rend) {
+        kb_ = kbase;
+        vb_ = vbase;
+        r0 = kt_ * BN;
+        rend = t.k_len;
         if constexpr (KIND == MFA_MASK_VARLEN) {
             if (m.block_table) {
                 // paged keys: the tile lies inside one page (page_size is a
@@ -925,10 +929,26 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || NW != 2) ? 2 : 1) void bwd_dq
                 rend = r + n;
             }
         }
-        stage_tile<D, BN>(kb_, 2 * f.ks1, r0, rend, dk_, wave, NW, lane);
-        stage_tile<D, BN>(vb_, 2 * f.vs1, r0, rend, dv_, wave, NW, lane);
     };
-    auto stage = [&](int kt_, int buf) { stage_to(kt_, sK + buf * TILEB, sV + buf * TILEB); };
+    auto stage = [&](int kt_, int buf) {
+        const char *kb_, *vb_;
+        int r0, rend;
+        tile_src(kt_, kb_, vb_, r0, rend);
+        stage_tile<D, BN>(kb_, 2 * f.ks1, r0, rend, sK + buf * TILEB, wave, NW, lane);
+        stage_tile<D, BN>(vb_, 2 * f.vs1, r0, rend, sV + buf * TILEB, wave, NW, lane);
+    };
+    // The next tile's K and V are staged by single instructions spread over
+    // the step's first operand groups (TileDma); lane offsets of this wave's
+    // instructions wave + NW*k, by k & 1.
+    using Dma = TileDma<D, BN>;
+    constexpr int NPW = Dma::NINST / NW;  // instructions per wave and tensor
+    static_assert(NPW * NW == Dma::NINST && NW >= 2, "tile rows must split evenly over the waves");
+    int k_loff[2], v_loff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        k_loff[j] = Dma::lane_off(wave + NW * j, lane, 2 * f.ks1);
+        v_loff[j] = Dma::lane_off(wave + NW * j, lane, 2 * f.vs1);
+    }
     // Block-id masks: wave 0 loads the raw key block ids of a partial (or
     // ragged) tile into a register (lane = key) with the tile's K/V, and at
     // the end of the step stores them, folded with the key validity bits,
@@ -976,7 +996,18 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || NW != 2) ? 2 : 1) void bwd_dq
         // wait for the loads into the other buffer
         auto step = [&](const char* __restrict__ k_, const char* __restrict__ v_, char* __restrict__ nk_,
                         char* __restrict__ nv_, const int32_t* __restrict__ kb_, int32_t* __restrict__ nkb_) {
-            if (has_next) stage_to(kt_n, nk_, nv_);
+            // Without a next tile the instructions are still issued, with an
+            // empty range (they write zeros into the free buffer), so that
+            // the MFMA phase carries no branch per instruction.
+            Dma dmk, dmv;
+            {
+                const char *kb_, *vb_;
+                int r0, rend;
+                tile_src(has_next ? kt_n : kt, kb_, vb_, r0, rend);
+                if (!has_next) rend = r0;
+                dmk.init(kb_, 2 * f.ks1, r0, rend);
+                dmv.init(vb_, 2 * f.vs1, r0, rend);
+            }
             const int kraw_n = kblk_raw(kt_n, has_next ? kind_n : kTileEmpty);
             // The two 32-key halves one after the other: S^T = K Q^T and
             // dP^T = V dO^T (G1 operand groups, two MFMAs each), then dS,
@@ -984,6 +1015,7 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || NW != 2) ? 2 : 1) void bwd_dq
             // groups). The LDS operand reads of all groups form one stream
             // issued PF groups ahead of their MFMAs (a ring of PF + 1 slots).
             constexpr int G1 = NKC, G2 = 2 * NDB, GH = G1 + G2, GT = NH * GH, PF = 3, RING = PF + 1;
+            static_assert(2 * NPW <= GT, "one staging instruction per operand group");
             bf16x8 ra[RING], rb[RING];
             auto load_group = [&](int i) {
                 const int h = i / GH, j = i % GH, slot = i % RING;
@@ -1016,6 +1048,11 @@ __global__ __launch_bounds__(NW * 64, (BN == 32 || NW != 2) ? 2 : 1) void bwd_dq
                     dph = f32x16{};
                 }
                 if (i + PF < GT) load_group(i + PF);
+                if (i < 2 * NPW) {
+                    const int k = i >> 1, ii = wave + NW * k;
+                    if (i & 1) dmv.issue(nv_, ii, v_loff[k & 1]);
+                    else dmk.issue(nk_, ii, k_loff[k & 1]);
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 if (j < G1) {
                     sh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[slot], qf[j], sh, 0, 0, 0);
