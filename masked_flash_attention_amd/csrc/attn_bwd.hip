@@ -206,16 +206,38 @@ __device__ __forceinline__ bool allowed_qk(const FwdDev& f, const MaskDev& m, in
 
 // Allowed bits of one 32-query half in the dK/dV layout: bit rr says whether
 // query qi0 + (rr>>2)*8 + 4*hh + (rr&3) may attend to this lane's key key_l.
+// Varlen windows and BSR blocks (causal or not) allow, for one key, the
+// queries whose distance query - key lies in one interval, below q_len: the
+// half's 32 query offsets form one run of bits [a, e], built as a mask, and
+// the lane's 16 offsets are four nibbles of it (a few instructions instead
+// of the per-element tests).
 template <int KIND>
 __device__ __forceinline__ uint32_t allowed_bits_T(const FwdDev& f, const MaskDev& m, int b, int q_len, int k_len,
                                                    int key_l, int qi0, int hh, int kblk, bool kval) {
-    uint32_t bits = 0;
+    if constexpr (KIND == MFA_MASK_VARLEN || KIND == MFA_MASK_BSR) {
+        if (!(key_l < k_len) || (KIND == MFA_MASK_BSR && !kval)) return 0u;
+        const int64_t d0 = (int64_t)qi0 - key_l;  // query offset 0 minus the key
+        int64_t a = 0, e = 31;                    // allowed offsets within the half
+        if (m.causal) a = max(a, -d0);
+        if constexpr (KIND == MFA_MASK_VARLEN) {
+            if (m.win_right >= 0) a = max(a, -(int64_t)m.win_right - d0);
+            if (m.win_left >= 0) e = min(e, (int64_t)m.win_left - d0);
+        }
+        e = min(e, (int64_t)q_len - 1 - qi0);
+        if (e < a) return 0u;
+        const int w = (int)(e - a + 1);  // 1..32 offsets from a (0..31)
+        const uint32_t run = w >= 32 ? 0xFFFFFFFFu : ((1u << w) - 1u) << (int)a;
+        const uint32_t t = run >> (4 * hh);
+        return (t & 0xFu) | ((t >> 4) & 0xF0u) | ((t >> 8) & 0xF00u) | ((t >> 12) & 0xF000u);
+    } else {
+        uint32_t bits = 0;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-        const int i = qi0 + (rr >> 2) * 8 + 4 * hh + (rr & 3);
-        bits |= (allowed_qk<KIND>(f, m, b, q_len, k_len, key_l, i, kblk, kval) ? 1u : 0u) << rr;
+        for (int rr = 0; rr < 16; ++rr) {
+            const int i = qi0 + (rr >> 2) * 8 + 4 * hh + (rr & 3);
+            bits |= (allowed_qk<KIND>(f, m, b, q_len, k_len, key_l, i, kblk, kval) ? 1u : 0u) << rr;
+        }
+        return bits;
     }
-    return bits;
 }
 
 // The 64-key block of one dK/dV workgroup: (batch or varlen sequence, kv
