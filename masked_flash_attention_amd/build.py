@@ -66,9 +66,38 @@ def hipcc():
     raise RuntimeError("hipcc not found (ROCm is required to build libmfa)")
 
 
+def _backend_option_ok(opt):
+    """Whether this compiler's backend accepts `-mllvm opt` (such options
+    come and go between LLVM versions)."""
+    probe = os.path.join(BUILD, "_probe.hip")
+    with open(probe, "w") as fh:
+        fh.write("__global__ void k() {}\n")
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "--offload-device-only", "-mllvm", opt, "-x", "hip", "-c",
+                        probe, "-o", probe + ".o"], capture_output=True, text=True)
+    return r.returncode == 0
+
+
+def _usable_flags(src):
+    """flags_for(src), less any backend option the compiler rejects (the
+    build then proceeds without that tuning, and says so)."""
+    flags, out, i = flags_for(src), [], 0
+    while i < len(flags):
+        if flags[i] == "-mllvm" and i + 1 < len(flags):
+            if _backend_option_ok(flags[i + 1]):
+                out += flags[i:i + 2]
+            else:
+                print(f"warning: hipcc rejects -mllvm {flags[i + 1]}; building {src} without it", file=sys.stderr)
+            i += 2
+        else:
+            out.append(flags[i])
+            i += 1
+    return out
+
+
 def _compile(src, debug):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + flags_for(src) + (["-g"] if debug else []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + _usable_flags(src) + (["-g"] if debug else []) + ["-x", "hip", "-c", os.path.join(CSRC, src),
+                                                                         "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
