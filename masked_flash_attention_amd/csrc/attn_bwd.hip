@@ -293,10 +293,13 @@ __device__ __forceinline__ KeyBlock key_block(const BwdDev& p, const MaskDev& m,
     kb.seq = -1;
     if constexpr (KIND == MFA_MASK_VARLEN) {
         const int nKbm = (m.max_k + 63) / 64;
-        // plain numbering: sequences differ in length, and round-robin over
-        // the XCDs keeps their work balanced
-        kb.kbk = wg_id % nKbm;
-        const int sh = wg_id / nKbm;
+        // runs of 8 consecutive key blocks of a (sequence, kv head) on one
+        // XCD (they share most of their window's Q and dO in that XCD's
+        // L2), the runs round-robin over the XCDs, so that long sequences
+        // still spread over all of them
+        const int wg = xcd_runs(wg_id, n_wg, 8);
+        kb.kbk = wg % nKbm;
+        const int sh = wg / nKbm;
         kb.hk = sh % f.Hkv;
         const int seq = sh / f.Hkv;
         kb.q_base = m.cu_q[seq];
