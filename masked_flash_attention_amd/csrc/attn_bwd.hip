@@ -240,6 +240,17 @@ __device__ __forceinline__ uint32_t allowed_bits_T(const FwdDev& f, const MaskDe
     }
 }
 
+// Workgroup w runs on XCD w % 8. This numbering puts runs of C consecutive
+// logical ids on one XCD and deals the runs round-robin over the XCDs:
+// neighbours share an L2 while each XCD still gets every eighth run. Ids
+// past the last whole round of 8 runs keep their plain number.
+__device__ __forceinline__ int xcd_runs(int w, int total, int C) {
+    const int span = 8 * C;
+    if (w >= total / span * span) return w;
+    const int r = w >> 3;
+    return ((r / C) * 8 + (w & 7)) * C + r % C;
+}
+
 // The 64-key block of one dK/dV workgroup: (batch or varlen sequence, kv
 // head, key block) and the query / key extents it works in.
 struct KeyBlock {

@@ -119,17 +119,6 @@ __device__ __forceinline__ int xcd_logical(int w, int total, int remap) {
     return (w & 7) * (total >> 3) + (w >> 3);
 }
 
-// As above, with runs of C consecutive logical ids on one XCD and the runs
-// dealt round-robin over the XCDs: neighbours share an L2 while each XCD
-// still gets every eighth run. Ids past the last whole round of 8 runs keep
-// their plain number.
-__device__ __forceinline__ int xcd_runs(int w, int total, int C) {
-    const int span = 8 * C;
-    if (w >= total / span * span) return w;
-    const int r = w >> 3;
-    return ((r / C) * 8 + (w & 7)) * C + r % C;
-}
-
 // 64 consecutive entries of a device list held one per lane of the wave,
 // with the following 64 already requested: get(pos) for a non-decreasing
 // wave-uniform pos is a v_readlane instead of a dependent global load.
