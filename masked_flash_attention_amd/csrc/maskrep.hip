@@ -167,9 +167,12 @@ constexpr int kCmpCols = 256;   // 4 key tiles of 64 per workgroup
 constexpr int kCmpPasses = kCmpRows / 16;
 
 __device__ __forceinline__ uint32_t pack4(uint32_t w) {
-    // 4 mask bytes -> 4 bits (bit k = byte k != 0)
+    // 4 mask bytes -> 4 bits (bit k = byte k != 0). nz keeps bit 7 of each
+    // byte; the high half of nz * (2^25 + 2^18 + 2^11 + 2^4) moves bits 7, 15,
+    // 23, 31 to 32..35, and none of the other partial products reaches or
+    // carries into those four bits.
     const uint32_t nz = (((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w) & 0x80808080u;
-    return (((nz >> 7) * 0x01020408u) >> 24) & 0xFu;
+    return __umulhi(nz, 0x02040810u) & 0xFu;
 }
 
 // Body shared by the dense-mask and the predicate tile builders: one
@@ -275,42 +278,76 @@ __global__ __launch_bounds__(256) void compact_tiles_kernel(const uint8_t* mask,
 // 16l .. 16l+15), so every load is a fully used 1 KB run and every row's
 // fine words leave as one 128-byte store.
 constexpr int kWideCols = 1024;
+constexpr int kCmpRPW = 16;
 
-__global__ __launch_bounds__(512) void compact_tiles_wide_kernel(const uint8_t* mask, int Nq, int Nk, int nKt,
-                                                                 bool bm64, uint8_t* tile_kind, uint32_t* fine_bits) {
-    __shared__ uint64_t s_any[8], s_all[8];
+template <int RPW>  // rows per wave; the workgroup's kCmpRows / RPW waves cover the strip
+__global__ __launch_bounds__(64 * (kCmpRows / RPW)) void compact_tiles_wide_kernel(const uint8_t* mask, int Nq, int Nk,
+                                                                                   int nKt, bool bm64,
+                                                                                   uint8_t* tile_kind,
+                                                                                   uint32_t* fine_bits) {
+    constexpr int NWV = kCmpRows / RPW;
+    __shared__ uint64_t s_any[NWV], s_all[NWV];
     const int qt = blockIdx.y;
     const int col0 = blockIdx.x * kWideCols;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: row tests stay scalar
     const int col = col0 + 16 * lane;
     const int W = (Nk + 31) / 32;
     const bool col_ok = col + 16 <= Nk;  // Nk is a multiple of 16 here
-    const int r0 = qt * kCmpRows + wave * 16;
-    u32x4 v[16];
+    const int r0 = qt * kCmpRows + wave * RPW;
+    // Every load is issued unconditionally, so that each row's packing can
+    // start as soon as that row has landed (a load under a branch would make
+    // the compiler wait for all sixteen first): rows past Nq re-read row
+    // Nq - 1 and columns past Nk re-read column 0 of the row, and their bits
+    // are zeroed after packing.
+    const int rc0 = min(r0, Nq - 1);
+    const int n_in = min(RPW, Nq - rc0);  // rows of the wave that exist (>= 1)
+    const uint8_t* p = mask + (int64_t)rc0 * Nk + (col_ok ? col : 0);
+    u32x4 v[RPW];
 #pragma unroll
-    for (int ps = 0; ps < 16; ++ps) {
-        const int r = r0 + ps;
-        v[ps] = (r < Nq && col_ok) ? __builtin_nontemporal_load((const u32x4*)(mask + (int64_t)r * Nk + col))
-                                   : u32x4{0u, 0u, 0u, 0u};
+    for (int ps = 0; ps < RPW; ++ps) {
+        v[ps] = __builtin_nontemporal_load((const u32x4*)p);
+        if (ps + 1 < n_in) p += Nk;
     }
+    // the even lane of each pair stores the pair's 32-bit word, one row apart
+    const int wi = col0 / 32 + (lane >> 1);
+    uint32_t* fb = fine_bits + (int64_t)rc0 * W + wi;
+    const bool store_lane = (lane & 1) == 0 && wi < W;
     uint64_t any = 0, all = ~0ull;
 #pragma unroll
-    for (int ps = 0; ps < 16; ++ps) {
+    for (int ps = 0; ps < RPW; ++ps) {
         const int r = r0 + ps;
-        const uint32_t bits = pack4(v[ps][0]) | (pack4(v[ps][1]) << 4) | (pack4(v[ps][2]) << 8) | (pack4(v[ps][3]) << 12);
+        const bool ok = r < Nq && col_ok;
+        // opaque to the optimiser, so that the load stays where it was issued
+        // instead of being sunk into a branch under `ok`
+        u32x4 x = v[ps];
+        asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
+        // 16 bytes -> 16 bits. nz keeps bit 7 of each byte (set iff the byte
+        // is nonzero); the high half of nz * (2^25 + 2^18 + 2^11 + 2^4) holds
+        // bits 7, 15, 23, 31 at 0..3, the multiplier shifted by 4 puts them
+        // at 4..7, and no other partial product lands in (or carries into)
+        // the kept bits.
+        uint32_t nz[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) nz[d] = (((x[d] & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x[d]) & 0x80808080u;
+        const uint32_t lo = (__umulhi(nz[0], 0x02040810u) & 0xFu) | (__umulhi(nz[1], 0x20408100u) & 0xF0u);
+        const uint32_t hb = (__umulhi(nz[2], 0x02040810u) & 0xFu) | (__umulhi(nz[3], 0x20408100u) & 0xF0u);
+        const uint32_t bits = ok ? lo | (hb << 8) : 0u;
         any |= __builtin_amdgcn_ballot_w64(bits != 0u);
-        all &= __builtin_amdgcn_ballot_w64(r < Nq && col_ok && bits == 0xFFFFu);
-        // lane pairs (even, odd) form one 32-bit word of the row
-        const uint32_t hi = __shfl_xor(bits, 1);
-        const int wi = col0 / 32 + (lane >> 1);
-        if (r < Nq && (lane & 1) == 0 && wi < W) fine_bits[(int64_t)r * W + wi] = bits | (hi << 16);
+        all &= __builtin_amdgcn_ballot_w64(bits == 0xFFFFu);  // bits is 0 where !ok
+        // lane pairs (even, odd) form one 32-bit word of the row; the
+        // partner's bits come through a DPP quad permutation [1, 0, 3, 2]
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)bits, 0xB1, 0xF, 0xF, false);
+        if (r < Nq && store_lane) fb[0] = bits | (hi << 16);
+        if (ps + 1 < n_in) fb += W;
     }
     if (lane == 0) {
         s_any[wave] = any;
         s_all[wave] = all;
     }
     __syncthreads();
-    // thread t < 32: half h = t / 16 (waves 4h .. 4h+3), key tile j = t % 16 (lanes 4j .. 4j+3)
+    // thread t < 32: half h = t / 16 (the strip's 64-row half h, waves h*NWV/2 ..), key tile j = t % 16
+    // (lanes 4j .. 4j+3)
     const int t = threadIdx.x;
     if (t < 32) {
         const int h = t >> 4, j = t & 15, kt = col0 / 64 + j;
@@ -318,9 +355,9 @@ __global__ __launch_bounds__(512) void compact_tiles_wide_kernel(const uint8_t* 
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                a[hh] = a[hh] || ((s_any[hh * 4 + w] >> (4 * j)) & 0xFull) != 0;
-                f[hh] = f[hh] && ((s_all[hh * 4 + w] >> (4 * j)) & 0xFull) == 0xFull;
+            for (int w = 0; w < NWV / 2; ++w) {
+                a[hh] = a[hh] || ((s_any[hh * (NWV / 2) + w] >> (4 * j)) & 0xFull) != 0;
+                f[hh] = f[hh] && ((s_all[hh * (NWV / 2) + w] >> (4 * j)) & 0xFull) == 0xFull;
             }
         if (kt < nKt) {
             if (bm64) {
@@ -1006,7 +1043,8 @@ hipError_t launch_compact(const uint8_t* mask, int Nq, int Nk, int BM, uint8_t* 
         const dim3 grid((Nk + kCmpCols - 1) / kCmpCols, nStrips);
         const bool vec = (Nk % 16 == 0) && (((uintptr_t)mask & 15) == 0);
         if (vec)
-            hipLaunchKernelGGL(compact_tiles_wide_kernel, dim3((Nk + kWideCols - 1) / kWideCols, nStrips), dim3(512),
+            hipLaunchKernelGGL(compact_tiles_wide_kernel<kCmpRPW>, dim3((Nk + kWideCols - 1) / kWideCols, nStrips),
+                               dim3(64 * (kCmpRows / kCmpRPW)),
                                0, s, mask, Nq, Nk, nKt, bm64, tile_kind, fine_bits);
         else
             hipLaunchKernelGGL(compact_tiles_kernel<false>, grid, dim3(256), 0, s, mask, Nq, Nk, nKt, bm64,
