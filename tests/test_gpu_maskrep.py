@@ -80,7 +80,7 @@ def _check_compaction(m, BM=128):
 
 
 @pytest.mark.parametrize("case", ["causal8192", "random_vec", "random_ragged", "all_true", "all_false",
-                                  "one_col", "one_row", "tall", "rows65536"])
+                                  "one_col", "one_row", "tall", "rows65536", "ragged_wide", "ragged_wide_small"])
 def test_compact_dense_mask_bit_exact(case):
     note(f"compaction {case}")
     rng = np.random.default_rng(11)
@@ -100,6 +100,12 @@ def test_compact_dense_mask_bit_exact(case):
         m = rng.random((1, 4096)) < 0.5
     elif case == "tall":
         m = rng.random((2000, 48)) < 0.9
+    elif case in ("ragged_wide", "ragged_wide_small"):
+        # row length a multiple of 16 but not of 1024 (lanes past the end of a
+        # row re-read its start and are zeroed) and a row count that ends
+        # inside a wave's 16 rows (rows past the end re-read the last row)
+        m = W.random_dense_mask(1000, 8000, 0.3, seed=4) if case == "ragged_wide" else rng.random((17, 1040)) < 0.5
+        _check_compaction(m, BM=64)
     else:
         # 65,536 query rows (512 tile rows x 16 key tiles): the CSR takes the
         # linear count / scan / fill path
