@@ -121,8 +121,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
     f32x16 o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-    float M = 0.f;       // scaled running max (log2 units); 0 until m_set
-    bool m_set = false;  // the row has seen an allowed key
+    float M = 0.f;  // scaled running max (log2 units); 0 until the row has seen an allowed key
+    // threshold of the shifted tile max that moves M: -inf until the row has
+    // seen an allowed key (its first finite max sets M), kTau after that
+    float thr = -INFINITY;
     float l_part = 0.f;
 
     // ---- staging of K/V tiles: direct global->LDS buffer loads ----
@@ -347,12 +349,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16_kernel(FwdDev p, Mas
             float T = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
             T = max_both_halves(T);
             // T = -inf: no allowed key of this row in the tile, M stays
-            const bool need = T > kTau || (!m_set && T > -INFINITY);
+            const bool need = T > thr;
             if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
                 const float sh = need ? T : 0.f;
-                const float alpha = (need && m_set) ? fast_exp2(-T) : 1.f;
+                const float alpha = (need && thr == kTau) ? fast_exp2(-T) : 1.f;
                 M += sh;
-                m_set = m_set || need;
+                thr = need ? kTau : thr;
                 l_part *= alpha;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)

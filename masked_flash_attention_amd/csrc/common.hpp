@@ -224,7 +224,11 @@ __device__ __forceinline__ float other_half(float x) {
 
 __device__ __forceinline__ float max_both_halves(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+    // one v_max_f32: fmaxf would first quiet both operands (the compiler
+    // cannot tell that integer-typed lane data holds no signalling NaN)
+    float m;
+    asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(__int_as_float(r[0])), "v"(__int_as_float(r[1])));
+    return m;
 }
 
 __device__ __forceinline__ float sum_both_halves(float x) {
