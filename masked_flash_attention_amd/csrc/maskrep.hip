@@ -5,6 +5,8 @@
 
 #include <algorithm>
 
+#include <type_traits>
+
 #include "sched.hpp"
 
 namespace mfa {
@@ -311,36 +313,68 @@ __global__ __launch_bounds__(64 * (kCmpRows / RPW)) void compact_tiles_wide_kern
     }
     // the even lane of each pair stores the pair's 32-bit word, one row apart
     const int wi = col0 / 32 + (lane >> 1);
-    uint32_t* fb = fine_bits + (int64_t)rc0 * W + wi;
+    uint32_t* const fb0 = fine_bits + (int64_t)rc0 * W + wi;
     const bool store_lane = (lane & 1) == 0 && wi < W;
-    uint64_t any = 0, all = ~0ull;
-#pragma unroll
-    for (int ps = 0; ps < RPW; ++ps) {
-        const int r = r0 + ps;
-        const bool ok = r < Nq && col_ok;
-        // opaque to the optimiser, so that the load stays where it was issued
-        // instead of being sunk into a branch under `ok`
-        u32x4 x = v[ps];
-        asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
-        // 16 bytes -> 16 bits. nz keeps bit 7 of each byte (set iff the byte
-        // is nonzero); the high half of nz * (2^25 + 2^18 + 2^11 + 2^4) holds
-        // bits 7, 15, 23, 31 at 0..3, the multiplier shifted by 4 puts them
-        // at 4..7, and no other partial product lands in (or carries into)
-        // the kept bits.
-        uint32_t nz[4];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) nz[d] = (((x[d] & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x[d]) & 0x80808080u;
-        const uint32_t lo = (__umulhi(nz[0], 0x02040810u) & 0xFu) | (__umulhi(nz[1], 0x20408100u) & 0xF0u);
-        const uint32_t hb = (__umulhi(nz[2], 0x02040810u) & 0xFu) | (__umulhi(nz[3], 0x20408100u) & 0xF0u);
-        const uint32_t bits = ok ? lo | (hb << 8) : 0u;
-        any |= __builtin_amdgcn_ballot_w64(bits != 0u);
-        all &= __builtin_amdgcn_ballot_w64(bits == 0xFFFFu);  // bits is 0 where !ok
+    // OR and AND of the lane's row bits over the wave's rows: the tile
+    // flags are ballots of these at the end (bits is 0 where !ok)
+    uint32_t or_bits = 0u, and_bits = 0xFFFFu;
+    // Folds a row's 16 bits into the flags and stores its fine words.
+    auto emit = [&](uint32_t bits, int r, uint32_t*& fb, int ps) {
+        or_bits |= bits;
+        and_bits &= bits;
         // lane pairs (even, odd) form one 32-bit word of the row; the
         // partner's bits come through a DPP quad permutation [1, 0, 3, 2]
         const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)bits, 0xB1, 0xF, 0xF, false);
         if (r < Nq && store_lane) fb[0] = bits | (hi << 16);
         if (ps + 1 < n_in) fb += W;
+    };
+    // First pass, for bytes of 0 or 1 (a bool mask): the byte-wise dot
+    // product with weights 1, 2, 4, 8 (16, 32, 64, 128 for the second dword)
+    // is the row's bits. `seen` ORs every byte read, so bits 1..7 of its bytes
+    // stay clear unless some byte is above 1.
+    uint32_t seen = 0u;
+    {
+        uint32_t* fb = fb0;
+#pragma unroll
+        for (int ps = 0; ps < RPW; ++ps) {
+            const int r = r0 + ps;
+            const bool ok = r < Nq && col_ok;
+            const u32x4 x = v[ps];
+            // a use the optimiser cannot see through, so that the load stays
+            // where it was issued instead of being sunk into a branch
+            asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
+            seen |= x[0] | x[1] | x[2] | x[3];
+            const uint32_t lo =
+                __builtin_amdgcn_udot4(x[0], 0x08040201u, __builtin_amdgcn_udot4(x[1], 0x80402010u, 0u, false), false);
+            const uint32_t hb =
+                __builtin_amdgcn_udot4(x[2], 0x08040201u, __builtin_amdgcn_udot4(x[3], 0x80402010u, 0u, false), false);
+            emit(ok ? lo | (hb << 8) : 0u, r, fb, ps);
+        }
     }
+    // A wave that read any byte above 1 (in its rows, the clamped re-reads
+    // included) packs its rows again with a nonzero test per byte and stores
+    // again: nz keeps bit 7 of each byte (set iff the byte is nonzero); the
+    // high half of nz * (2^25 + 2^18 + 2^11 + 2^4) holds bits 7, 15, 23, 31
+    // at 0..3, the multiplier shifted by 4 puts them at 4..7, and no other
+    // partial product lands in (or carries into) the kept bits.
+    if (__builtin_amdgcn_ballot_w64((seen & 0xFEFEFEFEu) != 0u) != 0) {
+        or_bits = 0u;
+        and_bits = 0xFFFFu;
+        uint32_t* fb = fb0;
+#pragma unroll
+        for (int ps = 0; ps < RPW; ++ps) {
+            const int r = r0 + ps;
+            const bool ok = r < Nq && col_ok;
+            uint32_t nz[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) nz[d] = (((v[ps][d] & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | v[ps][d]) & 0x80808080u;
+            const uint32_t lo = (__umulhi(nz[0], 0x02040810u) & 0xFu) | (__umulhi(nz[1], 0x20408100u) & 0xF0u);
+            const uint32_t hb = (__umulhi(nz[2], 0x02040810u) & 0xFu) | (__umulhi(nz[3], 0x20408100u) & 0xF0u);
+            emit(ok ? lo | (hb << 8) : 0u, r, fb, ps);
+        }
+    }
+    const uint64_t any = __builtin_amdgcn_ballot_w64(or_bits != 0u);
+    const uint64_t all = __builtin_amdgcn_ballot_w64(and_bits == 0xFFFFu);
     if (lane == 0) {
         s_any[wave] = any;
         s_all[wave] = all;
