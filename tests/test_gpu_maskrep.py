@@ -114,15 +114,26 @@ def test_compact_dense_mask_bit_exact(case):
     _check_compaction(m)
 
 
-def test_compact_nonbool_bytes_count_as_true():
-    note("compaction nonzero bytes")
+@pytest.mark.parametrize("case", ["dense_values", "sparse_values"])
+def test_compact_nonbool_bytes_count_as_true(case):
+    """Any nonzero byte attends. dense_values: every wave sees bytes above 1;
+    sparse_values: a 0/1 mask with a few bytes of 2..255, so that only the
+    waves that read one of them repack their rows with the exact test."""
+    note(f"compaction nonzero bytes {case}")
     rng = np.random.default_rng(5)
-    m = rng.integers(0, 4, (256, 512)).astype(np.uint8)
-    ref = M.compact_dense_mask(m != 0, 128, 64)
-    got = mfa.compact_dense_mask(to_dev(m))
-    torch.cuda.synchronize()
-    assert np.array_equal(_np(got["fine_bits"]).view(np.uint32), ref["fine_bits"])
-    assert np.array_equal(_np(got["tile_kind"]), ref["tile_kind"])
+    if case == "dense_values":
+        m = rng.integers(0, 4, (256, 512)).astype(np.uint8)
+    else:
+        m = (rng.random((1000, 2048)) < 0.4).astype(np.uint8)
+        idx = rng.integers(0, m.size, 12)
+        m.flat[idx] = rng.integers(2, 256, 12).astype(np.uint8)
+        m.flat[idx[:4]] = 0
+    for BM in (128, 64):
+        ref = M.compact_dense_mask(m != 0, BM, 64)
+        got = mfa.compact_dense_mask(to_dev(m), BM=BM)
+        torch.cuda.synchronize()
+        assert np.array_equal(_np(got["fine_bits"]).view(np.uint32), ref["fine_bits"])
+        assert np.array_equal(_np(got["tile_kind"]), ref["tile_kind"])
 
 
 @pytest.mark.parametrize("case", ["cfg5", "small_ragged", "wide_rows", "many_kv_blocks"])
