@@ -73,6 +73,29 @@ def test_tiles_small(dtype, layout, D, maskcase):
     compare_attention(_bshd(out, layout), f64(lse), ro, rl, _tol(dtype))
 
 
+@pytest.mark.parametrize("maskcase", ["random", "causal", "late_start"])
+def test_tiles_peaked_scores(maskcase):
+    """q and k scaled by 6 (score spread ~36x the unit case): the running max
+    moves by far more than the lazy-rescale margin on many tiles, so the
+    rescale path and the first-key threshold of each row are exercised.
+    late_start: half of the rows see no key in their first key tiles."""
+    note(f"tiles peaked {maskcase}")
+    B, H, Sq, Sk, D = 1, 2, 300, 700, 128
+    if maskcase == "random":
+        m = W.random_dense_mask(Sq, Sk, 0.3, seed=9)
+    elif maskcase == "causal":
+        m = np.tri(Sq, Sk, k=Sk - Sq, dtype=bool)
+    else:
+        m = np.ones((Sq, Sk), bool)
+        m[::2, :400] = False
+    q, k, v = _inputs((B, H, Sq, D), (B, H, Sk, D), 31, torch.bfloat16)
+    q, k = (q * 6).to(torch.bfloat16), (k * 6).to(torch.bfloat16)
+    out, lse = _run(q, k, v, mfa.MaskRep.tiles(mfa.compact_dense_mask(to_dev(m))), D ** -0.5, "bhsd",
+                    torch.bfloat16)
+    ro, rl = A.attention_fwd(_bshd(q, "bhsd"), _bshd(k, "bhsd"), _bshd(v, "bhsd"), m[None, None], D ** -0.5)
+    compare_attention(_bshd(out, "bhsd"), f64(lse), ro, rl, BF16_OUT_TOL)
+
+
 def test_tiles_causal_1024_and_none_mask():
     note("tiles causal 1024 + none")
     B, H, N, D = 1, 2, 1024, 128
