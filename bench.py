@@ -384,14 +384,17 @@ def main():
         mfa.attn_fwd(q, k, v, mfa.MaskRep.tiles(comp), scale, "bhsd", out=out, lse=lse)
         return comp
 
+    # host-side counting first: a pause between the warm-up and the timed
+    # steps would let the GPU clock drop before the first timed step
+    allowed = int(w["mask"].sum())
+    allowed_flops = 4.0 * D * allowed * B * H
+
     log("warmup")
     for _ in range(a.warmup):
         comp = step()
     torch.cuda.synchronize()
     nnz = int(comp["row_ptr"][-1].item())
     tile_flops = 4.0 * BM * BN * D * nnz * B * H
-    allowed = int(w["mask"].sum())
-    allowed_flops = 4.0 * D * allowed * B * H
 
     log(f"timing {a.steps} steps")
     torch.cuda.synchronize()
