@@ -124,13 +124,24 @@ def cpu_baseline(w, tile_flops_per_bh, seconds):
                       f"{dt:.1f} s; attended-tile FLOPs of the sample over that time"}
 
 
-def _time(fn, reps=10, warm=2):
+def _time(fn, reps=10, warm=2, warm_ms=50.0):
     """Mean ms per call of `reps` back-to-back calls between one pair of
     events: the host enqueues faster than these kernels run, so the figure
     is GPU time, without the per-call host preparation that a pair of events
-    around each call would include for sub-millisecond kernels."""
+    around each call would include for sub-millisecond kernels. Before them
+    the calls repeat for about warm_ms: each row's host-side setup leaves
+    the GPU idle, and two calls of a sub-millisecond kernel end before its
+    clock has come back up (block-id GQA forward 0.091 ms after two calls,
+    0.081-0.083 ms after 500)."""
     for _ in range(warm):
         fn()
+    torch.cuda.synchronize()
+    t0, n = time.perf_counter(), 0
+    while (time.perf_counter() - t0) * 1e3 < warm_ms:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
