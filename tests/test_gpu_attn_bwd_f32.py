@@ -65,6 +65,22 @@ def test_f32_tiles(D, maskcase, tile_m):
     _check(got, (rdq, rdk, rdv), f"tiles {maskcase} {tile_m}")
 
 
+def test_f32_tiles_peaked_scores():
+    """q and k scaled by 4 (nearly one-hot rows; the recomputed P subtracts
+    large LSE values): the fp32 passes still meet 1e-4."""
+    note("f32 bwd peaked")
+    Sq, Sk, D = 300, 333, 128
+    m = W.random_dense_mask(Sq, Sk, 0.35, seed=5)
+    q, k, v, do = W.tensors(720, [(1, Sq, 2, D), (1, Sk, 2, D), (1, Sk, 2, D), (1, Sq, 2, D)])
+    q, k = (q * 4).to(torch.bfloat16), (k * 4).to(torch.bfloat16)
+    rep = mfa.MaskRep.tiles(mfa.compact_dense_mask(to_dev(m)))
+    scale = D ** -0.5
+    out, lse, got = _run(q, k, v, do, rep, scale, "bshd")
+    rdq, rdk, rdv, ro, rl, _ = A.attention_bwd(q, k, v, do, m[None, None], scale)
+    compare_attention(f64(out), f64(lse), ro, rl, F32_OUT_TOL)
+    _check(got, (rdq, rdk, rdv), "peaked")
+
+
 def test_f32_tiles_bhsd_and_none():
     note("f32 bwd bhsd tiles + none")
     B, H, N, D = 1, 2, 200, 64

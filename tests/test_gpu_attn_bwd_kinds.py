@@ -12,7 +12,8 @@ import masked_flash_attention_amd as mfa
 from oracle import attention as A
 from oracle import masks as M
 import workloads as W
-from tests.gpu_util import BF16_OUT_TOL, DEV, f64, grad_tolerance, nan_like, note, tile_rows, to_dev
+from tests.gpu_util import (BF16_OUT_TOL, DEV, f64, grad_tolerance, grad_tolerance_terms, nan_like, note,
+                            tile_rows, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -58,6 +59,31 @@ def test_tiles_backward(D, kind, gqa):
     got = _run(q, k, v, do, rep, scale, "bshd")
     ref = A.attention_bwd(q, k, v, do, mask[None, None], scale)[:3]
     _check_grads(got, ref, tag=f"tiles {kind}")
+
+
+@pytest.mark.parametrize("kind", ["causal", "random"])
+def test_tiles_backward_peaked_scores(kind):
+    """q and k scaled by 4 (scores with a spread ~16x the unit case, nearly
+    one-hot rows): the recomputed P = exp2(S c - LSE log2 e) subtracts two
+    large numbers, and dS concentrates on the few keys near each row's max."""
+    note(f"tiles bwd peaked {kind}")
+    Sq, Sk, D = 300, 333, 128
+    mask = _tiles_case(kind, Sq, Sk, seed=77)
+    q, k, v, do = W.tensors(91, [(1, Sq, 2, D), (1, Sk, 2, D), (1, Sk, 2, D), (1, Sq, 2, D)])
+    q, k = (q * 4).to(torch.bfloat16), (k * 4).to(torch.bfloat16)
+    rep = mfa.MaskRep.tiles(mfa.compact_dense_mask(to_dev(mask)))
+    scale = D ** -0.5
+    got = _run(q, k, v, do, rep, scale, "bshd")
+    r = A.attention_bwd(q, k, v, do, mask[None, None], scale, term_sums=True)
+    # nearly one-hot rows: |O| ~ |v|, so Delta = dO.O from the stored bf16 O
+    # and dS from bf16 P carry the first-order storage error that the
+    # oracle's term sums bound (as for a strong positional bias)
+    for name, g, ref, ts in zip(("dq", "dk", "dv"), got, r[:3], r[6]):
+        g = f64(g)
+        assert np.all(np.isfinite(g)), f"peaked {kind} {name}: non-finite gradient"
+        excess = np.abs(g - ref) - grad_tolerance_terms(ref, ts)
+        i = np.unravel_index(int(np.argmax(excess)), excess.shape)
+        assert excess[i] <= 0, f"peaked {kind} {name}: |{g[i]:.5f} - {ref[i]:.5f}| over the bound at {i}"
 
 
 def test_tiles_backward_bhsd_layout_and_determinism():
